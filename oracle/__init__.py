@@ -1,0 +1,240 @@
+"""CPU oracle for the SAD hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never calls it, and it never calls the product path.
+
+The arithmetic lives in ``sadref.c`` (plain C, built with gcc, no FMA
+contraction).  This module only compiles it and marshals numpy arrays; see the
+C file for the definitions and the paper sections they follow.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+HERE = Path(__file__).resolve().parent
+SRC = HERE / "sadref.c"
+BUILD_DIR = HERE / "_build"
+LIB = BUILD_DIR / "libsadref.so"
+
+K = 8
+NONE = 0xFFFFFFFF
+REC = 12
+
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+          "-fno-finite-math-only", "-fopenmp", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> Path:
+    """Compile the oracle with gcc into ``oracle/_build/libsadref.so``."""
+    if LIB.exists() and not force and LIB.stat().st_mtime >= SRC.stat().st_mtime:
+        return LIB
+    BUILD_DIR.mkdir(exist_ok=True)
+    tmp = LIB.with_suffix(".so.tmp%d" % os.getpid())
+    subprocess.run(["gcc", *CFLAGS, str(SRC), "-o", str(tmp), "-lm"], check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        build(force=False)
+        L = C.CDLL(str(LIB))
+        f32p, u32p, f64p, i64p = (C.POINTER(C.c_float), C.POINTER(C.c_uint32),
+                                  C.POINTER(C.c_double), C.POINTER(C.c_int64))
+        i32, u32, u64, i64 = C.c_int32, C.c_uint32, C.c_uint64, C.c_int64
+        L.sadref_prepare_sites.argtypes = [f32p, i32, f32p]
+        L.sadref_brute_topk.argtypes = [f32p, i32, i32, i32, u32p]
+        L.sadref_propagate.argtypes = [f32p, i32, i32, i32, u32p, u32p, i32, u64, u32, i32]
+        L.sadref_propagate_pixels.argtypes = [f32p, i32, i32, i32, u32p, i32, u64, u32, i32, i64p, i64, u32p]
+        L.sadref_render_fwd.argtypes = [f32p, i32, i32, i32, u32p, f64p]
+        L.sadref_render_bwd.argtypes = [f32p, i32, i32, i32, u32p, f32p, f64p, f64p, f64p, f64p]
+        L.sadref_query_points.argtypes = [f32p, i32, i32, i32, u32p, f32p, i64, f64p]
+        L.sadref_adam_step.argtypes = [f32p, f32p, f32p, f32p, i32, i32, i32, f32p,
+                                       C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, f32p]
+        L.sadref_score.argtypes = [f32p, i32, u32, C.c_float, C.c_float]
+        L.sadref_score.restype = C.c_float
+        for name in ("sadref_exp_f32", "sadref_cos_f32", "sadref_sin_f32"):
+            getattr(L, name).argtypes = [C.c_float]
+            getattr(L, name).restype = C.c_float
+        L.sadref_splitmix64.argtypes = [u64, u64]
+        L.sadref_splitmix64.restype = u64
+        L.sadref_inject_id.argtypes = [u64, u32, u32, u32, i32]
+        L.sadref_inject_id.restype = u32
+        L.sadref_ambiguous_count.argtypes = []
+        L.sadref_ambiguous_count.restype = C.c_long
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray, ct):
+    return a.ctypes.data_as(C.POINTER(ct))
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _u32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.uint32)
+
+
+def set_threads(n: int | None) -> None:
+    """Thread count of the OpenMP loops (takes effect for the next parallel region)."""
+    if n is not None:
+        os.environ["OMP_NUM_THREADS"] = str(n)
+        try:
+            C.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+        except OSError:
+            pass
+
+
+def ambiguous_count() -> int:
+    """Number of prepared values whose float32 rounding the guard could not certify."""
+    return int(lib().sadref_ambiguous_count())
+
+
+def prepare_sites(params: np.ndarray) -> np.ndarray:
+    params = _f32(params).reshape(-1, REC)
+    out = np.empty_like(params)
+    lib().sadref_prepare_sites(_p(params, C.c_float), params.shape[0], _p(out, C.c_float))
+    return out
+
+
+def exp_f32(x: float) -> float:
+    return lib().sadref_exp_f32(x)
+
+
+def cos_f32(x: float) -> float:
+    return lib().sadref_cos_f32(x)
+
+
+def sin_f32(x: float) -> float:
+    return lib().sadref_sin_f32(x)
+
+
+def score(derived: np.ndarray, site: int, px: float, py: float) -> float:
+    derived = _f32(derived).reshape(-1, REC)
+    return lib().sadref_score(_p(derived, C.c_float), derived.shape[0], site, px, py)
+
+
+def brute_topk(derived: np.ndarray, h: int, w: int) -> np.ndarray:
+    derived = _f32(derived).reshape(-1, REC)
+    out = np.empty((h, w, K), dtype=np.uint32)
+    lib().sadref_brute_topk(_p(derived, C.c_float), derived.shape[0], h, w, _p(out, C.c_uint32))
+    return out
+
+
+def empty_map(h: int, w: int) -> np.ndarray:
+    return np.full((h, w, K), NONE, dtype=np.uint32)
+
+
+def splitmix64(seed: int, counter: int) -> int:
+    return int(lib().sadref_splitmix64(seed, counter))
+
+
+def inject_id(seed: int, pass_index: int, tile: int, j: int, n: int) -> int:
+    return int(lib().sadref_inject_id(seed, pass_index, tile, j, n))
+
+
+def propagate(derived: np.ndarray, h: int, w: int, prev: np.ndarray | None, stride: int,
+              seed: int, pass_index: int, inject: int = 64) -> np.ndarray:
+    derived = _f32(derived).reshape(-1, REC)
+    out = np.empty((h, w, K), dtype=np.uint32)
+    prev_p = None
+    if prev is not None:
+        prev = _u32(prev).reshape(h, w, K)
+        prev_p = _p(prev, C.c_uint32)
+    lib().sadref_propagate(_p(derived, C.c_float), derived.shape[0], h, w, prev_p, _p(out, C.c_uint32),
+                           stride, seed, pass_index, inject)
+    return out
+
+
+def propagate_pixels(derived: np.ndarray, h: int, w: int, prev: np.ndarray | None, stride: int,
+                     seed: int, pass_index: int, inject: int, pixels: np.ndarray) -> np.ndarray:
+    derived = _f32(derived).reshape(-1, REC)
+    pixels = np.ascontiguousarray(pixels, dtype=np.int64)
+    out = np.empty((pixels.shape[0], K), dtype=np.uint32)
+    prev_p = None
+    if prev is not None:
+        prev = _u32(prev).reshape(h, w, K)
+        prev_p = _p(prev, C.c_uint32)
+    lib().sadref_propagate_pixels(_p(derived, C.c_float), derived.shape[0], h, w, prev_p, stride, seed,
+                                  pass_index, inject, _p(pixels, C.c_int64), pixels.shape[0],
+                                  _p(out, C.c_uint32))
+    return out
+
+
+def propagate_schedule(derived: np.ndarray, h: int, w: int, prev: np.ndarray | None, strides,
+                       seed: int, first_pass: int = 0, inject: int = 64) -> np.ndarray:
+    """Successive passes, one per stride, with pass indices first_pass, first_pass+1, ..."""
+    cur = prev
+    for t, s in enumerate(strides):
+        cur = propagate(derived, h, w, cur, int(s), seed, first_pass + t, inject)
+    if cur is None:
+        cur = empty_map(h, w)
+    return cur
+
+
+def render_fwd(derived: np.ndarray, h: int, w: int, topk: np.ndarray) -> np.ndarray:
+    derived = _f32(derived).reshape(-1, REC)
+    topk = _u32(topk).reshape(h, w, K)
+    out = np.empty((h, w, 3), dtype=np.float64)
+    lib().sadref_render_fwd(_p(derived, C.c_float), derived.shape[0], h, w, _p(topk, C.c_uint32),
+                            _p(out, C.c_double))
+    return out
+
+
+def render_bwd(derived: np.ndarray, h: int, w: int, topk: np.ndarray, target: np.ndarray):
+    """Returns (grad [n][12] f64, grad_abs [n][12] f64, loss, image [h][w][3] f64)."""
+    derived = _f32(derived).reshape(-1, REC)
+    n = derived.shape[0]
+    topk = _u32(topk).reshape(h, w, K)
+    target = _f32(target).reshape(h, w, 3)
+    grad = np.zeros((n, REC), dtype=np.float64)
+    gabs = np.zeros((n, REC), dtype=np.float64)
+    loss = np.zeros(1, dtype=np.float64)
+    img = np.empty((h, w, 3), dtype=np.float64)
+    lib().sadref_render_bwd(_p(derived, C.c_float), n, h, w, _p(topk, C.c_uint32), _p(target, C.c_float),
+                            _p(grad, C.c_double), _p(gabs, C.c_double), _p(loss, C.c_double),
+                            _p(img, C.c_double))
+    return grad, gabs, float(loss[0]), img
+
+
+def query_points(derived: np.ndarray, h: int, w: int, topk: np.ndarray, xy: np.ndarray) -> np.ndarray:
+    derived = _f32(derived).reshape(-1, REC)
+    topk = _u32(topk).reshape(h, w, K)
+    xy = _f32(xy).reshape(-1, 2)
+    out = np.empty((xy.shape[0], 3), dtype=np.float64)
+    lib().sadref_query_points(_p(derived, C.c_float), derived.shape[0], h, w, _p(topk, C.c_uint32),
+                              _p(xy, C.c_float), xy.shape[0], _p(out, C.c_double))
+    return out
+
+
+def adam_step(params, grad, m, v, h: int, w: int, lr, beta1: float, beta2: float, eps: float,
+              bc1: float, bc2: float):
+    """In-place Adam on copies; returns (params, grad, m, v, derived)."""
+    params = _f32(params).reshape(-1, REC).copy()
+    grad = _f32(grad).reshape(-1, REC).copy()
+    m = _f32(m).reshape(-1, REC).copy()
+    v = _f32(v).reshape(-1, REC).copy()
+    lr = _f32(lr).reshape(5)
+    derived = np.empty_like(params)
+    lib().sadref_adam_step(_p(params, C.c_float), _p(grad, C.c_float), _p(m, C.c_float), _p(v, C.c_float),
+                           params.shape[0], h, w, _p(lr, C.c_float), beta1, beta2, eps, bc1, bc2,
+                           _p(derived, C.c_float))
+    return params, grad, m, v, derived
+
+
+def bias_corrections(beta1: float, beta2: float, t: int) -> tuple[float, float]:
+    """Adam's 1 - beta^t in float32, computed on the host as the step contract requires."""
+    return float(np.float32(1.0 - float(beta1) ** t)), float(np.float32(1.0 - float(beta2) ** t))

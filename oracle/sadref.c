@@ -1,0 +1,449 @@
+/*
+ * sadref.c -- plain CPU oracle for the Soft Anisotropic Diagrams (SAD) hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call this code:
+ * only the tests, the smoke check and the benchmark's CPU-baseline leg load it.
+ * It shares no code, header or constant table with the HIP library; the two
+ * meet only at the documented data formats (site records, top-K map).
+ *
+ * Source: "Soft Anisotropic Diagrams for Differentiable Image Representation"
+ * (Iinbor, Dou, Matusik; arXiv 2604.21984), paper body as published on
+ * paperpeel.com.  Each function names the section it follows.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math (no FMA
+ * contraction, IEEE round-to-nearest, no flush-to-zero), optional -fopenmp.
+ *
+ * Precision.  The paper keeps training site parameters in float32
+ * (Appendix B.2 "Site buffer").  The ranking score that decides the top-K
+ * lists is therefore evaluated in float32, one rounding per operation in a
+ * fixed order (score_at below).  Rendering, gradients and the loss are
+ * evaluated in float64 from those float32 scores and parameters.  Adam works
+ * on the float32 parameter buffer one float32 operation at a time.
+ *
+ * Layouts (row-major, little-endian):
+ *   params  [n][12] f32: x, y, log_tau, r, c_r, c_g, c_b, theta, log_s1, log_s2, 0, 0
+ *   derived [n][12] f32: x, y, tau, r, cos(theta), sin(theta), exp(-log_s1),
+ *                        exp(-log_s2), c_r, c_g, c_b, 0
+ *   topk    [h][w][8] u32: site ids, best first, 0xffffffff padding at the end
+ *   images  [h][w][3]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define K 8
+#define NONE 0xffffffffu
+#define REC 12
+
+/* ------------------------------------------------------------------------ */
+/* Site preparation: tau = exp(log tau) (Sec. 4.1), the rotation and the
+ * inverse scales of the anisotropic metric (Sec. 4.1, eq. for G_i).
+ * Each derived value is the float32 nearest to the exact real value
+ * (round-to-nearest-even of the mathematical function).  The value is
+ * computed in x87 extended precision and rounded once; a guard checks that the
+ * extended result is far enough from a float32 rounding boundary that its few
+ * ulps of library error cannot change the rounded float. */
+
+static long sadref_ambiguous_roundings = 0;
+
+static float round_ld_to_f32(long double v)
+{
+    if (!isfinite(v) || v == 0.0L) return (float)v;
+    long double lo = v, hi = v;
+    for (int i = 0; i < 4; ++i) {
+        lo = nextafterl(lo, -INFINITY);
+        hi = nextafterl(hi, INFINITY);
+    }
+    float f = (float)v;
+    if ((float)lo != f || (float)hi != f) sadref_ambiguous_roundings++;
+    return f;
+}
+
+long sadref_ambiguous_count(void) { return sadref_ambiguous_roundings; }
+
+float sadref_exp_f32(float x) { return round_ld_to_f32(expl((long double)x)); }
+float sadref_cos_f32(float x) { return round_ld_to_f32(cosl((long double)x)); }
+float sadref_sin_f32(float x) { return round_ld_to_f32(sinl((long double)x)); }
+
+/* Largest |theta| for which a site's rotation is evaluated; beyond it the
+ * prepared record marks the site inactive (x = -1). */
+#define THETA_LIMIT 1048576.0f
+
+void sadref_prepare_sites(const float *params, int32_t n, float *derived)
+{
+    for (int32_t i = 0; i < n; ++i) {
+        const float *p = params + (size_t)i * REC;
+        float *d = derived + (size_t)i * REC;
+        float theta = p[7];
+        int active = p[0] >= 0.0f && fabsf(theta) <= THETA_LIMIT;
+        d[0] = active ? p[0] : -1.0f;
+        d[1] = active ? p[1] : -1.0f;
+        d[2] = sadref_exp_f32(p[2]);
+        d[3] = p[3];
+        d[4] = active ? sadref_cos_f32(theta) : 1.0f;
+        d[5] = active ? sadref_sin_f32(theta) : 0.0f;
+        d[6] = sadref_exp_f32(-p[8]);
+        d[7] = sadref_exp_f32(-p[9]);
+        d[8] = p[4];
+        d[9] = p[5];
+        d[10] = p[6];
+        d[11] = 0.0f;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* The per-site logit (Sec. 4.2): l = -tau * (||x - p||_G - r), with
+ * G = R(theta) diag(s1^-2, s2^-2) R(theta)^T, so that
+ * ||x - p||_G = sqrt(a^2 + b^2), a = ((x-p).u) / s1, b = ((x-p).v) / s2,
+ * u = (cos, sin), v = (-sin, cos).  float32, one rounding per operation, in
+ * exactly this order. */
+static float score_at(const float *d, float px, float py)
+{
+    float dx = px - d[0];
+    float dy = py - d[1];
+    float a = (dx * d[4] + dy * d[5]) * d[6];
+    float b = (dy * d[4] - dx * d[5]) * d[7];
+    float q = a * a + b * b;
+    float dist = sqrtf(q) - d[3];
+    return -(d[2] * dist);
+}
+
+/* A site id names a usable site when it is in range and the site is active
+ * (Appendix B.2: x < 0 marks an inactive site, skipped by every kernel). */
+static int site_usable(const float *derived, int32_t n, uint32_t id)
+{
+    return id < (uint32_t)n && derived[(size_t)id * REC] >= 0.0f;
+}
+
+float sadref_score(const float *derived, int32_t n, uint32_t id, float px, float py)
+{
+    if (!site_usable(derived, n, id)) return NAN;
+    return score_at(derived + (size_t)id * REC, px, py);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Ranking: (l1, i1) comes before (l2, i2) iff l1 > l2, or l1 == l2 and
+ * i1 < i2.  Candidates whose score is NaN are dropped. */
+typedef struct { float s; uint32_t id; } cand_t;
+
+static int cand_cmp(const void *pa, const void *pb)
+{
+    const cand_t *a = (const cand_t *)pa, *b = (const cand_t *)pb;
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+    if (a->id < b->id) return -1;
+    if (a->id > b->id) return 1;
+    return 0;
+}
+
+/* topK of a candidate multiset: sort, drop repeated ids (a repeated id has the
+ * same score, so repeats sit next to each other), keep the first K, pad. */
+static void topk_of(cand_t *c, int nc, uint32_t *out)
+{
+    qsort(c, (size_t)nc, sizeof(cand_t), cand_cmp);
+    int m = 0;
+    for (int i = 0; i < nc && m < K; ++i) {
+        if (m > 0 && out[m - 1] == c[i].id) continue;
+        out[m++] = c[i].id;
+    }
+    for (; m < K; ++m) out[m] = NONE;
+}
+
+/* Add id to the candidate array if usable and its score is a number. */
+static int add_cand(cand_t *c, int nc, const float *derived, int32_t n, uint32_t id, float px, float py)
+{
+    if (!site_usable(derived, n, id)) return nc;
+    float s = score_at(derived + (size_t)id * REC, px, py);
+    if (isnan(s)) return nc;
+    c[nc].s = s;
+    c[nc].id = id;
+    return nc + 1;
+}
+
+/* Exact top-K over every site: the quantity the propagation approximates
+ * (Sec. 4.3, "approximate K-th order diagram query"). */
+void sadref_brute_topk(const float *derived, int32_t n, int32_t h, int32_t w, uint32_t *topk)
+{
+#pragma omp parallel
+    {
+        cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int32_t j = 0; j < h; ++j) {
+            for (int32_t i = 0; i < w; ++i) {
+                float px = (float)i + 0.5f, py = (float)j + 0.5f;
+                int nc = 0;
+                for (int32_t s = 0; s < n; ++s) nc = add_cand(c, nc, derived, n, (uint32_t)s, px, py);
+                topk_of(c, nc, topk + ((size_t)j * w + i) * K);
+            }
+        }
+        free(c);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stochastic injection (Sec. 4.3, global probe set G_t): J site ids per pass
+ * per 8x8 pixel tile, the same ids for every pixel of the tile.  The ids come
+ * from SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) used as a
+ * counter-based generator: the output for counter c is the SplitMix64 mix of
+ * seed + (c + 1) * golden-gamma, with c = pass << 32 | tile << 6 | j.  A
+ * 64-bit output z maps to [0, n) by Lemire's multiply-shift on its high word. */
+#define TILE 8
+
+uint64_t sadref_splitmix64(uint64_t seed, uint64_t counter)
+{
+    uint64_t z = seed + (counter + 1u) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+uint32_t sadref_inject_id(uint64_t seed, uint32_t pass_index, uint32_t tile, uint32_t j, int32_t n)
+{
+    uint64_t ctr = ((uint64_t)pass_index << 32) | ((uint64_t)tile << 6) | (uint64_t)j;
+    uint64_t z = sadref_splitmix64(seed, ctr);
+    return (uint32_t)(((z >> 32) * (uint64_t)(uint32_t)n) >> 32);
+}
+
+/* One propagation pass for one pixel (Sec. 4.3, eq. for C~_t and Figure 5):
+ * candidates = previous list of the pixel (temporal reuse) + previous lists of
+ * the 4 pixels at +-stride along each axis that lie inside the image (spatial
+ * propagation, read from the previous map only) + the tile's injected ids
+ * (global probe); the new list is the top-K of that set under the logit. */
+static void propagate_pixel(const float *derived, int32_t n, int32_t h, int32_t w,
+                            const uint32_t *prev, int32_t i, int32_t j, int32_t stride,
+                            uint64_t seed, uint32_t pass_index, int32_t inject,
+                            cand_t *c, uint32_t *out)
+{
+    float px = (float)i + 0.5f, py = (float)j + 0.5f;
+    int nc = 0;
+    if (prev) {
+        const int32_t nbr[5][2] = {{0, 0}, {stride, 0}, {-stride, 0}, {0, stride}, {0, -stride}};
+        for (int q = 0; q < 5; ++q) {
+            int32_t ii = i + nbr[q][0], jj = j + nbr[q][1];
+            if (ii < 0 || ii >= w || jj < 0 || jj >= h) continue;
+            const uint32_t *l = prev + ((size_t)jj * w + ii) * K;
+            for (int k = 0; k < K; ++k) nc = add_cand(c, nc, derived, n, l[k], px, py);
+        }
+    }
+    int32_t tiles_x = (w + TILE - 1) / TILE;
+    uint32_t tile = (uint32_t)((j / TILE) * tiles_x + (i / TILE));
+    for (int32_t q = 0; q < inject; ++q)
+        nc = add_cand(c, nc, derived, n, sadref_inject_id(seed, pass_index, tile, (uint32_t)q, n), px, py);
+    topk_of(c, nc, out);
+}
+
+void sadref_propagate(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *prev,
+                      uint32_t *next, int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject)
+{
+#pragma omp parallel
+    {
+        cand_t c[5 * K + 64];
+#pragma omp for schedule(static)
+        for (int32_t j = 0; j < h; ++j)
+            for (int32_t i = 0; i < w; ++i)
+                propagate_pixel(derived, n, h, w, prev, i, j, stride, seed, pass_index, inject, c,
+                                next + ((size_t)j * w + i) * K);
+    }
+}
+
+/* The same pass evaluated only at the listed pixels (index j*w + i). */
+void sadref_propagate_pixels(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *prev,
+                             int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject,
+                             const int64_t *pix, int64_t npix, uint32_t *out)
+{
+    cand_t c[5 * K + 64];
+    for (int64_t t = 0; t < npix; ++t)
+        propagate_pixel(derived, n, h, w, prev, (int32_t)(pix[t] % w), (int32_t)(pix[t] / w), stride,
+                        seed, pass_index, inject, c, out + (size_t)t * K);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Soft additively weighted rendering (Sec. 4.2): softmax of the logits over
+ * the pixel's list, then the weighted colour blend.  Entries that name no
+ * usable site or whose float32 logit is not finite are skipped; an empty list
+ * renders black.  The max logit is subtracted before exponentiation
+ * (Appendix B.4). */
+typedef struct {
+    int n;
+    uint32_t id[K];
+    float l[K];       /* float32 logit, as ranked */
+    double w[K];      /* softmax weight */
+    double c[3];      /* blended colour */
+} pix_eval_t;
+
+static void eval_point(const float *derived, int32_t n, const uint32_t *list, float px, float py, pix_eval_t *e)
+{
+    e->n = 0;
+    for (int k = 0; k < K; ++k) {
+        uint32_t id = list[k];
+        if (!site_usable(derived, n, id)) continue;
+        float l = score_at(derived + (size_t)id * REC, px, py);
+        if (!isfinite(l)) continue;
+        e->id[e->n] = id;
+        e->l[e->n] = l;
+        e->n++;
+    }
+    e->c[0] = e->c[1] = e->c[2] = 0.0;
+    if (e->n == 0) return;
+    double m = -INFINITY;
+    for (int k = 0; k < e->n; ++k) m = fmax(m, (double)e->l[k]);
+    double z = 0.0;
+    for (int k = 0; k < e->n; ++k) {
+        e->w[k] = exp((double)e->l[k] - m);
+        z += e->w[k];
+    }
+    for (int k = 0; k < e->n; ++k) {
+        e->w[k] /= z;
+        const float *d = derived + (size_t)e->id[k] * REC;
+        for (int ch = 0; ch < 3; ++ch) e->c[ch] += e->w[k] * (double)d[8 + ch];
+    }
+}
+
+void sadref_render_fwd(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk, double *image)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t j = 0; j < h; ++j) {
+        for (int32_t i = 0; i < w; ++i) {
+            pix_eval_t e;
+            size_t p = (size_t)j * w + i;
+            eval_point(derived, n, topk + p * K, (float)i + 0.5f, (float)j + 0.5f, &e);
+            for (int ch = 0; ch < 3; ++ch) image[p * 3 + ch] = e.c[ch];
+        }
+    }
+}
+
+/* Random access (Sec. 6.6, render-only from cached lists): a point (qx, qy)
+ * uses the list of the pixel that contains it, clamped into the image, and
+ * the logits are evaluated at the point itself.  Non-finite points give NaN. */
+void sadref_query_points(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
+                         const float *xy, int64_t m, double *rgb)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < m; ++t) {
+        float qx = xy[2 * t], qy = xy[2 * t + 1];
+        if (!isfinite(qx) || !isfinite(qy)) {
+            rgb[3 * t] = rgb[3 * t + 1] = rgb[3 * t + 2] = NAN;
+            continue;
+        }
+        double fx = floor((double)qx), fy = floor((double)qy);
+        int32_t i = fx < 0 ? 0 : (fx > (double)(w - 1) ? w - 1 : (int32_t)fx);
+        int32_t j = fy < 0 ? 0 : (fy > (double)(h - 1) ? h - 1 : (int32_t)fy);
+        pix_eval_t e;
+        eval_point(derived, n, topk + ((size_t)j * w + i) * K, qx, qy, &e);
+        for (int ch = 0; ch < 3; ++ch) rgb[3 * t + ch] = e.c[ch];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Loss and hand-derived gradients (Sec. 6.1 loss, Appendix B.4).
+ * L = sum_x sum_ch (c(x) - I(x))^2 / P, P = H*W (the per-pixel normalisation
+ * of Appendix B.4).  With g = dL/dc(x) = 2 (c - I) / P and, for list entry k
+ * (site i), delta_k = dL/dl_k = w_k (g.c_i - g.c):
+ *   colour  += w_k g
+ *   log tau += delta_k l_k        (dl/dlog tau = l)
+ *   r       += tau delta_k        (dl/dr = tau)
+ *   with kappa = -tau delta_k / (2 sqrt q) when q > 0:
+ *   x       += kappa * (-2) (a is1 cos - b is2 sin)
+ *   y       += kappa * (-2) (a is1 sin + b is2 cos)
+ *   theta   += kappa * 2 a_r b_r (is1^2 - is2^2)
+ *   log s1  += kappa * (-2 a^2),  log s2 += kappa * (-2 b^2)
+ * where a_r = dx cos + dy sin, b_r = dy cos - dx sin, a = a_r is1, b = b_r is2.
+ * At q == 0 (pixel centre on the site) the position and metric terms are 0.
+ * Everything is float64; sums run in pixel order then list order.
+ * grad and grad_abs ([n][12], parameter-record layout) are accumulated into;
+ * grad_abs receives the sum of |term| (the scale of each sum). */
+void sadref_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
+                       const float *target, double *grad, double *grad_abs, double *loss, double *image)
+{
+    const double inv_p = 1.0 / ((double)h * (double)w);
+    double lsum = 0.0;
+    for (int32_t j = 0; j < h; ++j) {
+        for (int32_t i = 0; i < w; ++i) {
+            size_t p = (size_t)j * w + i;
+            float px = (float)i + 0.5f, py = (float)j + 0.5f;
+            pix_eval_t e;
+            eval_point(derived, n, topk + p * K, px, py, &e);
+            double g[3];
+            for (int ch = 0; ch < 3; ++ch) {
+                double r = e.c[ch] - (double)target[p * 3 + ch];
+                lsum += r * r;
+                g[ch] = 2.0 * r * inv_p;
+                if (image) image[p * 3 + ch] = e.c[ch];
+            }
+            double gc = g[0] * e.c[0] + g[1] * e.c[1] + g[2] * e.c[2];
+            for (int k = 0; k < e.n; ++k) {
+                const float *d = derived + (size_t)e.id[k] * REC;
+                double tau = d[2], cs = d[4], sn = d[5], is1 = d[6], is2 = d[7];
+                double gci = g[0] * d[8] + g[1] * d[9] + g[2] * d[10];
+                double delta = e.w[k] * (gci - gc);
+                double t[12] = {0};
+                t[4] = e.w[k] * g[0];
+                t[5] = e.w[k] * g[1];
+                t[6] = e.w[k] * g[2];
+                t[2] = delta * (double)e.l[k];
+                t[3] = tau * delta;
+                double dx = (double)px - (double)d[0], dy = (double)py - (double)d[1];
+                double ar = dx * cs + dy * sn, br = dy * cs - dx * sn;
+                double a = ar * is1, b = br * is2;
+                double q = a * a + b * b;
+                if (q > 0.0) {
+                    double kappa = -tau * delta / (2.0 * sqrt(q));
+                    t[0] = kappa * -2.0 * (a * is1 * cs - b * is2 * sn);
+                    t[1] = kappa * -2.0 * (a * is1 * sn + b * is2 * cs);
+                    t[7] = kappa * 2.0 * ar * br * (is1 * is1 - is2 * is2);
+                    t[8] = kappa * -2.0 * a * a;
+                    t[9] = kappa * -2.0 * b * b;
+                }
+                double *G = grad + (size_t)e.id[k] * REC;
+                double *A = grad_abs ? grad_abs + (size_t)e.id[k] * REC : NULL;
+                for (int q2 = 0; q2 < 10; ++q2) {
+                    G[q2] += t[q2];
+                    if (A) A[q2] += fabs(t[q2]);
+                }
+            }
+        }
+    }
+    if (loss) *loss += lsum * inv_p;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Adam (Kingma and Ba, ICLR 2015) on the float32 site buffer (Sec. 5:
+ * per-parameter base learning rates, fixed betas and epsilon), then the
+ * projection of Sec. 4.1 (positions clamped to the image).  lr[5] holds the
+ * rates of the groups (x, y), log tau, r, colour, (theta, log s1, log s2).
+ * One float32 rounding per operation, in this order:
+ *   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g)
+ *   p = p - lr * ((m / bc1) / (sqrt(v / bc2) + eps))
+ * bc1 = 1 - b1^t and bc2 = 1 - b2^t come from the caller.  Inactive sites
+ * (x < 0) are left as they are.  The gradient record is zeroed and the
+ * derived record rewritten (as sadref_prepare_sites) for every site. */
+static const int lr_group[10] = {0, 0, 1, 2, 3, 3, 3, 4, 4, 4};
+
+void sadref_adam_step(float *params, float *grad, float *m, float *v, int32_t n, int32_t h, int32_t w,
+                      const float *lr, float beta1, float beta2, float eps, float bc1, float bc2, float *derived)
+{
+    float omb1 = 1.0f - beta1, omb2 = 1.0f - beta2;
+    for (int32_t i = 0; i < n; ++i) {
+        float *p = params + (size_t)i * REC;
+        float *g = grad + (size_t)i * REC;
+        float *mm = m + (size_t)i * REC;
+        float *vv = v + (size_t)i * REC;
+        if (p[0] >= 0.0f) {
+            for (int k = 0; k < 10; ++k) {
+                float gk = g[k];
+                mm[k] = beta1 * mm[k] + omb1 * gk;
+                vv[k] = beta2 * vv[k] + omb2 * (gk * gk);
+                float mhat = mm[k] / bc1;
+                float vhat = vv[k] / bc2;
+                float step = mhat / (sqrtf(vhat) + eps);
+                p[k] = p[k] - lr[lr_group[k]] * step;
+            }
+            p[0] = fminf(fmaxf(p[0], 0.0f), (float)w);
+            p[1] = fminf(fmaxf(p[1], 0.0f), (float)h);
+        }
+        for (int k = 0; k < REC; ++k) g[k] = 0.0f;
+        if (derived) sadref_prepare_sites(p, 1, derived + (size_t)i * REC);
+    }
+}

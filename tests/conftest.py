@@ -1,0 +1,25 @@
+"""Shared pytest configuration.
+
+Tests marked ``gpu`` need an MI355X (gfx950) and the built HIP library; every
+other test runs on the CPU.  The CPU oracle is built on first use.
+"""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD Instinct GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session")
+def ref():
+    import oracle
+
+    oracle.build(force=False)
+    return oracle
