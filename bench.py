@@ -1,0 +1,174 @@
+"""Throughput of the SAD hot path on one MI355X.
+
+Workload (default): 768x512 RGB float32 target, 50,000 sites, K = 8.  One
+step = 4 top-K propagation passes (strides 8, 4, 2, 1, 64 injected sites per
+8x8 tile) + forward render + backward with the loss, on a map warmed by 16
+passes of the jump-flood schedule (untimed).  Metric: Mpixel-iters/s = H*W per
+step / step time.  All inputs are synthetic (synth.C2) and already resident in
+GPU memory when the timed region starts.
+
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded
+around every launch inside the timed region, on the stream the kernels run on
+(torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(h: int, w: int, n: int, n_pass: int) -> dict:
+    """Bytes the method must move (not counting re-reads served by caches).
+    propagate: read + write one 32-byte list per pixel per pass.
+    backward:  read list (32 B) + target (12 B) per pixel, read the 48-byte
+               prepared record and read-modify-write the 40-byte gradient
+               record (80 B) per site."""
+    p = h * w
+    prop = 64 * p
+    bwd = p * (32 + 12) + n * (48 + 80)
+    step = n_pass * 64 * p + 12 * p + n * 128  # fused-step count: the last pass feeds the backward directly
+    return {"propagate": prop, "render_bwd": bwd, "step": step}
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """The oracle as it stands, timed on the host cores on whole C2 steps
+    (4 passes + backward over the full image) until ~budget_s seconds."""
+    import numpy as np
+
+    import oracle as ref
+    import synth
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    ref.set_threads(threads)
+    p = wl.make_sites()
+    tgt = wl.make_target()
+    d = ref.prepare_sites(p)
+    warm = synth.jfa_strides(wl.h, wl.w, wl.warm_passes)
+    cur = ref.propagate_schedule(d, wl.h, wl.w, None, warm, wl.inject_seed, 0, wl.inject)
+    pi = len(warm)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        cur = ref.propagate_schedule(d, wl.h, wl.w, cur, wl.strides, wl.inject_seed, pi, wl.inject)
+        pi += len(wl.strides)
+        ref.render_bwd(d, wl.h, wl.w, cur, tgt)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    value = wl.h * wl.w * steps / el / 1e6
+    return {"value": round(value, 4), "unit": "Mpixel-iters/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} full {wl.w}x{wl.h} steps (4 passes + forward/backward), {el:.1f} s, "
+                      f"{threads} OpenMP threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the SAD hot path here has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from voronoi_rendering_amd import ops
+    from voronoi_rendering_amd.pipeline import SadField
+
+    wl = synth.C2
+    dev = torch.device("cuda", 0)
+    params = torch.from_numpy(wl.make_sites()).to(dev)
+    target = torch.from_numpy(wl.make_target()).to(dev)
+    f = SadField(params, wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+    f.warm(wl.warm_passes)
+    torch.cuda.synchronize()
+
+    strides = list(wl.strides)
+    stream = torch.cuda.current_stream(dev)
+    ev = []  # (kind, start, end)
+
+    def step(record: bool):
+        for s in strides:
+            if record:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            f.propagate([s])
+            if record:
+                b.record(stream)
+                ev.append(("propagate", a, b))
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+        f.forward_backward(target)
+        if record:
+            b.record(stream)
+            ev.append(("render_bwd", a, b))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per = {}
+    for kind, a, b in ev:
+        per.setdefault(kind, []).append(a.elapsed_time(b) * 1e-3)
+    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    ms_per_step = elapsed / args.steps * 1e3
+    pix = wl.h * wl.w
+    value = pix / (elapsed / args.steps) / 1e6
+    ab = algorithmic_bytes(wl.h, wl.w, wl.n, len(strides))
+    total = {k: avg[k] * len(per[k]) / args.steps for k in avg}
+    dom = max(total, key=total.get)
+    achieved = ab[dom] / avg[dom] / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "kernel_us": round(avg[dom] * 1e6, 3),
+                "bytes_per_launch": ab[dom]}
+    out = {
+        "metric": "Mpixel-iters/s (propagate+fwd+bwd), 768x512 @ 50k sites; % HBM roofline",
+        "value": round(value, 2),
+        "unit": "Mpixel-iters/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "C2: 768x512 RGB f32, 50,000 sites, K=8, strides 8,4,2,1, 64 injected per 8x8 "
+                               "tile, forward+backward with loss",
+                   "pixels": pix, "sites": wl.n, "passes_per_step": len(strides), "parallelism": "single GPU"},
+        "step_frac_of_hbm_roofline": round(ab["step"] / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_us": {k: round(v * 1e6, 3) for k, v in avg.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

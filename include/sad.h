@@ -1,0 +1,199 @@
+/*
+ * sad.h -- C ABI of libsad.so, the MI355X (gfx950) hot path of
+ * Soft Anisotropic Diagrams (SAD): per-pixel top-K site lists maintained by
+ * jump-flood-style propagation with stochastic injection, and the soft
+ * anisotropic additively weighted (Apollonius) softmax render, its backward
+ * pass and the Adam update of the sites.
+ *
+ * Paper: "Soft Anisotropic Diagrams for Differentiable Image Representation"
+ * (Iinbor, Dou, Matusik; arXiv 2604.21984).  Section references below are to
+ * that paper.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All array pointers are DEVICE pointers owned by the caller; the library
+ *   allocates nothing and keeps no state between calls.  Host pointers are
+ *   marked as such.
+ * - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *   legacy default stream) and returns at once.  Kernel faults surface at the
+ *   caller's next synchronisation, as usual in HIP.
+ * - Return value: SAD_OK, or a negative status.  Arguments are checked before
+ *   anything is enqueued, so an error status means nothing ran.
+ *     SAD_EINVAL       negative size, NULL pointer where data is needed,
+ *                      misaligned pointer (arrays: 16 bytes), size limits
+ *                      exceeded, aliasing that the call forbids
+ *     SAD_EUNSUPPORTED a parameter outside what this build implements
+ *                      (inject_per_tile > 64)
+ *     SAD_EHIP         the HIP runtime refused the launch
+ *   sad_status_string() names a status.
+ * - Zero sizes are valid and enqueue nothing (except where an output must be
+ *   written, noted per call).
+ * - Limits: n <= 2^30 sites; h, w <= 2^15; M (query count) < 2^40.
+ * - Calls that overlap on one stream in the usual way are safe; calls that
+ *   write the same buffer from different streams without ordering race.
+ *
+ * Data formats (row-major, little-endian, float32 = IEEE binary32)
+ * ----------------------------------------------------------------
+ * Site parameters  params[n][12]  (Appendix B.2 "Site buffer": ten semantic
+ *   float32 values per site; here the metric is a rotation and two scales)
+ *     0 x, 1 y      position in pixels; x < 0 marks an inactive site
+ *     2 log_tau     log temperature (Sec. 4.1)
+ *     3 r           additive radius in units of the anisotropic norm
+ *     4,5,6         colour r, g, b
+ *     7 theta       rotation of the metric, radians, |theta| <= 2^20
+ *     8 log_s1, 9 log_s2   log scales (pixels) along the rotated axes
+ *     10, 11        padding (written as 0 by the library where it writes)
+ *   The metric is G = R(theta) diag(s1^-2, s2^-2) R(theta)^T (Sec. 4.1).
+ *
+ * Prepared sites  derived[n][12]  (what every pixel kernel reads)
+ *     0 x, 1 y, 2 tau, 3 r, 4 cos(theta), 5 sin(theta), 6 1/s1, 7 1/s2,
+ *     8,9,10 colour, 11 zero.
+ *   tau, cos, sin, 1/s1, 1/s2 are the float32 values nearest to the exact
+ *   exp/cos/sin of the float32 parameters (round to nearest even), so the
+ *   record is a pure function of params.  A site whose params x < 0 (or is
+ *   NaN) or whose |theta| > 2^20 (or is NaN) gets x = y = -1, cos = 1, sin = 0
+ *   and is skipped by every kernel.
+ *
+ * Top-K map  topk[h][w][8] uint32 (Sec. 4.6, Appendix B.2 "Top-K candidate
+ *   list": K = 8 site ids per pixel, empty slots 0xffffffff).  Each list holds
+ *   distinct ids, best first, empty slots last.
+ *
+ * Logit of site i at point (px, py) (Sec. 4.2, l_i = -tau_i d_i):
+ *   dx = px - x; dy = py - y;
+ *   a = (dx*cos + dy*sin) * (1/s1);  b = (dy*cos - dx*sin) * (1/s2);
+ *   q = a*a + b*b;  l = -(tau * (sqrt(q) - r))
+ *   float32, one IEEE rounding per operation in exactly this order, no fused
+ *   multiply-add, correctly rounded sqrt, subnormals kept.  Pixel (i, j) is
+ *   evaluated at its centre (i + 0.5, j + 0.5).
+ * Ranking: entry (l1, id1) precedes (l2, id2) iff l1 > l2, or l1 == l2 and
+ *   id1 < id2 (-0 == +0).  Candidates with a NaN logit are dropped.
+ */
+#ifndef SAD_H
+#define SAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAD_ABI_VERSION 1
+#define SAD_K 8
+#define SAD_SITE_STRIDE 12
+#define SAD_EMPTY 0xffffffffu
+#define SAD_TILE 8
+#define SAD_MAX_INJECT 64
+
+#define SAD_OK 0
+#define SAD_EINVAL (-1)
+#define SAD_EUNSUPPORTED (-2)
+#define SAD_EHIP (-3)
+
+/* Version of this interface (SAD_ABI_VERSION). */
+int sad_abi_version(void);
+
+/* Static, NUL-terminated name of a status code; never NULL. */
+const char *sad_status_string(int status);
+
+/*
+ * Prepare the per-site records the pixel kernels read (the "pack" step of
+ * Appendix B.2 / Table B13, and the exp(log tau) of Sec. 4.1).
+ *   params   [n][12] float32, read
+ *   derived  [n][12] float32, written (format above); must not overlap params
+ */
+int sad_prepare_sites(const float *params, int32_t n, float *derived, void *stream);
+
+/*
+ * One top-K propagation pass (Sec. 4.3: C~_t(x) = C_{t-1}(x) u P_t(x) u G_t(x),
+ * C_t(x) = topK of C~_t(x) under the logit; Figure 5).
+ * For every pixel x the candidate set is
+ *   - the ids of topk_prev at x (temporal reuse),
+ *   - the ids of topk_prev at x +- (stride, 0) and x +- (0, stride) that lie
+ *     inside the image (spatial propagation; only the previous map is read),
+ *   - the global probe: inject_per_tile ids drawn for x's 8x8 tile, shared by
+ *     all pixels of the tile,
+ * of which ids >= n and inactive sites are dropped; topk_next at x receives
+ * the first 8 distinct ids of that set in ranking order, padded with
+ * 0xffffffff.  The result does not depend on the order candidates are visited.
+ * Tile of pixel (i, j): (j / 8) * ceil(w / 8) + i / 8.
+ * Probe id j of tile T in pass t: z = SplitMix64 output for counter
+ *   c = t << 32 | T << 6 | j, i.e. z = mix(seed + (c + 1) * 0x9E3779B97F4A7C15)
+ *   with SplitMix64's finaliser mix; id = ((z >> 32) * n) >> 32.
+ *   derived     [n][12] prepared sites
+ *   topk_prev   [h][w][8], or NULL for an all-empty previous map
+ *   topk_next   [h][w][8], written; must not overlap topk_prev
+ *   stride      jump step, >= 1 (Sec. 4.3 schedule B/2, ..., 1, then 1)
+ *   seed        injection seed; pass_index: the pass counter t
+ *   inject_per_tile  0..64 probe ids per tile per pass
+ * Limit: ceil(h/8) * ceil(w/8) <= 2^26 tiles.
+ */
+int sad_propagate_topk(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk_prev,
+                       uint32_t *topk_next, int32_t stride, uint64_t seed, uint32_t pass_index,
+                       int32_t inject_per_tile, void *stream);
+
+/*
+ * Soft additively weighted render (Sec. 4.2): per pixel, the softmax of the
+ * logits of the listed sites, w_k = exp(l_k - m) / sum exp(l_j - m) with m the
+ * largest logit (Appendix B.4), and the blend c = sum w_k c_k.  List entries
+ * that name no usable site, or whose logit is not finite, are skipped; an
+ * empty list renders 0.
+ *   image  [h][w][3] float32, written
+ */
+int sad_render_fwd(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk, float *image,
+                   void *stream);
+
+/*
+ * Loss and hand-derived gradients (Sec. 6.1 loss; Appendix B.4).
+ * L = sum over pixels and channels of (c - target)^2 / (h*w).
+ * With g = 2 (c - target) / (h*w) and delta_k = w_k (g.c_i - g.c) for entry k
+ * (site i), the gradient record of site i receives, summed over pixels:
+ *   colour += w_k g;  log_tau += delta_k l_k;  r += tau delta_k;
+ *   and, when q > 0, with kappa = -tau delta_k / (2 sqrt q),
+ *   a_r = dx cos + dy sin, b_r = dy cos - dx sin, a = a_r/s1, b = b_r/s2:
+ *   x += -2 kappa (a cos/s1 - b sin/s2);  y += -2 kappa (a sin/s1 + b cos/s2);
+ *   theta += 2 kappa a_r b_r (1/s1^2 - 1/s2^2);
+ *   log_s1 += -2 kappa a^2;  log_s2 += -2 kappa b^2.
+ *   target  [h][w][3] float32, read
+ *   grad    [n][12] float32, ACCUMULATED into (+=) with float atomics, so the
+ *           summation order, and the last bits, vary from run to run;
+ *           entries 10, 11 are not touched
+ *   loss    NULL, or one float32 accumulated into (+= L)
+ *   image   NULL, or [h][w][3] float32 written with the rendered colours
+ */
+int sad_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
+                   const float *target, float *grad, float *loss, float *image, void *stream);
+
+/*
+ * One Adam step (Kingma & Ba) on the site parameters (Sec. 5: per-parameter
+ * base learning rates, fixed betas and epsilon), then the projection of
+ * Sec. 4.1 (positions clamped to [0, w] x [0, h]), then the prepared records
+ * rewritten.  Per parameter k < 10 of an active site (x >= 0), in float32,
+ * one rounding per operation, in this order:
+ *   m = b1*m + (1 - b1)*g;   v = b2*v + (1 - b2)*(g*g);
+ *   p = p - lr * ((m / bc1) / (sqrt(v / bc2) + eps))
+ * where (1 - b1) and (1 - b2) are float32 subtractions.  Inactive sites keep
+ * params, m and v.  Every site's gradient record is zeroed.
+ *   lr       HOST pointer to 5 float32 rates: (x, y), log_tau, r, colour,
+ *            (theta, log_s1, log_s2); read during the call
+ *   bias_corr1, bias_corr2   1 - beta1^t and 1 - beta2^t from the caller
+ *   derived  [n][12] written as by sad_prepare_sites, or NULL to skip
+ */
+int sad_adam_step(float *params, float *grad, float *m, float *v, int32_t n, int32_t h, int32_t w, const float *lr,
+                  float beta1, float beta2, float eps, float bias_corr1, float bias_corr2, float *derived,
+                  void *stream);
+
+/*
+ * Random access (Sec. 6.6, the render-only path from cached lists): point t
+ * at (qx, qy) uses the list of pixel (clamp(floor(qx), 0, w-1),
+ * clamp(floor(qy), 0, h-1)) and evaluates the logits at (qx, qy) itself, then
+ * blends as sad_render_fwd.  A non-finite coordinate gives NaN colour.
+ *   xy   [m][2] float32 (8-byte aligned), rgb [m][3] float32 written
+ */
+int sad_query_points(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk, const float *xy,
+                     int64_t m, float *rgb, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAD_H */

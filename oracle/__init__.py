@@ -195,7 +195,11 @@ def render_fwd(derived: np.ndarray, h: int, w: int, topk: np.ndarray) -> np.ndar
 
 
 def render_bwd(derived: np.ndarray, h: int, w: int, topk: np.ndarray, target: np.ndarray):
-    """Returns (grad [n][12] f64, grad_abs [n][12] f64, loss, image [h][w][3] f64)."""
+    """Returns (grad [n][12] f64, grad_mag [n][12] f64, loss, image [h][w][3] f64).
+
+    grad_mag is the running error magnitude of each gradient sum (see
+    sadref_render_bwd): it bounds how far a lower-precision evaluation of the
+    same sums can drift, cancellation included."""
     derived = _f32(derived).reshape(-1, REC)
     n = derived.shape[0]
     topk = _u32(topk).reshape(h, w, K)

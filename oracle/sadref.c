@@ -352,10 +352,16 @@ void sadref_query_points(const float *derived, int32_t n, int32_t h, int32_t w, 
  * where a_r = dx cos + dy sin, b_r = dy cos - dx sin, a = a_r is1, b = b_r is2.
  * At q == 0 (pixel centre on the site) the position and metric terms are 0.
  * Everything is float64; sums run in pixel order then list order.
- * grad and grad_abs ([n][12], parameter-record layout) are accumulated into;
- * grad_abs receives the sum of |term| (the scale of each sum). */
+ * grad and grad_mag ([n][12], parameter-record layout) are accumulated into.
+ * grad_mag receives, for every term, the same expression evaluated with the
+ * absolute value of each input and of each intermediate sum or difference
+ * (g uses |c| + |target|, delta uses |g|.|c_i| + |g|.|c|, a_r uses
+ * |dx cos| + |dy sin|, and so on).  This is the classical running bound on
+ * the rounding error of any evaluation of the expression in a lower
+ * precision: an evaluation with unit roundoff u and m operations is off by
+ * at most about m u times this magnitude, whatever cancellation occurs. */
 void sadref_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
-                       const float *target, double *grad, double *grad_abs, double *loss, double *image)
+                       const float *target, double *grad, double *grad_mag, double *loss, double *image)
 {
     const double inv_p = 1.0 / ((double)h * (double)w);
     double lsum = 0.0;
@@ -365,42 +371,57 @@ void sadref_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, co
             float px = (float)i + 0.5f, py = (float)j + 0.5f;
             pix_eval_t e;
             eval_point(derived, n, topk + p * K, px, py, &e);
-            double g[3];
+            double g[3], gm[3];
             for (int ch = 0; ch < 3; ++ch) {
                 double r = e.c[ch] - (double)target[p * 3 + ch];
                 lsum += r * r;
                 g[ch] = 2.0 * r * inv_p;
+                gm[ch] = 2.0 * (fabs(e.c[ch]) + fabs((double)target[p * 3 + ch])) * inv_p;
                 if (image) image[p * 3 + ch] = e.c[ch];
             }
             double gc = g[0] * e.c[0] + g[1] * e.c[1] + g[2] * e.c[2];
+            double gcm = gm[0] * fabs(e.c[0]) + gm[1] * fabs(e.c[1]) + gm[2] * fabs(e.c[2]);
             for (int k = 0; k < e.n; ++k) {
                 const float *d = derived + (size_t)e.id[k] * REC;
                 double tau = d[2], cs = d[4], sn = d[5], is1 = d[6], is2 = d[7];
                 double gci = g[0] * d[8] + g[1] * d[9] + g[2] * d[10];
+                double gcim = gm[0] * fabs((double)d[8]) + gm[1] * fabs((double)d[9]) + gm[2] * fabs((double)d[10]);
                 double delta = e.w[k] * (gci - gc);
-                double t[12] = {0};
-                t[4] = e.w[k] * g[0];
-                t[5] = e.w[k] * g[1];
-                t[6] = e.w[k] * g[2];
+                double deltam = e.w[k] * (gcim + gcm);
+                double t[12] = {0}, tm[12] = {0};
+                for (int ch = 0; ch < 3; ++ch) {
+                    t[4 + ch] = e.w[k] * g[ch];
+                    tm[4 + ch] = e.w[k] * gm[ch];
+                }
                 t[2] = delta * (double)e.l[k];
+                tm[2] = deltam * fabs((double)e.l[k]);
                 t[3] = tau * delta;
+                tm[3] = tau * deltam;
                 double dx = (double)px - (double)d[0], dy = (double)py - (double)d[1];
                 double ar = dx * cs + dy * sn, br = dy * cs - dx * sn;
+                double arm = fabs(dx * cs) + fabs(dy * sn), brm = fabs(dy * cs) + fabs(dx * sn);
                 double a = ar * is1, b = br * is2;
                 double q = a * a + b * b;
                 if (q > 0.0) {
                     double kappa = -tau * delta / (2.0 * sqrt(q));
+                    double kappam = tau * deltam / (2.0 * sqrt(q));
+                    double am = arm * is1, bm = brm * is2;
                     t[0] = kappa * -2.0 * (a * is1 * cs - b * is2 * sn);
                     t[1] = kappa * -2.0 * (a * is1 * sn + b * is2 * cs);
                     t[7] = kappa * 2.0 * ar * br * (is1 * is1 - is2 * is2);
                     t[8] = kappa * -2.0 * a * a;
                     t[9] = kappa * -2.0 * b * b;
+                    tm[0] = kappam * 2.0 * (am * is1 * fabs(cs) + bm * is2 * fabs(sn));
+                    tm[1] = kappam * 2.0 * (am * is1 * fabs(sn) + bm * is2 * fabs(cs));
+                    tm[7] = kappam * 2.0 * arm * brm * (is1 * is1 + is2 * is2);
+                    tm[8] = kappam * 2.0 * am * am;
+                    tm[9] = kappam * 2.0 * bm * bm;
                 }
                 double *G = grad + (size_t)e.id[k] * REC;
-                double *A = grad_abs ? grad_abs + (size_t)e.id[k] * REC : NULL;
+                double *A = grad_mag ? grad_mag + (size_t)e.id[k] * REC : NULL;
                 for (int q2 = 0; q2 < 10; ++q2) {
                     G[q2] += t[q2];
-                    if (A) A[q2] += fabs(t[q2]);
+                    if (A) A[q2] += tm[q2];
                 }
             }
         }

@@ -1,0 +1,72 @@
+"""Helpers for the GPU parity tests: moving seeded inputs to the device and
+results back, and the tolerances the comparisons use.
+
+Tolerances (floating-point outputs; integer outputs are compared bit for bit):
+- colours: |gpu - oracle| <= 1e-5 absolute.  The GPU blends in float32
+  from the same float32 logits the oracle uses; the oracle blends in float64.
+- gradients, per site and parameter: |gpu - oracle| <= 1e-4 |oracle|
+  + 1e-5 S, with S the oracle's running error magnitude of that sum (every
+  term evaluated with the absolute values of its inputs and intermediate
+  sums).  A float32 evaluation of a term with m roundings is off by at most
+  about m 2^-24 of its magnitude (m ~ 30 here), and a float32 sum in any
+  order adds at most (count - 1) 2^-24 of the summed magnitudes, typically
+  sqrt(count) 2^-24; 1e-5 = 168 x 2^-24 covers both for the sizes tested.
+- loss: relative 1e-5.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+COLOUR_ATOL = 1e-5
+GRAD_RTOL = 1e-4
+GRAD_STOL = 1e-5
+
+
+def dev() -> torch.device:
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU test run without a visible GPU")
+    return torch.device("cuda", 0)
+
+
+def to_gpu(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32)).to(dev())
+    return torch.from_numpy(a).to(dev())
+
+
+def map_to_np(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint32)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def assert_grad_close(gpu: np.ndarray, ref: np.ndarray, ref_abs: np.ndarray, what: str = "grad") -> None:
+    gpu = gpu[:, :10].astype(np.float64)
+    ref = ref[:, :10]
+    tol = GRAD_RTOL * np.abs(ref) + GRAD_STOL * ref_abs[:, :10]
+    err = np.abs(gpu - ref)
+    bad = err > tol
+    if bad.any():
+        i, k = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} entries out of tolerance; first site {i} param {k}: "
+                             f"gpu {gpu[i, k]!r} oracle {ref[i, k]!r} |term| sum {ref_abs[i, k]!r}")
+
+
+def assert_colour_close(gpu: np.ndarray, ref: np.ndarray, what: str = "colour") -> None:
+    err = np.abs(gpu.astype(np.float64) - ref)
+    nan_ok = np.isnan(gpu) & np.isnan(ref)
+    err[nan_ok] = 0
+    if not (err <= COLOUR_ATOL).all():
+        idx = np.unravel_index(np.nanargmax(err), err.shape)
+        raise AssertionError(f"{what}: max |diff| {np.nanmax(err):.3g} at {idx}")

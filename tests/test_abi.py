@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every symbol include/sad.h declares, and
+rejects invalid arguments before enqueueing any work (no GPU needed: every
+call here fails its argument checks, which run on the host)."""
+import ctypes as C
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from voronoi_rendering_amd import _native
+
+    if not _native.LIB_PATH.exists():
+        pytest.fail("libsad.so is not built (run __graft_entry__.build())")
+    return _native.lib()
+
+
+def declared_symbols():
+    text = (ROOT / "include" / "sad.h").read_text()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(sad_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ("sad_prepare_sites", "sad_propagate_topk", "sad_render_fwd", "sad_render_bwd",
+                 "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version"):
+        assert name in syms
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from voronoi_rendering_amd import _native
+
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+        assert name in _native.symbols(), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sad_abi_version() == 1
+    for st in (0, -1, -2, -3, 7):
+        assert lib.sad_status_string(st)
+
+
+EINVAL, EUNSUP = -1, -2
+P = 0x10000  # a 16-byte aligned stand-in address: never dereferenced, the checks fail first
+
+
+def test_prepare_rejects(lib):
+    assert lib.sad_prepare_sites(None, -1, None, None) == EINVAL
+    assert lib.sad_prepare_sites(None, 4, P, None) == EINVAL  # NULL params
+    assert lib.sad_prepare_sites(P + 4, 4, P + 4096, None) == EINVAL  # misaligned
+    assert lib.sad_prepare_sites(P, 4, P + 16, None) == EINVAL  # overlapping buffers
+    assert lib.sad_prepare_sites(P, (1 << 30) + 1, P + (1 << 40), None) == EINVAL
+    assert lib.sad_prepare_sites(None, 0, None, None) == 0  # empty: nothing to do
+
+
+def test_propagate_rejects(lib):
+    f = lib.sad_propagate_topk
+    ok = dict(derived=P, n=10, h=8, w=8, prev=None, nxt=P + 4096, stride=1, seed=0, pi=0, inj=64)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["derived"], a["n"], a["h"], a["w"], a["prev"], a["nxt"], a["stride"], a["seed"], a["pi"],
+                 a["inj"], None)
+
+    assert call(stride=0) == EINVAL
+    assert call(n=-1) == EINVAL
+    assert call(h=-2) == EINVAL
+    assert call(w=(1 << 15) + 1) == EINVAL
+    assert call(inj=-1) == EINVAL
+    assert call(inj=65) == EUNSUP
+    assert call(nxt=None) == EINVAL
+    assert call(derived=None) == EINVAL
+    assert call(prev=P + 4096) == EINVAL  # in place
+    assert call(prev=P + 4096 + 32 * 8) == EINVAL  # overlapping
+    assert call(nxt=P + 4100) == EINVAL  # misaligned
+    assert call(h=0, nxt=None) == 0  # empty image
+
+
+def test_render_query_adam_reject(lib):
+    assert lib.sad_render_fwd(P, 10, 8, 8, P + 4096, None, None) == EINVAL
+    assert lib.sad_render_fwd(P, 10, -8, 8, P + 4096, P + 8192, None) == EINVAL
+    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, None, None, None, None) == EINVAL
+    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P, None, None, None) == EINVAL  # grad aliases sites
+    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P + 65536, P + 2, None, None) == EINVAL
+    assert lib.sad_query_points(P, 10, 8, 8, P + 4096, P + 8192, -1, P + 65536, None) == EINVAL
+    assert lib.sad_query_points(P, 10, 8, 8, P + 4096, P + 8196, 5, P + 65536, None) == EINVAL  # xy misaligned
+    assert lib.sad_query_points(P, 10, 0, 8, P + 4096, P + 8192, 5, P + 65536, None) == EINVAL  # no lists
+    assert lib.sad_query_points(P, 10, 8, 8, P + 4096, None, 0, None, None) == 0
+    lr = (C.c_float * 5)(*([1e-3] * 5))
+    assert lib.sad_adam_step(P, P + 4096, P + 8192, P + 12288, 10, 8, 8, None, .9, .999, 1e-8, .1, .001, None,
+                             None) == EINVAL  # no rates
+    assert lib.sad_adam_step(P, P, P + 8192, P + 12288, 10, 8, 8, lr, .9, .999, 1e-8, .1, .001, None,
+                             None) == EINVAL  # params aliases grad
+    assert lib.sad_adam_step(P, P + 4096, P + 8192, P + 12288, -3, 8, 8, lr, .9, .999, 1e-8, .1, .001, None,
+                             None) == EINVAL

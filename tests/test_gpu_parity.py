@@ -1,0 +1,318 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Top-K maps, prepared records and Adam updates are compared bit for bit;
+colours, gradients and the loss within the tolerances of gpu_util.  Inputs
+come from the seeded generators in ``synth``; expected values only from the
+oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import (assert_colour_close, assert_grad_close, dev, map_to_np, say, to_gpu, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sad():
+    from voronoi_rendering_amd import ops
+
+    say("[gpu] device: " + torch.cuda.get_device_name(0))
+    return ops
+
+
+def gpu_schedule(ops, d_gpu, h, w, strides, seed, inject=64, first_pass=0, prev=None):
+    cur = prev if prev is not None else ops.empty_map(h, w, dev())
+    nxt = torch.empty_like(cur)
+    for t, s in enumerate(strides):
+        ops.propagate_topk(d_gpu, h, w, cur, nxt, stride=int(s), seed=seed, pass_index=first_pass + t, inject=inject)
+        cur, nxt = nxt, cur
+    return cur
+
+
+# ---------------------------------------------------------------- prepare
+
+def test_prepare_bit_exact(sad, ref):
+    p = np.concatenate([synth.C2.make_sites(), synth.C4.make_sites()[:100_000], synth.C3.make_sites()[:1000]])
+    extra = synth.sites(9, 16, 32, 32)
+    extra[0, 0] = -1.0  # inactive
+    extra[1, 7] = 2.0e6  # beyond the rotation range
+    extra[2, 7] = np.nan
+    extra[3, 7] = -0.0
+    extra[4, 8:10] = [90.0, -90.0]  # subnormal and infinite inverse scales
+    extra[5, 2] = 88.7  # tau near the float32 limit
+    extra[6, 7] = 1048575.9
+    extra[7, 7] = -3.0e5
+    extra[8, 0] = np.nan
+    p = np.concatenate([p, extra])
+    want = ref.prepare_sites(p)
+    got = to_np(sad.prepare_sites(to_gpu(p)))
+    assert ref.ambiguous_count() == 0
+    same = (got.view(np.uint32) == want.view(np.uint32)) | (np.isnan(got) & np.isnan(want))
+    assert same.all(), np.argwhere(~same)[:5]
+
+
+# ---------------------------------------------------------------- propagation
+
+def test_propagate_c1_every_pass(sad, ref):
+    """64x64, 256 sites, 20 passes from an empty map: every intermediate map
+    equals the oracle's, and the result is the exact top-8 at >= 99% of pixels."""
+    wl = synth.C1
+    p = wl.make_sites()
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p))
+    cur_ref, cur_gpu = None, sad.empty_map(wl.h, wl.w, dev())
+    nxt = torch.empty_like(cur_gpu)
+    for t, s in enumerate(wl.strides):
+        cur_ref = ref.propagate(d, wl.h, wl.w, cur_ref, s, wl.inject_seed, t, wl.inject)
+        sad.propagate_topk(dg, wl.h, wl.w, cur_gpu, nxt, stride=s, seed=wl.inject_seed, pass_index=t,
+                           inject=wl.inject)
+        cur_gpu, nxt = nxt, cur_gpu
+        got = map_to_np(cur_gpu)
+        assert np.array_equal(got, cur_ref), f"pass {t}: {np.argwhere(got != cur_ref)[:3]}"
+    exact = ref.brute_topk(d, wl.h, wl.w)
+    frac = (map_to_np(cur_gpu) == exact).all(-1).mean()
+    say(f"[gpu] C1 exact top-8 fraction after 20 passes: {frac:.4f}")
+    assert frac >= 0.99
+
+
+@pytest.mark.parametrize("h,w,n,strides,inject", [
+    (1, 1, 3, (1, 1), 64),
+    (1, 37, 20, (16, 4, 1), 64),
+    (45, 1, 20, (32, 2, 1), 5),
+    (13, 29, 300, (8, 4, 2, 1, 1), 64),
+    (67, 72, 1000, (64, 32, 16, 8, 4, 2, 1), 17),
+    (40, 40, 0, (1, 1), 64),  # no sites: lists stay empty
+    (24, 31, 50, (100, 1), 0),  # no injection: the map stays empty
+    (24, 31, 5, (1, 3), 1),
+])
+def test_propagate_ragged_and_edge_cases(sad, ref, h, w, n, strides, inject):
+    p = synth.sites(60 + h + n, n, h, w)
+    if n >= 10:
+        p[3, 0] = -1.0  # an inactive site
+        p[7] = p[5]  # identical sites: ties broken by index
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p)) if n > 0 else torch.zeros((0, 12), dtype=torch.float32, device=dev())
+    want = ref.propagate_schedule(d, h, w, None, strides, 77, 3, inject)
+    got = map_to_np(gpu_schedule(sad, dg, h, w, strides, 77, inject, first_pass=3))
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+def test_propagate_from_given_map_with_stale_ids(sad, ref):
+    """A previous map with out-of-range ids, inactive sites and duplicates."""
+    h, w, n = 30, 42, 200
+    p = synth.sites(70, n, h, w)
+    p[11, 0] = -2.0
+    d = ref.prepare_sites(p)
+    rng = np.random.default_rng(5)
+    prev = rng.integers(0, n + 40, (h, w, 8)).astype(np.uint32)
+    prev[rng.random((h, w, 8)) < 0.2] = 0xFFFFFFFF
+    prev[..., 3] = prev[..., 2]  # duplicates inside a list
+    prev[0, 0, :] = 11  # only an inactive site
+    want = ref.propagate(d, h, w, prev, 2, 5, 9, 64)
+    got = map_to_np(sad.propagate_topk(sad.prepare_sites(to_gpu(p)), h, w, to_gpu(prev), stride=2, seed=5,
+                                       pass_index=9, inject=64))
+    assert np.array_equal(got, want)
+
+
+@pytest.fixture(scope="module")
+def c2_state(sad, ref):
+    """The 768x512, 50k-site workload: 16 warm-up passes, then one step's
+    strides 8, 4, 2, 1, on both sides."""
+    wl = synth.C2
+    p = wl.make_sites()
+    d = ref.prepare_sites(p)
+    strides = synth.jfa_strides(wl.h, wl.w, wl.warm_passes) + list(wl.strides)
+    say(f"[gpu] C2 oracle: {len(strides)} passes at {wl.w}x{wl.h}, n={wl.n}")
+    m_ref = ref.propagate_schedule(d, wl.h, wl.w, None, strides, wl.inject_seed, 0, wl.inject)
+    dg = sad.prepare_sites(to_gpu(p))
+    m_gpu = gpu_schedule(sad, dg, wl.h, wl.w, strides, wl.inject_seed, wl.inject)
+    return wl, p, d, dg, m_ref, m_gpu
+
+
+def test_propagate_c2_full_map(c2_state):
+    wl, p, d, dg, m_ref, m_gpu = c2_state
+    got = map_to_np(m_gpu)
+    assert np.array_equal(got, m_ref), f"{(got != m_ref).any(-1).sum()} pixels differ"
+
+
+def test_propagate_is_deterministic(sad, c2_state):
+    wl, p, d, dg, m_ref, m_gpu = c2_state
+    a = sad.propagate_topk(dg, wl.h, wl.w, m_gpu, stride=1, seed=1, pass_index=99, inject=64)
+    b = sad.propagate_topk(dg, wl.h, wl.w, m_gpu, stride=1, seed=1, pass_index=99, inject=64)
+    assert torch.equal(a, b)
+
+
+def test_propagate_c4_full_map(sad, ref):
+    """2048x2048, 400k sites: 16 warm-up passes and the step strides
+    16, 8, 4, 2, 1 give the oracle's map bit for bit."""
+    wl = synth.C4
+    p = wl.make_sites()
+    d = ref.prepare_sites(p)
+    strides = synth.jfa_strides(wl.h, wl.w, wl.warm_passes) + list(wl.strides)
+    dg = sad.prepare_sites(to_gpu(p))
+    m_gpu = map_to_np(gpu_schedule(sad, dg, wl.h, wl.w, strides, wl.inject_seed, wl.inject))
+    cur = None
+    for t, s in enumerate(strides):
+        cur = ref.propagate(d, wl.h, wl.w, cur, s, wl.inject_seed, t, wl.inject)
+        say(f"[gpu] C4 oracle pass {t + 1}/{len(strides)} (stride {s})")
+    assert np.array_equal(m_gpu, cur), f"{(m_gpu != cur).any(-1).sum()} pixels differ"
+
+
+# ---------------------------------------------------------------- render / backward
+
+def test_render_fwd_c1_c2(sad, ref, c2_state):
+    wl1 = synth.C1
+    p1 = wl1.make_sites()
+    d1 = ref.prepare_sites(p1)
+    m1 = ref.brute_topk(d1, wl1.h, wl1.w)
+    got = to_np(sad.render_fwd(sad.prepare_sites(to_gpu(p1)), wl1.h, wl1.w, to_gpu(m1)))
+    assert_colour_close(got, ref.render_fwd(d1, wl1.h, wl1.w, m1), "C1 image")
+    wl, p, d, dg, m_ref, m_gpu = c2_state
+    got = to_np(sad.render_fwd(dg, wl.h, wl.w, to_gpu(m_ref)))
+    assert_colour_close(got, ref.render_fwd(d, wl.h, wl.w, m_ref), "C2 image")
+
+
+def test_render_bwd_c1(sad, ref):
+    wl = synth.C1
+    p = wl.make_sites()
+    p[9, 0] = -1.0  # an inactive site listed nowhere, and a stale list entry below
+    d = ref.prepare_sites(p)
+    m = ref.propagate_schedule(d, wl.h, wl.w, None, wl.strides, wl.inject_seed, 0, wl.inject)
+    m[5, 5, 7] = 9
+    m[6, 6, 7] = 100000
+    tgt = wl.make_target()
+    g_ref, g_abs, loss_ref, img_ref = ref.render_bwd(d, wl.h, wl.w, m, tgt)
+    dg = sad.prepare_sites(to_gpu(p))
+    grad = torch.zeros((wl.n, 12), dtype=torch.float32, device=dev())
+    loss = torch.zeros(1, dtype=torch.float32, device=dev())
+    img = torch.empty((wl.h, wl.w, 3), dtype=torch.float32, device=dev())
+    sad.render_bwd(dg, wl.h, wl.w, to_gpu(m), to_gpu(tgt), grad, loss, img)
+    assert_colour_close(to_np(img), img_ref, "C1 image from backward")
+    assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
+    g = to_np(grad)
+    assert_grad_close(g, g_ref, g_abs, "C1 gradients")
+    assert np.all(g[:, 10:] == 0)
+    # accumulation: a second call adds the same again
+    sad.render_bwd(dg, wl.h, wl.w, to_gpu(m), to_gpu(tgt), grad, loss, None)
+    assert_grad_close(to_np(grad), 2 * g_ref, 2 * g_abs, "C1 gradients, accumulated twice")
+
+
+def test_render_bwd_c2(sad, ref, c2_state):
+    wl, p, d, dg, m_ref, m_gpu = c2_state
+    tgt = wl.make_target()
+    g_ref, g_abs, loss_ref, _ = ref.render_bwd(d, wl.h, wl.w, m_ref, tgt)
+    grad = torch.zeros((wl.n, 12), dtype=torch.float32, device=dev())
+    loss = torch.zeros(1, dtype=torch.float32, device=dev())
+    sad.render_bwd(dg, wl.h, wl.w, m_gpu, to_gpu(tgt), grad, loss, None)
+    assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
+    assert_grad_close(to_np(grad), g_ref, g_abs, "C2 gradients")
+
+
+# ---------------------------------------------------------------- Adam
+
+def test_adam_bit_exact(sad, ref):
+    n, h, w = 50_000, 512, 768
+    p = synth.C2.make_sites()
+    p[17, 0] = -1.0
+    p[18, 0] = 0.0  # pushed below 0, clamped
+    p[19, 1] = float(h)  # pushed above h, clamped
+    rng = np.random.default_rng(3)
+    m = (rng.normal(0, 1e-3, (n, 12)) * (np.arange(12) < 10)).astype(np.float32)
+    v = (rng.random((n, 12)) * 1e-6 * (np.arange(12) < 10)).astype(np.float32)
+    g = synth.gradients(4, n)
+    g[18, 0], g[19, 1] = 1.0, -1.0
+    lr = np.array([1e-2, 1e-3, 2e-3, 3e-3, 4e-3], np.float32)
+    bc1, bc2 = ref.bias_corrections(0.9, 0.999, 7)
+    want = ref.adam_step(p, g, m, v, h, w, lr, 0.9, 0.999, 1e-8, bc1, bc2)
+    P, G, M, V = (to_gpu(x.copy()) for x in (p, g, m, v))
+    D = torch.empty_like(P)
+    sad.adam_step(P, G, M, V, h, w, lr.tolist(), 0.9, 0.999, 1e-8, bc1, bc2, D)
+    for name, gt, wt in zip(("params", "grad", "m", "v", "derived"), (P, G, M, V, D), want):
+        a = to_np(gt)
+        assert np.array_equal(a.view(np.uint32), wt.view(np.uint32)), (name, np.argwhere(a != wt)[:5])
+
+
+# ---------------------------------------------------------------- queries
+
+def test_query_points(sad, ref, c2_state):
+    wl, p, d, dg, m_ref, m_gpu = c2_state
+    xy = synth.queries(4005, 1 << 18, wl.h, wl.w)
+    xy[:4] = [[-5.0, 3.0], [wl.w + 9.5, wl.h + 0.25], [np.nan, 2.0], [1.0, -np.inf]]
+    got = to_np(sad.query_points(dg, wl.h, wl.w, m_gpu, to_gpu(xy)))
+    assert_colour_close(got, ref.query_points(d, wl.h, wl.w, m_ref, xy), "query colours")
+    # at pixel centres a query is the render itself, bit for bit
+    yy, xx = np.mgrid[0:wl.h, 0:wl.w]
+    centres = np.stack([xx.ravel() + 0.5, yy.ravel() + 0.5], 1).astype(np.float32)
+    q = to_np(sad.query_points(dg, wl.h, wl.w, m_gpu, to_gpu(centres)))
+    img = to_np(sad.render_fwd(dg, wl.h, wl.w, m_gpu)).reshape(-1, 3)
+    assert np.array_equal(q, img)
+
+
+def test_query_c5_full_batch_sampled(sad, ref):
+    """2^24 random points on the 768x512 / 50k-site representation (site
+    recipe of the small-scale workload, map warmed with 16 passes); 2^16
+    sampled outputs checked against the oracle."""
+    wl = synth.C5
+    p = wl.make_sites()
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p))
+    strides = synth.jfa_strides(wl.h, wl.w, wl.warm_passes)
+    m_gpu = gpu_schedule(sad, dg, wl.h, wl.w, strides, wl.inject_seed)
+    m_ref = ref.propagate_schedule(d, wl.h, wl.w, None, strides, wl.inject_seed, 0, 64)
+    assert np.array_equal(map_to_np(m_gpu), m_ref)
+    xy = wl.make_queries()
+    rgb = to_np(sad.query_points(dg, wl.h, wl.w, m_gpu, to_gpu(xy)))
+    idx = np.random.default_rng(0).choice(xy.shape[0], 1 << 16, replace=False)
+    assert_colour_close(rgb[idx], ref.query_points(d, wl.h, wl.w, m_ref, xy[idx]), "C5 sampled colours")
+
+
+# ---------------------------------------------------------------- training loop
+
+def test_training_first_iterations_track_oracle(sad, ref):
+    """The 768x512 / 50k-site fitting loop (tau = 1 at start, lr 1e-3, betas
+    0.9/0.999): 10 iterations of 4 passes + forward + backward + Adam on both
+    sides.  Float-atomic sums make gradients differ in the last bits, so the
+    trajectories are compared within tolerance: PSNR within 0.01 dB at every
+    iteration, nearly all lists and parameters equal."""
+    from voronoi_rendering_amd.pipeline import SadField
+
+    wl = synth.C3
+    p = wl.make_sites()
+    tgt = wl.make_target()
+    warm = synth.jfa_strides(wl.h, wl.w, wl.warm_passes)
+    lr = np.full(5, 1e-3, np.float32)
+    # oracle trajectory
+    d = ref.prepare_sites(p)
+    cur = ref.propagate_schedule(d, wl.h, wl.w, None, warm, wl.inject_seed, 0, 64)
+    pp, m, v = p.copy(), np.zeros_like(p), np.zeros_like(p)
+    psnr_ref, pi = [], len(warm)
+    for it in range(1, 11):
+        cur = ref.propagate_schedule(d, wl.h, wl.w, cur, wl.strides, wl.inject_seed, pi, 64)
+        pi += len(wl.strides)
+        g, _, loss, _ = ref.render_bwd(d, wl.h, wl.w, cur, tgt)
+        psnr_ref.append(10 * math.log10(3.0 / loss))
+        bc1, bc2 = ref.bias_corrections(0.9, 0.999, it)
+        pp, _, m, v, d = ref.adam_step(pp, g.astype(np.float32), m, v, wl.h, wl.w, lr, 0.9, 0.999, 1e-8, bc1, bc2)
+    # GPU trajectory
+    f = SadField(to_gpu(p), wl.h, wl.w, wl.inject_seed)
+    f.warm(wl.warm_passes)
+    target = to_gpu(tgt)
+    psnr_gpu = []
+    for it in range(10):
+        f.loss.zero_()
+        f.train_iter(wl.strides, target)
+        psnr_gpu.append(10 * math.log10(3.0 / f.loss.item()))
+    say("[gpu] C3 PSNR oracle " + " ".join(f"{x:.4f}" for x in psnr_ref))
+    say("[gpu] C3 PSNR gpu    " + " ".join(f"{x:.4f}" for x in psnr_gpu))
+    assert np.all(np.abs(np.array(psnr_gpu) - np.array(psnr_ref)) <= 0.01)
+    same_lists = (map_to_np(f.topk) == cur).all(-1).mean()
+    close = np.abs(to_np(f.params)[:, :10] - pp[:, :10]) <= 1e-5 * (1 + np.abs(pp[:, :10]))
+    say(f"[gpu] C3 after 10 iterations: lists equal {same_lists:.5f}, params within 1e-5: {close.mean():.5f}")
+    assert same_lists >= 0.999
+    assert close.mean() >= 0.99
+    assert np.all(np.abs(to_np(f.params)[:, :10] - pp[:, :10]) <= 10 * 2 * 1e-3 + 1e-4)

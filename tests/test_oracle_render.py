@@ -140,7 +140,7 @@ def test_gradients_match_autograd(ref):
     err = np.abs(grad[:, :10] - auto) / scale
     assert err.max() < 2e-5, err.max(0)
     assert np.all(grad[:, 10:] == 0)
-    assert np.all(gabs[:, :10] >= np.abs(grad[:, :10]) * (1 - 1e-12))
+    assert np.all(gabs[:, :10] >= np.abs(grad[:, :10]) * (1 - 1e-12))  # the magnitude bounds the value
 
 
 def test_gradients_match_finite_differences(ref):

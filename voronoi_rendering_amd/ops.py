@@ -1,0 +1,142 @@
+"""Thin torch-facing wrappers of the SAD C ABI (include/sad.h).
+
+PyTorch only provides device memory and the current stream: every wrapper
+checks shapes, dtypes and devices, passes raw pointers to libsad.so, and the
+work runs in the HIP kernels.  Top-K maps are torch.int32 tensors holding the
+uint32 site ids bit for bit (empty slot 0xffffffff reads as -1).
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Sequence
+
+import torch
+
+from . import _native
+
+K = 8
+REC = 12
+EMPTY_I32 = -1
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple | None = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (the SAD kernels have no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def prepare_sites(params: torch.Tensor, derived: torch.Tensor | None = None) -> torch.Tensor:
+    n = params.shape[0]
+    _need(params, "params", torch.float32, (n, REC))
+    if derived is None:
+        derived = torch.empty_like(params)
+    _need(derived, "derived", torch.float32, (n, REC))
+    _native.check("sad_prepare_sites", _native.lib().sad_prepare_sites(_ptr(params), n, _ptr(derived),
+                                                                        _stream(params)))
+    return derived
+
+
+def empty_map(h: int, w: int, device="cuda") -> torch.Tensor:
+    return torch.full((h, w, K), EMPTY_I32, dtype=torch.int32, device=device)
+
+
+def propagate_topk(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor | None = None,
+                   *, stride: int, seed: int, pass_index: int, inject: int = 64) -> torch.Tensor:
+    n = derived.shape[0]
+    _need(derived, "derived", torch.float32, (n, REC))
+    if prev is not None:
+        _need(prev, "prev", torch.int32, (h, w, K))
+    if out is None:
+        out = torch.empty((h, w, K), dtype=torch.int32, device=derived.device)
+    _need(out, "out", torch.int32, (h, w, K))
+    st = _native.lib().sad_propagate_topk(_ptr(derived), n, h, w, _ptr(prev), _ptr(out), int(stride),
+                                          int(seed) & 0xFFFFFFFFFFFFFFFF, int(pass_index) & 0xFFFFFFFF, int(inject),
+                                          _stream(derived))
+    _native.check("sad_propagate_topk", st)
+    return out
+
+
+def render_fwd(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, image: torch.Tensor | None = None
+               ) -> torch.Tensor:
+    n = derived.shape[0]
+    _need(derived, "derived", torch.float32, (n, REC))
+    _need(topk, "topk", torch.int32, (h, w, K))
+    if image is None:
+        image = torch.empty((h, w, 3), dtype=torch.float32, device=derived.device)
+    _need(image, "image", torch.float32, (h, w, 3))
+    _native.check("sad_render_fwd", _native.lib().sad_render_fwd(_ptr(derived), n, h, w, _ptr(topk), _ptr(image),
+                                                                  _stream(derived)))
+    return image
+
+
+def render_bwd(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target: torch.Tensor, grad: torch.Tensor,
+               loss: torch.Tensor | None = None, image: torch.Tensor | None = None) -> None:
+    """Accumulate the loss gradient into ``grad`` ([n][12]); optionally add the
+    loss into ``loss`` (one float32) and write the rendered image."""
+    n = derived.shape[0]
+    _need(derived, "derived", torch.float32, (n, REC))
+    _need(topk, "topk", torch.int32, (h, w, K))
+    _need(target, "target", torch.float32, (h, w, 3))
+    _need(grad, "grad", torch.float32, (n, REC))
+    if loss is not None:
+        _need(loss, "loss", torch.float32, (1,))
+    if image is not None:
+        _need(image, "image", torch.float32, (h, w, 3))
+    st = _native.lib().sad_render_bwd(_ptr(derived), n, h, w, _ptr(topk), _ptr(target), _ptr(grad), _ptr(loss),
+                                      _ptr(image), _stream(derived))
+    _native.check("sad_render_bwd", st)
+
+
+def adam_step(params: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor, h: int, w: int,
+              lr: Sequence[float], beta1: float, beta2: float, eps: float, bias_corr1: float, bias_corr2: float,
+              derived: torch.Tensor | None = None) -> None:
+    n = params.shape[0]
+    for t, name in ((params, "params"), (grad, "grad"), (m, "m"), (v, "v")):
+        _need(t, name, torch.float32, (n, REC))
+    if derived is not None:
+        _need(derived, "derived", torch.float32, (n, REC))
+    lr_arr = (C.c_float * 5)(*[float(x) for x in lr])
+    st = _native.lib().sad_adam_step(_ptr(params), _ptr(grad), _ptr(m), _ptr(v), n, h, w, lr_arr, beta1, beta2, eps,
+                                     bias_corr1, bias_corr2, _ptr(derived), _stream(params))
+    _native.check("sad_adam_step", st)
+
+
+def query_points(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, xy: torch.Tensor,
+                 rgb: torch.Tensor | None = None) -> torch.Tensor:
+    n = derived.shape[0]
+    m = xy.shape[0]
+    _need(derived, "derived", torch.float32, (n, REC))
+    _need(topk, "topk", torch.int32, (h, w, K))
+    _need(xy, "xy", torch.float32, (m, 2))
+    if rgb is None:
+        rgb = torch.empty((m, 3), dtype=torch.float32, device=derived.device)
+    _need(rgb, "rgb", torch.float32, (m, 3))
+    st = _native.lib().sad_query_points(_ptr(derived), n, h, w, _ptr(topk), _ptr(xy), m, _ptr(rgb),
+                                        _stream(derived))
+    _native.check("sad_query_points", st)
+    return rgb
+
+
+def jfa_strides(h: int, w: int, n_pass: int) -> list[int]:
+    """Jump steps of the warm-up schedule (Sec. 4.3): B/2, B/4, ..., 1, then 1,
+    with B the smallest power of two >= max(h, w)."""
+    b = 1
+    while b < max(h, w):
+        b *= 2
+    lb = b.bit_length() - 1
+    return [max(1, b >> (min(t, max(lb - 1, 0)) + 1)) for t in range(n_pass)]

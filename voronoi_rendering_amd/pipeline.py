@@ -1,0 +1,91 @@
+"""A GPU-resident SAD fitting loop built from the C-ABI calls.
+
+One training iteration (Sec. 5: no CPU work inside the loop besides launches)
+is: propagation passes over the top-K map, the forward + backward render that
+accumulates the site gradients and the loss, and the Adam step that also
+rewrites the prepared site records.  The map lives in two ping-pong buffers
+because a pass only reads the previous map.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Sequence
+
+import torch
+
+from . import ops
+
+
+@dataclass
+class AdamConfig:
+    lr: tuple = (1e-3, 1e-3, 1e-3, 1e-3, 1e-3)  # (x, y), log tau, r, colour, (theta, log s1, log s2)
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+
+
+def bias_corrections(beta1: float, beta2: float, t: int) -> tuple[float, float]:
+    """1 - beta^t for Adam step t, computed on the host in float64 and handed
+    to the kernel as float32."""
+    import numpy as np
+
+    return float(np.float32(1.0 - float(beta1) ** t)), float(np.float32(1.0 - float(beta2) ** t))
+
+
+@dataclass
+class SadField:
+    params: torch.Tensor  # [n][12] float32 on the GPU
+    h: int
+    w: int
+    seed: int
+    inject: int = 64
+    adam: AdamConfig = field(default_factory=AdamConfig)
+
+    def __post_init__(self):
+        dev = self.params.device
+        n = self.params.shape[0]
+        self.derived = ops.prepare_sites(self.params)
+        self.grad = torch.zeros((n, ops.REC), dtype=torch.float32, device=dev)
+        self.m = torch.zeros_like(self.grad)
+        self.v = torch.zeros_like(self.grad)
+        self.maps = [ops.empty_map(self.h, self.w, dev), ops.empty_map(self.h, self.w, dev)]
+        self.cur = 0
+        self.pass_index = 0
+        self.adam_t = 0
+        self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    @property
+    def topk(self) -> torch.Tensor:
+        return self.maps[self.cur]
+
+    def propagate(self, strides: Sequence[int]) -> None:
+        for s in strides:
+            ops.propagate_topk(self.derived, self.h, self.w, self.maps[self.cur], self.maps[1 - self.cur],
+                               stride=int(s), seed=self.seed, pass_index=self.pass_index, inject=self.inject)
+            self.cur = 1 - self.cur
+            self.pass_index += 1
+
+    def warm(self, n_pass: int) -> None:
+        """Fill the map from scratch with the warm-up jump schedule."""
+        self.propagate(ops.jfa_strides(self.h, self.w, n_pass))
+
+    def forward_backward(self, target: torch.Tensor, image: torch.Tensor | None = None) -> None:
+        ops.render_bwd(self.derived, self.h, self.w, self.topk, target, self.grad, self.loss, image)
+
+    def step(self, strides: Sequence[int], target: torch.Tensor) -> None:
+        """Propagation passes + forward + backward (gradients accumulate)."""
+        self.propagate(strides)
+        self.forward_backward(target)
+
+    def adam_step(self) -> None:
+        self.adam_t += 1
+        bc1, bc2 = bias_corrections(self.adam.beta1, self.adam.beta2, self.adam_t)
+        ops.adam_step(self.params, self.grad, self.m, self.v, self.h, self.w, self.adam.lr, self.adam.beta1,
+                      self.adam.beta2, self.adam.eps, bc1, bc2, self.derived)
+
+    def train_iter(self, strides: Sequence[int], target: torch.Tensor) -> None:
+        self.step(strides, target)
+        self.adam_step()
+
+    def render(self) -> torch.Tensor:
+        return ops.render_fwd(self.derived, self.h, self.w, self.topk)
