@@ -78,6 +78,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the SAD hot path here has no multi-GPU mode "
@@ -86,6 +88,15 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "launches": 5}))
+        return 0
 
     import synth
     from voronoi_rendering_amd import ops

@@ -71,6 +71,7 @@
 #ifndef SAD_H
 #define SAD_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -153,15 +154,25 @@ int sad_render_fwd(const float *derived, int32_t n, int32_t h, int32_t w, const 
  *   x += -2 kappa (a cos/s1 - b sin/s2);  y += -2 kappa (a sin/s1 + b cos/s2);
  *   theta += 2 kappa a_r b_r (1/s1^2 - 1/s2^2);
  *   log_s1 += -2 kappa a^2;  log_s2 += -2 kappa b^2.
- *   target  [h][w][3] float32, read
- *   grad    [n][12] float32, ACCUMULATED into (+=) with float atomics, so the
- *           summation order, and the last bits, vary from run to run;
- *           entries 10, 11 are not touched
- *   loss    NULL, or one float32 accumulated into (+= L)
- *   image   NULL, or [h][w][3] float32 written with the rendered colours
+ * The per-pixel terms are summed per site on chip, then per site across
+ * neighbouring image regions (Sec. 4.8 reduces gradients per tile for the
+ * same reason); only sites with very wide footprints use float atomics.
+ *   target     [h][w][3] float32, read
+ *   grad       [n][12] float32, ACCUMULATED into (+=); the summation order,
+ *              and so the last bits, vary from run to run; entries 10, 11
+ *              are not touched
+ *   loss       NULL, or one float32 accumulated into (+= L)
+ *   image      NULL, or [h][w][3] float32 written with the rendered colours
+ *   workspace  device scratch of at least sad_render_bwd_workspace_bytes(h, w)
+ *              bytes, 16-byte aligned, owned by the caller; its contents on
+ *              entry do not matter and it must not be in use by another call
+ *              at the same time
  */
+size_t sad_render_bwd_workspace_bytes(int32_t h, int32_t w);
+
 int sad_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
-                   const float *target, float *grad, float *loss, float *image, void *stream);
+                   const float *target, float *grad, float *loss, float *image, void *workspace,
+                   size_t workspace_bytes, void *stream);
 
 /*
  * One Adam step (Kingma & Ba) on the site parameters (Sec. 5: per-parameter

@@ -11,6 +11,10 @@ Tolerances (floating-point outputs; integer outputs are compared bit for bit):
   about m 2^-24 of its magnitude (m ~ 30 here), and a float32 sum in any
   order adds at most (count - 1) 2^-24 of the summed magnitudes, typically
   sqrt(count) 2^-24; 1e-5 = 168 x 2^-24 covers both for the sizes tested.
+  The GPU sums each site's contributions in 64-bit fixed point with
+  resolution 2^-E, 2^E = 2^45 * (the power of two >= h*w), rounding each
+  contribution toward zero; that adds at most count * 2^-E, count = the number of
+  pixels listing the site.
 - loss: relative 1e-5.
 """
 from __future__ import annotations
@@ -51,10 +55,23 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def assert_grad_close(gpu: np.ndarray, ref: np.ndarray, ref_abs: np.ndarray, what: str = "grad") -> None:
+def fixed_point_resolution(h: int, w: int) -> float:
+    e = 45
+    while (1 << (e - 45)) < h * w:
+        e += 1
+    return 2.0 ** -e
+
+
+def assert_grad_close(gpu: np.ndarray, ref: np.ndarray, ref_abs: np.ndarray, what: str = "grad",
+                      topk: np.ndarray | None = None, hw: tuple | None = None) -> None:
     gpu = gpu[:, :10].astype(np.float64)
     ref = ref[:, :10]
     tol = GRAD_RTOL * np.abs(ref) + GRAD_STOL * ref_abs[:, :10]
+    if topk is not None:
+        ids = topk.reshape(-1)
+        ids = ids[ids < ref.shape[0]].astype(np.int64)
+        count = np.bincount(ids, minlength=ref.shape[0]).astype(np.float64)
+        tol = tol + (count * fixed_point_resolution(*hw))[:, None]
     err = np.abs(gpu - ref)
     bad = err > tol
     if bad.any():

@@ -21,12 +21,13 @@ def lib():
 
 def declared_symbols():
     text = (ROOT / "include" / "sad.h").read_text()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(sad_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(sad_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_boundary():
     syms = declared_symbols()
     for name in ("sad_prepare_sites", "sad_propagate_topk", "sad_render_fwd", "sad_render_bwd",
+                 "sad_render_bwd_workspace_bytes",
                  "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version"):
         assert name in syms
 
@@ -84,9 +85,14 @@ def test_propagate_rejects(lib):
 def test_render_query_adam_reject(lib):
     assert lib.sad_render_fwd(P, 10, 8, 8, P + 4096, None, None) == EINVAL
     assert lib.sad_render_fwd(P, 10, -8, 8, P + 4096, P + 8192, None) == EINVAL
-    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, None, None, None, None) == EINVAL
-    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P, None, None, None) == EINVAL  # grad aliases sites
-    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P + 65536, P + 2, None, None) == EINVAL
+    WS = 1 << 30
+    wsb = lib.sad_render_bwd_workspace_bytes(8, 8)
+    assert wsb > 0 and lib.sad_render_bwd_workspace_bytes(-1, 8) == 0
+    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, None, None, None, WS, wsb, None) == EINVAL
+    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P, None, None, WS, wsb, None) == EINVAL  # grad aliases
+    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P + 65536, P + 2, None, WS, wsb, None) == EINVAL
+    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P + 65536, None, None, None, wsb, None) == EINVAL
+    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P + 65536, None, None, WS, wsb - 1, None) == EINVAL
     assert lib.sad_query_points(P, 10, 8, 8, P + 4096, P + 8192, -1, P + 65536, None) == EINVAL
     assert lib.sad_query_points(P, 10, 8, 8, P + 4096, P + 8196, 5, P + 65536, None) == EINVAL  # xy misaligned
     assert lib.sad_query_points(P, 10, 0, 8, P + 4096, P + 8192, 5, P + 65536, None) == EINVAL  # no lists

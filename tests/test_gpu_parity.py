@@ -195,11 +195,12 @@ def test_render_bwd_c1(sad, ref):
     assert_colour_close(to_np(img), img_ref, "C1 image from backward")
     assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
     g = to_np(grad)
-    assert_grad_close(g, g_ref, g_abs, "C1 gradients")
+    assert_grad_close(g, g_ref, g_abs, "C1 gradients", m, (wl.h, wl.w))
     assert np.all(g[:, 10:] == 0)
     # accumulation: a second call adds the same again
     sad.render_bwd(dg, wl.h, wl.w, to_gpu(m), to_gpu(tgt), grad, loss, None)
-    assert_grad_close(to_np(grad), 2 * g_ref, 2 * g_abs, "C1 gradients, accumulated twice")
+    assert_grad_close(to_np(grad), 2 * g_ref, 2 * g_abs, "C1 gradients, accumulated twice", np.concatenate([m, m]),
+                      (wl.h, wl.w))
 
 
 def test_render_bwd_c2(sad, ref, c2_state):
@@ -210,7 +211,7 @@ def test_render_bwd_c2(sad, ref, c2_state):
     loss = torch.zeros(1, dtype=torch.float32, device=dev())
     sad.render_bwd(dg, wl.h, wl.w, m_gpu, to_gpu(tgt), grad, loss, None)
     assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
-    assert_grad_close(to_np(grad), g_ref, g_abs, "C2 gradients")
+    assert_grad_close(to_np(grad), g_ref, g_abs, "C2 gradients", m_ref, (wl.h, wl.w))
 
 
 # ---------------------------------------------------------------- Adam

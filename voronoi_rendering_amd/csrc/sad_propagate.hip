@@ -2,21 +2,27 @@
 //
 // Mapping: one wavefront (64 lanes) per 8x8 pixel tile, one lane per pixel;
 // a 256-thread workgroup holds 4 consecutive tiles.  The tile is also the unit
-// of the global probe: its 64 injected ids are drawn once per wavefront, one
-// per lane, and shared by all pixels of the tile.
+// of the global probe: its injected ids are drawn once per wavefront, one per
+// lane, and shared by all pixels of the tile.
 //
-// Per lane the list is a sorted register array (TopK).  Candidates come from
-// the pixel's own previous list, the previous lists of the 4 pixels at
-// +-stride (read-only map, so the pass is a Jacobi update and the result does
-// not depend on scheduling) and the tile's probe ids.
-//
-// Culling of probe ids: each lane bounds its probe site's logit over the
-// whole tile (distance from the site to the tile's box of pixel centres times
-// the smaller inverse scale, see probe_may_enter) and the wavefront keeps only
-// the sites whose bound can beat the weakest current 8th-best logit of the
-// tile.  The bound includes the float32 rounding of the exact logit
-// evaluation, so a culled site can never enter any list: the culling changes
-// the work, not the result.
+// Work per lane, in the order that keeps the vector ALU busy the least:
+//  1. The pixel's previous list: 8 logits, then a sorting network puts the
+//     entries in ranking order (a list carried over from the previous pass is
+//     already in order unless the sites moved, and the network is skipped
+//     when every lane of the wavefront is in order).
+//  2. The 32 ids of the 4 neighbour lists at +-stride: each id is compared
+//     with the pixel's own 8 ids and only ids not already listed are queued,
+//     in LDS (one column per lane).  At small strides almost all neighbour
+//     ids are already listed.
+//  3. The queued ids are scored; an id whose logit cannot beat the current
+//     8th entry is dropped at once, the others wait in a short register
+//     buffer and are inserted (with the duplicate check) afterwards.
+//  4. The tile's probe ids: each lane bounds its probe site's logit over the
+//     whole tile (probe_may_enter) and the wavefront scores only the sites
+//     whose bound can beat the tile's weakest 8th entry.
+// The result equals the top-8 of the candidate set in ranking order, whatever
+// order the candidates are visited in: every step above only skips
+// candidates that provably cannot be among the 8 best.
 #include "sad_device.h"
 #include "sad_host.h"
 
@@ -31,14 +37,17 @@ struct PropArgs {
     uint32_t pass_index;
 };
 
-__device__ __forceinline__ void consider(TopK& t, const float* __restrict__ derived, uint32_t n, uint32_t id,
-                                         float px, float py) {
-    if (id >= n) return;  // also drops the EMPTY sentinel
+constexpr int QCAP = 4 * K;  // queued neighbour ids per lane (4 lists of 8)
+constexpr int PBUF = 4;      // register buffer of candidates awaiting insertion
+constexpr int WAVES_PER_WG = 4;
+
+// Logit of site id at (px, py), or NaN when the id names no usable site.
+__device__ __forceinline__ float site_logit(const float* __restrict__ derived, uint32_t n, uint32_t id, float px,
+                                            float py) {
+    if (id >= n) return __builtin_nanf("");
     Geo g = load_geo(derived, id);
-    if (!(g.g0.x >= 0.0f)) return;  // inactive site
-    float s = logit(g, px, py);
-    if (s != s) return;  // NaN logits are dropped
-    t.insert(s, id);
+    if (!(g.g0.x >= 0.0f)) return __builtin_nanf("");
+    return logit(g, px, py);
 }
 
 // Can the probe site (geometry g) rank among the 8 best of any pixel of the
@@ -70,9 +79,40 @@ __device__ __forceinline__ bool probe_may_enter(const Geo& g, float thr, float b
     return !(ub < thr);
 }
 
+// compare-exchange for the sorting network: entry i ends up ranking before j
+__device__ __forceinline__ void cex(TopK& t, int i, int j) {
+    bool sw = ranks_before(t.s[j], t.id[j], t.s[i], t.id[i]);
+    float si = t.s[i], sj = t.s[j];
+    uint32_t ii = t.id[i], ij = t.id[j];
+    t.s[i] = sw ? sj : si;
+    t.s[j] = sw ? si : sj;
+    t.id[i] = sw ? ij : ii;
+    t.id[j] = sw ? ii : ij;
+}
+
+__device__ __forceinline__ void sort8(TopK& t) {
+    cex(t, 0, 2); cex(t, 1, 3); cex(t, 4, 6); cex(t, 5, 7);
+    cex(t, 0, 4); cex(t, 1, 5); cex(t, 2, 6); cex(t, 3, 7);
+    cex(t, 0, 1); cex(t, 2, 3); cex(t, 4, 5); cex(t, 6, 7);
+    cex(t, 2, 4); cex(t, 3, 5);
+    cex(t, 1, 4); cex(t, 3, 6);
+    cex(t, 1, 2); cex(t, 3, 4); cex(t, 5, 6);
+}
+
+__device__ __forceinline__ bool in_list(const TopK& t, uint32_t v) {
+    bool f = false;
+#pragma unroll
+    for (int k = 0; k < K; ++k) f |= (t.id[k] == v);
+    return f;
+}
+
+constexpr int QBATCH = 4;  // queued ids scored per loop trip (their gathers overlap)
+
 __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
+    __shared__ uint32_t queue[WAVES_PER_WG][QCAP][WAVE];
     const int lane = threadIdx.x & (WAVE - 1);
-    const int tile = blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
+    const int wv = threadIdx.x / WAVE;
+    const int tile = blockIdx.x * WAVES_PER_WG + wv;
     if (tile >= a.n_tiles) return;  // uniform per wavefront
     const int tx = tile % a.tiles_x, ty = tile / a.tiles_x;
     const int i = tx * TILE + (lane & (TILE - 1));
@@ -80,49 +120,140 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
     const bool inside = i < a.w && j < a.h;
     const float px = (float)i + 0.5f, py = (float)j + 0.5f;
     const uint32_t n = (uint32_t)a.n;
+    const bool have_prev = inside && a.prev;
 
+    // Issue every independent load first: the pixel's list, the 4 neighbour
+    // lists and this lane's probe site.
+    uint32_t own[K];
+    uint32_t nbr[4][K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) own[k] = EMPTY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int k = 0; k < K; ++k) nbr[q][k] = EMPTY;
+    if (have_prev) {
+        const uint4* l = reinterpret_cast<const uint4*>(a.prev + ((size_t)j * a.w + i) * K);
+        const uint4 l0 = l[0], l1 = l[1];
+        own[0] = l0.x; own[1] = l0.y; own[2] = l0.z; own[3] = l0.w;
+        own[4] = l1.x; own[5] = l1.y; own[6] = l1.z; own[7] = l1.w;
+        const int nb[4][2] = {{a.stride, 0}, {-a.stride, 0}, {0, a.stride}, {0, -a.stride}};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ii = i + nb[q][0], jj = j + nb[q][1];
+            if (ii < 0 || ii >= a.w || jj < 0 || jj >= a.h) continue;
+            const uint4* m = reinterpret_cast<const uint4*>(a.prev + ((size_t)jj * a.w + ii) * K);
+            const uint4 m0 = m[0], m1 = m[1];
+            nbr[q][0] = m0.x; nbr[q][1] = m0.y; nbr[q][2] = m0.z; nbr[q][3] = m0.w;
+            nbr[q][4] = m1.x; nbr[q][5] = m1.y; nbr[q][6] = m1.z; nbr[q][7] = m1.w;
+        }
+    }
+    uint32_t pid = EMPTY;
+    Geo pg;
+    pg.g0 = make_float4(-1.f, -1.f, 0.f, 0.f);
+    pg.g1 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane < a.inject) {
+        pid = probe_id(a.seed, a.pass_index, (uint32_t)tile, (uint32_t)lane, n);
+        pg = load_geo(a.derived, pid);
+    }
+
+    // 1. the pixel's previous list, in ranking order
     TopK t;
     t.clear();
-    if (inside && a.prev) {
-        const int nb[5][2] = {{0, 0}, {a.stride, 0}, {-a.stride, 0}, {0, a.stride}, {0, -a.stride}};
 #pragma unroll
-        for (int q = 0; q < 5; ++q) {
-            int ii = i + nb[q][0], jj = j + nb[q][1];
-            if (ii < 0 || ii >= a.w || jj < 0 || jj >= a.h) continue;
-            const uint4* l = reinterpret_cast<const uint4*>(a.prev + ((size_t)jj * a.w + ii) * K);
-            uint4 l0 = l[0], l1 = l[1];
-            consider(t, a.derived, n, l0.x, px, py);
-            consider(t, a.derived, n, l0.y, px, py);
-            consider(t, a.derived, n, l0.z, px, py);
-            consider(t, a.derived, n, l0.w, px, py);
-            consider(t, a.derived, n, l1.x, px, py);
-            consider(t, a.derived, n, l1.y, px, py);
-            consider(t, a.derived, n, l1.z, px, py);
-            consider(t, a.derived, n, l1.w, px, py);
+    for (int k = 0; k < K; ++k) {
+        const float s = site_logit(a.derived, n, own[k], px, py);
+        if (s == s) {
+            t.s[k] = s;
+            t.id[k] = own[k];
+        }
+    }
+    bool ordered = true;
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k)
+        ordered &= ranks_before(t.s[k], t.id[k], t.s[k + 1], t.id[k + 1]) || t.id[k + 1] == EMPTY;
+    if (!__all(ordered)) {
+        sort8(t);
+        // a malformed previous list may repeat an id: rebuild such lists by insertion
+        bool dup = false;
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) dup |= (t.id[k] == t.id[k + 1] && t.id[k] != EMPTY);
+        if (__any(dup) && dup) {
+            TopK u;
+            u.clear();
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (t.id[k] != EMPTY) u.insert(t.s[k], t.id[k]);
+            t = u;
         }
     }
 
-    if (a.inject > 0) {
-        // the weakest 8th-best logit of the tile (+inf for lanes outside the image)
-        float thr = wave_min(inside ? t.s[K - 1] : __builtin_inff());
-        uint32_t pid = EMPTY;
-        bool keep = false;
-        if (lane < a.inject) {
-            pid = probe_id(a.seed, a.pass_index, (uint32_t)tile, (uint32_t)lane, n);
-            Geo g = load_geo(a.derived, pid);
-            if (g.g0.x >= 0.0f) {
-                float bx0 = (float)(tx * TILE) + 0.5f, by0 = (float)(ty * TILE) + 0.5f;
-                float bx1 = (float)min(tx * TILE + TILE - 1, a.w - 1) + 0.5f;
-                float by1 = (float)min(ty * TILE + TILE - 1, a.h - 1) + 0.5f;
-                keep = probe_may_enter(g, thr, bx0, bx1, by0, by1);
+    // 2. neighbour ids not already listed go to this lane's queue column
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t v = nbr[q][k];
+            if (v < n && !in_list(t, v)) {
+                queue[wv][cnt][lane] = v;
+                ++cnt;
             }
+        }
+
+    // 3. score queued ids, QBATCH at a time; those that may enter wait in a
+    //    register buffer and are inserted afterwards
+    float bs[PBUF];
+    uint32_t bi[PBUF];
+    int nb_used = 0;
+    for (int it = 0; __any(it < cnt); it += QBATCH) {
+        uint32_t v[QBATCH];
+        float sc[QBATCH];
+#pragma unroll
+        for (int b = 0; b < QBATCH; ++b) v[b] = (it + b < cnt) ? queue[wv][it + b][lane] : EMPTY;
+#pragma unroll
+        for (int b = 0; b < QBATCH; ++b) sc[b] = site_logit(a.derived, n, v[b], px, py);
+#pragma unroll
+        for (int b = 0; b < QBATCH; ++b) {
+            if (sc[b] == sc[b] && ranks_before(sc[b], v[b], t.s[K - 1], t.id[K - 1])) {
+                if (nb_used == PBUF) {  // buffer full: make room by inserting its oldest entry
+                    t.insert(bs[PBUF - 1], bi[PBUF - 1]);
+                    --nb_used;
+                }
+#pragma unroll
+                for (int c = PBUF - 1; c >= 1; --c) {
+                    bs[c] = bs[c - 1];
+                    bi[c] = bi[c - 1];
+                }
+                bs[0] = sc[b];
+                bi[0] = v[b];
+                ++nb_used;
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < PBUF; ++b)
+        if (b < nb_used) t.insert(bs[b], bi[b]);
+
+    // 4. the tile's probe ids, culled by the tile bound
+    if (a.inject > 0) {
+        const float thr = wave_min(inside ? t.s[K - 1] : __builtin_inff());
+        bool keep = false;
+        if (pg.g0.x >= 0.0f) {
+            const float bx0 = (float)(tx * TILE) + 0.5f, by0 = (float)(ty * TILE) + 0.5f;
+            const float bx1 = (float)min(tx * TILE + TILE - 1, a.w - 1) + 0.5f;
+            const float by1 = (float)min(ty * TILE + TILE - 1, a.h - 1) + 0.5f;
+            keep = probe_may_enter(pg, thr, bx0, bx1, by0, by1);
         }
         uint64_t mask = __ballot(keep);
         while (mask) {
-            int q = __builtin_ctzll(mask);
+            const int q = __builtin_ctzll(mask);
             mask &= mask - 1;
-            uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)pid, q);
-            if (inside) consider(t, a.derived, n, id, px, py);
+            const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)pid, q);
+            if (inside) {
+                const float s = site_logit(a.derived, n, id, px, py);
+                if (s == s) t.insert(s, id);
+            }
         }
     }
 
@@ -163,6 +294,7 @@ extern "C" int sad_propagate_topk(const float* derived, int32_t n, int32_t h, in
     a.n_tiles = (int32_t)ntiles;
     a.pass_index = pass_index;
     clear_error();
-    hipLaunchKernelGGL(k_propagate, dim3((unsigned)((ntiles + 3) / 4)), dim3(256), 0, as_stream(stream), a);
+    hipLaunchKernelGGL(k_propagate, dim3((unsigned)((ntiles + WAVES_PER_WG - 1) / WAVES_PER_WG)),
+                       dim3(WAVE * WAVES_PER_WG), 0, as_stream(stream), a);
     return launch_status();
 }

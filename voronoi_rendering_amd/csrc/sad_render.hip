@@ -69,6 +69,23 @@ __device__ __forceinline__ void eval_point(const float* __restrict__ derived, ui
     }
 }
 
+// Rotate the 8 list entries left by r (0..7): entry k moves to (k - r) mod 8.
+__device__ __forceinline__ void rotate_list(uint4& l0, uint4& l1, int r) {
+    uint32_t v[K] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+    for (int bit = 0; bit < 3; ++bit) {
+        const int sh = 1 << bit;
+        const bool on = (r >> bit) & 1;
+        uint32_t u[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) u[k] = on ? v[(k + sh) & (K - 1)] : v[k];
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = u[k];
+    }
+    l0 = make_uint4(v[0], v[1], v[2], v[3]);
+    l1 = make_uint4(v[4], v[5], v[6], v[7]);
+}
+
 struct PixArgs {
     const float* derived;
     const uint32_t* topk;
@@ -101,28 +118,105 @@ __global__ __launch_bounds__(256) void k_render_fwd(PixArgs a) {
     a.image[p * 3 + 2] = pe.c[2];
 }
 
-constexpr int HASH_SLOTS = 512;
-constexpr int HASH_PROBES = 16;
+// ---------------------------------------------------------------- backward
+//
+// A workgroup covers one region of 2 x 4 tiles (16 rows x 32 columns of
+// pixels), one wavefront per tile.  Per-pixel gradient contributions are
+// summed in LDS per site (open addressing keyed by site id, multiplicative
+// hash, linear probing over at most REGION_PROBES slots, keys claimed by
+// compare-and-swap).
+//
+// The LDS sums are exact 64-bit fixed-point integers: a contribution t
+// becomes t 2^E truncated toward zero, 2^E = 2^45 * (the power of two >= h*w), so
+// the resolution is 2^-45 of the 1/(h*w) scale every gradient carries, and
+// the integer adds are exact and independent of their order.  (LDS float
+// atomics are an order of magnitude slower than integer ones on this GPU.)
+// A contribution with |t 2^E| >= 2^53 (far outside the normal range) goes to
+// global memory as a float atomic instead, so a slot, which receives at most
+// one contribution per pixel of the region, never overflows.
+//
+// The sums then leave the workgroup without device-wide float atomics, which
+// on a multi-die GPU are carried out at the memory side and cost far more
+// than the arithmetic: every site has a home region (the one containing its
+// position), the workgroup writes its table (keys at the same slots, the
+// summed values of the sites whose home is in the 3 x 3 regions around it) to
+// a workspace, and a second kernel gives every site the sum of its entries in
+// the 9 tables around its home.  Sites listed by a region outside that
+// neighbourhood (very wide footprints) are added with float atomics
+// directly; their slot keeps a placeholder key so probe chains stay intact.
+constexpr int RT_X = 4, RT_Y = 2;  // tiles per region
+constexpr int REGION_W = RT_X * TILE, REGION_H = RT_Y * TILE;
+constexpr int REGION_WAVES = RT_X * RT_Y;
+constexpr int SLOTS = 256;
+constexpr int REGION_PROBES = 16;
 constexpr int NGRAD = 10;
+constexpr float FIX_LIMIT = 0x1p53f;  // |t 2^E| below this goes to the fixed-point sums
+constexpr uint32_t PLACEHOLDER = 0xfffffffeu;
 
-__global__ __launch_bounds__(256) void k_render_bwd(PixArgs a) {
-    __shared__ uint32_t keys[HASH_SLOTS];
-    __shared__ float acc[HASH_SLOTS * NGRAD];
-    __shared__ float wsum[256 / WAVE];
+struct RegionGrid {
+    int32_t rgx, rgy;
+};
 
-    for (int s = threadIdx.x; s < HASH_SLOTS; s += blockDim.x) keys[s] = EMPTY;
-    for (int s = threadIdx.x; s < HASH_SLOTS * NGRAD; s += blockDim.x) acc[s] = 0.0f;
+__host__ __device__ inline RegionGrid region_grid(int32_t h, int32_t w) {
+    return {(w + REGION_W - 1) / REGION_W, (h + REGION_H - 1) / REGION_H};
+}
+
+__device__ __forceinline__ uint32_t slot_hash(uint32_t id) { return (id * 2654435761u) >> 24; }  // 8 bits
+
+// home region of a site from its prepared position (same arithmetic in both kernels)
+__device__ __forceinline__ void home_region(float x, float y, RegionGrid rg, int& hx, int& hy) {
+    hx = min(max((int)floorf(x * (1.0f / REGION_W)), 0), rg.rgx - 1);
+    hy = min(max((int)floorf(y * (1.0f / REGION_H)), 0), rg.rgy - 1);
+}
+
+struct BwdArgs {
+    PixArgs p;
+    RegionGrid rg;
+    uint32_t* tkeys;  // [regions][SLOTS]
+    float* tvals;     // [regions][SLOTS][NGRAD]
+    float fix_scale;  // 2^E
+    double fix_inv;   // 2^-E
+};
+
+// x (already scaled to fixed point, |x| < 2^53) as a two's-complement 64-bit
+// integer, truncated toward zero.  Below 2^31 a 32-bit conversion does it.
+// From 2^31 up, x is a multiple of 2^8, so x - hi 2^32 with hi = floor(x 2^-32)
+// is a multiple of 2^8 below 2^32 and exactly representable: the split is exact.
+__device__ __forceinline__ unsigned long long to_fixed(float x) {
+    const long long small = (long long)(int32_t)x;
+    const float hi = floorf(x * 0x1p-32f);
+    const float lo = __builtin_fmaf(hi, -0x1p32f, x);
+    const long long big = (long long)(int32_t)hi * 4294967296ll + (long long)(uint32_t)lo;
+    return (unsigned long long)(fabsf(x) < 0x1p31f ? small : big);
+}
+
+__global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
+    __shared__ uint32_t keys[SLOTS];
+    __shared__ unsigned long long acc[NGRAD * SLOTS];
+    __shared__ float wsum[REGION_WAVES];
+    const PixArgs& a = b.p;
+
+    for (int s = threadIdx.x; s < SLOTS; s += blockDim.x) keys[s] = EMPTY;
+    for (int s = threadIdx.x; s < NGRAD * SLOTS; s += blockDim.x) acc[s] = 0ull;
     __syncthreads();
 
-    int i, j;
-    const bool inside = tile_pixel(a, i, j);
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    const int rx = blockIdx.x % b.rg.rgx, ry = blockIdx.x / b.rg.rgx;
+    const int tx = rx * RT_X + (wv % RT_X), ty = ry * RT_Y + (wv / RT_X);
+    const int i = tx * TILE + (lane & (TILE - 1)), j = ty * TILE + (lane / TILE);
+    const bool inside = i < a.w && j < a.h;
     float lsum = 0.0f;
     if (inside) {
         const size_t p = (size_t)j * a.w + i;
         const float px = (float)i + 0.5f, py = (float)j + 0.5f;
         const uint4* l = reinterpret_cast<const uint4*>(a.topk + p * K);
+        // Each lane visits its entries starting at its own offset (anti-diagonal
+        // of the tile), so neighbouring pixels with the same list add to
+        // different sites at each step instead of piling onto one LDS address.
+        uint4 l0 = l[0], l1 = l[1];
+        rotate_list(l0, l1, (lane + (lane >> 3)) & (K - 1));
         PointEval pe;
-        eval_point(a.derived, (uint32_t)a.n, l[0], l[1], px, py, pe);
+        eval_point(a.derived, (uint32_t)a.n, l0, l1, px, py, pe);
         float g[3];
 #pragma unroll
         for (int ch = 0; ch < 3; ++ch) {
@@ -161,11 +255,10 @@ __global__ __launch_bounds__(256) void k_render_bwd(PixArgs a) {
                 t[8] = -kap2 * aa * aa;
                 t[9] = -kap2 * bb * bb;
             }
-            // find or claim the site's slot
-            uint32_t h = (id * 2654435761u) >> 23;  // 9-bit multiplicative hash
+            const uint32_t h0 = slot_hash(id);
             int slot = -1;
-            for (int pr = 0; pr < HASH_PROBES; ++pr) {
-                const uint32_t s = (h + pr) & (HASH_SLOTS - 1);
+            for (int pr = 0; pr < REGION_PROBES; ++pr) {
+                const uint32_t s = (h0 + pr) & (SLOTS - 1);
                 uint32_t cur = keys[s];
                 if (cur == EMPTY) cur = atomicCAS(&keys[s], EMPTY, id);
                 if (cur == EMPTY || cur == id) {
@@ -173,30 +266,93 @@ __global__ __launch_bounds__(256) void k_render_bwd(PixArgs a) {
                     break;
                 }
             }
-            if (slot >= 0) {
 #pragma unroll
-                for (int q2 = 0; q2 < NGRAD; ++q2) atomicAdd(&acc[slot * NGRAD + q2], t[q2]);
-            } else {
-#pragma unroll
-                for (int q2 = 0; q2 < NGRAD; ++q2) unsafeAtomicAdd(&a.grad[(size_t)id * REC + q2], t[q2]);
+            for (int q2 = 0; q2 < NGRAD; ++q2) {
+                const float x = t[q2] * b.fix_scale;
+                if (slot >= 0 && fabsf(x) < FIX_LIMIT)
+                    atomicAdd(&acc[q2 * SLOTS + slot], to_fixed(x));
+                else
+                    unsafeAtomicAdd(&a.grad[(size_t)id * REC + q2], t[q2]);
             }
         }
     }
     if (a.loss) {
-        float ws = wave_sum(lsum);
-        if ((threadIdx.x & (WAVE - 1)) == 0) wsum[threadIdx.x / WAVE] = ws;
+        const float ws = wave_sum(lsum);
+        if (lane == 0) wsum[wv] = ws;
     }
     __syncthreads();
-    for (int s = threadIdx.x; s < HASH_SLOTS; s += blockDim.x) {
+    // publish the region's table
+    const int region = blockIdx.x;
+    for (int s = threadIdx.x; s < SLOTS; s += blockDim.x) {
         const uint32_t id = keys[s];
-        if (id == EMPTY) continue;
+        uint32_t key = id;
+        if (id != EMPTY) {
+            float v[NGRAD];
 #pragma unroll
-        for (int q2 = 0; q2 < NGRAD; ++q2) unsafeAtomicAdd(&a.grad[(size_t)id * REC + q2], acc[s * NGRAD + q2]);
+            for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] = (float)((double)(long long)acc[q2 * SLOTS + s] * b.fix_inv);
+            const float4 g0 = reinterpret_cast<const float4*>(a.derived + (size_t)id * REC)[0];
+            int hx, hy;
+            home_region(g0.x, g0.y, b.rg, hx, hy);
+            if (abs(hx - rx) <= 1 && abs(hy - ry) <= 1) {
+                float* dst = b.tvals + ((size_t)region * SLOTS + s) * NGRAD;
+#pragma unroll
+                for (int q2 = 0; q2 < NGRAD; ++q2) dst[q2] = v[q2];
+            } else {
+                key = PLACEHOLDER;
+#pragma unroll
+                for (int q2 = 0; q2 < NGRAD; ++q2) unsafeAtomicAdd(&a.grad[(size_t)id * REC + q2], v[q2]);
+            }
+        }
+        b.tkeys[(size_t)region * SLOTS + s] = key;
     }
     if (a.loss && threadIdx.x == 0) {
         float tot = 0.0f;
-        for (int k = 0; k < (int)(blockDim.x / WAVE); ++k) tot += wsum[k];
+        for (int k = 0; k < REGION_WAVES; ++k) tot += wsum[k];
         unsafeAtomicAdd(a.loss, tot * a.inv_p);
+    }
+}
+
+// Every active site adds the entries of the 9 region tables around its home.
+__global__ __launch_bounds__(256) void k_grad_gather(const float* __restrict__ derived, int32_t n, RegionGrid rg,
+                                                     const uint32_t* __restrict__ tkeys,
+                                                     const float* __restrict__ tvals, float* __restrict__ grad) {
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= n) return;
+    const float4 g0 = reinterpret_cast<const float4*>(derived + (size_t)s * REC)[0];
+    if (!(g0.x >= 0.0f)) return;
+    int hx, hy;
+    home_region(g0.x, g0.y, rg, hx, hy);
+    const uint32_t h0 = slot_hash((uint32_t)s);
+    float v[NGRAD];
+#pragma unroll
+    for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] = 0.0f;
+    bool any = false;
+    for (int dy = -1; dy <= 1; ++dy) {
+        const int ry = hy + dy;
+        if (ry < 0 || ry >= rg.rgy) continue;
+        for (int dx = -1; dx <= 1; ++dx) {
+            const int rx = hx + dx;
+            if (rx < 0 || rx >= rg.rgx) continue;
+            const size_t region = (size_t)ry * rg.rgx + rx;
+            const uint32_t* kk = tkeys + region * SLOTS;
+            for (int pr = 0; pr < REGION_PROBES; ++pr) {
+                const uint32_t slot = (h0 + pr) & (SLOTS - 1);
+                const uint32_t key = kk[slot];
+                if (key == (uint32_t)s) {
+                    const float* src = tvals + (region * SLOTS + slot) * NGRAD;
+#pragma unroll
+                    for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] += src[q2];
+                    any = true;
+                    break;
+                }
+                if (key == EMPTY) break;
+            }
+        }
+    }
+    if (any) {
+        float* gr = grad + (size_t)s * REC;
+#pragma unroll
+        for (int q2 = 0; q2 < NGRAD; ++q2) gr[q2] += v[q2];
     }
 }
 
@@ -266,22 +422,44 @@ extern "C" int sad_render_fwd(const float* derived, int32_t n, int32_t h, int32_
     return launch_status();
 }
 
+extern "C" size_t sad_render_bwd_workspace_bytes(int32_t h, int32_t w) {
+    if (!image_ok(h, w)) return 0;
+    const RegionGrid rg = region_grid(h, w);
+    return (size_t)rg.rgx * rg.rgy * SLOTS * (sizeof(uint32_t) + NGRAD * sizeof(float));
+}
+
 extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
-                              const float* target, float* grad, float* loss, float* image, void* stream) {
+                              const float* target, float* grad, float* loss, float* image, void* workspace,
+                              size_t workspace_bytes, void* stream) {
     int st = pix_common(derived, n, h, w, topk);
     if (st != SAD_OK) return st;
     const int64_t pix = int64_t(h) * w;
     if (!array_ok(target, pix, 4) || !array_ok(grad, n, 16)) return SAD_EINVAL;
     if ((loss && !aligned(loss, 4)) || (image && !aligned(image, 4))) return SAD_EINVAL;
     if (overlap(grad, int64_t(n) * REC * 4, derived, int64_t(n) * REC * 4)) return SAD_EINVAL;
+    const size_t need = sad_render_bwd_workspace_bytes(h, w);
+    if (pix > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)) return SAD_EINVAL;
+    if (overlap(workspace, (int64_t)need, grad, int64_t(n) * REC * 4)) return SAD_EINVAL;
     if (pix == 0) return SAD_OK;
-    PixArgs a = pix_args(derived, n, h, w, topk);
-    a.target = target;
-    a.grad = grad;
-    a.loss = loss;
-    a.image = image;
+    BwdArgs b;
+    b.p = pix_args(derived, n, h, w, topk);
+    b.p.target = target;
+    b.p.grad = grad;
+    b.p.loss = loss;
+    b.p.image = image;
+    b.rg = region_grid(h, w);
+    const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
+    b.tkeys = reinterpret_cast<uint32_t*>(workspace);
+    b.tvals = reinterpret_cast<float*>(b.tkeys + nreg * SLOTS);
+    int e = 45;  // 2^E = 2^45 * (smallest power of two >= h*w)
+    while ((int64_t(1) << (e - 45)) < pix) ++e;
+    b.fix_scale = ldexpf(1.0f, e);
+    b.fix_inv = ldexp(1.0, -e);
     clear_error();
-    hipLaunchKernelGGL(k_render_bwd, dim3((a.n_tiles + 3) / 4), dim3(256), 0, as_stream(stream), a);
+    hipLaunchKernelGGL(k_render_bwd, dim3((unsigned)nreg), dim3(WAVE * REGION_WAVES), 0, as_stream(stream), b);
+    if (n > 0)
+        hipLaunchKernelGGL(k_grad_gather, dim3((n + 255) / 256), dim3(256), 0, as_stream(stream), derived, n, b.rg,
+                           b.tkeys, b.tvals, grad);
     return launch_status();
 }
 

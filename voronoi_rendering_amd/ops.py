@@ -84,8 +84,24 @@ def render_fwd(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, image:
     return image
 
 
+_workspaces: dict = {}
+
+
+def bwd_workspace(h: int, w: int, device) -> torch.Tensor:
+    """A per-device scratch buffer for render_bwd, grown on demand and reused.
+    Calls that share it must be ordered (one stream, or explicit waits)."""
+    need = int(_native.lib().sad_render_bwd_workspace_bytes(h, w))
+    dev = torch.device(device)
+    ws = _workspaces.get(dev)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        _workspaces[dev] = ws
+    return ws
+
+
 def render_bwd(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target: torch.Tensor, grad: torch.Tensor,
-               loss: torch.Tensor | None = None, image: torch.Tensor | None = None) -> None:
+               loss: torch.Tensor | None = None, image: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> None:
     """Accumulate the loss gradient into ``grad`` ([n][12]); optionally add the
     loss into ``loss`` (one float32) and write the rendered image."""
     n = derived.shape[0]
@@ -97,8 +113,11 @@ def render_bwd(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target
         _need(loss, "loss", torch.float32, (1,))
     if image is not None:
         _need(image, "image", torch.float32, (h, w, 3))
+    if workspace is None:
+        workspace = bwd_workspace(h, w, derived.device)
     st = _native.lib().sad_render_bwd(_ptr(derived), n, h, w, _ptr(topk), _ptr(target), _ptr(grad), _ptr(loss),
-                                      _ptr(image), _stream(derived))
+                                      _ptr(image), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(derived))
     _native.check("sad_render_bwd", st)
 
 
