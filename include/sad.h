@@ -120,17 +120,26 @@ int sad_prepare_sites(const float *params, int32_t n, float *derived, void *stre
  * Probe id j of tile T in pass t: z = SplitMix64 output for counter
  *   c = t << 32 | T << 6 | j, i.e. z = mix(seed + (c + 1) * 0x9E3779B97F4A7C15)
  *   with SplitMix64's finaliser mix; id = ((z >> 32) * n) >> 32.
- *   derived     [n][12] prepared sites
- *   topk_prev   [h][w][8], or NULL for an all-empty previous map
- *   topk_next   [h][w][8], written; must not overlap topk_prev
- *   stride      jump step, >= 1 (Sec. 4.3 schedule B/2, ..., 1, then 1)
- *   seed        injection seed; pass_index: the pass counter t
+ *   derived      [n][12] prepared sites
+ *   topk_prev    [h][w][8], or NULL for an all-empty previous map
+ *   scores_prev  NULL, or [h][w][8] float32: the logits of topk_prev's entries
+ *                under `derived` exactly as the logit formula gives them, as
+ *                written to scores_next by the pass that produced topk_prev
+ *                with the same prepared sites.  It saves recomputing them; a
+ *                score map made before the sites changed gives wrong lists.
+ *                Requires topk_prev.
+ *   topk_next    [h][w][8], written
+ *   scores_next  NULL, or [h][w][8] float32 written with the logits of
+ *                topk_next's entries (-inf for empty slots)
+ *   No two of the four maps may overlap.
+ *   stride       jump step, >= 1 (Sec. 4.3 schedule B/2, ..., 1, then 1)
+ *   seed         injection seed; pass_index: the pass counter t
  *   inject_per_tile  0..64 probe ids per tile per pass
  * Limit: ceil(h/8) * ceil(w/8) <= 2^26 tiles.
  */
 int sad_propagate_topk(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk_prev,
-                       uint32_t *topk_next, int32_t stride, uint64_t seed, uint32_t pass_index,
-                       int32_t inject_per_tile, void *stream);
+                       const float *scores_prev, uint32_t *topk_next, float *scores_next, int32_t stride,
+                       uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, void *stream);
 
 /*
  * Soft additively weighted render (Sec. 4.2): per pixel, the softmax of the

@@ -61,12 +61,13 @@ def test_prepare_rejects(lib):
 
 def test_propagate_rejects(lib):
     f = lib.sad_propagate_topk
-    ok = dict(derived=P, n=10, h=8, w=8, prev=None, nxt=P + 4096, stride=1, seed=0, pi=0, inj=64)
+    ok = dict(derived=P, n=10, h=8, w=8, prev=None, sprev=None, nxt=P + 4096, snext=None, stride=1, seed=0, pi=0,
+              inj=64)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["derived"], a["n"], a["h"], a["w"], a["prev"], a["nxt"], a["stride"], a["seed"], a["pi"],
-                 a["inj"], None)
+        return f(a["derived"], a["n"], a["h"], a["w"], a["prev"], a["sprev"], a["nxt"], a["snext"], a["stride"],
+                 a["seed"], a["pi"], a["inj"], None)
 
     assert call(stride=0) == EINVAL
     assert call(n=-1) == EINVAL
@@ -79,6 +80,10 @@ def test_propagate_rejects(lib):
     assert call(prev=P + 4096) == EINVAL  # in place
     assert call(prev=P + 4096 + 32 * 8) == EINVAL  # overlapping
     assert call(nxt=P + 4100) == EINVAL  # misaligned
+    assert call(sprev=P + 65536) == EINVAL  # scores without a previous map
+    assert call(prev=P + 65536, sprev=P + 65536) == EINVAL  # scores alias the map
+    assert call(snext=P + 4096) == EINVAL  # the two outputs alias
+    assert call(snext=P + 65540) == EINVAL  # misaligned scores
     assert call(h=0, nxt=None) == 0  # empty image
 
 

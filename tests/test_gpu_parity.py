@@ -140,6 +140,35 @@ def test_propagate_c2_full_map(c2_state):
     assert np.array_equal(got, m_ref), f"{(got != m_ref).any(-1).sum()} pixels differ"
 
 
+def test_propagate_with_score_maps(sad, ref, c2_state):
+    """Passes chained through score maps (the previous pass's logits reused)
+    give the oracle's lists bit for bit, and the score map holds exactly the
+    float32 logits of the listed sites."""
+    wl, p, d, dg, m_ref, m_gpu = c2_state
+    strides = (8, 4, 2, 1, 1)
+    cur = m_gpu
+    sc = None
+    for t, s in enumerate(strides):
+        out_s = torch.empty((wl.h, wl.w, 8), dtype=torch.float32, device=dev())
+        cur = sad.propagate_topk(dg, wl.h, wl.w, cur, stride=s, seed=7, pass_index=500 + t, inject=64,
+                                 prev_scores=sc, out_scores=out_s)
+        sc = out_s
+    want = ref.propagate_schedule(d, wl.h, wl.w, m_ref, strides, 7, 500, 64)
+    got = map_to_np(cur)
+    assert np.array_equal(got, want), f"{(got != want).any(-1).sum()} pixels differ"
+    scores = to_np(sc)
+    rng = np.random.default_rng(2)
+    for pix in rng.choice(wl.h * wl.w, 300, replace=False):
+        j, i = divmod(int(pix), wl.w)
+        for k in range(8):
+            sid = int(got[j, i, k])
+            if sid == 0xFFFFFFFF:
+                assert scores[j, i, k] == -np.inf
+            else:
+                assert np.float32(ref.score(d, sid, i + 0.5, j + 0.5)).view(np.uint32) == \
+                    scores[j, i, k].view(np.uint32)
+
+
 def test_propagate_is_deterministic(sad, c2_state):
     wl, p, d, dg, m_ref, m_gpu = c2_state
     a = sad.propagate_topk(dg, wl.h, wl.w, m_gpu, stride=1, seed=1, pass_index=99, inject=64)

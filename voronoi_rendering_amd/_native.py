@@ -22,7 +22,8 @@ _SIGS = {
     "sad_status_string": (C.c_char_p, [C.c_int]),
     "sad_prepare_sites": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
     "sad_propagate_topk": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
-                                     C.c_int32, C.c_uint64, C.c_uint32, C.c_int32, C.c_void_p]),
+                                     C.c_void_p, C.c_void_p, C.c_int32, C.c_uint64, C.c_uint32, C.c_int32,
+                                     C.c_void_p]),
     "sad_render_fwd": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p]),
     "sad_render_bwd_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),

@@ -31,7 +31,9 @@ namespace sad {
 struct PropArgs {
     const float* derived;
     const uint32_t* prev;
+    const float* prev_scores;  // nullable: logits of prev's entries under derived
     uint32_t* next;
+    float* next_scores;        // nullable: logits of next's entries are written here
     uint64_t seed;
     int32_t n, h, w, stride, inject, tiles_x, n_tiles;
     uint32_t pass_index;
@@ -125,6 +127,7 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
     // Issue every independent load first: the pixel's list, the 4 neighbour
     // lists and this lane's probe site.
     uint32_t own[K];
+    float own_s[K];
     uint32_t nbr[4][K];
 #pragma unroll
     for (int k = 0; k < K; ++k) own[k] = EMPTY;
@@ -137,6 +140,12 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
         const uint4 l0 = l[0], l1 = l[1];
         own[0] = l0.x; own[1] = l0.y; own[2] = l0.z; own[3] = l0.w;
         own[4] = l1.x; own[5] = l1.y; own[6] = l1.z; own[7] = l1.w;
+        if (a.prev_scores) {
+            const float4* ls = reinterpret_cast<const float4*>(a.prev_scores + ((size_t)j * a.w + i) * K);
+            const float4 s0 = ls[0], s1 = ls[1];
+            own_s[0] = s0.x; own_s[1] = s0.y; own_s[2] = s0.z; own_s[3] = s0.w;
+            own_s[4] = s1.x; own_s[5] = s1.y; own_s[6] = s1.z; own_s[7] = s1.w;
+        }
         const int nb[4][2] = {{a.stride, 0}, {-a.stride, 0}, {0, a.stride}, {0, -a.stride}};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -157,15 +166,26 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
         pg = load_geo(a.derived, pid);
     }
 
-    // 1. the pixel's previous list, in ranking order
+    // 1. the pixel's previous list, in ranking order (its logits come from the
+    //    caller's score map when the sites have not changed since it was made)
     TopK t;
     t.clear();
+    if (a.prev_scores) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const float s = site_logit(a.derived, n, own[k], px, py);
-        if (s == s) {
-            t.s[k] = s;
-            t.id[k] = own[k];
+        for (int k = 0; k < K; ++k) {
+            if (have_prev && own[k] < n && own_s[k] == own_s[k]) {
+                t.s[k] = own_s[k];
+                t.id[k] = own[k];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float s = site_logit(a.derived, n, own[k], px, py);
+            if (s == s) {
+                t.s[k] = s;
+                t.id[k] = own[k];
+            }
         }
     }
     bool ordered = true;
@@ -261,6 +281,11 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
         uint4* o = reinterpret_cast<uint4*>(a.next + ((size_t)j * a.w + i) * K);
         o[0] = make_uint4(t.id[0], t.id[1], t.id[2], t.id[3]);
         o[1] = make_uint4(t.id[4], t.id[5], t.id[6], t.id[7]);
+        if (a.next_scores) {
+            float4* os = reinterpret_cast<float4*>(a.next_scores + ((size_t)j * a.w + i) * K);
+            os[0] = make_float4(t.s[0], t.s[1], t.s[2], t.s[3]);
+            os[1] = make_float4(t.s[4], t.s[5], t.s[6], t.s[7]);
+        }
     }
 }
 
@@ -269,21 +294,33 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
 using namespace sad;
 
 extern "C" int sad_propagate_topk(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk_prev,
-                                  uint32_t* topk_next, int32_t stride, uint64_t seed, uint32_t pass_index,
-                                  int32_t inject_per_tile, void* stream) {
+                                  const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride,
+                                  uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, void* stream) {
     if (!sites_ok(n) || !image_ok(h, w) || stride < 1 || inject_per_tile < 0) return SAD_EINVAL;
     if (inject_per_tile > SAD_MAX_INJECT) return SAD_EUNSUPPORTED;
     const int64_t pix = int64_t(h) * w;
+    const int64_t mbytes = pix * K * 4;
     if (!array_ok(derived, n, 16) || !array_ok(topk_next, pix, 16)) return SAD_EINVAL;
-    if (topk_prev && !aligned(topk_prev, 16)) return SAD_EINVAL;
-    if (overlap(topk_prev, pix * K * 4, topk_next, pix * K * 4)) return SAD_EINVAL;
+    if ((topk_prev && !aligned(topk_prev, 16)) || (scores_prev && !aligned(scores_prev, 16)) ||
+        (scores_next && !aligned(scores_next, 16)))
+        return SAD_EINVAL;
+    if (scores_prev && !topk_prev) return SAD_EINVAL;
+    const void* outs[2] = {topk_next, scores_next};
+    const void* ins[2] = {topk_prev, scores_prev};
+    for (int o = 0; o < 2; ++o)
+        for (int q = 0; q < 2; ++q)
+            if (overlap(outs[o], mbytes, ins[q], mbytes)) return SAD_EINVAL;
+    if (overlap(topk_next, mbytes, scores_next, mbytes) || overlap(topk_prev, mbytes, scores_prev, mbytes))
+        return SAD_EINVAL;
     const int64_t ntiles = int64_t(tiles_x(w)) * tiles_y(h);
     if (ntiles > MAX_TILES) return SAD_EINVAL;
     if (pix == 0) return SAD_OK;
     PropArgs a;
     a.derived = derived;
     a.prev = topk_prev;
+    a.prev_scores = scores_prev;
     a.next = topk_next;
+    a.next_scores = scores_next;
     a.seed = seed;
     a.n = n;
     a.h = h;

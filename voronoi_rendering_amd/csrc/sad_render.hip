@@ -172,7 +172,8 @@ __device__ __forceinline__ void home_region(float x, float y, RegionGrid rg, int
 struct BwdArgs {
     PixArgs p;
     RegionGrid rg;
-    uint32_t* tkeys;  // [regions][SLOTS]
+    uint32_t* tkeys;  // [regions][SLOTS] site id, EMPTY or PLACEHOLDER
+    int32_t* thome;   // [regions][SLOTS] home region of the site (valid with a site id)
     float* tvals;     // [regions][SLOTS][NGRAD]
     float fix_scale;  // 2^E
     double fix_inv;   // 2^-E
@@ -297,6 +298,7 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
                 float* dst = b.tvals + ((size_t)region * SLOTS + s) * NGRAD;
 #pragma unroll
                 for (int q2 = 0; q2 < NGRAD; ++q2) dst[q2] = v[q2];
+                b.thome[(size_t)region * SLOTS + s] = hy * b.rg.rgx + hx;
             } else {
                 key = PLACEHOLDER;
 #pragma unroll
@@ -312,47 +314,74 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
     }
 }
 
-// Every active site adds the entries of the 9 region tables around its home.
-__global__ __launch_bounds__(256) void k_grad_gather(const float* __restrict__ derived, int32_t n, RegionGrid rg,
-                                                     const uint32_t* __restrict__ tkeys,
-                                                     const float* __restrict__ tvals, float* __restrict__ grad) {
-    const int s = blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= n) return;
-    const float4 g0 = reinterpret_cast<const float4*>(derived + (size_t)s * REC)[0];
-    if (!(g0.x >= 0.0f)) return;
-    int hx, hy;
-    home_region(g0.x, g0.y, rg, hx, hy);
-    const uint32_t h0 = slot_hash((uint32_t)s);
-    float v[NGRAD];
+// One workgroup per region R: it reads the tables of the 3 x 3 regions
+// around R (coalesced), keeps the entries whose site has its home in R, sums
+// them per site in LDS, table by table in a fixed order, and adds each sum to
+// the site's gradient record.  Every site with contributions in the tables
+// has exactly one home, so exactly one workgroup updates it, without atomics;
+// the result does not depend on scheduling.
+constexpr int GATHER_SLOTS = 512;
+
+__global__ __launch_bounds__(SLOTS) void k_grad_gather(RegionGrid rg, const uint32_t* __restrict__ tkeys,
+                                                       const int32_t* __restrict__ thome,
+                                                       const float* __restrict__ tvals, float* __restrict__ grad) {
+    __shared__ uint32_t gkeys[GATHER_SLOTS];
+    __shared__ float gacc[GATHER_SLOTS * NGRAD];
+    const int R = blockIdx.x;
+    const int rx = R % rg.rgx, ry = R / rg.rgx;
+    for (int s = threadIdx.x; s < GATHER_SLOTS; s += blockDim.x) gkeys[s] = EMPTY;
+    for (int s = threadIdx.x; s < GATHER_SLOTS * NGRAD; s += blockDim.x) gacc[s] = 0.0f;
+    // this thread's slot in each of the 9 tables: keys and homes loaded up front
+    uint32_t key[9];
+    int table[9];
 #pragma unroll
-    for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] = 0.0f;
-    bool any = false;
-    for (int dy = -1; dy <= 1; ++dy) {
-        const int ry = hy + dy;
-        if (ry < 0 || ry >= rg.rgy) continue;
-        for (int dx = -1; dx <= 1; ++dx) {
-            const int rx = hx + dx;
-            if (rx < 0 || rx >= rg.rgx) continue;
-            const size_t region = (size_t)ry * rg.rgx + rx;
-            const uint32_t* kk = tkeys + region * SLOTS;
-            for (int pr = 0; pr < REGION_PROBES; ++pr) {
-                const uint32_t slot = (h0 + pr) & (SLOTS - 1);
-                const uint32_t key = kk[slot];
-                if (key == (uint32_t)s) {
-                    const float* src = tvals + (region * SLOTS + slot) * NGRAD;
-#pragma unroll
-                    for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] += src[q2];
-                    any = true;
-                    break;
-                }
-                if (key == EMPTY) break;
-            }
+    for (int t = 0; t < 9; ++t) {
+        const int tx = rx + (t % 3) - 1, ty = ry + (t / 3) - 1;
+        table[t] = (tx >= 0 && tx < rg.rgx && ty >= 0 && ty < rg.rgy) ? ty * rg.rgx + tx : -1;
+        key[t] = EMPTY;
+        if (table[t] >= 0) {
+            const size_t e = (size_t)table[t] * SLOTS + threadIdx.x;
+            const uint32_t k = tkeys[e];
+            if (k < PLACEHOLDER && thome[e] == R) key[t] = k;
         }
     }
-    if (any) {
-        float* gr = grad + (size_t)s * REC;
+    __syncthreads();
+    for (int t = 0; t < 9; ++t) {
+        if (key[t] != EMPTY) {
+            const uint32_t id = key[t];
+            const float* src = tvals + ((size_t)table[t] * SLOTS + threadIdx.x) * NGRAD;
+            float v[NGRAD];
 #pragma unroll
-        for (int q2 = 0; q2 < NGRAD; ++q2) gr[q2] += v[q2];
+            for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] = src[q2];
+            int slot = -1;
+            const uint32_t h0 = (id * 2654435761u) >> 23;  // 9 bits
+            for (int pr = 0; pr < GATHER_SLOTS; ++pr) {
+                const uint32_t sl = (h0 + pr) & (GATHER_SLOTS - 1);
+                uint32_t cur = gkeys[sl];
+                if (cur == EMPTY) cur = atomicCAS(&gkeys[sl], EMPTY, id);
+                if (cur == EMPTY || cur == id) {
+                    slot = (int)sl;
+                    break;
+                }
+            }
+            // within one table a site occupies one slot, so this thread is the
+            // only writer of the slot until the next barrier
+            if (slot >= 0) {
+#pragma unroll
+                for (int q2 = 0; q2 < NGRAD; ++q2) gacc[slot * NGRAD + q2] += v[q2];
+            } else {
+#pragma unroll
+                for (int q2 = 0; q2 < NGRAD; ++q2) unsafeAtomicAdd(&grad[(size_t)id * REC + q2], v[q2]);
+            }
+        }
+        __syncthreads();
+    }
+    for (int s = threadIdx.x; s < GATHER_SLOTS; s += blockDim.x) {
+        const uint32_t id = gkeys[s];
+        if (id == EMPTY) continue;
+        float* gr = grad + (size_t)id * REC;
+#pragma unroll
+        for (int q2 = 0; q2 < NGRAD; ++q2) gr[q2] += gacc[s * NGRAD + q2];
     }
 }
 
@@ -425,7 +454,7 @@ extern "C" int sad_render_fwd(const float* derived, int32_t n, int32_t h, int32_
 extern "C" size_t sad_render_bwd_workspace_bytes(int32_t h, int32_t w) {
     if (!image_ok(h, w)) return 0;
     const RegionGrid rg = region_grid(h, w);
-    return (size_t)rg.rgx * rg.rgy * SLOTS * (sizeof(uint32_t) + NGRAD * sizeof(float));
+    return (size_t)rg.rgx * rg.rgy * SLOTS * (2 * sizeof(uint32_t) + NGRAD * sizeof(float));
 }
 
 extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
@@ -450,16 +479,16 @@ extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_
     b.rg = region_grid(h, w);
     const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
     b.tkeys = reinterpret_cast<uint32_t*>(workspace);
-    b.tvals = reinterpret_cast<float*>(b.tkeys + nreg * SLOTS);
+    b.thome = reinterpret_cast<int32_t*>(b.tkeys + nreg * SLOTS);
+    b.tvals = reinterpret_cast<float*>(b.thome + nreg * SLOTS);
     int e = 45;  // 2^E = 2^45 * (smallest power of two >= h*w)
     while ((int64_t(1) << (e - 45)) < pix) ++e;
     b.fix_scale = ldexpf(1.0f, e);
     b.fix_inv = ldexp(1.0, -e);
     clear_error();
     hipLaunchKernelGGL(k_render_bwd, dim3((unsigned)nreg), dim3(WAVE * REGION_WAVES), 0, as_stream(stream), b);
-    if (n > 0)
-        hipLaunchKernelGGL(k_grad_gather, dim3((n + 255) / 256), dim3(256), 0, as_stream(stream), derived, n, b.rg,
-                           b.tkeys, b.tvals, grad);
+    hipLaunchKernelGGL(k_grad_gather, dim3((unsigned)nreg), dim3(SLOTS), 0, as_stream(stream), b.rg, b.tkeys, b.thome,
+                       b.tvals, grad);
     return launch_status();
 }
 

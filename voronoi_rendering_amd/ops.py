@@ -56,17 +56,25 @@ def empty_map(h: int, w: int, device="cuda") -> torch.Tensor:
 
 
 def propagate_topk(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor | None = None,
-                   *, stride: int, seed: int, pass_index: int, inject: int = 64) -> torch.Tensor:
+                   *, stride: int, seed: int, pass_index: int, inject: int = 64,
+                   prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None) -> torch.Tensor:
+    """One propagation pass.  ``prev_scores`` (optional) must hold the logits of
+    ``prev``'s entries under ``derived`` as a previous pass wrote them to its
+    ``out_scores``; pass it only while the sites are unchanged."""
     n = derived.shape[0]
     _need(derived, "derived", torch.float32, (n, REC))
     if prev is not None:
         _need(prev, "prev", torch.int32, (h, w, K))
+    if prev_scores is not None:
+        _need(prev_scores, "prev_scores", torch.float32, (h, w, K))
     if out is None:
         out = torch.empty((h, w, K), dtype=torch.int32, device=derived.device)
     _need(out, "out", torch.int32, (h, w, K))
-    st = _native.lib().sad_propagate_topk(_ptr(derived), n, h, w, _ptr(prev), _ptr(out), int(stride),
-                                          int(seed) & 0xFFFFFFFFFFFFFFFF, int(pass_index) & 0xFFFFFFFF, int(inject),
-                                          _stream(derived))
+    if out_scores is not None:
+        _need(out_scores, "out_scores", torch.float32, (h, w, K))
+    st = _native.lib().sad_propagate_topk(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
+                                          _ptr(out_scores), int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                          int(pass_index) & 0xFFFFFFFF, int(inject), _stream(derived))
     _native.check("sad_propagate_topk", st)
     return out
 

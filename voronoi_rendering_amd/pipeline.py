@@ -49,6 +49,9 @@ class SadField:
         self.m = torch.zeros_like(self.grad)
         self.v = torch.zeros_like(self.grad)
         self.maps = [ops.empty_map(self.h, self.w, dev), ops.empty_map(self.h, self.w, dev)]
+        # logits of each map's entries, valid while the sites do not change
+        self.scores = [torch.empty((self.h, self.w, ops.K), dtype=torch.float32, device=dev) for _ in range(2)]
+        self.scores_valid = False
         self.cur = 0
         self.pass_index = 0
         self.adam_t = 0
@@ -61,9 +64,16 @@ class SadField:
     def propagate(self, strides: Sequence[int]) -> None:
         for s in strides:
             ops.propagate_topk(self.derived, self.h, self.w, self.maps[self.cur], self.maps[1 - self.cur],
-                               stride=int(s), seed=self.seed, pass_index=self.pass_index, inject=self.inject)
+                               stride=int(s), seed=self.seed, pass_index=self.pass_index, inject=self.inject,
+                               prev_scores=self.scores[self.cur] if self.scores_valid else None,
+                               out_scores=self.scores[1 - self.cur])
             self.cur = 1 - self.cur
             self.pass_index += 1
+            self.scores_valid = True
+
+    def sites_changed(self) -> None:
+        """The prepared sites were rewritten: the cached logits are stale."""
+        self.scores_valid = False
 
     def warm(self, n_pass: int) -> None:
         """Fill the map from scratch with the warm-up jump schedule."""
@@ -82,6 +92,7 @@ class SadField:
         bc1, bc2 = bias_corrections(self.adam.beta1, self.adam.beta2, self.adam_t)
         ops.adam_step(self.params, self.grad, self.m, self.v, self.h, self.w, self.adam.lr, self.adam.beta1,
                       self.adam.beta2, self.adam.eps, bc1, bc2, self.derived)
+        self.sites_changed()
 
     def train_iter(self, strides: Sequence[int], target: torch.Tensor) -> None:
         self.step(strides, target)
