@@ -29,6 +29,13 @@ __device__ __forceinline__ Geo load_geo(const float* __restrict__ derived, uint3
     return g;
 }
 
+// Geometry of site id, or of site 0 when id is out of range (the caller then
+// discards the result); requires n >= 1.  The load does not depend on any
+// branch, so a batch of these can be in flight together.
+__device__ __forceinline__ Geo load_geo_clamped(const float* __restrict__ derived, uint32_t n, uint32_t id) {
+    return load_geo(derived, id < n ? id : 0u);
+}
+
 // Logit of Sec. 4.2, l = -tau (||x - p||_G - r), evaluated in float32 in the
 // documented order (the file is built without contraction; sqrtf is the
 // correctly rounded square root).
@@ -40,6 +47,13 @@ __device__ __forceinline__ float logit(const Geo& g, float px, float py) {
     float q = a * a + b * b;
     float d = __builtin_sqrtf(q) - g.g0.w;
     return -(g.g0.z * d);
+}
+
+// The logit of a loaded site, or NaN when the id was out of range or the site
+// is inactive (x < 0 or NaN).
+__device__ __forceinline__ float usable_logit(const Geo& g, bool in_range, float px, float py) {
+    const float s = logit(g, px, py);
+    return (in_range && g.g0.x >= 0.0f) ? s : __builtin_nanf("");
 }
 
 // (s1, i1) ranks before (s2, i2)
@@ -102,10 +116,22 @@ __device__ __forceinline__ uint32_t probe_id(uint64_t seed, uint32_t pass_index,
     return (uint32_t)(((z >> 32) * (uint64_t)n) >> 32);
 }
 
+// Minimum over the wavefront with DPP lane moves (no LDS round trips):
+// quad swaps, half-row and row mirrors, then the row broadcasts 15 and 31
+// fold rows together; lane 63 ends with the minimum of all 64 lanes.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off, WAVE));
-    return v;
+    v = fminf(v, dpp_f32<0xb1, 0xf>(v));   // quad_perm [1,0,3,2]
+    v = fminf(v, dpp_f32<0x4e, 0xf>(v));   // quad_perm [2,3,0,1]
+    v = fminf(v, dpp_f32<0x141, 0xf>(v));  // row_half_mirror
+    v = fminf(v, dpp_f32<0x140, 0xf>(v));  // row_mirror
+    v = fminf(v, dpp_f32<0x142, 0xa>(v));  // row_bcast:15 into rows 1 and 3
+    v = fminf(v, dpp_f32<0x143, 0xc>(v));  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

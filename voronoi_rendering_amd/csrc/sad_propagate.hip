@@ -43,13 +43,11 @@ constexpr int QCAP = 4 * K;  // queued neighbour ids per lane (4 lists of 8)
 constexpr int PBUF = 4;      // register buffer of candidates awaiting insertion
 constexpr int WAVES_PER_WG = 4;
 
-// Logit of site id at (px, py), or NaN when the id names no usable site.
+// Logit of site id at (px, py), or NaN when the id names no usable site
+// (requires n >= 1).
 __device__ __forceinline__ float site_logit(const float* __restrict__ derived, uint32_t n, uint32_t id, float px,
                                             float py) {
-    if (id >= n) return __builtin_nanf("");
-    Geo g = load_geo(derived, id);
-    if (!(g.g0.x >= 0.0f)) return __builtin_nanf("");
-    return logit(g, px, py);
+    return usable_logit(load_geo_clamped(derived, n, id), id < n, px, py);
 }
 
 // Can the probe site (geometry g) rank among the 8 best of any pixel of the
@@ -166,7 +164,25 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
         pg = load_geo(a.derived, pid);
     }
 
-    // 1. the pixel's previous list, in ranking order (its logits come from the
+    // 1. neighbour ids not already in the pixel's list go to this lane's queue
+    //    column (membership only needs the ids, so this runs before any logit
+    //    and the 32 neighbour ids stop occupying registers early)
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t v = nbr[q][k];
+            bool listed = false;
+#pragma unroll
+            for (int k2 = 0; k2 < K; ++k2) listed |= (own[k2] == v);
+            if (v < n && !listed) {
+                queue[wv][cnt][lane] = v;
+                ++cnt;
+            }
+        }
+
+    // 2. the pixel's previous list, in ranking order (its logits come from the
     //    caller's score map when the sites have not changed since it was made)
     TopK t;
     t.clear();
@@ -178,13 +194,20 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
                 t.id[k] = own[k];
             }
         }
-    } else {
+    } else if (n > 0) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const float s = site_logit(a.derived, n, own[k], px, py);
-            if (s == s) {
-                t.s[k] = s;
-                t.id[k] = own[k];
+        for (int half = 0; half < 2; ++half) {
+            Geo og[K / 2];
+#pragma unroll
+            for (int k = 0; k < K / 2; ++k) og[k] = load_geo_clamped(a.derived, n, own[half * 4 + k]);
+#pragma unroll
+            for (int k = 0; k < K / 2; ++k) {
+                const int kk = half * 4 + k;
+                const float s = usable_logit(og[k], own[kk] < n, px, py);
+                if (s == s) {
+                    t.s[kk] = s;
+                    t.id[kk] = own[kk];
+                }
             }
         }
     }
@@ -208,19 +231,6 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
         }
     }
 
-    // 2. neighbour ids not already listed go to this lane's queue column
-    int cnt = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const uint32_t v = nbr[q][k];
-            if (v < n && !in_list(t, v)) {
-                queue[wv][cnt][lane] = v;
-                ++cnt;
-            }
-        }
-
     // 3. score queued ids, QBATCH at a time; those that may enter wait in a
     //    register buffer and are inserted afterwards
     float bs[PBUF];
@@ -231,8 +241,11 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
         float sc[QBATCH];
 #pragma unroll
         for (int b = 0; b < QBATCH; ++b) v[b] = (it + b < cnt) ? queue[wv][it + b][lane] : EMPTY;
+        Geo qg[QBATCH];
 #pragma unroll
-        for (int b = 0; b < QBATCH; ++b) sc[b] = site_logit(a.derived, n, v[b], px, py);
+        for (int b = 0; b < QBATCH; ++b) qg[b] = load_geo_clamped(a.derived, n, v[b]);
+#pragma unroll
+        for (int b = 0; b < QBATCH; ++b) sc[b] = usable_logit(qg[b], v[b] < n, px, py);
 #pragma unroll
         for (int b = 0; b < QBATCH; ++b) {
             if (sc[b] == sc[b] && ranks_before(sc[b], v[b], t.s[K - 1], t.id[K - 1])) {
@@ -267,11 +280,21 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
         }
         uint64_t mask = __ballot(keep);
         while (mask) {
+            // the survivor's record is already in lane q's registers: broadcast it
             const int q = __builtin_ctzll(mask);
             mask &= mask - 1;
             const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)pid, q);
+            Geo g;
+            g.g0.x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g0.x), q));
+            g.g0.y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g0.y), q));
+            g.g0.z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g0.z), q));
+            g.g0.w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g0.w), q));
+            g.g1.x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.x), q));
+            g.g1.y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.y), q));
+            g.g1.z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.z), q));
+            g.g1.w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.w), q));
             if (inside) {
-                const float s = site_logit(a.derived, n, id, px, py);
+                const float s = logit(g, px, py);  // a survivor is an active site (checked above)
                 if (s == s) t.insert(s, id);
             }
         }

@@ -36,16 +36,21 @@ __device__ __forceinline__ void eval_point(const float* __restrict__ derived, ui
     for (int k = 0; k < K; ++k) {
         pe.id[k] = EMPTY;
         pe.l[k] = 0.0f;
-        uint32_t id = ids[k];
-        if (id >= nsites) continue;
-        Geo g = load_geo(derived, id);
-        if (!(g.g0.x >= 0.0f)) continue;
-        float s = logit(g, px, py);
-        if (!finitef(s)) continue;
-        pe.id[k] = id;
-        pe.l[k] = s;
-        mx = fmaxf(mx, s);
-        pe.n++;
+    }
+    if (nsites > 0) {
+        // all record loads first (clamped ids, no branches), then the logits
+        Geo g[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) g[k] = load_geo_clamped(derived, nsites, ids[k]);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float s = usable_logit(g[k], ids[k] < nsites, px, py);
+            if (!finitef(s)) continue;  // also drops NaN: unusable entries
+            pe.id[k] = ids[k];
+            pe.l[k] = s;
+            mx = fmaxf(mx, s);
+            pe.n++;
+        }
     }
     float z = 0.0f;
     pe.c[0] = pe.c[1] = pe.c[2] = 0.0f;
