@@ -43,6 +43,29 @@ def algorithmic_bytes(h: int, w: int, n: int, n_pass: int) -> dict:
     return {"propagate": prop, "render_bwd": bwd, "step": step}
 
 
+KERNEL_OF = {"propagate": "k_propagate", "render_bwd": "k_render_bwd"}
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch of the kernel from the committed rocprofv3 counter
+    summary (scaled FETCH_SIZE + WRITE_SIZE), or None when the kernel's sources
+    changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "hbm_counters_768x512.json")
+    try:
+        data = json.load(open(path))
+        rec = data["kernels"][KERNEL_OF[kind]]
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return int(rec["bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, budget_s: float) -> dict:
     """The oracle as it stands, timed on the host cores on whole C2 steps
     (4 passes + backward over the full image) until ~budget_s seconds."""
@@ -166,7 +189,7 @@ def main() -> int:
     dom = max(total, key=total.get)
     achieved = ab[dom] / avg[dom] / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom), "kernel": dom,
                 "kernel_us": round(avg[dom] * 1e6, 3),
                 "bytes_per_launch": ab[dom]}
     out = {
