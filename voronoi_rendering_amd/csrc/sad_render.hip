@@ -198,55 +198,153 @@ __device__ __forceinline__ unsigned long long to_fixed(float x) {
 
 __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
     __shared__ uint32_t keys[SLOTS];
+    __shared__ float4 recs[SLOTS * 3];  // prepared record of the site in each slot
     __shared__ unsigned long long acc[NGRAD * SLOTS];
     __shared__ float wsum[REGION_WAVES];
     const PixArgs& a = b.p;
+    const uint32_t n = (uint32_t)a.n;
 
     for (int s = threadIdx.x; s < SLOTS; s += blockDim.x) keys[s] = EMPTY;
     for (int s = threadIdx.x; s < NGRAD * SLOTS; s += blockDim.x) acc[s] = 0ull;
-    __syncthreads();
 
     const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
     const int rx = blockIdx.x % b.rg.rgx, ry = blockIdx.x / b.rg.rgx;
     const int tx = rx * RT_X + (wv % RT_X), ty = ry * RT_Y + (wv / RT_X);
     const int i = tx * TILE + (lane & (TILE - 1)), j = ty * TILE + (lane / TILE);
     const bool inside = i < a.w && j < a.h;
+    const size_t p = (size_t)j * a.w + i;
+    const float px = (float)i + 0.5f, py = (float)j + 0.5f;
+
+    // The pixel's list, each lane starting at its own offset (anti-diagonal of
+    // the tile) so that neighbouring pixels with the same list add to different
+    // sites at each step.
+    uint32_t ids[K];
+    float tg[3] = {0.f, 0.f, 0.f};
+    {
+        uint4 l0 = make_uint4(EMPTY, EMPTY, EMPTY, EMPTY), l1 = l0;
+        if (inside) {
+            const uint4* l = reinterpret_cast<const uint4*>(a.topk + p * K);
+            l0 = l[0];
+            l1 = l[1];
+            tg[0] = a.target[p * 3 + 0];
+            tg[1] = a.target[p * 3 + 1];
+            tg[2] = a.target[p * 3 + 2];
+        }
+        rotate_list(l0, l1, (lane + (lane >> 3)) & (K - 1));
+        ids[0] = l0.x; ids[1] = l0.y; ids[2] = l0.z; ids[3] = l0.w;
+        ids[4] = l1.x; ids[5] = l1.y; ids[6] = l1.z; ids[7] = l1.w;
+    }
+    __syncthreads();  // keys cleared
+
+    // 1. claim a slot for every listed site: all 8 probes of a lane go out
+    //    together, round by round, instead of one chain per entry
+    int slot[K], pos[K];
+    uint32_t pend = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        slot[k] = -1;
+        pos[k] = (int)slot_hash(ids[k]);
+        if (ids[k] < n) pend |= 1u << k;
+    }
+    for (int round = 0; round < REGION_PROBES && __any(pend != 0); ++round) {
+        uint32_t cur[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) cur[k] = ((pend >> k) & 1) ? keys[pos[k]] : 0u;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (((pend >> k) & 1) && cur[k] == EMPTY) cur[k] = atomicCAS(&keys[pos[k]], EMPTY, ids[k]);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (!((pend >> k) & 1)) continue;
+            if (cur[k] == EMPTY || cur[k] == ids[k]) {
+                slot[k] = pos[k];
+                pend &= ~(1u << k);
+            } else {
+                pos[k] = (pos[k] + 1) & (SLOTS - 1);
+            }
+        }
+    }
+    __syncthreads();
+
+    // 2. every claimed site's record is read from memory once, into LDS
+    for (int s = threadIdx.x; s < SLOTS; s += blockDim.x) {
+        const uint32_t id = keys[s];
+        if (id == EMPTY) continue;
+        const float4* r = reinterpret_cast<const float4*>(a.derived + (size_t)id * REC);
+        recs[s * 3 + 0] = r[0];
+        recs[s * 3 + 1] = r[1];
+        recs[s * 3 + 2] = r[2];
+    }
+    __syncthreads();
+
+    // 3. forward and backward of the pixel, records from LDS (an entry whose
+    //    probe chain ran out reads its record from memory)
+    // part q (0: x y tau r, 1: cos sin 1/s1 1/s2, 2: colour) of entry k's record
+    auto rec = [&](int k, int q) -> float4 {
+        return slot[k] >= 0 ? recs[slot[k] * 3 + q]
+                            : reinterpret_cast<const float4*>(a.derived + (size_t)ids[k] * REC)[q];
+    };
     float lsum = 0.0f;
     if (inside) {
-        const size_t p = (size_t)j * a.w + i;
-        const float px = (float)i + 0.5f, py = (float)j + 0.5f;
-        const uint4* l = reinterpret_cast<const uint4*>(a.topk + p * K);
-        // Each lane visits its entries starting at its own offset (anti-diagonal
-        // of the tile), so neighbouring pixels with the same list add to
-        // different sites at each step instead of piling onto one LDS address.
-        uint4 l0 = l[0], l1 = l[1];
-        rotate_list(l0, l1, (lane + (lane >> 3)) & (K - 1));
-        PointEval pe;
-        eval_point(a.derived, (uint32_t)a.n, l0, l1, px, py, pe);
+        float l[K], e[K];
+        bool use[K];
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            use[k] = false;
+            l[k] = 0.0f;
+            if (ids[k] >= n) continue;
+            Geo g;
+            g.g0 = rec(k, 0);
+            g.g1 = rec(k, 1);
+            const float s = usable_logit(g, true, px, py);
+            if (!finitef(s)) continue;
+            use[k] = true;
+            l[k] = s;
+            mx = fmaxf(mx, s);
+        }
+        float z = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            e[k] = use[k] ? __expf(l[k] - mx) : 0.0f;
+            z += e[k];
+        }
+        float c[3] = {0.f, 0.f, 0.f};
+        if (z > 0.0f) {
+            const float iz = 1.0f / z;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if (!use[k]) continue;
+                e[k] *= iz;
+                const float4 col = rec(k, 2);
+                c[0] += e[k] * col.x;
+                c[1] += e[k] * col.y;
+                c[2] += e[k] * col.z;
+            }
+        }
         float g[3];
 #pragma unroll
         for (int ch = 0; ch < 3; ++ch) {
-            float r = pe.c[ch] - a.target[p * 3 + ch];
+            const float r = c[ch] - tg[ch];
             lsum += r * r;
             g[ch] = 2.0f * r * a.inv_p;
-            if (a.image) a.image[p * 3 + ch] = pe.c[ch];
+            if (a.image) a.image[p * 3 + ch] = c[ch];
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const uint32_t id = pe.id[k];
-            if (id == EMPTY) continue;
-            const float4* rec = reinterpret_cast<const float4*>(a.derived + (size_t)id * REC);
-            const float4 g0 = rec[0], g1 = rec[1], col = rec[2];
-            const float w = pe.e[k];
+            if (!use[k]) continue;
+            const uint32_t id = ids[k];
+            const float w = e[k];
+            const float4 g0 = rec(k, 0), g1 = rec(k, 1), col = rec(k, 2);
             const float tau = g0.z, cs = g1.x, sn = g1.y, is1 = g1.z, is2 = g1.w;
             // g.(c_i - c): differences first, so a site coloured like the pixel
             // does not lose its gradient to cancellation
-            const float delta = w * (g[0] * (col.x - pe.c[0]) + g[1] * (col.y - pe.c[1]) + g[2] * (col.z - pe.c[2]));
+            const float delta = w * (g[0] * (col.x - c[0]) + g[1] * (col.y - c[1]) + g[2] * (col.z - c[2]));
             float t[NGRAD];
             t[4] = w * g[0];
             t[5] = w * g[1];
             t[6] = w * g[2];
-            t[2] = delta * pe.l[k];
+            t[2] = delta * l[k];
             t[3] = tau * delta;
             const float dx = px - g0.x, dy = py - g0.y;
             const float ar = dx * cs + dy * sn, br = dy * cs - dx * sn;
@@ -261,22 +359,11 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
                 t[8] = -kap2 * aa * aa;
                 t[9] = -kap2 * bb * bb;
             }
-            const uint32_t h0 = slot_hash(id);
-            int slot = -1;
-            for (int pr = 0; pr < REGION_PROBES; ++pr) {
-                const uint32_t s = (h0 + pr) & (SLOTS - 1);
-                uint32_t cur = keys[s];
-                if (cur == EMPTY) cur = atomicCAS(&keys[s], EMPTY, id);
-                if (cur == EMPTY || cur == id) {
-                    slot = (int)s;
-                    break;
-                }
-            }
 #pragma unroll
             for (int q2 = 0; q2 < NGRAD; ++q2) {
                 const float x = t[q2] * b.fix_scale;
-                if (slot >= 0 && fabsf(x) < FIX_LIMIT)
-                    atomicAdd(&acc[q2 * SLOTS + slot], to_fixed(x));
+                if (slot[k] >= 0 && fabsf(x) < FIX_LIMIT)
+                    atomicAdd(&acc[q2 * SLOTS + slot[k]], to_fixed(x));
                 else
                     unsafeAtomicAdd(&a.grad[(size_t)id * REC + q2], t[q2]);
             }
@@ -287,7 +374,7 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
         if (lane == 0) wsum[wv] = ws;
     }
     __syncthreads();
-    // publish the region's table
+    // 4. publish the region's table
     const int region = blockIdx.x;
     for (int s = threadIdx.x; s < SLOTS; s += blockDim.x) {
         const uint32_t id = keys[s];
@@ -296,9 +383,9 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
             float v[NGRAD];
 #pragma unroll
             for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] = (float)((double)(long long)acc[q2 * SLOTS + s] * b.fix_inv);
-            const float4 g0 = reinterpret_cast<const float4*>(a.derived + (size_t)id * REC)[0];
+            const float4 r0 = recs[s * 3 + 0];
             int hx, hy;
-            home_region(g0.x, g0.y, b.rg, hx, hy);
+            home_region(r0.x, r0.y, b.rg, hx, hy);
             if (abs(hx - rx) <= 1 && abs(hy - ry) <= 1) {
                 float* dst = b.tvals + ((size_t)region * SLOTS + s) * NGRAD;
 #pragma unroll
