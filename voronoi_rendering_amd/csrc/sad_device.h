@@ -16,6 +16,17 @@ constexpr uint32_t EMPTY = SAD_EMPTY;
 constexpr int TILE = SAD_TILE;
 constexpr int WAVE = 64;
 
+// Workgroups are dealt to the chip's 8 XCDs in turn (workgroup b runs on XCD
+// b mod 8), each XCD with its own L2.  xcd_block renumbers them so that each
+// XCD receives one contiguous range of logical indices out of g: with
+// row-major tiles that is a band of the image, whose neighbour lists and
+// site records then stay within one L2.  A bijection on [0, g).
+__device__ __forceinline__ int xcd_block(int b, int g) {
+    const int q = g >> 3, r = g & 7;
+    const int x = b & 7, k = b >> 3;
+    return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
 // Site geometry as the logit needs it: g0 = (x, y, tau, r), g1 = (cos, sin, 1/s1, 1/s2).
 struct Geo {
     float4 g0, g1;
@@ -75,28 +86,26 @@ struct TopK {
         }
     }
 
-    // Insert a candidate with a non-NaN logit.  An id already in the list
-    // carries the same logit, so it is recognised and skipped.
-    __device__ __forceinline__ void insert(float sc, uint32_t cid) {
-        if (!ranks_before(sc, cid, s[K - 1], id[K - 1])) return;
+    // Insert (sc, cid) when ok; ok must be false for a NaN logit.  An id
+    // already in the list carries the same logit, so it is recognised and
+    // skipped.  Branch-free: every lane runs the same selects, and the list
+    // stays in the same registers whatever the outcome.
+    __device__ __forceinline__ void insert_if(float sc, uint32_t cid, bool ok) {
         bool dup = false;
 #pragma unroll
         for (int k = 0; k < K; ++k) dup |= (id[k] == cid);
-        if (dup) return;
+        ok = ok && !dup;
+        // b[k]: the candidate ranks before entry k (b[k - 1] implies b[k])
         bool b[K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) b[k] = ranks_before(sc, cid, s[k], id[k]);
+        for (int k = 0; k < K; ++k) b[k] = ok && ranks_before(sc, cid, s[k], id[k]);
 #pragma unroll
         for (int k = K - 1; k >= 1; --k) {
-            float ns = b[k - 1] ? s[k - 1] : (b[k] ? sc : s[k]);
-            uint32_t ni = b[k - 1] ? id[k - 1] : (b[k] ? cid : id[k]);
-            s[k] = ns;
-            id[k] = ni;
+            s[k] = b[k - 1] ? s[k - 1] : (b[k] ? sc : s[k]);
+            id[k] = b[k - 1] ? id[k - 1] : (b[k] ? cid : id[k]);
         }
-        if (b[0]) {
-            s[0] = sc;
-            id[0] = cid;
-        }
+        s[0] = b[0] ? sc : s[0];
+        id[0] = b[0] ? cid : id[0];
     }
 };
 

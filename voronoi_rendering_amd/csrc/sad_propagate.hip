@@ -6,23 +6,26 @@
 // lane, and shared by all pixels of the tile.
 //
 // Work per lane, in the order that keeps the vector ALU busy the least:
-//  1. The pixel's previous list: 8 logits, then a sorting network puts the
-//     entries in ranking order (a list carried over from the previous pass is
-//     already in order unless the sites moved, and the network is skipped
-//     when every lane of the wavefront is in order).
-//  2. The 32 ids of the 4 neighbour lists at +-stride: each id is compared
-//     with the pixel's own 8 ids and only ids not already listed are queued,
-//     in LDS (one column per lane).  At small strides almost all neighbour
-//     ids are already listed.
-//  3. The queued ids are scored; an id whose logit cannot beat the current
-//     8th entry is dropped at once, the others wait in a short register
-//     buffer and are inserted (with the duplicate check) afterwards.
-//  4. The tile's probe ids: each lane bounds its probe site's logit over the
+//  1. The pixel's previous list: 8 logits (or the caller's score map), then
+//     a sorting network puts the entries in ranking order (a list carried
+//     over from the previous pass is already in order unless the sites moved,
+//     and the network is skipped when every lane of the wavefront is in
+//     order).
+//  2. The neighbour lists, two at a time (16 ids): each id is compared with
+//     the ids now in the pixel's list and only ids not already listed are
+//     queued, in LDS (one column per lane).  At small strides almost all
+//     neighbour ids are already listed.  The queued ids are scored against
+//     the list's current 8th entry; the few that beat it are compacted, with
+//     their logits, to the front of the column and then inserted.  Keeping
+//     insertion out of the scoring loop leaves that loop free of divergent
+//     updates of the list.
+//  3. The tile's probe ids: each lane bounds its probe site's logit over the
 //     whole tile (probe_may_enter) and the wavefront scores only the sites
 //     whose bound can beat the tile's weakest 8th entry.
 // The result equals the top-8 of the candidate set in ranking order, whatever
 // order the candidates are visited in: every step above only skips
-// candidates that provably cannot be among the 8 best.
+// candidates that provably cannot be among the 8 best (the 8th entry only
+// improves as candidates are inserted).
 #include "sad_device.h"
 #include "sad_host.h"
 
@@ -39,8 +42,7 @@ struct PropArgs {
     uint32_t pass_index;
 };
 
-constexpr int QCAP = 4 * K;  // queued neighbour ids per lane (4 lists of 8)
-constexpr int PBUF = 4;      // register buffer of candidates awaiting insertion
+constexpr int QCAP = 2 * K;  // queued neighbour ids per lane (2 lists of 8)
 constexpr int WAVES_PER_WG = 4;
 
 // Logit of site id at (px, py), or NaN when the id names no usable site
@@ -99,20 +101,14 @@ __device__ __forceinline__ void sort8(TopK& t) {
     cex(t, 1, 2); cex(t, 3, 4); cex(t, 5, 6);
 }
 
-__device__ __forceinline__ bool in_list(const TopK& t, uint32_t v) {
-    bool f = false;
-#pragma unroll
-    for (int k = 0; k < K; ++k) f |= (t.id[k] == v);
-    return f;
-}
-
 constexpr int QBATCH = 4;  // queued ids scored per loop trip (their gathers overlap)
 
 __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
-    __shared__ uint32_t queue[WAVES_PER_WG][QCAP][WAVE];
+    __shared__ uint32_t queue[WAVES_PER_WG][QCAP][WAVE];  // queued ids, then survivors' ids
+    __shared__ float qscore[WAVES_PER_WG][QCAP][WAVE];    // survivors' logits
     const int lane = threadIdx.x & (WAVE - 1);
     const int wv = threadIdx.x / WAVE;
-    const int tile = blockIdx.x * WAVES_PER_WG + wv;
+    const int tile = xcd_block(blockIdx.x, gridDim.x) * WAVES_PER_WG + wv;
     if (tile >= a.n_tiles) return;  // uniform per wavefront
     const int tx = tile % a.tiles_x, ty = tile / a.tiles_x;
     const int i = tx * TILE + (lane & (TILE - 1));
@@ -164,25 +160,7 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
         pg = load_geo(a.derived, pid);
     }
 
-    // 1. neighbour ids not already in the pixel's list go to this lane's queue
-    //    column (membership only needs the ids, so this runs before any logit
-    //    and the 32 neighbour ids stop occupying registers early)
-    int cnt = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const uint32_t v = nbr[q][k];
-            bool listed = false;
-#pragma unroll
-            for (int k2 = 0; k2 < K; ++k2) listed |= (own[k2] == v);
-            if (v < n && !listed) {
-                queue[wv][cnt][lane] = v;
-                ++cnt;
-            }
-        }
-
-    // 2. the pixel's previous list, in ranking order (its logits come from the
+    // 1. the pixel's previous list, in ranking order (its logits come from the
     //    caller's score map when the sites have not changed since it was made)
     TopK t;
     t.clear();
@@ -221,54 +199,69 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
         bool dup = false;
 #pragma unroll
         for (int k = 0; k < K - 1; ++k) dup |= (t.id[k] == t.id[k + 1] && t.id[k] != EMPTY);
-        if (__any(dup) && dup) {
+        if (__any(dup)) {
             TopK u;
             u.clear();
 #pragma unroll
-            for (int k = 0; k < K; ++k)
-                if (t.id[k] != EMPTY) u.insert(t.s[k], t.id[k]);
-            t = u;
-        }
-    }
-
-    // 3. score queued ids, QBATCH at a time; those that may enter wait in a
-    //    register buffer and are inserted afterwards
-    float bs[PBUF];
-    uint32_t bi[PBUF];
-    int nb_used = 0;
-    for (int it = 0; __any(it < cnt); it += QBATCH) {
-        uint32_t v[QBATCH];
-        float sc[QBATCH];
+            for (int k = 0; k < K; ++k) u.insert_if(t.s[k], t.id[k], t.id[k] != EMPTY);
 #pragma unroll
-        for (int b = 0; b < QBATCH; ++b) v[b] = (it + b < cnt) ? queue[wv][it + b][lane] : EMPTY;
-        Geo qg[QBATCH];
-#pragma unroll
-        for (int b = 0; b < QBATCH; ++b) qg[b] = load_geo_clamped(a.derived, n, v[b]);
-#pragma unroll
-        for (int b = 0; b < QBATCH; ++b) sc[b] = usable_logit(qg[b], v[b] < n, px, py);
-#pragma unroll
-        for (int b = 0; b < QBATCH; ++b) {
-            if (sc[b] == sc[b] && ranks_before(sc[b], v[b], t.s[K - 1], t.id[K - 1])) {
-                if (nb_used == PBUF) {  // buffer full: make room by inserting its oldest entry
-                    t.insert(bs[PBUF - 1], bi[PBUF - 1]);
-                    --nb_used;
-                }
-#pragma unroll
-                for (int c = PBUF - 1; c >= 1; --c) {
-                    bs[c] = bs[c - 1];
-                    bi[c] = bi[c - 1];
-                }
-                bs[0] = sc[b];
-                bi[0] = v[b];
-                ++nb_used;
+            for (int k = 0; k < K; ++k) {
+                t.s[k] = dup ? u.s[k] : t.s[k];
+                t.id[k] = dup ? u.id[k] : t.id[k];
             }
         }
     }
-#pragma unroll
-    for (int b = 0; b < PBUF; ++b)
-        if (b < nb_used) t.insert(bs[b], bi[b]);
 
-    // 4. the tile's probe ids, culled by the tile bound
+    // 2. the neighbour lists, two at a time
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        // ids not in the pixel's list go to this lane's queue column; every id
+        // is written at the current end of the column and kept only if fresh
+        // (the write index never passes the id's own position)
+        int cnt = 0;
+#pragma unroll
+        for (int q = 2 * half; q < 2 * half + 2; ++q)
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const uint32_t v = nbr[q][k];
+                bool fresh = v < n;
+#pragma unroll
+                for (int k2 = 0; k2 < K; ++k2) fresh &= (t.id[k2] != v);
+                queue[wv][cnt][lane] = v;
+                cnt += fresh ? 1 : 0;
+            }
+        // score the queued ids, QBATCH at a time, against the current 8th
+        // entry; ids that beat it move with their logits to the front of the
+        // column (the write index ns never passes the position just read)
+        const float ts = t.s[K - 1];
+        const uint32_t ti = t.id[K - 1];
+        int ns = 0;
+        for (int it = 0; __any(it < cnt); it += QBATCH) {
+            uint32_t v[QBATCH];
+#pragma unroll
+            for (int b = 0; b < QBATCH; ++b) v[b] = (it + b < cnt) ? queue[wv][it + b][lane] : EMPTY;
+            Geo qg[QBATCH];
+#pragma unroll
+            for (int b = 0; b < QBATCH; ++b) qg[b] = load_geo_clamped(a.derived, n, v[b]);
+#pragma unroll
+            for (int b = 0; b < QBATCH; ++b) {
+                const float sc = usable_logit(qg[b], v[b] < n, px, py);
+                const bool pass = sc == sc && ranks_before(sc, v[b], ts, ti);
+                queue[wv][ns][lane] = v[b];
+                qscore[wv][ns][lane] = sc;
+                ns += pass ? 1 : 0;
+            }
+        }
+        // insert the survivors
+        for (int u = 0; __any(u < ns); ++u) {
+            const bool live = u < ns;
+            const uint32_t v = live ? queue[wv][u][lane] : EMPTY;
+            const float sc = live ? qscore[wv][u][lane] : 0.0f;
+            t.insert_if(sc, v, live);
+        }
+    }
+
+    // 3. the tile's probe ids, culled by the tile bound
     if (a.inject > 0) {
         const float thr = wave_min(inside ? t.s[K - 1] : __builtin_inff());
         bool keep = false;
@@ -293,10 +286,9 @@ __global__ __launch_bounds__(256) void k_propagate(PropArgs a) {
             g.g1.y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.y), q));
             g.g1.z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.z), q));
             g.g1.w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.w), q));
-            if (inside) {
-                const float s = logit(g, px, py);  // a survivor is an active site (checked above)
-                if (s == s) t.insert(s, id);
-            }
+            const float s = logit(g, px, py);  // a survivor is an active site (checked above)
+            const bool ok = inside && s == s;
+            if (__any(ok && ranks_before(s, id, t.s[K - 1], t.id[K - 1]))) t.insert_if(s, id, ok);
         }
     }
 

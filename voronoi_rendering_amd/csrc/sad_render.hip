@@ -104,7 +104,7 @@ struct PixArgs {
 
 __device__ __forceinline__ bool tile_pixel(const PixArgs& a, int& i, int& j) {
     const int lane = threadIdx.x & (WAVE - 1);
-    const int tile = blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
+    const int tile = xcd_block(blockIdx.x, gridDim.x) * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
     const int tx = tile % a.tiles_x, ty = tile / a.tiles_x;
     i = tx * TILE + (lane & (TILE - 1));
     j = ty * TILE + (lane / TILE);
@@ -208,7 +208,8 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
     for (int s = threadIdx.x; s < NGRAD * SLOTS; s += blockDim.x) acc[s] = 0ull;
 
     const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
-    const int rx = blockIdx.x % b.rg.rgx, ry = blockIdx.x / b.rg.rgx;
+    const int reg = xcd_block(blockIdx.x, gridDim.x);
+    const int rx = reg % b.rg.rgx, ry = reg / b.rg.rgx;
     const int tx = rx * RT_X + (wv % RT_X), ty = ry * RT_Y + (wv / RT_X);
     const int i = tx * TILE + (lane & (TILE - 1)), j = ty * TILE + (lane / TILE);
     const bool inside = i < a.w && j < a.h;
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
     }
     __syncthreads();
     // 4. publish the region's table
-    const int region = blockIdx.x;
+    const int region = reg;
     for (int s = threadIdx.x; s < SLOTS; s += blockDim.x) {
         const uint32_t id = keys[s];
         uint32_t key = id;
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(SLOTS) void k_grad_gather(RegionGrid rg, const uint
                                                        const float* __restrict__ tvals, float* __restrict__ grad) {
     __shared__ uint32_t gkeys[GATHER_SLOTS];
     __shared__ float gacc[GATHER_SLOTS * NGRAD];
-    const int R = blockIdx.x;
+    const int R = xcd_block(blockIdx.x, gridDim.x);
     const int rx = R % rg.rgx, ry = R / rg.rgx;
     for (int s = threadIdx.x; s < GATHER_SLOTS; s += blockDim.x) gkeys[s] = EMPTY;
     for (int s = threadIdx.x; s < GATHER_SLOTS * NGRAD; s += blockDim.x) gacc[s] = 0.0f;
