@@ -3,7 +3,8 @@
 Workload (default): 768x512 RGB float32 target, 50,000 sites, K = 8.  One
 step = 4 top-K propagation passes (strides 8, 4, 2, 1, 64 injected sites per
 8x8 tile) + forward render + backward with the loss, on a map warmed by 16
-passes of the jump-flood schedule (untimed).  Metric: Mpixel-iters/s = H*W per
+passes of the jump-flood schedule (untimed).  The timed steps run the last
+pass and the backward as one call (sad_step_fused).  Metric: Mpixel-iters/s = H*W per
 step / step time.  All inputs are synthetic (synth.C2) and already resident in
 GPU memory when the timed region starts.
 
@@ -12,8 +13,9 @@ lists (as after an Adam update); the following passes reuse the logits the
 previous pass wrote.
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events recorded
-around every launch inside the timed region, on the stream the kernels run on
-(torch's current stream).
+around every call in up to 50 further steps made of separate calls (the same
+kernels as the fused call), on the stream the kernels run on (torch's current
+stream).
 """
 from __future__ import annotations
 
@@ -32,14 +34,16 @@ HBM_PEAK_GBS = 8000.0
 
 def algorithmic_bytes(h: int, w: int, n: int, n_pass: int) -> dict:
     """Bytes the method must move (not counting re-reads served by caches).
-    propagate: read + write one 32-byte list per pixel per pass.
-    backward:  read list (32 B) + target (12 B) per pixel, read the 48-byte
-               prepared record and read-modify-write the 40-byte gradient
-               record (80 B) per site."""
+    propagate:  read + write one 32-byte list per pixel per pass.
+    render_bwd: read list (32 B) + target (12 B) per pixel, read the 48-byte
+                prepared record and read-modify-write the 40-byte gradient
+                record (80 B) per site.
+    step:       the whole step with the last list handed from the pass to the
+                backward: 64 B per pixel per pass + the target + 128 B per site."""
     p = h * w
     prop = 64 * p
     bwd = p * (32 + 12) + n * (48 + 80)
-    step = n_pass * 64 * p + 12 * p + n * 128  # fused-step count: the last pass feeds the backward directly
+    step = n_pass * 64 * p + 12 * p + n * 128
     return {"propagate": prop, "render_bwd": bwd, "step": step}
 
 
@@ -145,21 +149,21 @@ def main() -> int:
         # In training the Adam update rewrites the sites between steps, so the
         # first pass of every step recomputes the previous lists' logits.
         f.sites_changed()
+        if not record:
+            f.step(strides, target, fused=True)
+            return
+        # the same launches, one call each, with events around each kernel
         for s in strides:
-            if record:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-            f.propagate([s])
-            if record:
-                b.record(stream)
-                ev.append(("propagate", a, b))
-        if record:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-        f.forward_backward(target)
-        if record:
+            f.propagate([s])
             b.record(stream)
-            ev.append(("render_bwd", a, b))
+            ev.append(("propagate", a, b))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        f.forward_backward(target)
+        b.record(stream)
+        ev.append(("render_bwd", a, b))
 
     for _ in range(args.warmup):
         step(False)

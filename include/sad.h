@@ -184,6 +184,26 @@ int sad_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, const 
                    size_t workspace_bytes, void *stream);
 
 /*
+ * One training-iteration pass in one call: a propagation pass followed by
+ * the loss and gradients over the lists it produced (the one-pass update of
+ * a training iteration, Sec. 6.6 / Table 9, then Sec. 4.8 / Appendix B.4).
+ * Equivalent to sad_propagate_topk(derived, n, h, w, topk_prev, scores_prev,
+ * topk_next, scores_next, stride, seed, pass_index, inject_per_tile) then
+ * sad_render_bwd(derived, n, h, w, topk_next, target, grad, loss, image,
+ * workspace, workspace_bytes): topk_next, scores_next and image are the same
+ * bits; grad and loss differ only by summation order, as between two calls
+ * of sad_render_bwd.  Every argument is checked before any work is enqueued,
+ * so a rejected call leaves all buffers untouched.
+ * Arguments, formats and checks are those of the two calls; in addition
+ * topk_next and scores_next must not overlap target, grad, loss, image,
+ * workspace or derived.
+ */
+int sad_step_fused(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk_prev,
+                   const float *scores_prev, uint32_t *topk_next, float *scores_next, int32_t stride, uint64_t seed,
+                   uint32_t pass_index, int32_t inject_per_tile, const float *target, float *grad, float *loss,
+                   float *image, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One Adam step (Kingma & Ba) on the site parameters (Sec. 5: per-parameter
  * base learning rates, fixed betas and epsilon), then the projection of
  * Sec. 4.1 (positions clamped to [0, w] x [0, h]), then the prepared records

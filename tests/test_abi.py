@@ -27,7 +27,7 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     syms = declared_symbols()
     for name in ("sad_prepare_sites", "sad_propagate_topk", "sad_render_fwd", "sad_render_bwd",
-                 "sad_render_bwd_workspace_bytes",
+                 "sad_render_bwd_workspace_bytes", "sad_step_fused",
                  "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version"):
         assert name in syms
 
@@ -109,3 +109,36 @@ def test_render_query_adam_reject(lib):
                              None) == EINVAL  # params aliases grad
     assert lib.sad_adam_step(P, P + 4096, P + 8192, P + 12288, -3, 8, 8, lr, .9, .999, 1e-8, .1, .001, None,
                              None) == EINVAL
+
+
+def test_step_fused_rejects(lib):
+    f = lib.sad_step_fused
+    WS = 1 << 30
+    wsb = lib.sad_render_bwd_workspace_bytes(8, 8)
+    ok = dict(derived=P, n=10, h=8, w=8, prev=None, sprev=None, nxt=P + 4096, snext=None, stride=1, seed=0, pi=0,
+              inj=64, tgt=P + 8192, grad=P + 65536, loss=None, img=None, ws=WS, wsb=wsb)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["derived"], a["n"], a["h"], a["w"], a["prev"], a["sprev"], a["nxt"], a["snext"], a["stride"],
+                 a["seed"], a["pi"], a["inj"], a["tgt"], a["grad"], a["loss"], a["img"], a["ws"], a["wsb"], None)
+
+    # the checks of the propagation pass
+    assert call(stride=0) == EINVAL
+    assert call(inj=65) == EUNSUP
+    assert call(nxt=None) == EINVAL
+    assert call(prev=P + 4096) == EINVAL
+    # the checks of the backward pass
+    assert call(tgt=None) == EINVAL
+    assert call(grad=None) == EINVAL
+    assert call(grad=P) == EINVAL  # aliases derived
+    assert call(ws=None) == EINVAL
+    assert call(wsb=wsb - 1) == EINVAL
+    assert call(loss=P + 2) == EINVAL
+    # the pass's outputs against everything else the step touches
+    assert call(nxt=P + 8192) == EINVAL  # over the target
+    assert call(snext=P + 65536) == EINVAL  # over the gradients
+    assert call(nxt=WS) == EINVAL  # over the workspace
+    assert call(snext=P + 12288, img=P + 12288) == EINVAL  # image over the scores
+    assert call(nxt=P + 16384, loss=P + 16384 + 64) == EINVAL  # loss inside the list map
+    assert call(h=0, nxt=None, tgt=None) == 0  # empty image: nothing to do

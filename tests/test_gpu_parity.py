@@ -243,6 +243,70 @@ def test_render_bwd_c2(sad, ref, c2_state):
     assert_grad_close(to_np(grad), g_ref, g_abs, "C2 gradients", m_ref, (wl.h, wl.w))
 
 
+# ---------------------------------------------------------------- fused pass + backward
+
+def fused_vs_oracle(sad, ref, d, dg, h, w, prev_np, prev_gpu, stride, seed, t, inject, tgt, prev_scores=None,
+                    label=""):
+    """One fused call against the oracle's pass then backward, and against
+    the two separate GPU calls."""
+    m1 = ref.propagate(d, h, w, prev_np, stride, seed, t, inject)
+    g_ref, g_abs, loss_ref, img_ref = ref.render_bwd(d, h, w, m1, tgt)
+    n = d.shape[0]
+    outs = []
+    for fused in (True, False):
+        out = torch.empty((h, w, 8), dtype=torch.int32, device=dev())
+        osc = torch.empty((h, w, 8), dtype=torch.float32, device=dev())
+        grad = torch.zeros((n, 12), dtype=torch.float32, device=dev())
+        loss = torch.zeros(1, dtype=torch.float32, device=dev())
+        img = torch.empty((h, w, 3), dtype=torch.float32, device=dev())
+        if fused:
+            sad.step_fused(dg, h, w, prev_gpu, out, to_gpu(tgt), grad, stride=stride, seed=seed, pass_index=t,
+                           inject=inject, prev_scores=prev_scores, out_scores=osc, loss=loss, image=img)
+        else:
+            sad.propagate_topk(dg, h, w, prev_gpu, out, stride=stride, seed=seed, pass_index=t, inject=inject,
+                               prev_scores=prev_scores, out_scores=osc)
+            sad.render_bwd(dg, h, w, out, to_gpu(tgt), grad, loss, img)
+        outs.append((map_to_np(out), to_np(osc), to_np(grad), loss.item(), to_np(img)))
+    (lf, sf, gf, lossf, imf), (lc, sc_, gc, lossc, imc) = outs
+    assert np.array_equal(lf, m1), f"{label}: {(lf != m1).any(-1).sum()} pixels differ from the oracle"
+    assert np.array_equal(lf, lc)
+    assert np.array_equal(sf.view(np.uint32), sc_.view(np.uint32)), f"{label}: score maps differ"
+    assert np.array_equal(imf.view(np.uint32), imc.view(np.uint32)), f"{label}: images differ"
+    assert_colour_close(imf, img_ref, f"{label} image")
+    assert abs(lossf - loss_ref) <= 1e-5 * loss_ref
+    assert_grad_close(gf, g_ref, g_abs, f"{label} gradients", m1, (h, w))
+    assert np.all(gf[:, 10:] == 0)
+    return lf, sf
+
+
+def test_step_fused_c2(sad, ref, c2_state):
+    """The fused last pass + backward on the 768x512 map: first without a
+    score map (as after an Adam step), then chained through the score map it
+    wrote."""
+    wl, p, d, dg, m_ref, m_gpu = c2_state
+    tgt = wl.make_target()
+    lst, sc = fused_vs_oracle(sad, ref, d, dg, wl.h, wl.w, m_ref, m_gpu, 1, wl.inject_seed, 700, wl.inject, tgt,
+                              label="C2 fused")
+    fused_vs_oracle(sad, ref, d, dg, wl.h, wl.w, lst, to_gpu(lst), 2, wl.inject_seed, 701, wl.inject, tgt,
+                    prev_scores=to_gpu(sc), label="C2 fused, score map")
+
+
+@pytest.mark.parametrize("h,w,n,stride,inject", [(37, 53, 200, 2, 64), (16, 32, 40, 1, 7), (9, 70, 64, 8, 64)])
+def test_step_fused_ragged(sad, ref, h, w, n, stride, inject):
+    """Images that end inside a tile and inside a backward region, an inactive
+    site and a stale list entry; also the first pass from an empty map."""
+    p = synth.sites(31 + h, n, h, w, synth.SMALL_SCALES)
+    p[3, 0] = -1.0
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p))
+    rng = np.random.default_rng(h * w)
+    tgt = rng.random((h, w, 3)).astype(np.float32)
+    fused_vs_oracle(sad, ref, d, dg, h, w, None, None, stride, 5, 0, inject, tgt, label=f"{h}x{w} from empty")
+    m = ref.propagate_schedule(d, h, w, None, synth.jfa_strides(h, w, 6), 5, 1, inject)
+    m[0, 0, 7] = 3  # the inactive site, left in a list
+    fused_vs_oracle(sad, ref, d, dg, h, w, m, to_gpu(m), stride, 5, 9, inject, tgt, label=f"{h}x{w}")
+
+
 # ---------------------------------------------------------------- Adam
 
 def test_adam_bit_exact(sad, ref):

@@ -1,0 +1,343 @@
+// sad_propagate.h -- one top-K propagation pass (Sec. 4.3, Figure 5) over
+// one pixel tile, as a device function shared by the propagation kernel and
+// the fused last-pass + backward kernel.
+//
+// Mapping: one wavefront (64 lanes) per 8x8 pixel tile, one lane per pixel.
+// The tile is also the unit of the global probe: its injected ids are drawn
+// once per wavefront, one per lane, and shared by all pixels of the tile.
+//
+// Work per lane, in the order that keeps the vector ALU busy the least:
+//  1. The pixel's previous list: 8 logits (or the caller's score map), then
+//     a sorting network puts the entries in ranking order (a list carried
+//     over from the previous pass is already in order unless the sites moved,
+//     and the network is skipped when every lane of the wavefront is in
+//     order).
+//  2. The neighbour lists, two at a time (16 ids): each id is compared with
+//     the ids now in the pixel's list and only ids not already listed are
+//     queued, in LDS (one column per lane).  At small strides almost all
+//     neighbour ids are already listed.  The queued ids are scored against
+//     the list's current 8th entry; the few that beat it are compacted, with
+//     their logits, to the front of the column and then inserted.  Keeping
+//     insertion out of the scoring loop leaves that loop free of divergent
+//     updates of the list.
+//  3. The tile's probe ids: each lane bounds its probe site's logit over the
+//     whole tile (probe_may_enter) and the wavefront scores only the sites
+//     whose bound can beat the tile's weakest 8th entry.
+// The result equals the top-8 of the candidate set in ranking order, whatever
+// order the candidates are visited in: every step above only skips
+// candidates that provably cannot be among the 8 best (the 8th entry only
+// improves as candidates are inserted).
+#pragma once
+
+#include "sad_device.h"
+#include "sad_host.h"
+
+namespace sad {
+
+struct PropArgs {
+    const float* derived;
+    const uint32_t* prev;
+    const float* prev_scores;  // nullable: logits of prev's entries under derived
+    uint32_t* next;
+    float* next_scores;        // nullable: logits of next's entries are written here
+    uint64_t seed;
+    int32_t n, h, w, stride, inject, tiles_x, n_tiles;
+    uint32_t pass_index;
+};
+
+constexpr int QCAP = 2 * K;  // queued neighbour ids per lane (2 lists of 8)
+
+// Can the probe site (geometry g) rank among the 8 best of any pixel of the
+// tile whose pixel centres span [bx0, bx1] x [by0, by1], given that every
+// pixel of the tile already holds 8 entries of logit >= thr?
+//
+// For every pixel centre P of the box, ||P - p||_G >= m ||P - p||_2 >= m D,
+// with m the smaller inverse scale and D the distance from p to the box, so
+// the exact logit is at most -tau (m D - r).  The float32 evaluation of the
+// logit differs from the exact one by at most tau u ((8.5 kappa + 4) sqrt(q)
+// + 2 |r|), u = 2^-24, kappa = M/m the anisotropy ratio; for kappa <= 1024
+// this is below 2^-8 (tau sqrt(q) + tau |r|).  The bound therefore keeps a
+// 2^-8 relative margin on both terms, which also covers the rounding of the
+// bound's own evaluation.  Sites with non-finite values or extreme anisotropy
+// are never culled.
+__device__ __forceinline__ bool probe_may_enter(const Geo& g, float thr, float bx0, float bx1, float by0,
+                                                float by1) {
+    float tau = g.g0.z, r = g.g0.w, is1 = g.g1.z, is2 = g.g1.w;
+    float m = fminf(is1, is2), M = fmaxf(is1, is2);
+    bool boundable = finitef(g.g0.x) && finitef(g.g0.y) && finitef(tau) && finitef(r) && finitef(M) && m > 0.0f &&
+                     M <= 1024.0f * m;
+    if (!boundable) return true;
+    float ex = fmaxf(fmaxf(bx0 - g.g0.x, g.g0.x - bx1), 0.0f);
+    float ey = fmaxf(fmaxf(by0 - g.g0.y, g.g0.y - by1), 0.0f);
+    float dist = __builtin_sqrtf(ex * ex + ey * ey);
+    float A = tau * (m * dist);
+    float C = tau * r;
+    float ub = (C - A * (1.0f - 0x1p-8f)) + 0x1p-8f * (tau * fabsf(r));
+    return !(ub < thr);
+}
+
+// compare-exchange for the sorting network: entry i ends up ranking before j
+__device__ __forceinline__ void cex(TopK& t, int i, int j) {
+    bool sw = ranks_before(t.s[j], t.id[j], t.s[i], t.id[i]);
+    float si = t.s[i], sj = t.s[j];
+    uint32_t ii = t.id[i], ij = t.id[j];
+    t.s[i] = sw ? sj : si;
+    t.s[j] = sw ? si : sj;
+    t.id[i] = sw ? ij : ii;
+    t.id[j] = sw ? ii : ij;
+}
+
+__device__ __forceinline__ void sort8(TopK& t) {
+    cex(t, 0, 2); cex(t, 1, 3); cex(t, 4, 6); cex(t, 5, 7);
+    cex(t, 0, 4); cex(t, 1, 5); cex(t, 2, 6); cex(t, 3, 7);
+    cex(t, 0, 1); cex(t, 2, 3); cex(t, 4, 5); cex(t, 6, 7);
+    cex(t, 2, 4); cex(t, 3, 5);
+    cex(t, 1, 4); cex(t, 3, 6);
+    cex(t, 1, 2); cex(t, 3, 4); cex(t, 5, 6);
+}
+
+constexpr int QBATCH = 4;  // queued ids scored per loop trip (their gathers overlap)
+
+// One propagation pass over one 8x8 tile (tile < a.n_tiles), one lane of the
+// calling wavefront per pixel.  queue and qscore are this wavefront's LDS
+// columns (QCAP rows of WAVE).  Writes the pixel's new list (and its logits
+// when a.next_scores is set) and leaves it in t, in ranking order.  No
+// workgroup barrier inside.
+__device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint32_t (*queue)[WAVE],
+                                               float (*qscore)[WAVE], TopK& t) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int tx = tile % a.tiles_x, ty = tile / a.tiles_x;
+    const int i = tx * TILE + (lane & (TILE - 1));
+    const int j = ty * TILE + (lane / TILE);
+    const bool inside = i < a.w && j < a.h;
+    const float px = (float)i + 0.5f, py = (float)j + 0.5f;
+    const uint32_t n = (uint32_t)a.n;
+    const bool have_prev = inside && a.prev;
+
+    // Issue every independent load first: the pixel's list, the 4 neighbour
+    // lists and this lane's probe site.
+    uint32_t own[K];
+    float own_s[K];
+    uint32_t nbr[4][K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) own[k] = EMPTY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int k = 0; k < K; ++k) nbr[q][k] = EMPTY;
+    if (have_prev) {
+        const uint4* l = reinterpret_cast<const uint4*>(a.prev + ((size_t)j * a.w + i) * K);
+        const uint4 l0 = l[0], l1 = l[1];
+        own[0] = l0.x; own[1] = l0.y; own[2] = l0.z; own[3] = l0.w;
+        own[4] = l1.x; own[5] = l1.y; own[6] = l1.z; own[7] = l1.w;
+        if (a.prev_scores) {
+            const float4* ls = reinterpret_cast<const float4*>(a.prev_scores + ((size_t)j * a.w + i) * K);
+            const float4 s0 = ls[0], s1 = ls[1];
+            own_s[0] = s0.x; own_s[1] = s0.y; own_s[2] = s0.z; own_s[3] = s0.w;
+            own_s[4] = s1.x; own_s[5] = s1.y; own_s[6] = s1.z; own_s[7] = s1.w;
+        }
+        const int nb[4][2] = {{a.stride, 0}, {-a.stride, 0}, {0, a.stride}, {0, -a.stride}};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ii = i + nb[q][0], jj = j + nb[q][1];
+            if (ii < 0 || ii >= a.w || jj < 0 || jj >= a.h) continue;
+            const uint4* m = reinterpret_cast<const uint4*>(a.prev + ((size_t)jj * a.w + ii) * K);
+            const uint4 m0 = m[0], m1 = m[1];
+            nbr[q][0] = m0.x; nbr[q][1] = m0.y; nbr[q][2] = m0.z; nbr[q][3] = m0.w;
+            nbr[q][4] = m1.x; nbr[q][5] = m1.y; nbr[q][6] = m1.z; nbr[q][7] = m1.w;
+        }
+    }
+    uint32_t pid = EMPTY;
+    Geo pg;
+    pg.g0 = make_float4(-1.f, -1.f, 0.f, 0.f);
+    pg.g1 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane < a.inject) {
+        pid = probe_id(a.seed, a.pass_index, (uint32_t)tile, (uint32_t)lane, n);
+        pg = load_geo(a.derived, pid);
+    }
+
+    // 1. the pixel's previous list, in ranking order (its logits come from the
+    //    caller's score map when the sites have not changed since it was made)
+    t.clear();
+    if (a.prev_scores) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (have_prev && own[k] < n && own_s[k] == own_s[k]) {
+                t.s[k] = own_s[k];
+                t.id[k] = own[k];
+            }
+        }
+    } else if (n > 0) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            Geo og[K / 2];
+#pragma unroll
+            for (int k = 0; k < K / 2; ++k) og[k] = load_geo_clamped(a.derived, n, own[half * 4 + k]);
+#pragma unroll
+            for (int k = 0; k < K / 2; ++k) {
+                const int kk = half * 4 + k;
+                const float s = usable_logit(og[k], own[kk] < n, px, py);
+                if (s == s) {
+                    t.s[kk] = s;
+                    t.id[kk] = own[kk];
+                }
+            }
+        }
+    }
+    bool ordered = true;
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k)
+        ordered &= ranks_before(t.s[k], t.id[k], t.s[k + 1], t.id[k + 1]) || t.id[k + 1] == EMPTY;
+    if (!__all(ordered)) {
+        sort8(t);
+        // a malformed previous list may repeat an id: rebuild such lists by insertion
+        bool dup = false;
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) dup |= (t.id[k] == t.id[k + 1] && t.id[k] != EMPTY);
+        if (__any(dup)) {
+            TopK u;
+            u.clear();
+#pragma unroll
+            for (int k = 0; k < K; ++k) u.insert_if(t.s[k], t.id[k], t.id[k] != EMPTY);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                t.s[k] = dup ? u.s[k] : t.s[k];
+                t.id[k] = dup ? u.id[k] : t.id[k];
+            }
+        }
+    }
+
+    // 2. the neighbour lists, two at a time
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        // ids not in the pixel's list go to this lane's queue column; every id
+        // is written at the current end of the column and kept only if fresh
+        // (the write index never passes the id's own position)
+        int cnt = 0;
+#pragma unroll
+        for (int q = 2 * half; q < 2 * half + 2; ++q)
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const uint32_t v = nbr[q][k];
+                bool fresh = v < n;
+#pragma unroll
+                for (int k2 = 0; k2 < K; ++k2) fresh &= (t.id[k2] != v);
+                queue[cnt][lane] = v;
+                cnt += fresh ? 1 : 0;
+            }
+        // score the queued ids, QBATCH at a time, against the current 8th
+        // entry; ids that beat it move with their logits to the front of the
+        // column (the write index ns never passes the position just read)
+        const float ts = t.s[K - 1];
+        const uint32_t ti = t.id[K - 1];
+        int ns = 0;
+        for (int it = 0; __any(it < cnt); it += QBATCH) {
+            uint32_t v[QBATCH];
+#pragma unroll
+            for (int b = 0; b < QBATCH; ++b) v[b] = (it + b < cnt) ? queue[it + b][lane] : EMPTY;
+            Geo qg[QBATCH];
+#pragma unroll
+            for (int b = 0; b < QBATCH; ++b) qg[b] = load_geo_clamped(a.derived, n, v[b]);
+#pragma unroll
+            for (int b = 0; b < QBATCH; ++b) {
+                const float sc = usable_logit(qg[b], v[b] < n, px, py);
+                const bool pass = sc == sc && ranks_before(sc, v[b], ts, ti);
+                queue[ns][lane] = v[b];
+                qscore[ns][lane] = sc;
+                ns += pass ? 1 : 0;
+            }
+        }
+        // insert the survivors
+        for (int u = 0; __any(u < ns); ++u) {
+            const bool live = u < ns;
+            const uint32_t v = live ? queue[u][lane] : EMPTY;
+            const float sc = live ? qscore[u][lane] : 0.0f;
+            t.insert_if(sc, v, live);
+        }
+    }
+
+    // 3. the tile's probe ids, culled by the tile bound
+    if (a.inject > 0) {
+        const float thr = wave_min(inside ? t.s[K - 1] : __builtin_inff());
+        bool keep = false;
+        if (pg.g0.x >= 0.0f) {
+            const float bx0 = (float)(tx * TILE) + 0.5f, by0 = (float)(ty * TILE) + 0.5f;
+            const float bx1 = (float)min(tx * TILE + TILE - 1, a.w - 1) + 0.5f;
+            const float by1 = (float)min(ty * TILE + TILE - 1, a.h - 1) + 0.5f;
+            keep = probe_may_enter(pg, thr, bx0, bx1, by0, by1);
+        }
+        uint64_t mask = __ballot(keep);
+        while (mask) {
+            // the survivor's record is already in lane q's registers: broadcast it
+            const int q = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)pid, q);
+            Geo g;
+            g.g0.x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g0.x), q));
+            g.g0.y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g0.y), q));
+            g.g0.z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g0.z), q));
+            g.g0.w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g0.w), q));
+            g.g1.x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.x), q));
+            g.g1.y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.y), q));
+            g.g1.z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.z), q));
+            g.g1.w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.w), q));
+            const float s = logit(g, px, py);  // a survivor is an active site (checked above)
+            const bool ok = inside && s == s;
+            if (__any(ok && ranks_before(s, id, t.s[K - 1], t.id[K - 1]))) t.insert_if(s, id, ok);
+        }
+    }
+
+    if (inside) {
+        uint4* o = reinterpret_cast<uint4*>(a.next + ((size_t)j * a.w + i) * K);
+        o[0] = make_uint4(t.id[0], t.id[1], t.id[2], t.id[3]);
+        o[1] = make_uint4(t.id[4], t.id[5], t.id[6], t.id[7]);
+        if (a.next_scores) {
+            float4* os = reinterpret_cast<float4*>(a.next_scores + ((size_t)j * a.w + i) * K);
+            os[0] = make_float4(t.s[0], t.s[1], t.s[2], t.s[3]);
+            os[1] = make_float4(t.s[4], t.s[5], t.s[6], t.s[7]);
+        }
+    }
+}
+
+// Argument checks of a propagation pass (shared by the entry points that run
+// one) and its kernel arguments.  Returns SAD_OK with a filled in, or the
+// error status.
+inline int prop_setup(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk_prev,
+                      const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride,
+                      uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, PropArgs& a) {
+    if (!sites_ok(n) || !image_ok(h, w) || stride < 1 || inject_per_tile < 0) return SAD_EINVAL;
+    if (inject_per_tile > SAD_MAX_INJECT) return SAD_EUNSUPPORTED;
+    const int64_t pix = int64_t(h) * w;
+    const int64_t mbytes = pix * K * 4;
+    if (!array_ok(derived, n, 16) || !array_ok(topk_next, pix, 16)) return SAD_EINVAL;
+    if ((topk_prev && !aligned(topk_prev, 16)) || (scores_prev && !aligned(scores_prev, 16)) ||
+        (scores_next && !aligned(scores_next, 16)))
+        return SAD_EINVAL;
+    if (scores_prev && !topk_prev) return SAD_EINVAL;
+    const void* outs[2] = {topk_next, scores_next};
+    const void* ins[2] = {topk_prev, scores_prev};
+    for (int o = 0; o < 2; ++o)
+        for (int q = 0; q < 2; ++q)
+            if (overlap(outs[o], mbytes, ins[q], mbytes)) return SAD_EINVAL;
+    if (overlap(topk_next, mbytes, scores_next, mbytes) || overlap(topk_prev, mbytes, scores_prev, mbytes))
+        return SAD_EINVAL;
+    const int64_t ntiles = int64_t(tiles_x(w)) * tiles_y(h);
+    if (ntiles > MAX_TILES) return SAD_EINVAL;
+    a.derived = derived;
+    a.prev = topk_prev;
+    a.prev_scores = scores_prev;
+    a.next = topk_next;
+    a.next_scores = scores_next;
+    a.seed = seed;
+    a.n = n;
+    a.h = h;
+    a.w = w;
+    a.stride = stride;
+    a.inject = n > 0 ? inject_per_tile : 0;
+    a.tiles_x = tiles_x(w);
+    a.n_tiles = (int32_t)ntiles;
+    a.pass_index = pass_index;
+    return SAD_OK;
+}
+
+}  // namespace sad

@@ -12,8 +12,7 @@
 // claimed by compare-and-swap), then each occupied slot is flushed with one
 // global float atomic per parameter.  A contribution whose site finds no slot
 // within the probe bound goes straight to global memory.
-#include "sad_device.h"
-#include "sad_host.h"
+#include "sad_propagate.h"
 
 namespace sad {
 
@@ -550,9 +549,13 @@ extern "C" size_t sad_render_bwd_workspace_bytes(int32_t h, int32_t w) {
     return (size_t)rg.rgx * rg.rgy * SLOTS * (2 * sizeof(uint32_t) + NGRAD * sizeof(float));
 }
 
-extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
-                              const float* target, float* grad, float* loss, float* image, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+namespace sad {
+
+// Argument checks of a backward pass over the list map topk, and its kernel
+// arguments.  Returns SAD_OK with b filled in, or the error status.
+inline int bwd_setup(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
+                     const float* target, float* grad, float* loss, float* image, void* workspace,
+                     size_t workspace_bytes, BwdArgs& b) {
     int st = pix_common(derived, n, h, w, topk);
     if (st != SAD_OK) return st;
     const int64_t pix = int64_t(h) * w;
@@ -562,8 +565,6 @@ extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_
     const size_t need = sad_render_bwd_workspace_bytes(h, w);
     if (pix > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)) return SAD_EINVAL;
     if (overlap(workspace, (int64_t)need, grad, int64_t(n) * REC * 4)) return SAD_EINVAL;
-    if (pix == 0) return SAD_OK;
-    BwdArgs b;
     b.p = pix_args(derived, n, h, w, topk);
     b.p.target = target;
     b.p.grad = grad;
@@ -578,11 +579,58 @@ extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_
     while ((int64_t(1) << (e - 45)) < pix) ++e;
     b.fix_scale = ldexpf(1.0f, e);
     b.fix_inv = ldexp(1.0, -e);
+    return SAD_OK;
+}
+
+int bwd_launch(const BwdArgs& b, void* stream) {
+    const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
     clear_error();
     hipLaunchKernelGGL(k_render_bwd, dim3((unsigned)nreg), dim3(WAVE * REGION_WAVES), 0, as_stream(stream), b);
     hipLaunchKernelGGL(k_grad_gather, dim3((unsigned)nreg), dim3(SLOTS), 0, as_stream(stream), b.rg, b.tkeys, b.thome,
-                       b.tvals, grad);
+                       b.tvals, b.p.grad);
     return launch_status();
+}
+
+}  // namespace sad
+
+extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
+                              const float* target, float* grad, float* loss, float* image, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    BwdArgs b;
+    const int st = bwd_setup(derived, n, h, w, topk, target, grad, loss, image, workspace, workspace_bytes, b);
+    if (st != SAD_OK) return st;
+    if (int64_t(h) * w == 0) return SAD_OK;
+    return bwd_launch(b, stream);
+}
+
+extern "C" int sad_step_fused(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk_prev,
+                              const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride,
+                              uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, const float* target,
+                              float* grad, float* loss, float* image, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    PropArgs pa;
+    int st = prop_setup(derived, n, h, w, topk_prev, scores_prev, topk_next, scores_next, stride, seed, pass_index,
+                        inject_per_tile, pa);
+    if (st != SAD_OK) return st;
+    BwdArgs b;
+    st = bwd_setup(derived, n, h, w, topk_next, target, grad, loss, image, workspace, workspace_bytes, b);
+    if (st != SAD_OK) return st;
+    // the pass's outputs must not share memory with anything else the step reads or writes
+    const int64_t pix = int64_t(h) * w, mbytes = pix * K * 4, gbytes = int64_t(n) * REC * 4;
+    const size_t need = sad_render_bwd_workspace_bytes(h, w);
+    const void* outs[2] = {topk_next, scores_next};
+    const void* others[6] = {target, grad, loss, image, workspace, derived};
+    const int64_t obytes[6] = {pix * 12, gbytes, 4, pix * 12, (int64_t)need, gbytes};
+    for (int o = 0; o < 2; ++o)
+        for (int q = 0; q < 6; ++q)
+            if (overlap(outs[o], mbytes, others[q], obytes[q])) return SAD_EINVAL;
+    if (pix == 0) return SAD_OK;
+    // every check has passed: the pass, then the backward over its lists, in
+    // stream order
+    st = sad_propagate_topk(derived, n, h, w, topk_prev, scores_prev, topk_next, scores_next, stride, seed, pass_index,
+                            inject_per_tile, stream);
+    if (st != SAD_OK) return st;
+    return bwd_launch(b, stream);
 }
 
 extern "C" int sad_query_points(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,

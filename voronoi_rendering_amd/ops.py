@@ -129,6 +129,39 @@ def render_bwd(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target
     _native.check("sad_render_bwd", st)
 
 
+def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor,
+               target: torch.Tensor, grad: torch.Tensor, *, stride: int, seed: int, pass_index: int,
+               inject: int = 64, prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None,
+               loss: torch.Tensor | None = None, image: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """propagate_topk(...) into ``out`` followed by render_bwd over ``out``, in
+    one call (the new lists feed the backward directly)."""
+    n = derived.shape[0]
+    _need(derived, "derived", torch.float32, (n, REC))
+    if prev is not None:
+        _need(prev, "prev", torch.int32, (h, w, K))
+    if prev_scores is not None:
+        _need(prev_scores, "prev_scores", torch.float32, (h, w, K))
+    _need(out, "out", torch.int32, (h, w, K))
+    if out_scores is not None:
+        _need(out_scores, "out_scores", torch.float32, (h, w, K))
+    _need(target, "target", torch.float32, (h, w, 3))
+    _need(grad, "grad", torch.float32, (n, REC))
+    if loss is not None:
+        _need(loss, "loss", torch.float32, (1,))
+    if image is not None:
+        _need(image, "image", torch.float32, (h, w, 3))
+    if workspace is None:
+        workspace = bwd_workspace(h, w, derived.device)
+    st = _native.lib().sad_step_fused(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
+                                      _ptr(out_scores), int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                      int(pass_index) & 0xFFFFFFFF, int(inject), _ptr(target), _ptr(grad),
+                                      _ptr(loss), _ptr(image), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(derived))
+    _native.check("sad_step_fused", st)
+    return out
+
+
 def adam_step(params: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor, h: int, w: int,
               lr: Sequence[float], beta1: float, beta2: float, eps: float, bias_corr1: float, bias_corr2: float,
               derived: torch.Tensor | None = None) -> None:

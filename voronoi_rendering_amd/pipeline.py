@@ -82,10 +82,21 @@ class SadField:
     def forward_backward(self, target: torch.Tensor, image: torch.Tensor | None = None) -> None:
         ops.render_bwd(self.derived, self.h, self.w, self.topk, target, self.grad, self.loss, image)
 
-    def step(self, strides: Sequence[int], target: torch.Tensor) -> None:
-        """Propagation passes + forward + backward (gradients accumulate)."""
-        self.propagate(strides)
-        self.forward_backward(target)
+    def step(self, strides: Sequence[int], target: torch.Tensor, fused: bool = True) -> None:
+        """Propagation passes + forward + backward (gradients accumulate).  With
+        ``fused`` the last pass and the backward run as one call."""
+        if not fused or len(strides) == 0:
+            self.propagate(strides)
+            self.forward_backward(target)
+            return
+        self.propagate(strides[:-1])
+        ops.step_fused(self.derived, self.h, self.w, self.maps[self.cur], self.maps[1 - self.cur], target, self.grad,
+                       stride=int(strides[-1]), seed=self.seed, pass_index=self.pass_index, inject=self.inject,
+                       prev_scores=self.scores[self.cur] if self.scores_valid else None,
+                       out_scores=self.scores[1 - self.cur], loss=self.loss)
+        self.cur = 1 - self.cur
+        self.pass_index += 1
+        self.scores_valid = True
 
     def adam_step(self) -> None:
         self.adam_t += 1
@@ -94,8 +105,8 @@ class SadField:
                       self.adam.beta2, self.adam.eps, bc1, bc2, self.derived)
         self.sites_changed()
 
-    def train_iter(self, strides: Sequence[int], target: torch.Tensor) -> None:
-        self.step(strides, target)
+    def train_iter(self, strides: Sequence[int], target: torch.Tensor, fused: bool = True) -> None:
+        self.step(strides, target, fused)
         self.adam_step()
 
     def render(self) -> torch.Tensor:
