@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void k_render_fwd(PixArgs a) {
 // position), the workgroup writes its table (keys at the same slots, the
 // summed values of the sites whose home is in the 3 x 3 regions around it) to
 // a workspace, and a second kernel gives every site the sum of its entries in
-// the 9 tables around its home.  Sites listed by a region outside that
+// the 9 tables around its home (found by the same hash probing).  Sites listed by a region outside that
 // neighbourhood (very wide footprints) are added with float atomics
 // directly; their slot keeps a placeholder key so probe chains stay intact.
 constexpr int RT_X = 4, RT_Y = 2;  // tiles per region
@@ -154,7 +154,7 @@ constexpr int REGION_WAVES = RT_X * RT_Y;
 constexpr int SLOTS = 256;
 constexpr int REGION_PROBES = 16;
 constexpr int NGRAD = 10;
-constexpr float FIX_LIMIT = 0x1p53f;  // |t 2^E| below this goes to the fixed-point sums
+constexpr double FIX_LIMIT_HI = 0x1p21;  // |t 2^E| < 2^53, i.e. |t 2^(E-32)| < 2^21, goes to the fixed-point sums
 constexpr uint32_t PLACEHOLDER = 0xfffffffeu;
 
 struct RegionGrid {
@@ -176,23 +176,20 @@ __device__ __forceinline__ void home_region(float x, float y, RegionGrid rg, int
 struct BwdArgs {
     PixArgs p;
     RegionGrid rg;
-    uint32_t* tkeys;  // [regions][SLOTS] site id, EMPTY or PLACEHOLDER
-    int32_t* thome;   // [regions][SLOTS] home region of the site (valid with a site id)
-    float* tvals;     // [regions][SLOTS][NGRAD]
-    float fix_scale;  // 2^E
-    double fix_inv;   // 2^-E
+    uint32_t* tkeys;      // [regions][SLOTS] site id, EMPTY or PLACEHOLDER
+    float* tvals;         // [regions][SLOTS][NGRAD]
+    double fix_scale_hi;  // 2^(E-32)
+    double fix_inv;       // 2^-E
 };
 
-// x (already scaled to fixed point, |x| < 2^53) as a two's-complement 64-bit
-// integer, truncated toward zero.  Below 2^31 a 32-bit conversion does it.
-// From 2^31 up, x is a multiple of 2^8, so x - hi 2^32 with hi = floor(x 2^-32)
-// is a multiple of 2^8 below 2^32 and exactly representable: the split is exact.
-__device__ __forceinline__ unsigned long long to_fixed(float x) {
-    const long long small = (long long)(int32_t)x;
-    const float hi = floorf(x * 0x1p-32f);
-    const float lo = __builtin_fmaf(hi, -0x1p32f, x);
-    const long long big = (long long)(int32_t)hi * 4294967296ll + (long long)(uint32_t)lo;
-    return (unsigned long long)(fabsf(x) < 0x1p31f ? small : big);
+// The fixed-point value of a term t, given u = t 2^(E-32) (exact in double,
+// |u| < 2^21): floor(t 2^E) as a 64-bit two's-complement integer.  With
+// hi = floor(u) and f = u - hi in [0, 1) (both exact), t 2^E = hi 2^32 + f 2^32
+// and 0 <= f 2^32 < 2^32: hi is the upper word and floor(f 2^32) the lower.
+__device__ __forceinline__ unsigned long long to_fixed(double u) {
+    const double hi = floor(u);
+    const double lo = (u - hi) * 4294967296.0;
+    return ((unsigned long long)(uint32_t)(int32_t)hi << 32) | (unsigned long long)(uint32_t)lo;
 }
 
 __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
@@ -218,6 +215,7 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
     // The pixel's list, each lane starting at its own offset (anti-diagonal of
     // the tile) so that neighbouring pixels with the same list add to different
     // sites at each step.
+    const int rot = (lane + (lane >> 3)) & (K - 1);
     uint32_t ids[K];
     float tg[3] = {0.f, 0.f, 0.f};
     {
@@ -230,7 +228,7 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
             tg[1] = a.target[p * 3 + 1];
             tg[2] = a.target[p * 3 + 2];
         }
-        rotate_list(l0, l1, (lane + (lane >> 3)) & (K - 1));
+        rotate_list(l0, l1, rot);
         ids[0] = l0.x; ids[1] = l0.y; ids[2] = l0.z; ids[3] = l0.w;
         ids[4] = l1.x; ids[5] = l1.y; ids[6] = l1.z; ids[7] = l1.w;
     }
@@ -361,9 +359,9 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
             }
 #pragma unroll
             for (int q2 = 0; q2 < NGRAD; ++q2) {
-                const float x = t[q2] * b.fix_scale;
-                if (slot[k] >= 0 && fabsf(x) < FIX_LIMIT)
-                    atomicAdd(&acc[q2 * SLOTS + slot[k]], to_fixed(x));
+                const double u = (double)t[q2] * b.fix_scale_hi;
+                if (slot[k] >= 0 && fabs(u) < FIX_LIMIT_HI)
+                    atomicAdd(&acc[q2 * SLOTS + slot[k]], to_fixed(u));
                 else
                     unsafeAtomicAdd(&a.grad[(size_t)id * REC + q2], t[q2]);
             }
@@ -390,7 +388,6 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
                 float* dst = b.tvals + ((size_t)region * SLOTS + s) * NGRAD;
 #pragma unroll
                 for (int q2 = 0; q2 < NGRAD; ++q2) dst[q2] = v[q2];
-                b.thome[(size_t)region * SLOTS + s] = hy * b.rg.rgx + hx;
             } else {
                 key = PLACEHOLDER;
 #pragma unroll
@@ -406,74 +403,71 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
     }
 }
 
-// One workgroup per region R: it reads the tables of the 3 x 3 regions
-// around R (coalesced), keeps the entries whose site has its home in R, sums
-// them per site in LDS, table by table in a fixed order, and adds each sum to
-// the site's gradient record.  Every site with contributions in the tables
-// has exactly one home, so exactly one workgroup updates it, without atomics;
-// the result does not depend on scheduling.
-constexpr int GATHER_SLOTS = 512;
+// Every site gets the sum of its entries in the tables of the 3 x 3 regions
+// around its home region.  A workgroup takes GATHER_SITES sites with one thread
+// per (site, table): the thread finds the site in its table by the probing the
+// backward used (stopping at an empty slot or after REGION_PROBES slots) and
+// loads the entry; then one thread per site adds the 9 partial sums in a fixed
+// order to the site's gradient record.  One writer per site, no atomics, and a
+// result that does not depend on scheduling.  A site found in no table is not
+// touched.
+constexpr int GATHER_SITES = 28;  // 28 x 9 = 252 threads
 
-__global__ __launch_bounds__(SLOTS) void k_grad_gather(RegionGrid rg, const uint32_t* __restrict__ tkeys,
-                                                       const int32_t* __restrict__ thome,
-                                                       const float* __restrict__ tvals, float* __restrict__ grad) {
-    __shared__ uint32_t gkeys[GATHER_SLOTS];
-    __shared__ float gacc[GATHER_SLOTS * NGRAD];
-    const int R = xcd_block(blockIdx.x, gridDim.x);
-    const int rx = R % rg.rgx, ry = R / rg.rgx;
-    for (int s = threadIdx.x; s < GATHER_SLOTS; s += blockDim.x) gkeys[s] = EMPTY;
-    for (int s = threadIdx.x; s < GATHER_SLOTS * NGRAD; s += blockDim.x) gacc[s] = 0.0f;
-    // this thread's slot in each of the 9 tables: keys and homes loaded up front
-    uint32_t key[9];
-    int table[9];
+__global__ __launch_bounds__(256) void k_grad_gather(RegionGrid rg, const uint32_t* __restrict__ tkeys,
+                                                     const float* __restrict__ tvals,
+                                                     const float* __restrict__ derived, float* __restrict__ grad,
+                                                     int32_t n) {
+    __shared__ float part[GATHER_SITES][9][NGRAD];
+    __shared__ int found[GATHER_SITES][9];
+    const int ls = threadIdx.x / 9, t = threadIdx.x % 9;
+    const int site = blockIdx.x * GATHER_SITES + ls;
+    if (ls < GATHER_SITES) {
+        float v[NGRAD];
 #pragma unroll
-    for (int t = 0; t < 9; ++t) {
-        const int tx = rx + (t % 3) - 1, ty = ry + (t / 3) - 1;
-        table[t] = (tx >= 0 && tx < rg.rgx && ty >= 0 && ty < rg.rgy) ? ty * rg.rgx + tx : -1;
-        key[t] = EMPTY;
-        if (table[t] >= 0) {
-            const size_t e = (size_t)table[t] * SLOTS + threadIdx.x;
-            const uint32_t k = tkeys[e];
-            if (k < PLACEHOLDER && thome[e] == R) key[t] = k;
-        }
-    }
-    __syncthreads();
-    for (int t = 0; t < 9; ++t) {
-        if (key[t] != EMPTY) {
-            const uint32_t id = key[t];
-            const float* src = tvals + ((size_t)table[t] * SLOTS + threadIdx.x) * NGRAD;
-            float v[NGRAD];
+        for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] = 0.0f;
+        int hit = 0;
+        if (site < n) {
+            int hx, hy;
+            home_region(derived[(size_t)site * REC], derived[(size_t)site * REC + 1], rg, hx, hy);
+            const int tx = hx + (t % 3) - 1, ty = hy + (t / 3) - 1;
+            if (tx >= 0 && tx < rg.rgx && ty >= 0 && ty < rg.rgy) {
+                const size_t base = (size_t)(ty * rg.rgx + tx) * SLOTS;
+                uint32_t pos = slot_hash((uint32_t)site);
+                for (int pr = 0; pr < REGION_PROBES; ++pr) {
+                    const uint32_t key = tkeys[base + pos];
+                    if (key == (uint32_t)site) {
+                        const float* src = tvals + (base + pos) * NGRAD;
 #pragma unroll
-            for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] = src[q2];
-            int slot = -1;
-            const uint32_t h0 = (id * 2654435761u) >> 23;  // 9 bits
-            for (int pr = 0; pr < GATHER_SLOTS; ++pr) {
-                const uint32_t sl = (h0 + pr) & (GATHER_SLOTS - 1);
-                uint32_t cur = gkeys[sl];
-                if (cur == EMPTY) cur = atomicCAS(&gkeys[sl], EMPTY, id);
-                if (cur == EMPTY || cur == id) {
-                    slot = (int)sl;
-                    break;
+                        for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] = src[q2];
+                        hit = 1;
+                        break;
+                    }
+                    if (key == EMPTY) break;
+                    pos = (pos + 1) & (SLOTS - 1);
                 }
             }
-            // within one table a site occupies one slot, so this thread is the
-            // only writer of the slot until the next barrier
-            if (slot >= 0) {
-#pragma unroll
-                for (int q2 = 0; q2 < NGRAD; ++q2) gacc[slot * NGRAD + q2] += v[q2];
-            } else {
-#pragma unroll
-                for (int q2 = 0; q2 < NGRAD; ++q2) unsafeAtomicAdd(&grad[(size_t)id * REC + q2], v[q2]);
-            }
         }
-        __syncthreads();
-    }
-    for (int s = threadIdx.x; s < GATHER_SLOTS; s += blockDim.x) {
-        const uint32_t id = gkeys[s];
-        if (id == EMPTY) continue;
-        float* gr = grad + (size_t)id * REC;
 #pragma unroll
-        for (int q2 = 0; q2 < NGRAD; ++q2) gr[q2] += gacc[s * NGRAD + q2];
+        for (int q2 = 0; q2 < NGRAD; ++q2) part[ls][t][q2] = v[q2];
+        found[ls][t] = hit;
+    }
+    __syncthreads();
+    const int s2 = blockIdx.x * GATHER_SITES + (int)threadIdx.x;
+    if (threadIdx.x < GATHER_SITES && s2 < n) {
+        int any = 0;
+        float sum[NGRAD];
+#pragma unroll
+        for (int q2 = 0; q2 < NGRAD; ++q2) sum[q2] = 0.0f;
+        for (int t2 = 0; t2 < 9; ++t2) {
+            any |= found[threadIdx.x][t2];
+#pragma unroll
+            for (int q2 = 0; q2 < NGRAD; ++q2) sum[q2] += part[threadIdx.x][t2][q2];
+        }
+        if (any) {
+            float* gr = grad + (size_t)s2 * REC;
+#pragma unroll
+            for (int q2 = 0; q2 < NGRAD; ++q2) gr[q2] += sum[q2];
+        }
     }
 }
 
@@ -546,7 +540,7 @@ extern "C" int sad_render_fwd(const float* derived, int32_t n, int32_t h, int32_
 extern "C" size_t sad_render_bwd_workspace_bytes(int32_t h, int32_t w) {
     if (!image_ok(h, w)) return 0;
     const RegionGrid rg = region_grid(h, w);
-    return (size_t)rg.rgx * rg.rgy * SLOTS * (2 * sizeof(uint32_t) + NGRAD * sizeof(float));
+    return (size_t)rg.rgx * rg.rgy * SLOTS * (sizeof(uint32_t) + NGRAD * sizeof(float));
 }
 
 namespace sad {
@@ -573,11 +567,10 @@ inline int bwd_setup(const float* derived, int32_t n, int32_t h, int32_t w, cons
     b.rg = region_grid(h, w);
     const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
     b.tkeys = reinterpret_cast<uint32_t*>(workspace);
-    b.thome = reinterpret_cast<int32_t*>(b.tkeys + nreg * SLOTS);
-    b.tvals = reinterpret_cast<float*>(b.thome + nreg * SLOTS);
+    b.tvals = reinterpret_cast<float*>(b.tkeys + nreg * SLOTS);
     int e = 45;  // 2^E = 2^45 * (smallest power of two >= h*w)
     while ((int64_t(1) << (e - 45)) < pix) ++e;
-    b.fix_scale = ldexpf(1.0f, e);
+    b.fix_scale_hi = ldexp(1.0, e - 32);
     b.fix_inv = ldexp(1.0, -e);
     return SAD_OK;
 }
@@ -586,8 +579,10 @@ int bwd_launch(const BwdArgs& b, void* stream) {
     const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
     clear_error();
     hipLaunchKernelGGL(k_render_bwd, dim3((unsigned)nreg), dim3(WAVE * REGION_WAVES), 0, as_stream(stream), b);
-    hipLaunchKernelGGL(k_grad_gather, dim3((unsigned)nreg), dim3(SLOTS), 0, as_stream(stream), b.rg, b.tkeys, b.thome,
-                       b.tvals, b.p.grad);
+    if (b.p.n > 0)
+        hipLaunchKernelGGL(k_grad_gather, dim3((unsigned)((b.p.n + GATHER_SITES - 1) / GATHER_SITES)),
+                           dim3(GATHER_SITES * 9), 0, as_stream(stream), b.rg, b.tkeys, b.tvals, b.p.derived,
+                           b.p.grad, b.p.n);
     return launch_status();
 }
 
