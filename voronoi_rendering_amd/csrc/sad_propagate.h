@@ -115,36 +115,46 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
     const bool have_prev = inside && a.prev;
 
     // Issue every independent load first: the pixel's list, the 4 neighbour
-    // lists and this lane's probe site.
+    // lists and this lane's probe site.  Every list load reads a pixel inside
+    // the image (coordinates clamped), so no load waits on a branch; nb_ok
+    // marks the neighbours that exist, and a lane off the image uses no list.
     uint32_t own[K];
     float own_s[K];
     uint32_t nbr[4][K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) own[k] = EMPTY;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int k = 0; k < K; ++k) nbr[q][k] = EMPTY;
-    if (have_prev) {
-        const uint4* l = reinterpret_cast<const uint4*>(a.prev + ((size_t)j * a.w + i) * K);
+    bool nb_ok[4];
+    const int nb[4][2] = {{a.stride, 0}, {-a.stride, 0}, {0, a.stride}, {0, -a.stride}};
+    if (a.prev) {  // uniform
+        const size_t pc = (size_t)min(j, a.h - 1) * a.w + min(i, a.w - 1);
+        const uint4* l = reinterpret_cast<const uint4*>(a.prev + pc * K);
         const uint4 l0 = l[0], l1 = l[1];
         own[0] = l0.x; own[1] = l0.y; own[2] = l0.z; own[3] = l0.w;
         own[4] = l1.x; own[5] = l1.y; own[6] = l1.z; own[7] = l1.w;
         if (a.prev_scores) {
-            const float4* ls = reinterpret_cast<const float4*>(a.prev_scores + ((size_t)j * a.w + i) * K);
+            const float4* ls = reinterpret_cast<const float4*>(a.prev_scores + pc * K);
             const float4 s0 = ls[0], s1 = ls[1];
             own_s[0] = s0.x; own_s[1] = s0.y; own_s[2] = s0.z; own_s[3] = s0.w;
             own_s[4] = s1.x; own_s[5] = s1.y; own_s[6] = s1.z; own_s[7] = s1.w;
         }
-        const int nb[4][2] = {{a.stride, 0}, {-a.stride, 0}, {0, a.stride}, {0, -a.stride}};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int ii = i + nb[q][0], jj = j + nb[q][1];
-            if (ii < 0 || ii >= a.w || jj < 0 || jj >= a.h) continue;
-            const uint4* m = reinterpret_cast<const uint4*>(a.prev + ((size_t)jj * a.w + ii) * K);
+            nb_ok[q] = inside && ii >= 0 && ii < a.w && jj >= 0 && jj < a.h;
+            const size_t pq = (size_t)min(max(jj, 0), a.h - 1) * a.w + min(max(ii, 0), a.w - 1);
+            const uint4* m = reinterpret_cast<const uint4*>(a.prev + pq * K);
             const uint4 m0 = m[0], m1 = m[1];
             nbr[q][0] = m0.x; nbr[q][1] = m0.y; nbr[q][2] = m0.z; nbr[q][3] = m0.w;
             nbr[q][4] = m1.x; nbr[q][5] = m1.y; nbr[q][6] = m1.z; nbr[q][7] = m1.w;
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) own[k] = inside ? own[k] : EMPTY;
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) own[k] = EMPTY;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            nb_ok[q] = false;
+#pragma unroll
+            for (int k = 0; k < K; ++k) nbr[q][k] = EMPTY;
         }
     }
     uint32_t pid = EMPTY;
@@ -219,7 +229,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const uint32_t v = nbr[q][k];
-                bool fresh = v < n;
+                bool fresh = nb_ok[q] && v < n;
 #pragma unroll
                 for (int k2 = 0; k2 < K; ++k2) fresh &= (t.id[k2] != v);
                 queue[cnt][lane] = v;

@@ -11,7 +11,7 @@ constexpr int WAVES_PER_WG = 4;
 __global__ __launch_bounds__(WAVE* WAVES_PER_WG) void k_propagate(PropArgs a) {
     __shared__ uint32_t queue[WAVES_PER_WG][QCAP][WAVE];  // queued ids, then survivors' ids
     __shared__ float qscore[WAVES_PER_WG][QCAP][WAVE];    // survivors' logits
-    const int wv = threadIdx.x / WAVE;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);  // uniform: tile arithmetic stays scalar
     const int tile = xcd_block(blockIdx.x, gridDim.x) * WAVES_PER_WG + wv;
     if (tile >= a.n_tiles) return;  // uniform per wavefront
     TopK t;
