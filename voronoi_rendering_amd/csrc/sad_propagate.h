@@ -158,13 +158,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
         }
     }
     uint32_t pid = EMPTY;
-    Geo pg;
-    pg.g0 = make_float4(-1.f, -1.f, 0.f, 0.f);
-    pg.g1 = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane < a.inject) {
-        pid = probe_id(a.seed, a.pass_index, (uint32_t)tile, (uint32_t)lane, n);
-        pg = load_geo(a.derived, pid);
-    }
+    if (lane < a.inject) pid = probe_id(a.seed, a.pass_index, (uint32_t)tile, (uint32_t)lane, n);
 
     // 1. the pixel's previous list, in ranking order (its logits come from the
     //    caller's score map when the sites have not changed since it was made)
@@ -268,6 +262,10 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
 
     // 3. the tile's probe ids, culled by the tile bound
     if (a.inject > 0) {
+        Geo pg;
+        pg.g0 = make_float4(-1.f, -1.f, 0.f, 0.f);
+        pg.g1 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (lane < a.inject) pg = load_geo(a.derived, pid);
         const float thr = wave_min(inside ? t.s[K - 1] : __builtin_inff());
         bool keep = false;
         if (pg.g0.x >= 0.0f) {
