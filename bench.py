@@ -102,6 +102,62 @@ def cpu_baseline(wl, budget_s: float) -> dict:
                       f"{threads} OpenMP threads"}
 
 
+def secondary(torch, synth, ops, SadField) -> dict:
+    """The other workloads, timed briefly with inputs resident on the GPU (not
+    the headline): the 2048x2048 / 400k-site step, a training iteration
+    (step + Adam, the 768x512 training workload) and the Adam step alone, and
+    2^24 random-access queries on a 768x512 / 50k-site map."""
+    dev = torch.device("cuda", 0)
+
+    def per_call(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    out = {}
+    wl = synth.C4
+    f = SadField(torch.from_numpy(wl.make_sites()).to(dev), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+    tgt = torch.from_numpy(wl.make_target()).to(dev)
+    f.warm(wl.warm_passes)
+
+    def step4():
+        f.sites_changed()
+        f.step(list(wl.strides), tgt, fused=True)
+
+    t = per_call(step4, 10)
+    out["step_2048x2048_400k"] = {"Mpixel_iters_per_s": round(wl.h * wl.w / t / 1e6, 1), "ms_per_step": round(t * 1e3, 4),
+                                  "passes_per_step": len(wl.strides)}
+    del f, tgt
+    wl = synth.C3
+    f = SadField(torch.from_numpy(wl.make_sites()).to(dev), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+    tgt = torch.from_numpy(wl.make_target()).to(dev)
+    f.warm(wl.warm_passes)
+    t = per_call(lambda: f.train_iter(list(wl.strides), tgt), 50)
+    out["training_iteration_768x512_50k"] = {"ms_per_iteration": round(t * 1e3, 4),
+                                             "Mpixel_iters_per_s": round(wl.h * wl.w / t / 1e6, 1)}
+    t = per_call(f.adam_step, 50)
+    adam_bytes = 9 * 48 * wl.n  # params, grad, m, v read; params, m, v, grad, derived written
+    out["adam_step_50k"] = {"us": round(t * 1e6, 2), "GB_per_s": round(adam_bytes / t / 1e9, 1),
+                            "algorithmic_bytes": adam_bytes}
+    del f, tgt
+    wl = synth.C5
+    f = SadField(torch.from_numpy(wl.make_sites()).to(dev), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+    f.warm(wl.warm_passes)
+    xy = torch.from_numpy(wl.make_queries()).to(dev)
+    rgb = torch.empty((xy.shape[0], 3), dtype=torch.float32, device=dev)
+    t = per_call(lambda: ops.query_points(f.derived, wl.h, wl.w, f.topk, xy, rgb), 5)
+    m = xy.shape[0]
+    out["query_2e24_points"] = {"Mqueries_per_s": round(m / t / 1e6, 1), "ms": round(t * 1e3, 3),
+                                "GB_per_s_algorithmic": round(52 * m / t / 1e9, 1)}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +165,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads' timings")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -217,6 +274,8 @@ def main() -> int:
                          "around the step's passes (per-pass average), one around the backward (with the gather)",
         "roofline": roofline,
     }
+    if not args.no_secondary:
+        out["secondary"] = secondary(torch, synth, ops, SadField)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(out), flush=True)

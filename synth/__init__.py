@@ -132,9 +132,15 @@ def target_noise_edges(seed: int, h: int, w: int, n_waves: int = 8, n_edges: int
         rad = rng.uniform(16.0, 96.0)
         ang = rng.uniform(0, 2 * math.pi)
         delta = rng.uniform(-0.3, 0.3, 3)
-        dxp, dyp = px - cx, py - cy
+        # only the disc's bounding box (with a pixel of margin) can be inside;
+        # the test itself is evaluated exactly as over the whole image
+        i0, i1 = max(0, int(math.floor(cx - rad)) - 1), min(w, int(math.ceil(cx + rad)) + 1)
+        j0, j1 = max(0, int(math.floor(cy - rad)) - 1), min(h, int(math.ceil(cy + rad)) + 1)
+        if i0 >= i1 or j0 >= j1:
+            continue
+        dxp, dyp = px[j0:j1, i0:i1] - cx, py[j0:j1, i0:i1] - cy
         mask = (dxp * dxp + dyp * dyp <= rad * rad) & (math.cos(ang) * dxp + math.sin(ang) * dyp > 0)
-        img[mask] += delta
+        img[j0:j1, i0:i1][mask] += delta
     return np.clip(img, 0.0, 1.0).astype(np.float32)
 
 
