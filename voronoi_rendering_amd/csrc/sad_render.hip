@@ -184,8 +184,12 @@ struct BwdArgs {
 
 // The fixed-point value of a term t, given u = t 2^(E-32) (exact in double,
 // |u| < 2^21): floor(t 2^E) as a 64-bit two's-complement integer.  With
-// hi = floor(u) and f = u - hi in [0, 1) (both exact), t 2^E = hi 2^32 + f 2^32
-// and 0 <= f 2^32 < 2^32: hi is the upper word and floor(f 2^32) the lower.
+// hi = floor(u) and f = u - hi in [0, 1), t 2^E = hi 2^32 + f 2^32 and
+// 0 <= f 2^32 < 2^32: hi is the upper word and floor(f 2^32) the lower.  f is
+// exact except for a tiny negative u, where f = 1 - |u| is rounded to double;
+// the lower word is then off by less than one unit (2^-E), within the
+// resolution of the sums.  (In float32 that rounding would cost up to 2^8
+// units, which the gradient tolerance does not cover.)
 __device__ __forceinline__ unsigned long long to_fixed(double u) {
     const double hi = floor(u);
     const double lo = (u - hi) * 4294967296.0;
