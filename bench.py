@@ -102,6 +102,46 @@ def cpu_baseline(wl, budget_s: float) -> dict:
                       f"{threads} OpenMP threads"}
 
 
+def cpu_other(include_2048: bool) -> dict:
+    """The oracle on the other workloads: the 64x64 run (20 passes from an
+    empty map + backward), 2^20 of the 2^24 random queries on the 768x512
+    query map (rate extrapolated linearly), and with include_2048 one
+    2048x2048 step after the oracle's own 16-pass warm-up (about a minute)."""
+    import oracle as ref
+    import synth
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    ref.set_threads(threads)
+    out = {"cores": threads, "kind": "oracle"}
+    wl = synth.C1
+    d = ref.prepare_sites(wl.make_sites())
+    tgt = wl.make_target()
+    t0 = time.perf_counter()
+    m = ref.propagate_schedule(d, wl.h, wl.w, None, wl.strides, wl.inject_seed, 0, wl.inject)
+    ref.render_bwd(d, wl.h, wl.w, m, tgt)
+    out["run_64x64_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+    wl = synth.C5
+    d = ref.prepare_sites(wl.make_sites())
+    m = ref.propagate_schedule(d, wl.h, wl.w, None, synth.jfa_strides(wl.h, wl.w, wl.warm_passes), wl.inject_seed,
+                               0, wl.inject)
+    xy = wl.make_queries(1 << 20)
+    t0 = time.perf_counter()
+    ref.query_points(d, wl.h, wl.w, m, xy)
+    out["query_Mqueries_per_s"] = round((1 << 20) / (time.perf_counter() - t0) / 1e6, 3)
+    out["query_sample"] = "2^20 of the 2^24 points, rate extrapolated linearly"
+    if include_2048:
+        wl = synth.C4
+        d = ref.prepare_sites(wl.make_sites())
+        tgt = wl.make_target()
+        m = ref.propagate_schedule(d, wl.h, wl.w, None, synth.jfa_strides(wl.h, wl.w, wl.warm_passes),
+                                   wl.inject_seed, 0, wl.inject)
+        t0 = time.perf_counter()
+        m = ref.propagate_schedule(d, wl.h, wl.w, m, wl.strides, wl.inject_seed, wl.warm_passes, wl.inject)
+        ref.render_bwd(d, wl.h, wl.w, m, tgt)
+        out["step_2048x2048_Mpixel_iters_per_s"] = round(wl.h * wl.w / (time.perf_counter() - t0) / 1e6, 4)
+    return out
+
+
 def secondary(torch, synth, ops, SadField) -> dict:
     """The other workloads, timed briefly with inputs resident on the GPU (not
     the headline): the 2048x2048 / 400k-site step, a training iteration
@@ -121,6 +161,16 @@ def secondary(torch, synth, ops, SadField) -> dict:
         return a.elapsed_time(b) * 1e-3 / reps
 
     out = {}
+    wl = synth.C1
+    p1 = torch.from_numpy(wl.make_sites()).to(dev)
+    tgt1 = torch.from_numpy(wl.make_target()).to(dev)
+
+    def run1():
+        f1 = SadField(p1, wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+        f1.step(list(wl.strides), tgt1, fused=True)
+
+    t = per_call(run1, 20)
+    out["run_64x64_20_passes"] = {"ms": round(t * 1e3, 4), "note": "launch-bound: 20 passes + backward, setup included"}
     wl = synth.C4
     f = SadField(torch.from_numpy(wl.make_sites()).to(dev), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
     tgt = torch.from_numpy(wl.make_target()).to(dev)
@@ -166,6 +216,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads' timings")
+    ap.add_argument("--cpu-all", action="store_true",
+                    help="also time the oracle on one 2048x2048 step (adds about a minute)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -278,6 +330,7 @@ def main() -> int:
         out["secondary"] = secondary(torch, synth, ops, SadField)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        out["cpu_other"] = cpu_other(args.cpu_all)
     print(json.dumps(out), flush=True)
     return 0
 
