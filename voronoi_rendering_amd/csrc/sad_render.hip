@@ -2,16 +2,11 @@
 // backward pass with the per-site gradient reduction (Sec. 4.8, Appendix
 // B.4), and random-access queries (Sec. 6.6).
 //
-// Pixel kernels use the same mapping as the propagation pass: one wavefront
-// per 8x8 tile, 4 consecutive tiles per 256-thread workgroup, so a workgroup
-// covers a 32x8 pixel strip.
-//
-// Gradient reduction: many pixels of a strip share sites, so the per-pixel
-// contributions are first summed in LDS, in an open-addressing table keyed by
-// site id (multiplicative hash, linear probing, bounded probe count; keys
-// claimed by compare-and-swap), then each occupied slot is flushed with one
-// global float atomic per parameter.  A contribution whose site finds no slot
-// within the probe bound goes straight to global memory.
+// The forward render uses the same mapping as the propagation pass: one
+// wavefront per 8x8 tile, 4 consecutive tiles per 256-thread workgroup.  The
+// backward works on regions of 2 x 4 tiles and reduces the per-site gradient
+// terms in two stages (described before k_render_bwd); queries take one
+// thread per point.
 #include "sad_propagate.h"
 
 namespace sad {
@@ -131,7 +126,7 @@ __global__ __launch_bounds__(256) void k_render_fwd(PixArgs a) {
 // compare-and-swap).
 //
 // The LDS sums are exact 64-bit fixed-point integers: a contribution t
-// becomes t 2^E truncated toward zero, 2^E = 2^45 * (the power of two >= h*w), so
+// becomes floor(t 2^E), 2^E = 2^45 * (the power of two >= h*w), so
 // the resolution is 2^-45 of the 1/(h*w) scale every gradient carries, and
 // the integer adds are exact and independent of their order.  (LDS float
 // atomics are an order of magnitude slower than integer ones on this GPU.)
@@ -145,9 +140,10 @@ __global__ __launch_bounds__(256) void k_render_fwd(PixArgs a) {
 // position), the workgroup writes its table (keys at the same slots, the
 // summed values of the sites whose home is in the 3 x 3 regions around it) to
 // a workspace, and a second kernel gives every site the sum of its entries in
-// the 9 tables around its home (found by the same hash probing).  Sites listed by a region outside that
-// neighbourhood (very wide footprints) are added with float atomics
-// directly; their slot keeps a placeholder key so probe chains stay intact.
+// the 9 tables around its home (found by the same hash probing).  Sites
+// listed by a region outside that neighbourhood (very wide footprints) are
+// added with float atomics directly; their slot keeps a placeholder key so
+// probe chains stay intact.
 constexpr int RT_X = 4, RT_Y = 2;  // tiles per region
 constexpr int REGION_W = RT_X * TILE, REGION_H = RT_Y * TILE;
 constexpr int REGION_WAVES = RT_X * RT_Y;
