@@ -307,6 +307,49 @@ def test_step_fused_ragged(sad, ref, h, w, n, stride, inject):
     fused_vs_oracle(sad, ref, d, dg, h, w, m, to_gpu(m), stride, 5, 9, inject, tgt, label=f"{h}x{w}")
 
 
+def test_step_fused_without_sites(sad, ref):
+    """No sites: the pass leaves every list empty, the image is 0 and the
+    loss is the target's mean square, as the oracle gives."""
+    h, w = 9, 13
+    p = np.zeros((0, 12), dtype=np.float32)
+    d = ref.prepare_sites(p)
+    tgt = np.random.default_rng(1).random((h, w, 3)).astype(np.float32)
+    m_ref = ref.propagate(d, h, w, None, 1, 5, 0, 64)
+    _, _, loss_ref, img_ref = ref.render_bwd(d, h, w, m_ref, tgt)
+    dg = torch.zeros((0, 12), dtype=torch.float32, device=dev())
+    out = torch.empty((h, w, 8), dtype=torch.int32, device=dev())
+    grad = torch.zeros((0, 12), dtype=torch.float32, device=dev())
+    loss = torch.zeros(1, dtype=torch.float32, device=dev())
+    img = torch.full((h, w, 3), 7.0, dtype=torch.float32, device=dev())
+    sad.step_fused(dg, h, w, None, out, to_gpu(tgt), grad, stride=1, seed=5, pass_index=0, inject=64, loss=loss,
+                   image=img)
+    assert np.array_equal(map_to_np(out), m_ref)
+    assert np.array_equal(to_np(img), img_ref)
+    assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
+
+
+def test_pipeline_step_fused_equals_separate_calls(sad, ref):
+    """SadField.step with the fused call and with separate calls give the same
+    lists and score maps, and gradients within the tolerance, over three
+    steps of the 64x64 workload from an empty map."""
+    from voronoi_rendering_amd.pipeline import SadField
+
+    wl = synth.C1
+    p = to_gpu(wl.make_sites())
+    tgt = to_gpu(wl.make_target())
+    fields = [SadField(p.clone(), wl.h, wl.w, wl.inject_seed, inject=wl.inject) for _ in range(2)]
+    for _ in range(3):
+        for f, fused in zip(fields, (True, False)):
+            f.step([4, 2, 1], tgt, fused=fused)
+    a, b = fields
+    assert torch.equal(a.topk, b.topk)
+    assert torch.equal(a.scores[a.cur], b.scores[b.cur])
+    # the same kernels either way; terms that go to float atomics (very large
+    # ones) may be summed in another order
+    ga, gb = to_np(a.grad).astype(np.float64), to_np(b.grad).astype(np.float64)
+    assert np.all(np.abs(ga - gb) <= 1e-5 * np.abs(gb) + 1e-6 * np.abs(gb).max(axis=0))
+
+
 # ---------------------------------------------------------------- Adam
 
 def test_adam_bit_exact(sad, ref):
