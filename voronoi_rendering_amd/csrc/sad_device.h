@@ -86,15 +86,23 @@ struct TopK {
         }
     }
 
+    // Is v one of the listed ids?  Written as a minimum of differences (one
+    // vector compare at the end) rather than 8 compares whose lane masks are
+    // combined on the scalar unit: the chain of vector-to-scalar dependencies
+    // costs more than the few extra vector instructions.
+    __device__ __forceinline__ bool has(uint32_t v) const {
+        uint32_t mn = v ^ id[0];
+#pragma unroll
+        for (int k = 1; k < K; ++k) mn = min(mn, v ^ id[k]);
+        return mn == 0u;
+    }
+
     // Insert (sc, cid) when ok; ok must be false for a NaN logit.  An id
     // already in the list carries the same logit, so it is recognised and
     // skipped.  Branch-free: every lane runs the same selects, and the list
     // stays in the same registers whatever the outcome.
     __device__ __forceinline__ void insert_if(float sc, uint32_t cid, bool ok) {
-        bool dup = false;
-#pragma unroll
-        for (int k = 0; k < K; ++k) dup |= (id[k] == cid);
-        ok = ok && !dup;
+        ok = ok && !has(cid);
         // b[k]: the candidate ranks before entry k (b[k - 1] implies b[k])
         bool b[K];
 #pragma unroll

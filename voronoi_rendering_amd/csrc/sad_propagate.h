@@ -223,9 +223,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const uint32_t v = nbr[q][k];
-                bool fresh = nb_ok[q] && v < n;
-#pragma unroll
-                for (int k2 = 0; k2 < K; ++k2) fresh &= (t.id[k2] != v);
+                const bool fresh = nb_ok[q] && v < n && !t.has(v);
                 queue[cnt][lane] = v;
                 cnt += fresh ? 1 : 0;
             }
