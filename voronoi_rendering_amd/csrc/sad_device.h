@@ -67,9 +67,10 @@ __device__ __forceinline__ float usable_logit(const Geo& g, bool in_range, float
     return (in_range && g.g0.x >= 0.0f) ? s : __builtin_nanf("");
 }
 
-// (s1, i1) ranks before (s2, i2)
+// (s1, i1) ranks before (s2, i2).  Bitwise operators: the three compares are
+// independent and no branch is formed around them.
 __device__ __forceinline__ bool ranks_before(float s1, uint32_t i1, float s2, uint32_t i2) {
-    return s1 > s2 || (s1 == s2 && i1 < i2);
+    return (s1 > s2) | ((s1 == s2) & (i1 < i2));
 }
 
 // Sorted list of the best K (logit, id) pairs seen so far, in registers.
@@ -102,11 +103,11 @@ struct TopK {
     // skipped.  Branch-free: every lane runs the same selects, and the list
     // stays in the same registers whatever the outcome.
     __device__ __forceinline__ void insert_if(float sc, uint32_t cid, bool ok) {
-        ok = ok && !has(cid);
+        ok = ok & !has(cid);
         // b[k]: the candidate ranks before entry k (b[k - 1] implies b[k])
         bool b[K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) b[k] = ok && ranks_before(sc, cid, s[k], id[k]);
+        for (int k = 0; k < K; ++k) b[k] = ok & ranks_before(sc, cid, s[k], id[k]);
 #pragma unroll
         for (int k = K - 1; k >= 1; --k) {
             s[k] = b[k - 1] ? s[k - 1] : (b[k] ? sc : s[k]);

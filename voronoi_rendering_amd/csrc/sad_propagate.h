@@ -243,7 +243,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
 #pragma unroll
             for (int b = 0; b < QBATCH; ++b) {
                 const float sc = usable_logit(qg[b], v[b] < n, px, py);
-                const bool pass = sc == sc && ranks_before(sc, v[b], ts, ti);
+                const bool pass = (sc == sc) & ranks_before(sc, v[b], ts, ti);
                 queue[ns][lane] = v[b];
                 qscore[ns][lane] = sc;
                 ns += pass ? 1 : 0;
