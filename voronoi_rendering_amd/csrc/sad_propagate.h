@@ -64,16 +64,16 @@ __device__ __forceinline__ bool probe_may_enter(const Geo& g, float thr, float b
                                                 float by1) {
     float tau = g.g0.z, r = g.g0.w, is1 = g.g1.z, is2 = g.g1.w;
     float m = fminf(is1, is2), M = fmaxf(is1, is2);
-    bool boundable = finitef(g.g0.x) && finitef(g.g0.y) && finitef(tau) && finitef(r) && finitef(M) && m > 0.0f &&
-                     M <= 1024.0f * m;
-    if (!boundable) return true;
+    const bool fin_x = finitef(g.g0.x), fin_y = finitef(g.g0.y), fin_tau = finitef(tau), fin_r = finitef(r),
+               fin_m = finitef(M);
+    const bool boundable = fin_x & fin_y & fin_tau & fin_r & fin_m & (m > 0.0f) & (M <= 1024.0f * m);
     float ex = fmaxf(fmaxf(bx0 - g.g0.x, g.g0.x - bx1), 0.0f);
     float ey = fmaxf(fmaxf(by0 - g.g0.y, g.g0.y - by1), 0.0f);
     float dist = __builtin_sqrtf(ex * ex + ey * ey);
     float A = tau * (m * dist);
     float C = tau * r;
     float ub = (C - A * (1.0f - 0x1p-8f)) + 0x1p-8f * (tau * fabsf(r));
-    return !(ub < thr);
+    return !boundable | !(ub < thr);  // values of an unboundable site are not used
 }
 
 // compare-exchange for the sorting network: entry i ends up ranking before j
@@ -109,7 +109,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
     const int tx = tile % a.tiles_x, ty = tile / a.tiles_x;
     const int i = tx * TILE + (lane & (TILE - 1));
     const int j = ty * TILE + (lane / TILE);
-    const bool inside = i < a.w && j < a.h;
+    const bool inside = (i < a.w) & (j < a.h);
     const float px = (float)i + 0.5f, py = (float)j + 0.5f;
     const uint32_t n = (uint32_t)a.n;
     const bool have_prev = inside && a.prev;
@@ -138,7 +138,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int ii = i + nb[q][0], jj = j + nb[q][1];
-            nb_ok[q] = inside && ii >= 0 && ii < a.w && jj >= 0 && jj < a.h;
+            nb_ok[q] = inside & (ii >= 0) & (ii < a.w) & (jj >= 0) & (jj < a.h);
             const size_t pq = (size_t)min(max(jj, 0), a.h - 1) * a.w + min(max(ii, 0), a.w - 1);
             const uint4* m = reinterpret_cast<const uint4*>(a.prev + pq * K);
             const uint4 m0 = m[0], m1 = m[1];
@@ -166,7 +166,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
     if (a.prev_scores) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            if (have_prev && own[k] < n && own_s[k] == own_s[k]) {
+            if (have_prev & (own[k] < n) & (own_s[k] == own_s[k])) {
                 t.s[k] = own_s[k];
                 t.id[k] = own[k];
             }
@@ -191,7 +191,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
     bool ordered = true;
 #pragma unroll
     for (int k = 0; k < K - 1; ++k)
-        ordered &= ranks_before(t.s[k], t.id[k], t.s[k + 1], t.id[k + 1]) || t.id[k + 1] == EMPTY;
+        ordered &= ranks_before(t.s[k], t.id[k], t.s[k + 1], t.id[k + 1]) | (t.id[k + 1] == EMPTY);
     if (!__all(ordered)) {
         sort8(t);
         // a malformed previous list may repeat an id: rebuild such lists by insertion
@@ -223,7 +223,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const uint32_t v = nbr[q][k];
-                const bool fresh = nb_ok[q] && v < n && !t.has(v);
+                const bool fresh = nb_ok[q] & (v < n) & !t.has(v);
                 queue[cnt][lane] = v;
                 cnt += fresh ? 1 : 0;
             }
@@ -288,8 +288,8 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
             g.g1.z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.z), q));
             g.g1.w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.w), q));
             const float s = logit(g, px, py);  // a survivor is an active site (checked above)
-            const bool ok = inside && s == s;
-            if (__any(ok && ranks_before(s, id, t.s[K - 1], t.id[K - 1]))) t.insert_if(s, id, ok);
+            const bool ok = inside & (s == s);
+            if (__any(ok & ranks_before(s, id, t.s[K - 1], t.id[K - 1]))) t.insert_if(s, id, ok);
         }
     }
 
