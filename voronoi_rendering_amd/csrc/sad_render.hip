@@ -19,6 +19,7 @@ struct PointEval {
     float l[K];
     float e[K];  // exp(l - max), later normalised to weights
     float c[3];
+    float4 col[K];  // colour part of each entry's record
 };
 
 __device__ __forceinline__ void eval_point(const float* __restrict__ derived, uint32_t nsites, const uint4 l0,
@@ -32,10 +33,14 @@ __device__ __forceinline__ void eval_point(const float* __restrict__ derived, ui
         pe.l[k] = 0.0f;
     }
     if (nsites > 0) {
-        // all record loads first (clamped ids, no branches), then the logits
+        // all record loads first, colours included (clamped ids, no branches):
+        // one round trip to memory for the whole record set, then the logits
         Geo g[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) g[k] = load_geo_clamped(derived, nsites, ids[k]);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            pe.col[k] = reinterpret_cast<const float4*>(derived + (size_t)(ids[k] < nsites ? ids[k] : 0u) * REC)[2];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const float s = usable_logit(g[k], ids[k] < nsites, px, py);
@@ -61,7 +66,7 @@ __device__ __forceinline__ void eval_point(const float* __restrict__ derived, ui
     for (int k = 0; k < K; ++k) {
         if (pe.id[k] == EMPTY) continue;
         pe.e[k] *= iz;
-        const float4 col = reinterpret_cast<const float4*>(derived + (size_t)pe.id[k] * REC)[2];
+        const float4 col = pe.col[k];
         pe.c[0] += pe.e[k] * col.x;
         pe.c[1] += pe.e[k] * col.y;
         pe.c[2] += pe.e[k] * col.z;
