@@ -44,32 +44,31 @@ __device__ __forceinline__ void eval_point(const float* __restrict__ derived, ui
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const float s = usable_logit(g[k], ids[k] < nsites, px, py);
-            if (!finitef(s)) continue;  // also drops NaN: unusable entries
-            pe.id[k] = ids[k];
-            pe.l[k] = s;
-            mx = fmaxf(mx, s);
-            pe.n++;
+            const bool ok = finitef(s);  // also drops NaN: unusable entries
+            pe.id[k] = ok ? ids[k] : EMPTY;
+            pe.l[k] = ok ? s : 0.0f;
+            mx = ok ? fmaxf(mx, s) : mx;
+            pe.n += ok ? 1 : 0;
         }
     }
     float z = 0.0f;
     pe.c[0] = pe.c[1] = pe.c[2] = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        pe.e[k] = 0.0f;
-        if (pe.id[k] == EMPTY) continue;
-        pe.e[k] = __expf(pe.l[k] - mx);
+        const float ek = __expf(pe.l[k] - mx);
+        pe.e[k] = pe.id[k] != EMPTY ? ek : 0.0f;
         z += pe.e[k];
     }
     if (pe.n == 0) return;
     float iz = 1.0f / z;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        if (pe.id[k] == EMPTY) continue;
+        const bool on = pe.id[k] != EMPTY;
         pe.e[k] *= iz;
         const float4 col = pe.col[k];
-        pe.c[0] += pe.e[k] * col.x;
-        pe.c[1] += pe.e[k] * col.y;
-        pe.c[2] += pe.e[k] * col.z;
+        pe.c[0] += on ? pe.e[k] * col.x : 0.0f;
+        pe.c[1] += on ? pe.e[k] * col.y : 0.0f;
+        pe.c[2] += on ? pe.e[k] * col.z : 0.0f;
     }
 }
 
