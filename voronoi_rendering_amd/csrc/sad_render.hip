@@ -7,6 +7,8 @@
 // backward works on regions of 2 x 4 tiles and reduces the per-site gradient
 // terms in two stages (described before k_render_bwd); queries take one
 // thread per point.
+#include <type_traits>
+
 #include "sad_propagate.h"
 
 namespace sad {
@@ -279,15 +281,26 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
     }
     __syncthreads();
 
-    // 3. forward and backward of the pixel, records from LDS (an entry whose
-    //    probe chain ran out reads its record from memory)
+    // 3. forward and backward of the pixel, records from LDS.  When an entry
+    //    of some lane of the wavefront found no slot (its probe chain ran
+    //    out), the wavefront takes a copy of this code that reads such
+    //    records from memory; otherwise every record read is an LDS read
+    //    (one pointer that may point to either memory would make every read a
+    //    slower generic load).
     // part q (0: x y tau r, 1: cos sin 1/s1 1/s2, 2: colour) of entry k's record
-    auto rec = [&](int k, int q) -> float4 {
-        return slot[k] >= 0 ? recs[slot[k] * 3 + q]
-                            : reinterpret_cast<const float4*>(a.derived + (size_t)ids[k] * REC)[q];
-    };
+    bool slotted = true;
+#pragma unroll
+    for (int k = 0; k < K; ++k) slotted &= (ids[k] >= n) | (slot[k] >= 0);
     float lsum = 0.0f;
-    if (inside) {
+    auto fwd_bwd = [&](auto lds_only) {
+        auto rec = [&](int k, int q) -> float4 {
+            if constexpr (decltype(lds_only)::value)
+                return recs[(slot[k] >= 0 ? slot[k] : 0) * 3 + q];
+            else
+                return slot[k] >= 0 ? recs[slot[k] * 3 + q]
+                                    : reinterpret_cast<const float4*>(a.derived + (size_t)ids[k] * REC)[q];
+        };
+        if (!inside) return;
         float l[K], e[K];
         bool use[K];
         float mx = -__builtin_inff();
@@ -370,7 +383,11 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
                     unsafeAtomicAdd(&a.grad[(size_t)id * REC + q2], t[q2]);
             }
         }
-    }
+    };
+    if (__all(slotted))
+        fwd_bwd(std::true_type{});
+    else
+        fwd_bwd(std::false_type{});
     if (a.loss) {
         const float ws = wave_sum(lsum);
         if (lane == 0) wsum[wv] = ws;
