@@ -119,6 +119,30 @@ def test_propagate_from_given_map_with_stale_ids(sad, ref):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("n", [65535, 65536])
+def test_propagate_at_the_16_bit_id_boundary(sad, ref, n):
+    """Site counts on both sides of the packed 16-bit membership test, with
+    previous lists holding ids whose low 16 bits equal those of listed ids
+    (v + 2^16, 2^16 - 1, EMPTY): out-of-range ids must be dropped and never
+    mistaken for listed ones."""
+    h, w = 45, 58
+    p = synth.sites(80 + n, n, h, w)
+    d = ref.prepare_sites(p)
+    base = ref.propagate_schedule(d, h, w, None, (32, 16, 8, 4, 2, 1), 9, 0, 64).astype(np.int64)
+    rng = np.random.default_rng(n)
+    prev = base.copy()
+    r = rng.random(prev.shape)
+    prev[r < 0.25] = (base[r < 0.25] % 65536) + 65536  # aliases of listed ids, all >= n
+    prev[(r >= 0.25) & (r < 0.3)] = 65535  # in range only when n = 65536
+    prev[(r >= 0.3) & (r < 0.35)] = 0xFFFFFFFF
+    prev = prev.astype(np.uint32)
+    dg = sad.prepare_sites(to_gpu(p))
+    for stride in (1, 3):
+        want = ref.propagate(d, h, w, prev, stride, 4, 12, 64)
+        got = map_to_np(sad.propagate_topk(dg, h, w, to_gpu(prev), stride=stride, seed=4, pass_index=12, inject=64))
+        assert np.array_equal(got, want), f"stride {stride}: {np.argwhere(got != want)[:5]}"
+
+
 @pytest.fixture(scope="module")
 def c2_state(sad, ref):
     """The 768x512, 50k-site workload: 16 warm-up passes, then one step's

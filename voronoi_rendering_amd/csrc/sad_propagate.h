@@ -98,11 +98,37 @@ __device__ __forceinline__ void sort8(TopK& t) {
 
 constexpr int QBATCH = 4;  // queued ids scored per loop trip (their gathers overlap)
 
+// Largest site count for which every usable id fits in 16 bits and differs
+// from the low half of EMPTY.
+constexpr int32_t SMALL_IDS_MAX = 0xFFFF;
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Which of the 16 ids c (< n <= SMALL_IDS_MAX, or any value the caller
+// discards) are in the list t?  Two ids share a register, one per 16-bit
+// half, and are compared with every list id copied into both halves; a packed
+// 16-bit minimum of the differences then answers for both at once.
+__device__ __forceinline__ void listed16(const TopK& t, const uint32_t (&c)[2 * K], bool (&in)[2 * K]) {
+    uint32_t rep[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) rep[k] = __builtin_amdgcn_perm(t.id[k], t.id[k], 0x01000100u);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const uint32_t pr = __builtin_amdgcn_perm(c[2 * j + 1], c[2 * j], 0x05040100u);
+        u16x2 m = __builtin_bit_cast(u16x2, pr ^ rep[0]);
+#pragma unroll
+        for (int k = 1; k < K; ++k) m = __builtin_elementwise_min(m, __builtin_bit_cast(u16x2, pr ^ rep[k]));
+        in[2 * j] = m.x == 0;
+        in[2 * j + 1] = m.y == 0;
+    }
+}
+
 // One propagation pass over one 8x8 tile (tile < a.n_tiles), one lane of the
 // calling wavefront per pixel.  queue and qscore are this wavefront's LDS
 // columns (QCAP rows of WAVE).  Writes the pixel's new list (and its logits
 // when a.next_scores is set) and leaves it in t, in ranking order.  No
-// workgroup barrier inside.
+// workgroup barrier inside.  SMALL_IDS requires a.n <= SMALL_IDS_MAX.
+template <bool SMALL_IDS>
 __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint32_t (*queue)[WAVE],
                                                float (*qscore)[WAVE], TopK& t) {
     const int lane = threadIdx.x & (WAVE - 1);
@@ -217,13 +243,23 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
         // ids not in the pixel's list go to this lane's queue column; every id
         // is written at the current end of the column and kept only if fresh
         // (the write index never passes the id's own position)
+        bool listed[2 * K];
+        if constexpr (SMALL_IDS) {
+            uint32_t c[2 * K];
+#pragma unroll
+            for (int k = 0; k < 2 * K; ++k) c[k] = nbr[2 * half + k / K][k % K];
+            listed16(t, c, listed);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 2 * K; ++k) listed[k] = t.has(nbr[2 * half + k / K][k % K]);
+        }
         int cnt = 0;
 #pragma unroll
         for (int q = 2 * half; q < 2 * half + 2; ++q)
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const uint32_t v = nbr[q][k];
-                const bool fresh = nb_ok[q] & (v < n) & !t.has(v);
+                const bool fresh = nb_ok[q] & (v < n) & !listed[(q - 2 * half) * K + k];
                 queue[cnt][lane] = v;
                 cnt += fresh ? 1 : 0;
             }

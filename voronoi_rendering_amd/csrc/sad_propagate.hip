@@ -8,6 +8,7 @@ namespace sad {
 
 constexpr int WAVES_PER_WG = 4;
 
+template <bool SMALL_IDS>
 __global__ __launch_bounds__(WAVE* WAVES_PER_WG) void k_propagate(PropArgs a) {
     __shared__ uint32_t queue[WAVES_PER_WG][QCAP][WAVE];  // queued ids, then survivors' ids
     __shared__ float qscore[WAVES_PER_WG][QCAP][WAVE];    // survivors' logits
@@ -15,7 +16,7 @@ __global__ __launch_bounds__(WAVE* WAVES_PER_WG) void k_propagate(PropArgs a) {
     const int tile = xcd_block(blockIdx.x, gridDim.x) * WAVES_PER_WG + wv;
     if (tile >= a.n_tiles) return;  // uniform per wavefront
     TopK t;
-    propagate_tile(a, tile, queue[wv], qscore[wv], t);
+    propagate_tile<SMALL_IDS>(a, tile, queue[wv], qscore[wv], t);
 }
 
 }  // namespace sad
@@ -31,7 +32,10 @@ extern "C" int sad_propagate_topk(const float* derived, int32_t n, int32_t h, in
     if (st != SAD_OK) return st;
     if (a.n_tiles == 0) return SAD_OK;
     clear_error();
-    hipLaunchKernelGGL(k_propagate, dim3((unsigned)((a.n_tiles + WAVES_PER_WG - 1) / WAVES_PER_WG)),
-                       dim3(WAVE * WAVES_PER_WG), 0, as_stream(stream), a);
+    const dim3 grid((unsigned)((a.n_tiles + WAVES_PER_WG - 1) / WAVES_PER_WG)), block(WAVE * WAVES_PER_WG);
+    if (a.n <= SMALL_IDS_MAX)
+        hipLaunchKernelGGL(k_propagate<true>, grid, block, 0, as_stream(stream), a);
+    else
+        hipLaunchKernelGGL(k_propagate<false>, grid, block, 0, as_stream(stream), a);
     return launch_status();
 }
