@@ -29,6 +29,8 @@
 // improves as candidates are inserted).
 #pragma once
 
+#include <type_traits>
+
 #include "sad_device.h"
 #include "sad_host.h"
 
@@ -104,17 +106,25 @@ constexpr int32_t SMALL_IDS_MAX = 0xFFFF;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// Which of the 16 ids c (< n <= SMALL_IDS_MAX, or any value the caller
-// discards) are in the list t?  Two ids share a register, one per 16-bit
-// half, and are compared with every list id copied into both halves; a packed
-// 16-bit minimum of the differences then answers for both at once.
-__device__ __forceinline__ void listed16(const TopK& t, const uint32_t (&c)[2 * K], bool (&in)[2 * K]) {
+// Two ids in the halves of one register (a in the low half), each clamped to
+// 0xFFFF: an id >= 2^16 becomes 0xFFFF, which is >= n and is never a usable
+// id when n <= SMALL_IDS_MAX.
+__device__ __forceinline__ uint32_t pack16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_u16(a, b));
+}
+
+// Which of 16 packed ids (pairs[j] holds ids 2j and 2j + 1, as pack16 makes
+// them) are in the list t?  Each pair is compared with every list id copied
+// into both halves; a packed 16-bit minimum of the differences answers for
+// both ids at once.  Only meaningful for ids < n <= SMALL_IDS_MAX (the list
+// holds such ids or EMPTY).
+__device__ __forceinline__ void listed16(const TopK& t, const uint32_t (&pairs)[K], bool (&in)[2 * K]) {
     uint32_t rep[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) rep[k] = __builtin_amdgcn_perm(t.id[k], t.id[k], 0x01000100u);
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-        const uint32_t pr = __builtin_amdgcn_perm(c[2 * j + 1], c[2 * j], 0x05040100u);
+        const uint32_t pr = pairs[j];
         u16x2 m = __builtin_bit_cast(u16x2, pr ^ rep[0]);
 #pragma unroll
         for (int k = 1; k < K; ++k) m = __builtin_elementwise_min(m, __builtin_bit_cast(u16x2, pr ^ rep[k]));
@@ -123,14 +133,21 @@ __device__ __forceinline__ void listed16(const TopK& t, const uint32_t (&c)[2 * 
     }
 }
 
+// Queue entry type: 16-bit ids when they fit.
+template <bool SMALL_IDS>
+using QueueId = std::conditional_t<SMALL_IDS, uint16_t, uint32_t>;
+
 // One propagation pass over one 8x8 tile (tile < a.n_tiles), one lane of the
 // calling wavefront per pixel.  queue and qscore are this wavefront's LDS
 // columns (QCAP rows of WAVE).  Writes the pixel's new list (and its logits
 // when a.next_scores is set) and leaves it in t, in ranking order.  No
-// workgroup barrier inside.  SMALL_IDS requires a.n <= SMALL_IDS_MAX.
+// workgroup barrier inside.  SMALL_IDS requires a.n <= SMALL_IDS_MAX; the
+// neighbour lists are then held as packed 16-bit pairs and queued as 16-bit
+// ids, which leaves registers and LDS for more wavefronts per compute unit.
 template <bool SMALL_IDS>
-__device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint32_t (*queue)[WAVE],
+__device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, QueueId<SMALL_IDS> (*queue)[WAVE],
                                                float (*qscore)[WAVE], TopK& t) {
+    constexpr int NW = SMALL_IDS ? K / 2 : K;  // registers per neighbour list
     const int lane = threadIdx.x & (WAVE - 1);
     const int tx = tile % a.tiles_x, ty = tile / a.tiles_x;
     const int i = tx * TILE + (lane & (TILE - 1));
@@ -146,7 +163,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
     // marks the neighbours that exist, and a lane off the image uses no list.
     uint32_t own[K];
     float own_s[K];
-    uint32_t nbr[4][K];
+    uint32_t nbr[4][NW];  // ids, or pack16 pairs of ids
     bool nb_ok[4];
     const int nb[4][2] = {{a.stride, 0}, {-a.stride, 0}, {0, a.stride}, {0, -a.stride}};
     if (a.prev) {  // uniform
@@ -168,8 +185,13 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
             const size_t pq = (size_t)min(max(jj, 0), a.h - 1) * a.w + min(max(ii, 0), a.w - 1);
             const uint4* m = reinterpret_cast<const uint4*>(a.prev + pq * K);
             const uint4 m0 = m[0], m1 = m[1];
-            nbr[q][0] = m0.x; nbr[q][1] = m0.y; nbr[q][2] = m0.z; nbr[q][3] = m0.w;
-            nbr[q][4] = m1.x; nbr[q][5] = m1.y; nbr[q][6] = m1.z; nbr[q][7] = m1.w;
+            if constexpr (SMALL_IDS) {
+                nbr[q][0] = pack16(m0.x, m0.y); nbr[q][1] = pack16(m0.z, m0.w);
+                nbr[q][2] = pack16(m1.x, m1.y); nbr[q][3] = pack16(m1.z, m1.w);
+            } else {
+                nbr[q][0] = m0.x; nbr[q][1] = m0.y; nbr[q][2] = m0.z; nbr[q][3] = m0.w;
+                nbr[q][4] = m1.x; nbr[q][5] = m1.y; nbr[q][6] = m1.z; nbr[q][7] = m1.w;
+            }
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) own[k] = inside ? own[k] : EMPTY;
@@ -180,7 +202,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
         for (int q = 0; q < 4; ++q) {
             nb_ok[q] = false;
 #pragma unroll
-            for (int k = 0; k < K; ++k) nbr[q][k] = EMPTY;
+            for (int k = 0; k < NW; ++k) nbr[q][k] = EMPTY;
         }
     }
     uint32_t pid = EMPTY;
@@ -245,10 +267,10 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
         // (the write index never passes the id's own position)
         bool listed[2 * K];
         if constexpr (SMALL_IDS) {
-            uint32_t c[2 * K];
+            uint32_t pairs[K];
 #pragma unroll
-            for (int k = 0; k < 2 * K; ++k) c[k] = nbr[2 * half + k / K][k % K];
-            listed16(t, c, listed);
+            for (int k = 0; k < K; ++k) pairs[k] = nbr[2 * half + k / NW][k % NW];
+            listed16(t, pairs, listed);
         } else {
 #pragma unroll
             for (int k = 0; k < 2 * K; ++k) listed[k] = t.has(nbr[2 * half + k / K][k % K]);
@@ -258,9 +280,13 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
         for (int q = 2 * half; q < 2 * half + 2; ++q)
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const uint32_t v = nbr[q][k];
+                uint32_t v;
+                if constexpr (SMALL_IDS)
+                    v = (k & 1) ? nbr[q][k / 2] >> 16 : nbr[q][k / 2] & 0xFFFFu;
+                else
+                    v = nbr[q][k];
                 const bool fresh = nb_ok[q] & (v < n) & !listed[(q - 2 * half) * K + k];
-                queue[cnt][lane] = v;
+                queue[cnt][lane] = (QueueId<SMALL_IDS>)v;
                 cnt += fresh ? 1 : 0;
             }
         // score the queued ids, QBATCH at a time, against the current 8th
@@ -272,7 +298,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
         for (int it = 0; __any(it < cnt); it += QBATCH) {
             uint32_t v[QBATCH];
 #pragma unroll
-            for (int b = 0; b < QBATCH; ++b) v[b] = (it + b < cnt) ? queue[it + b][lane] : EMPTY;
+            for (int b = 0; b < QBATCH; ++b) v[b] = (it + b < cnt) ? (uint32_t)queue[it + b][lane] : EMPTY;
             Geo qg[QBATCH];
 #pragma unroll
             for (int b = 0; b < QBATCH; ++b) qg[b] = load_geo_clamped(a.derived, n, v[b]);
@@ -280,7 +306,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
             for (int b = 0; b < QBATCH; ++b) {
                 const float sc = usable_logit(qg[b], v[b] < n, px, py);
                 const bool pass = (sc == sc) & ranks_before(sc, v[b], ts, ti);
-                queue[ns][lane] = v[b];
+                queue[ns][lane] = (QueueId<SMALL_IDS>)v[b];  // a passing id is < n
                 qscore[ns][lane] = sc;
                 ns += pass ? 1 : 0;
             }
@@ -288,7 +314,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, uint
         // insert the survivors
         for (int u = 0; __any(u < ns); ++u) {
             const bool live = u < ns;
-            const uint32_t v = live ? queue[u][lane] : EMPTY;
+            const uint32_t v = live ? (uint32_t)queue[u][lane] : EMPTY;
             const float sc = live ? qscore[u][lane] : 0.0f;
             t.insert_if(sc, v, live);
         }

@@ -9,8 +9,9 @@ namespace sad {
 constexpr int WAVES_PER_WG = 4;
 
 template <bool SMALL_IDS>
-__global__ __launch_bounds__(WAVE* WAVES_PER_WG) void k_propagate(PropArgs a) {
-    __shared__ uint32_t queue[WAVES_PER_WG][QCAP][WAVE];  // queued ids, then survivors' ids
+__global__ __launch_bounds__(WAVE* WAVES_PER_WG) __attribute__((amdgpu_waves_per_eu(SMALL_IDS ? 6 : 1)))
+void k_propagate(PropArgs a) {
+    __shared__ QueueId<SMALL_IDS> queue[WAVES_PER_WG][QCAP][WAVE];  // queued ids, then survivors' ids
     __shared__ float qscore[WAVES_PER_WG][QCAP][WAVE];    // survivors' logits
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);  // uniform: tile arithmetic stays scalar
     const int tile = xcd_block(blockIdx.x, gridDim.x) * WAVES_PER_WG + wv;
