@@ -119,6 +119,27 @@ def test_propagate_from_given_map_with_stale_ids(sad, ref):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("n", [5000, 70000])
+def test_propagate_full_neighbour_queue(sad, ref, n):
+    """Every queued neighbour id survives: pixels with an empty list between
+    pixels holding 8 distinct ids each, so the 16 ids of a pair of
+    neighbour lists are all fresh and all beat the empty 8th entry (the
+    scoring batches then reach the end of the queue); both id widths."""
+    h, w = 37, 70
+    p = synth.sites(90 + n % 7, n, h, w)
+    d = ref.prepare_sites(p)
+    rng = np.random.default_rng(n)
+    prev = np.full((h, w, 8), 0xFFFFFFFF, dtype=np.uint32)
+    ys, xs = np.mgrid[0:h, 0:w]
+    full = (xs + ys) % 2 == 0
+    prev[full] = np.stack([rng.choice(n, 8, replace=False) for _ in range(int(full.sum()))]).astype(np.uint32)
+    dg = sad.prepare_sites(to_gpu(p))
+    for stride in (1, 3):
+        want = ref.propagate(d, h, w, prev, stride, 6, 21, 64)
+        got = map_to_np(sad.propagate_topk(dg, h, w, to_gpu(prev), stride=stride, seed=6, pass_index=21, inject=64))
+        assert np.array_equal(got, want), f"stride {stride}: {np.argwhere(got != want)[:5]}"
+
+
 @pytest.mark.parametrize("n", [65535, 65536])
 def test_propagate_at_the_16_bit_id_boundary(sad, ref, n):
     """Site counts on both sides of the packed 16-bit membership test, with

@@ -98,7 +98,7 @@ __device__ __forceinline__ void sort8(TopK& t) {
     cex(t, 1, 2); cex(t, 3, 4); cex(t, 5, 6);
 }
 
-constexpr int QBATCH = 4;  // queued ids scored per loop trip (their gathers overlap)
+constexpr int QBATCH = 3;  // queued ids scored per loop trip (their gathers overlap)
 
 // Largest site count for which every usable id fits in 16 bits and differs
 // from the low half of EMPTY.
@@ -291,23 +291,30 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
             }
         // score the queued ids, QBATCH at a time, against the current 8th
         // entry; ids that beat it move with their logits to the front of the
-        // column (the write index ns never passes the position just read)
+        // column (the write index ns never passes the position just read).
+        // The last batch may reach past the column's QCAP rows (QBATCH need
+        // not divide QCAP): its rows are clamped for the read (the value is
+        // then not used) and its slots past cnt write nothing, so that a
+        // column whose every id passes is not written past its end.
         const float ts = t.s[K - 1];
         const uint32_t ti = t.id[K - 1];
         int ns = 0;
-        for (int it = 0; __any(it < cnt); it += QBATCH) {
+        for (int it = 0; __any(it < cnt); it += QBATCH) {  // it is uniform
             uint32_t v[QBATCH];
 #pragma unroll
-            for (int b = 0; b < QBATCH; ++b) v[b] = (it + b < cnt) ? (uint32_t)queue[it + b][lane] : EMPTY;
+            for (int b = 0; b < QBATCH; ++b)
+                v[b] = (it + b < cnt) ? (uint32_t)queue[min(it + b, QCAP - 1)][lane] : EMPTY;
             Geo qg[QBATCH];
 #pragma unroll
             for (int b = 0; b < QBATCH; ++b) qg[b] = load_geo_clamped(a.derived, n, v[b]);
 #pragma unroll
             for (int b = 0; b < QBATCH; ++b) {
                 const float sc = usable_logit(qg[b], v[b] < n, px, py);
-                const bool pass = (sc == sc) & ranks_before(sc, v[b], ts, ti);
-                queue[ns][lane] = (QueueId<SMALL_IDS>)v[b];  // a passing id is < n
-                qscore[ns][lane] = sc;
+                const bool pass = (sc == sc) & ranks_before(sc, v[b], ts, ti);  // false past cnt
+                if (it + b < cnt) {  // then ns <= it + b < cnt <= QCAP
+                    queue[ns][lane] = (QueueId<SMALL_IDS>)v[b];  // a passing id is < n
+                    qscore[ns][lane] = sc;
+                }
                 ns += pass ? 1 : 0;
             }
         }
