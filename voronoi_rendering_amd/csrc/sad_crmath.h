@@ -3,7 +3,14 @@
 // its float32 parameters, so every value is the float32 nearest to the exact
 // real result).
 //
-// Method: evaluate in double-double arithmetic (an unevaluated sum hi + lo of
+// Two stages.  A plain double evaluation (relative error below 2^-50) settles
+// almost every argument: its float32 rounding is taken when the whole
+// interval y (1 -+ 2^-46) around the double result y rounds to one float32
+// (rounding is monotone, so the exact value, which lies inside, rounds to the
+// same float32).  Otherwise (about one argument in 2^21, and NaN) the
+// double-double evaluation below decides.
+//
+// Double-double stage: evaluate in double-double arithmetic (an unevaluated sum hi + lo of
 // two doubles, about 106 significant bits; Dekker 1971, with the exact
 // product from a fused multiply-add), then round hi + lo to float32 once.
 //   exp:  x = k ln2 + r, |r| <= ln2/2 (Cody-Waite with a two-part ln2),
@@ -193,11 +200,8 @@ SAD_HD inline float round_dd_to_f32(double hi, double lo) {
 #define SAD_PIO2_2 0x1.1a62633145c07p-54
 #define SAD_PIO2_3 -0x1.f1976b7ed8fbcp-110
 
-SAD_HD inline float exp_cr(float xf) {
-    double x = (double)xf;
-    if (xf != xf) return xf;
-    if (x > 89.0) return __builtin_inff();
-    if (x < -104.0) return 0.0f;
+// e^x as a double-double, for a float32 x in [-104, 89]
+SAD_HD inline dd exp_dd(double x) {
     double k = __builtin_rint(x * 1.4426950408889634);
     dd kl = two_prod(k, SAD_LN2_HI);
     dd kl2 = two_prod(k, SAD_LN2_LO);
@@ -208,17 +212,20 @@ SAD_HD inline float exp_cr(float xf) {
     for (int n = 19; n >= 0; --n) s = dd_add(dd_mul(s, r), EXP_C[n]);
     int ki = (int)k;
     double scale = __builtin_ldexp(1.0, ki);
-    return round_dd_to_f32(s.hi * scale, s.lo * scale);
+    return {s.hi * scale, s.lo * scale};
 }
 
-// sin and cos of a float32 argument with |x| < 2^20
-SAD_HD inline void sincos_cr(float xf, float* s_out, float* c_out) {
-    if (xf == 0.0f) {  // keeps the sign of a zero argument in sin
-        *s_out = xf;
-        *c_out = 1.0f;
-        return;
-    }
+SAD_HD inline float exp_cr_dd(float xf) {
     double x = (double)xf;
+    if (xf != xf) return xf;
+    if (x > 89.0) return __builtin_inff();
+    if (x < -104.0) return 0.0f;
+    const dd v = exp_dd(x);
+    return round_dd_to_f32(v.hi, v.lo);
+}
+
+// sin and cos as double-doubles, for a float32 x with |x| < 2^20
+SAD_HD inline void sincos_dd(double x, dd* s_out, dd* c_out) {
     double k = __builtin_rint(x * 0.63661977236758138);  // x * 2/pi
     dd t1 = two_prod(k, SAD_PIO2_1);
     dd t2 = two_prod(k, SAD_PIO2_2);
@@ -248,8 +255,121 @@ SAD_HD inline void sincos_cr(float xf, float* s_out, float* c_out) {
         so = dd_neg(cs);
         co = sn;
     }
+    *s_out = so;
+    *c_out = co;
+}
+
+SAD_HD inline void sincos_cr_dd(float xf, float* s_out, float* c_out) {
+    if (xf == 0.0f) {  // keeps the sign of a zero argument in sin
+        *s_out = xf;
+        *c_out = 1.0f;
+        return;
+    }
+    dd so, co;
+    sincos_dd((double)xf, &so, &co);
     *s_out = round_dd_to_f32(so.hi, so.lo);
     *c_out = round_dd_to_f32(co.hi, co.lo);
+}
+
+// ---- double stage ---------------------------------------------------------
+//
+// Split constants (printed by gen_crmath_coeffs.py): the leading parts have few
+// significant bits, so k times them is exact for every k that occurs.
+// ln 2 = SAD_LN2_A + SAD_LN2_B + O(2^-85); SAD_LN2_A has 32 significant bits
+#define SAD_LN2_A 0x1.62e42fee00000p-1
+#define SAD_LN2_B 0x1.a39ef35793c76p-33
+// pi/2 = SAD_PIO2_A + SAD_PIO2_B + SAD_PIO2_C + O(2^-118); A and B have 33 significant bits
+#define SAD_PIO2_A 0x1.921fb54400000p+0
+#define SAD_PIO2_B 0x1.0b4611a600000p-34
+#define SAD_PIO2_C 0x1.3198a2e037073p-69
+
+// Called when the double stage leaves an argument to the double-double stage
+// (a counting hook for host tests; empty otherwise).
+#ifndef SAD_CR_FALLBACK_HOOK
+#define SAD_CR_FALLBACK_HOOK()
+#endif
+
+constexpr double CR_BAND = 0x1p-46;  // > 16 x the double stage's error bound
+
+// The float32 rounding of every value in y (1 -+ CR_BAND), if it is one
+// float32 (then *out holds it).  A NaN y never settles.
+SAD_HD inline bool settle_f32(double y, float* out) {
+    const float a = (float)(y * (1.0 - CR_BAND));
+    const float b = (float)(y * (1.0 + CR_BAND));
+    *out = a;
+    return a == b;
+}
+
+// exp in double: x = k ln2 + r with k = rint(x / ln2), |k| <= 150.  k SAD_LN2_A
+// is exact (40 bits) and x - k SAD_LN2_A is exact (the two are within a
+// factor of 2 when k != 0), so r carries two roundings: |dr| <= 2u|r| + 2^-77
+// (u = 2^-53).  e^r for |r| <= 0.347 from its Taylor series to degree 13
+// (remainder < 2^-56 relative) in Horner form with fused multiply-adds and
+// double coefficients: the roundings of the steps and of the coefficients
+// add at most 6u relative.  Scaling by 2^k is exact.  Total < 2^-50.
+SAD_HD inline double exp_d(double x) {  // float32 x in [-104, 89]
+    const double k = __builtin_rint(x * 1.4426950408889634);
+    const double r = (x - k * SAD_LN2_A) - k * SAD_LN2_B;
+    double p = EXP_C[13].hi;
+#pragma unroll
+    for (int n = 12; n >= 0; --n) p = __builtin_fma(p, r, EXP_C[n].hi);
+    return __builtin_ldexp(p, (int)k);
+}
+
+SAD_HD inline float exp_cr(float xf) {
+    if (xf != xf) return xf;
+    const double x = (double)xf;
+    if (x > 89.0) return __builtin_inff();
+    if (x < -104.0) return 0.0f;
+    float out;
+    if (settle_f32(exp_d(x), &out)) return out;
+    SAD_CR_FALLBACK_HOOK();
+    return exp_cr_dd(xf);
+}
+
+// sin and cos in double for |x| < 2^20: x = k pi/2 + r, |r| <= pi/4, with
+// k SAD_PIO2_A and k SAD_PIO2_B exact (|k| < 2^20) and x - k SAD_PIO2_A exact,
+// so r carries two roundings plus the 2^-118 truncation of pi/2 times k:
+// relative error < 2u + 2^-57 even for the |r| near 2^-30 that float32
+// arguments reach.  With z = r^2 <= 0.618, sin r = r (1 + z S1 + ... + z^9 S9)
+// and cos r = 1 + z C1 + ... + z^9 C9 (remainders below 2^-70), Horner form
+// with fused multiply-adds: at most about 5u relative for sin and 4u for cos
+// (cos r >= 0.707 on the interval).  Total < 2^-50.
+SAD_HD inline void sincos_d(double x, double* s_out, double* c_out) {  // float32 x, |x| < 2^20
+    const double k = __builtin_rint(x * 0.63661977236758138);
+    const double r = ((x - k * SAD_PIO2_A) - k * SAD_PIO2_B) - k * SAD_PIO2_C;
+    const double z = r * r;
+    double ps = SIN_C[9].hi, pc = COS_C[9].hi;
+#pragma unroll
+    for (int n = 8; n >= 0; --n) {
+        ps = __builtin_fma(ps, z, SIN_C[n].hi);
+        pc = __builtin_fma(pc, z, COS_C[n].hi);
+    }
+    const double sr = r * ps;
+    const long long q = (long long)k & 3;
+    *s_out = q == 0 ? sr : q == 1 ? pc : q == 2 ? -sr : -pc;
+    *c_out = q == 0 ? pc : q == 1 ? -sr : q == 2 ? -pc : sr;
+}
+
+SAD_HD inline void sincos_cr(float xf, float* s_out, float* c_out) {
+    if (xf == 0.0f) {  // keeps the sign of a zero argument in sin
+        *s_out = xf;
+        *c_out = 1.0f;
+        return;
+    }
+    const double x = (double)xf;
+    if (__builtin_fabs(x) < 0x1p20) {  // false for NaN
+        double sv, cv;
+        sincos_d(x, &sv, &cv);
+        float so, co;
+        if (settle_f32(sv, &so) && settle_f32(cv, &co)) {
+            *s_out = so;
+            *c_out = co;
+            return;
+        }
+    }
+    SAD_CR_FALLBACK_HOOK();
+    sincos_cr_dd(xf, s_out, c_out);
 }
 
 }  // namespace sad
