@@ -106,8 +106,9 @@ def cpu_baseline(wl, budget_s: float) -> dict:
 def cpu_other(include_2048: bool) -> dict:
     """The oracle on the other workloads: the 64x64 run (20 passes from an
     empty map + backward), 2^20 of the 2^24 random queries on the 768x512
-    query map (rate extrapolated linearly), and with include_2048 one
-    2048x2048 step after the oracle's own 16-pass warm-up (about a minute)."""
+    query map (rate extrapolated linearly), one 768x512 step on one thread,
+    and with include_2048 one 2048x2048 step after the oracle's own 16-pass
+    warm-up (about a minute)."""
     import oracle as ref
     import synth
 
@@ -130,6 +131,18 @@ def cpu_other(include_2048: bool) -> dict:
     ref.query_points(d, wl.h, wl.w, m, xy)
     out["query_Mqueries_per_s"] = round((1 << 20) / (time.perf_counter() - t0) / 1e6, 3)
     out["query_sample"] = "2^20 of the 2^24 points, rate extrapolated linearly"
+    # one whole 768x512 step on a single thread, beside the all-core figure
+    wl = synth.C2
+    d = ref.prepare_sites(wl.make_sites())
+    tgt = wl.make_target()
+    m = ref.propagate_schedule(d, wl.h, wl.w, None, synth.jfa_strides(wl.h, wl.w, wl.warm_passes), wl.inject_seed,
+                               0, wl.inject)
+    ref.set_threads(1)
+    t0 = time.perf_counter()
+    m = ref.propagate_schedule(d, wl.h, wl.w, m, wl.strides, wl.inject_seed, wl.warm_passes, wl.inject)
+    ref.render_bwd(d, wl.h, wl.w, m, tgt)
+    out["step_768x512_one_thread_Mpixel_iters_per_s"] = round(wl.h * wl.w / (time.perf_counter() - t0) / 1e6, 4)
+    ref.set_threads(threads)
     if include_2048:
         wl = synth.C4
         d = ref.prepare_sites(wl.make_sites())
@@ -322,6 +335,36 @@ def main() -> int:
         step(True)
     torch.cuda.synchronize()
 
+    # per-pass durations by stride: one event pair per pass (each pair adds a
+    # small gap of its own), over a few more steps
+    by_stride = {s: [] for s in strides}
+    evs = []
+    for _ in range(min(args.steps, 20)):
+        f.sites_changed()
+        for s_ in strides:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f.propagate([s_])
+            b.record(stream)
+            evs.append((s_, a, b))
+        f.forward_backward(target)
+    torch.cuda.synchronize()
+    for s_, a, b in evs:
+        by_stride[s_].append(a.elapsed_time(b) * 1e3)
+    # a plain device copy of 256 MiB: the bandwidth this machine's HBM reaches
+    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+
     per = {}
     for kind, a, b, launches in ev:
         per.setdefault(kind, []).append((a.elapsed_time(b) * 1e-3 / launches, launches))
@@ -336,7 +379,9 @@ def main() -> int:
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom), "kernel": dom,
                 "kernel_us": round(avg[dom] * 1e6, 3),
-                "bytes_per_launch": ab[dom]}
+                "bytes_per_launch": ab[dom],
+                "copy_GBps_measured": round(copy_gbs, 1),
+                "frac_of_measured_copy": round(achieved / copy_gbs, 4)}
     out = {
         "metric": "Mpixel-iters/s (propagate+fwd+bwd), 768x512 @ 50k sites; % HBM roofline",
         "value": round(value, 2),
@@ -355,6 +400,7 @@ def main() -> int:
                    "pixels": pix, "sites": wl.n, "passes_per_step": len(strides), "parallelism": "single GPU"},
         "step_frac_of_hbm_roofline": round(ab["step"] / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_us": {k: round(v * 1e6, 3) for k, v in avg.items()},
+        "pass_us_by_stride": {str(k): round(float(np.median(v)), 3) for k, v in by_stride.items()},
         "kernel_timing": f"HIP events on the launch stream over {ev_steps} further steps of separate calls: one pair "
                          "around the step's passes (per-pass average), one around the backward (with the gather)",
         "roofline": roofline,

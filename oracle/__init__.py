@@ -58,6 +58,7 @@ def lib() -> C.CDLL:
         L.sadref_propagate_pixels.argtypes = [f32p, i32, i32, i32, u32p, i32, u64, u32, i32, i64p, i64, u32p]
         L.sadref_render_fwd.argtypes = [f32p, i32, i32, i32, u32p, f64p]
         L.sadref_render_bwd.argtypes = [f32p, i32, i32, i32, u32p, f32p, f64p, f64p, f64p, f64p]
+        L.sadref_site_stats.argtypes = [f32p, i32, i32, i32, u32p, f32p, f64p, f64p]
         L.sadref_query_points.argtypes = [f32p, i32, i32, i32, u32p, f32p, i64, f64p]
         L.sadref_adam_step.argtypes = [f32p, f32p, f32p, f32p, i32, i32, i32, f32p,
                                        C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, f32p]
@@ -212,6 +213,22 @@ def render_bwd(derived: np.ndarray, h: int, w: int, topk: np.ndarray, target: np
                             _p(grad, C.c_double), _p(gabs, C.c_double), _p(loss, C.c_double),
                             _p(img, C.c_double))
     return grad, gabs, float(loss[0]), img
+
+
+def site_stats(derived: np.ndarray, h: int, w: int, topk: np.ndarray, target: np.ndarray):
+    """Per-site budget statistics (Sec. 4.5, Appendix B.5): returns (stats
+    [n][8] f64, stats_mag [n][8] f64) with columns mass, energy, removal
+    delta, sum w dx, sum w dy, sum w dx^2, sum w dx dy, sum w dy^2 (see
+    sadref_site_stats); stats_mag holds the sums of the terms' magnitudes."""
+    derived = _f32(derived).reshape(-1, REC)
+    n = derived.shape[0]
+    topk = _u32(topk).reshape(h, w, K)
+    target = _f32(target).reshape(h, w, 3)
+    stats = np.zeros((n, 8), dtype=np.float64)
+    mag = np.zeros((n, 8), dtype=np.float64)
+    lib().sadref_site_stats(_p(derived, C.c_float), n, h, w, _p(topk, C.c_uint32), _p(target, C.c_float),
+                            _p(stats, C.c_double), _p(mag, C.c_double))
+    return stats, mag
 
 
 def query_points(derived: np.ndarray, h: int, w: int, topk: np.ndarray, xy: np.ndarray) -> np.ndarray:

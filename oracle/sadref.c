@@ -430,6 +430,69 @@ void sadref_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, co
 }
 
 /* ------------------------------------------------------------------------ */
+/* Budget statistics (Sec. 4.5, "Adaptive Budget: Densify and Prune", and
+ * Appendix B.5, "Densification scores" and "Pruning").  For every site, over
+ * the pixels whose usable entries include it, with the softmax weight w, the
+ * rendered colour c and the target I of the pixel:
+ *   [0] mass           sum w
+ *   [1] energy         sum w |c - I|^2
+ *   [2] removal delta  sum (|c' - I|^2 - |c - I|^2), where c' is the blend of
+ *                      the pixel's other usable entries with their weights
+ *                      renormalised (Sec. 4.5 writes it as (c - w c_k)/(1 - w)),
+ *                      or black when the site is the pixel's only entry
+ *   [3] sum w dx   [4] sum w dy   [5] sum w dx^2   [6] sum w dx dy   [7] sum w dy^2
+ *                      with (dx, dy) = pixel centre - site position: the
+ *                      weighted second moments of Appendix B.5 taken about the
+ *                      site (their zeroth moment is the mass)
+ * stats [n][8] and stats_mag [n][8] (sums of the absolute values of the same
+ * terms, or NULL) are accumulated into (+=). */
+void sadref_site_stats(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
+                       const float *target, double *stats, double *stats_mag)
+{
+    for (int32_t j = 0; j < h; ++j) {
+        for (int32_t i = 0; i < w; ++i) {
+            size_t p = (size_t)j * w + i;
+            float px = (float)i + 0.5f, py = (float)j + 0.5f;
+            pix_eval_t e;
+            eval_point(derived, n, topk + p * K, px, py, &e);
+            const float *I = target + p * 3;
+            double err = 0.0;
+            for (int ch = 0; ch < 3; ++ch) err += (e.c[ch] - I[ch]) * (e.c[ch] - I[ch]);
+            for (int k = 0; k < e.n; ++k) {
+                /* the blend without entry k, its weights taken from the logits
+                 * relative to the largest remaining one */
+                double m = -INFINITY, z = 0.0, cp[3] = {0.0, 0.0, 0.0};
+                for (int q = 0; q < e.n; ++q)
+                    if (q != k) m = fmax(m, (double)e.l[q]);
+                for (int q = 0; q < e.n; ++q) {
+                    if (q == k) continue;
+                    const float *dq = derived + (size_t)e.id[q] * REC;
+                    double eq = exp((double)e.l[q] - m);
+                    z += eq;
+                    for (int ch = 0; ch < 3; ++ch) cp[ch] += eq * (double)dq[8 + ch];
+                }
+                double err2 = 0.0;
+                for (int ch = 0; ch < 3; ++ch) {
+                    if (z > 0.0) cp[ch] /= z;
+                    err2 += (cp[ch] - I[ch]) * (cp[ch] - I[ch]);
+                }
+                const float *d = derived + (size_t)e.id[k] * REC;
+                double wk = e.w[k];
+                double dx = (double)px - (double)d[0], dy = (double)py - (double)d[1];
+                double t[8] = {wk, wk * err, err2 - err, wk * dx, wk * dy, wk * dx * dx, wk * dx * dy, wk * dy * dy};
+                double *S = stats + (size_t)e.id[k] * 8;
+                for (int q2 = 0; q2 < 8; ++q2) S[q2] += t[q2];
+                if (stats_mag) {
+                    /* the removal delta is a difference: its scale is the sum of the two errors */
+                    double *A = stats_mag + (size_t)e.id[k] * 8;
+                    for (int q2 = 0; q2 < 8; ++q2) A[q2] += q2 == 2 ? err2 + err : fabs(t[q2]);
+                }
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Adam (Kingma and Ba, ICLR 2015) on the float32 site buffer (Sec. 5:
  * per-parameter base learning rates, fixed betas and epsilon), then the
  * projection of Sec. 4.1 (positions clamped to the image).  lr[5] holds the

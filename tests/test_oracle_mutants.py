@@ -33,6 +33,11 @@ MUTANTS = [
     ("softmax sign", "e->w[k] = exp((double)e->l[k] - m);", "e->w[k] = exp(m - (double)e->l[k]);"),
     ("adam without bias correction", "float vhat = vv[k] / bc2;", "float vhat = vv[k];"),
     ("no position clamp", "p[1] = fminf(fmaxf(p[1], 0.0f), (float)h);", "(void)h;"),
+    ("energy unweighted", "double t[8] = {wk, wk * err,", "double t[8] = {wk, err,"),
+    ("removal blend not renormalised", "if (z > 0.0) cp[ch] /= z;", "(void)z;"),
+    ("moment about the wrong axis", "double wk = e.w[k];\n                double dx = (double)px - (double)d[0], dy = (double)py - (double)d[1];",
+     "double wk = e.w[k];\n                double dx = (double)px - (double)d[0], dy = (double)py - (double)d[0];"),
+    ("cross moment missing the weight", "wk * dx * dy, wk * dy * dy};", "dx * dy, wk * dy * dy};"),
 ]
 
 
