@@ -189,8 +189,9 @@ def encode_run(torch, synth, SadField, wl, tgt, iters: int) -> dict:
 def secondary(torch, synth, ops, SadField) -> dict:
     """The other workloads, timed briefly with inputs resident on the GPU (not
     the headline): the 2048x2048 / 400k-site step, a training iteration
-    (step + Adam, the 768x512 training workload) and the Adam step alone, and
-    2^24 random-access queries on a 768x512 / 50k-site map."""
+    (step + Adam, the 768x512 training workload), the Adam step alone and the
+    budget statistics pass, the 1,000-iteration encode, and 2^24
+    random-access queries on a 768x512 / 50k-site map."""
     dev = torch.device("cuda", 0)
 
     def per_call(fn, reps):
@@ -239,7 +240,13 @@ def secondary(torch, synth, ops, SadField) -> dict:
     adam_bytes = 9 * 48 * wl.n  # params, grad, m, v read; params, m, v, grad, derived written
     out["adam_step_50k"] = {"us": round(t * 1e6, 2), "GB_per_s": round(adam_bytes / t / 1e9, 1),
                             "algorithmic_bytes": adam_bytes}
-    del f
+    stats = torch.zeros((wl.n, ops.NSTAT), dtype=torch.float32, device=dev)
+    ws = ops.bwd_workspace(wl.h, wl.w, dev)
+    t = per_call(lambda: ops.site_stats(f.derived, wl.h, wl.w, f.topk, tgt, stats, ws), 20)
+    stat_bytes = wl.h * wl.w * (32 + 12) + wl.n * (48 + 2 * 32)  # lists, target; records, stats read + written
+    out["site_stats_768x512_50k"] = {"us": round(t * 1e6, 2), "GB_per_s": round(stat_bytes / t / 1e9, 1),
+                                     "algorithmic_bytes": stat_bytes}
+    del f, stats, ws
     out["encode_768x512_50k_1000_iterations"] = encode_run(torch, synth, SadField, wl, tgt, 1000)
     del tgt
     wl = synth.C5

@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 1
+#define SAD_ABI_VERSION 2
 #define SAD_K 8
 #define SAD_SITE_STRIDE 12
 #define SAD_EMPTY 0xffffffffu
@@ -182,6 +182,30 @@ size_t sad_render_bwd_workspace_bytes(int32_t h, int32_t w);
 int sad_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
                    const float *target, float *grad, float *loss, float *image, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/*
+ * Per-site budget statistics over the map topk, the inputs of densification
+ * and pruning (Sec. 4.5, "Adaptive Budget: Densify and Prune"; Appendix B.5).
+ * For every site, summed over the pixels whose usable entries include it,
+ * with w the site's softmax weight at the pixel, c the rendered colour and I
+ * the target, stats[i][0..7] receive:
+ *   [0] mass   sum w                [1] energy  sum w |c - I|^2
+ *   [2] removal delta  sum (|c' - I|^2 - |c - I|^2): c' is the blend of the
+ *       pixel's other usable entries with their weights renormalised (black
+ *       when the site is the only one), so this is the change of the summed
+ *       squared error if the site were switched off and the lists kept
+ *   [3] sum w dx   [4] sum w dy   [5] sum w dx^2   [6] sum w dx dy
+ *   [7] sum w dy^2   with (dx, dy) = pixel centre - site position (the
+ *       weighted second moments about the site; their zeroth is the mass)
+ *   target     [h][w][3] float32, read
+ *   stats      [n][8] float32, 16-byte aligned, ACCUMULATED into (+=); the
+ *              summation order, and so the last bits, may vary between runs
+ *   workspace  as for sad_render_bwd (sad_render_bwd_workspace_bytes(h, w))
+ * Sums per site are formed as in sad_render_bwd (per-region on-chip sums,
+ * then one gather per site).
+ */
+int sad_site_stats(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
+                   const float *target, float *stats, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One training-iteration pass in one call: a propagation pass followed by

@@ -16,6 +16,11 @@ Tolerances (floating-point outputs; integer outputs are compared bit for bit):
   contribution toward zero; that adds at most count * 2^-E, count = the number of
   pixels listing the site.
 - loss: relative 1e-5.
+- budget statistics, per site and column: the gradients' bar (1e-4 |oracle|
+  + 1e-5 S, S the oracle's sum of the terms' magnitudes; for the removal
+  delta, of the two squared errors it subtracts) plus count * 2^-E_q, the
+  resolution of the GPU's fixed-point sums of that column (2^E_q chosen per
+  column from the range of its terms).
 """
 from __future__ import annotations
 
@@ -78,6 +83,33 @@ def assert_grad_close(gpu: np.ndarray, ref: np.ndarray, ref_abs: np.ndarray, wha
         i, k = np.argwhere(bad)[0]
         raise AssertionError(f"{what}: {bad.sum()} entries out of tolerance; first site {i} param {k}: "
                              f"gpu {gpu[i, k]!r} oracle {ref[i, k]!r} |term| sum {ref_abs[i, k]!r}")
+
+
+def stats_resolution(h: int, w: int) -> np.ndarray:
+    """Per-column resolution of the GPU's fixed-point statistics sums: 2^-E_q
+    with E_q = 52, 50, 49 for mass, energy and removal delta and 52 - lg,
+    52 - 2 lg for the first and second moments, 2^lg >= max(h, w)."""
+    lg = 0
+    while (1 << lg) < max(h, w):
+        lg += 1
+    e = np.array([52, 50, 49, 52 - lg, 52 - lg, 52 - 2 * lg, 52 - 2 * lg, 52 - 2 * lg], dtype=np.float64)
+    return 2.0 ** -e
+
+
+def assert_stats_close(gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray, topk: np.ndarray, hw: tuple,
+                       what: str = "stats", calls: int = 1) -> None:
+    """ref and mag cover all `calls` accumulated calls over the map topk."""
+    gpu = gpu.astype(np.float64)
+    ids = topk.reshape(-1)
+    ids = ids[ids < ref.shape[0]].astype(np.int64)
+    count = calls * np.bincount(ids, minlength=ref.shape[0]).astype(np.float64)
+    tol = GRAD_RTOL * np.abs(ref) + GRAD_STOL * mag + count[:, None] * stats_resolution(*hw)[None, :]
+    err = np.abs(gpu - ref)
+    bad = ~(err <= tol)
+    if bad.any():
+        i, k = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} entries out of tolerance; first site {i} column {k}: "
+                             f"gpu {gpu[i, k]!r} oracle {ref[i, k]!r} magnitude {mag[i, k]!r}")
 
 
 def assert_colour_close(gpu: np.ndarray, ref: np.ndarray, what: str = "colour") -> None:

@@ -27,7 +27,7 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     syms = declared_symbols()
     for name in ("sad_prepare_sites", "sad_propagate_topk", "sad_render_fwd", "sad_render_bwd",
-                 "sad_render_bwd_workspace_bytes", "sad_step_fused",
+                 "sad_render_bwd_workspace_bytes", "sad_step_fused", "sad_site_stats",
                  "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version"):
         assert name in syms
 
@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sad_abi_version() == 1
+    assert lib.sad_abi_version() == 2
     for st in (0, -1, -2, -3, 7):
         assert lib.sad_status_string(st)
 
@@ -142,3 +142,25 @@ def test_step_fused_rejects(lib):
     assert call(snext=P + 12288, img=P + 12288) == EINVAL  # image over the scores
     assert call(nxt=P + 16384, loss=P + 16384 + 64) == EINVAL  # loss inside the list map
     assert call(h=0, nxt=None, tgt=None) == 0  # empty image: nothing to do
+
+
+def test_site_stats_rejects(lib):
+    f = lib.sad_site_stats
+    WS = 1 << 30
+    wsb = lib.sad_render_bwd_workspace_bytes(8, 8)
+    ok = dict(derived=P, n=10, h=8, w=8, topk=P + 4096, tgt=P + 8192, stats=P + 65536, ws=WS, wsb=wsb)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["derived"], a["n"], a["h"], a["w"], a["topk"], a["tgt"], a["stats"], a["ws"], a["wsb"], None)
+
+    assert call(n=-1) == EINVAL
+    assert call(topk=None) == EINVAL
+    assert call(tgt=None) == EINVAL
+    assert call(stats=None) == EINVAL
+    assert call(stats=P + 65536 + 4) == EINVAL  # misaligned
+    assert call(stats=P + 16) == EINVAL  # overlaps the site records
+    assert call(ws=None) == EINVAL
+    assert call(wsb=wsb - 1) == EINVAL
+    assert call(stats=WS + 64) == EINVAL  # inside the workspace
+    assert call(h=0, topk=None, tgt=None, ws=None) == 0  # empty image: nothing to do

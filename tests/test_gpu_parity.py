@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import synth
-from gpu_util import (assert_colour_close, assert_grad_close, dev, map_to_np, say, to_gpu, to_np)
+from gpu_util import (assert_colour_close, assert_grad_close, assert_stats_close, dev, map_to_np, say, to_gpu,
+                      to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -286,6 +287,52 @@ def test_render_bwd_c2(sad, ref, c2_state):
     sad.render_bwd(dg, wl.h, wl.w, m_gpu, to_gpu(tgt), grad, loss, None)
     assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
     assert_grad_close(to_np(grad), g_ref, g_abs, "C2 gradients", m_ref, (wl.h, wl.w))
+
+
+# ---------------------------------------------------------------- budget statistics
+
+def stats_vs_oracle(sad, ref, d, dg, h, w, m_np, tgt, label, stats=None, times=1):
+    st_ref, mag = ref.site_stats(d, h, w, m_np, tgt)
+    st = sad.site_stats(dg, h, w, to_gpu(m_np), to_gpu(tgt), stats)
+    assert_stats_close(to_np(st), times * st_ref, times * mag, m_np, (h, w), label, calls=times)
+    return st
+
+
+def test_site_stats_c1(sad, ref):
+    """64x64 / 256 sites: the exact top-8 map, then a map with empty lists,
+    out-of-range ids and an inactive site."""
+    wl = synth.C1
+    p = wl.make_sites()
+    p[5, 0] = -1.0
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p))
+    tgt = wl.make_target()
+    m = ref.brute_topk(d, wl.h, wl.w)
+    stats_vs_oracle(sad, ref, d, dg, wl.h, wl.w, m, tgt, "C1 exact map")
+    rng = np.random.default_rng(3)
+    m2 = m.copy()
+    m2[rng.random(m2.shape[:2]) < 0.05] = 0xFFFFFFFF
+    m2[..., 7][rng.random(m2.shape[:2]) < 0.2] = 5
+    m2[..., 6][rng.random(m2.shape[:2]) < 0.1] = 999
+    stats_vs_oracle(sad, ref, d, dg, wl.h, wl.w, m2, tgt, "C1 map with gaps")
+
+
+def test_site_stats_c2_accumulates(sad, ref, c2_state):
+    """The 768x512 / 50k-site map after warm-up and one step; a second call
+    adds the same sums again."""
+    wl, p, d, dg, m_ref, m_gpu = c2_state
+    tgt = wl.make_target()
+    st = stats_vs_oracle(sad, ref, d, dg, wl.h, wl.w, m_ref, tgt, "C2 statistics")
+    stats_vs_oracle(sad, ref, d, dg, wl.h, wl.w, m_ref, tgt, "C2 statistics, second call", stats=st, times=2)
+
+
+@pytest.mark.parametrize("h,w,n", [(13, 29, 300), (1, 37, 20), (45, 58, 1), (70, 9, 2000)])
+def test_site_stats_ragged(sad, ref, h, w, n):
+    p = synth.sites(40 + n, n, h, w)
+    d = ref.prepare_sites(p)
+    m = ref.propagate_schedule(d, h, w, None, synth.jfa_strides(h, w, 12), 8, 0, 64)
+    tgt = np.random.default_rng(n).random((h, w, 3)).astype(np.float32)
+    stats_vs_oracle(sad, ref, d, sad.prepare_sites(to_gpu(p)), h, w, m, tgt, f"{h}x{w}, n={n}")
 
 
 # ---------------------------------------------------------------- fused pass + backward

@@ -7,6 +7,7 @@
 // backward works on regions of 2 x 4 tiles and reduces the per-site gradient
 // terms in two stages (described before k_render_bwd); queries take one
 // thread per point.
+#include <algorithm>
 #include <type_traits>
 
 #include "sad_propagate.h"
@@ -156,6 +157,8 @@ constexpr int REGION_WAVES = RT_X * RT_Y;
 constexpr int SLOTS = 256;
 constexpr int REGION_PROBES = 16;
 constexpr int NGRAD = 10;
+constexpr int NSTAT = 8;
+constexpr int NTERM_MAX = 10;
 constexpr double FIX_LIMIT_HI = 0x1p21;  // |t 2^E| < 2^53, i.e. |t 2^(E-32)| < 2^21, goes to the fixed-point sums
 constexpr uint32_t PLACEHOLDER = 0xfffffffeu;
 
@@ -175,13 +178,25 @@ __device__ __forceinline__ void home_region(float x, float y, RegionGrid rg, int
     hy = min(max((int)floorf(y * (1.0f / REGION_H)), 0), rg.rgy - 1);
 }
 
+// What a region pass sums per site from every list entry: the loss
+// gradients (into grad [n][12]) or the budget statistics (into stats [n][8]).
+struct GradSums {
+    static constexpr int N = NGRAD;
+    static constexpr int STRIDE = REC;
+};
+struct StatSums {
+    static constexpr int N = NSTAT;
+    static constexpr int STRIDE = NSTAT;
+};
+
 struct BwdArgs {
     PixArgs p;
     RegionGrid rg;
-    uint32_t* tkeys;      // [regions][SLOTS] site id, EMPTY or PLACEHOLDER
-    float* tvals;         // [regions][SLOTS][NGRAD]
-    double fix_scale_hi;  // 2^(E-32)
-    double fix_inv;       // 2^-E
+    uint32_t* tkeys;                  // [regions][SLOTS] site id, EMPTY or PLACEHOLDER
+    float* tvals;                     // [regions][SLOTS][N]
+    float* out;                       // [n][STRIDE], accumulated into
+    double fix_scale_hi[NTERM_MAX];   // per term: 2^(E_q - 32)
+    double fix_inv[NTERM_MAX];        // per term: 2^-E_q
 };
 
 // The fixed-point value of a term t, given u = t 2^(E-32) (exact in double,
@@ -198,16 +213,18 @@ __device__ __forceinline__ unsigned long long to_fixed(double u) {
     return ((unsigned long long)(uint32_t)(int32_t)hi << 32) | (unsigned long long)(uint32_t)lo;
 }
 
+template <class S>
 __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
+    constexpr bool GRAD = std::is_same_v<S, GradSums>;
     __shared__ uint32_t keys[SLOTS];
     __shared__ float4 recs[SLOTS * 3];  // prepared record of the site in each slot
-    __shared__ unsigned long long acc[NGRAD * SLOTS];
+    __shared__ unsigned long long acc[S::N * SLOTS];
     __shared__ float wsum[REGION_WAVES];
     const PixArgs& a = b.p;
     const uint32_t n = (uint32_t)a.n;
 
     for (int s = threadIdx.x; s < SLOTS; s += blockDim.x) keys[s] = EMPTY;
-    for (int s = threadIdx.x; s < NGRAD * SLOTS; s += blockDim.x) acc[s] = 0ull;
+    for (int s = threadIdx.x; s < S::N * SLOTS; s += blockDim.x) acc[s] = 0ull;
 
     const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
     const int reg = xcd_block(blockIdx.x, gridDim.x);
@@ -325,6 +342,7 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
             z += e[k];
         }
         float c[3] = {0.f, 0.f, 0.f};
+        float cl[GRAD ? 1 : K][3];  // the entries' colours (statistics only)
         if (z > 0.0f) {
             const float iz = 1.0f / z;
 #pragma unroll
@@ -335,52 +353,119 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
                 c[0] += e[k] * col.x;
                 c[1] += e[k] * col.y;
                 c[2] += e[k] * col.z;
+                if constexpr (!GRAD) {
+                    cl[k][0] = col.x;
+                    cl[k][1] = col.y;
+                    cl[k][2] = col.z;
+                }
             }
         }
-        float g[3];
+        // entry k's terms go to its slot's fixed-point sums, or to memory when
+        // it has no slot or a term is outside the fixed-point range
+        auto add_terms = [&](int k, uint32_t id, const float (&t)[S::N]) {
 #pragma unroll
-        for (int ch = 0; ch < 3; ++ch) {
-            const float r = c[ch] - tg[ch];
-            lsum += r * r;
-            g[ch] = 2.0f * r * a.inv_p;
-            if (a.image) a.image[p * 3 + ch] = c[ch];
-        }
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            if (!use[k]) continue;
-            const uint32_t id = ids[k];
-            const float w = e[k];
-            const float4 g0 = rec(k, 0), g1 = rec(k, 1), col = rec(k, 2);
-            const float tau = g0.z, cs = g1.x, sn = g1.y, is1 = g1.z, is2 = g1.w;
-            // g.(c_i - c): differences first, so a site coloured like the pixel
-            // does not lose its gradient to cancellation
-            const float delta = w * (g[0] * (col.x - c[0]) + g[1] * (col.y - c[1]) + g[2] * (col.z - c[2]));
-            float t[NGRAD];
-            t[4] = w * g[0];
-            t[5] = w * g[1];
-            t[6] = w * g[2];
-            t[2] = delta * l[k];
-            t[3] = tau * delta;
-            const float dx = px - g0.x, dy = py - g0.y;
-            const float ar = dx * cs + dy * sn, br = dy * cs - dx * sn;
-            const float aa = ar * is1, bb = br * is2;
-            const float q = aa * aa + bb * bb;
-            t[0] = t[1] = t[7] = t[8] = t[9] = 0.0f;
-            if (q > 0.0f) {
-                const float kap2 = -tau * delta * __builtin_amdgcn_rsqf(q);  // 2 kappa
-                t[0] = -kap2 * (aa * is1 * cs - bb * is2 * sn);
-                t[1] = -kap2 * (aa * is1 * sn + bb * is2 * cs);
-                t[7] = kap2 * ar * br * ((is1 - is2) * (is1 + is2));  // 1/s1^2 - 1/s2^2 without cancellation
-                t[8] = -kap2 * aa * aa;
-                t[9] = -kap2 * bb * bb;
-            }
-#pragma unroll
-            for (int q2 = 0; q2 < NGRAD; ++q2) {
-                const double u = (double)t[q2] * b.fix_scale_hi;
+            for (int q2 = 0; q2 < S::N; ++q2) {
+                const double u = (double)t[q2] * b.fix_scale_hi[q2];
                 if (slot[k] >= 0 && fabs(u) < FIX_LIMIT_HI)
                     atomicAdd(&acc[q2 * SLOTS + slot[k]], to_fixed(u));
                 else
-                    unsafeAtomicAdd(&a.grad[(size_t)id * REC + q2], t[q2]);
+                    unsafeAtomicAdd(&b.out[(size_t)id * S::STRIDE + q2], t[q2]);
+            }
+        };
+        if constexpr (GRAD) {
+            float g[3];
+#pragma unroll
+            for (int ch = 0; ch < 3; ++ch) {
+                const float r = c[ch] - tg[ch];
+                lsum += r * r;
+                g[ch] = 2.0f * r * a.inv_p;
+                if (a.image) a.image[p * 3 + ch] = c[ch];
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if (!use[k]) continue;
+                const uint32_t id = ids[k];
+                const float w = e[k];
+                const float4 g0 = rec(k, 0), g1 = rec(k, 1), col = rec(k, 2);
+                const float tau = g0.z, cs = g1.x, sn = g1.y, is1 = g1.z, is2 = g1.w;
+                // g.(c_i - c): differences first, so a site coloured like the pixel
+                // does not lose its gradient to cancellation
+                const float delta = w * (g[0] * (col.x - c[0]) + g[1] * (col.y - c[1]) + g[2] * (col.z - c[2]));
+                float t[NGRAD];
+                t[4] = w * g[0];
+                t[5] = w * g[1];
+                t[6] = w * g[2];
+                t[2] = delta * l[k];
+                t[3] = tau * delta;
+                const float dx = px - g0.x, dy = py - g0.y;
+                const float ar = dx * cs + dy * sn, br = dy * cs - dx * sn;
+                const float aa = ar * is1, bb = br * is2;
+                const float q = aa * aa + bb * bb;
+                t[0] = t[1] = t[7] = t[8] = t[9] = 0.0f;
+                if (q > 0.0f) {
+                    const float kap2 = -tau * delta * __builtin_amdgcn_rsqf(q);  // 2 kappa
+                    t[0] = -kap2 * (aa * is1 * cs - bb * is2 * sn);
+                    t[1] = -kap2 * (aa * is1 * sn + bb * is2 * cs);
+                    t[7] = kap2 * ar * br * ((is1 - is2) * (is1 + is2));  // 1/s1^2 - 1/s2^2 without cancellation
+                    t[8] = -kap2 * aa * aa;
+                    t[9] = -kap2 * bb * bb;
+                }
+                add_terms(k, id, t);
+            }
+        } else {
+            // budget statistics: mass, energy, removal delta, moments about the site
+            float err = 0.0f;
+#pragma unroll
+            for (int ch = 0; ch < 3; ++ch) err += (c[ch] - tg[ch]) * (c[ch] - tg[ch]);
+            // c' of an entry (the blend of the other usable entries) from the
+            // normalised weights, which include the largest one (>= 1/8); for
+            // the entry holding the largest logit the others are re-weighted
+            // relative to the largest remaining logit, so that their blend
+            // survives even when their normalised weights underflow
+            int top = -1;
+#pragma unroll
+            for (int k = 0; k < K; ++k) top = (top < 0 && use[k] && l[k] == mx) ? k : top;
+            float m2 = -__builtin_inff();
+#pragma unroll
+            for (int k = 0; k < K; ++k) m2 = (use[k] && k != top) ? fmaxf(m2, l[k]) : m2;
+            float ct[3] = {0.f, 0.f, 0.f}, zt = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if (!use[k] || k == top) continue;
+                const float ek = __expf(l[k] - m2);
+                zt += ek;
+                ct[0] += ek * cl[k][0];
+                ct[1] += ek * cl[k][1];
+                ct[2] += ek * cl[k][2];
+            }
+            const float izt = zt > 0.0f ? 1.0f / zt : 0.0f;  // no other entry: c' is black
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if (!use[k]) continue;
+                float cp[3] = {0.f, 0.f, 0.f}, zk = 0.0f;
+#pragma unroll
+                for (int j2 = 0; j2 < K; ++j2) {
+                    if (j2 == k || !use[j2]) continue;
+                    zk += e[j2];
+                    cp[0] += e[j2] * cl[j2][0];
+                    cp[1] += e[j2] * cl[j2][1];
+                    cp[2] += e[j2] * cl[j2][2];
+                }
+                const bool is_top = k == top;
+                const float izk = is_top ? izt : 1.0f / zk;
+                const float w = e[k];
+                // |c' - I|^2 - |c - I|^2 = (c' - c).(c' + c - 2I) with c' - c = w (c' - c_k)
+                float dl = 0.0f;
+#pragma unroll
+                for (int ch = 0; ch < 3; ++ch) {
+                    const float cpc = (is_top ? ct[ch] : cp[ch]) * izk;
+                    dl += (cpc - cl[k][ch]) * (cpc + c[ch] - 2.0f * tg[ch]);
+                }
+                const float4 g0 = rec(k, 0);
+                const float dx = px - g0.x, dy = py - g0.y;
+                const float wdx = w * dx, wdy = w * dy;
+                const float t[NSTAT] = {w, w * err, w * dl, wdx, wdy, wdx * dx, wdx * dy, wdy * dy};
+                add_terms(k, ids[k], t);
             }
         }
     };
@@ -399,20 +484,20 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
         const uint32_t id = keys[s];
         uint32_t key = id;
         if (id != EMPTY) {
-            float v[NGRAD];
+            float v[S::N];
 #pragma unroll
-            for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] = (float)((double)(long long)acc[q2 * SLOTS + s] * b.fix_inv);
+            for (int q2 = 0; q2 < S::N; ++q2) v[q2] = (float)((double)(long long)acc[q2 * SLOTS + s] * b.fix_inv[q2]);
             const float4 r0 = recs[s * 3 + 0];
             int hx, hy;
             home_region(r0.x, r0.y, b.rg, hx, hy);
             if (abs(hx - rx) <= 1 && abs(hy - ry) <= 1) {
-                float* dst = b.tvals + ((size_t)region * SLOTS + s) * NGRAD;
+                float* dst = b.tvals + ((size_t)region * SLOTS + s) * S::N;
 #pragma unroll
-                for (int q2 = 0; q2 < NGRAD; ++q2) dst[q2] = v[q2];
+                for (int q2 = 0; q2 < S::N; ++q2) dst[q2] = v[q2];
             } else {
                 key = PLACEHOLDER;
 #pragma unroll
-                for (int q2 = 0; q2 < NGRAD; ++q2) unsafeAtomicAdd(&a.grad[(size_t)id * REC + q2], v[q2]);
+                for (int q2 = 0; q2 < S::N; ++q2) unsafeAtomicAdd(&b.out[(size_t)id * S::STRIDE + q2], v[q2]);
             }
         }
         b.tkeys[(size_t)region * SLOTS + s] = key;
@@ -429,23 +514,24 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
 // per (site, table): the thread finds the site in its table by the probing the
 // backward used (stopping at an empty slot or after REGION_PROBES slots) and
 // loads the entry; then one thread per site adds the 9 partial sums in a fixed
-// order to the site's gradient record.  One writer per site, no atomics, and a
-// result that does not depend on scheduling.  A site found in no table is not
-// touched.
+// order to the site's output record (gradient or statistics).  One writer per
+// site, no atomics, and a result that does not depend on scheduling.  A site
+// found in no table is not touched.
 constexpr int GATHER_SITES = 28;  // 28 x 9 = 252 threads
 
+template <class S>
 __global__ __launch_bounds__(256) void k_grad_gather(RegionGrid rg, const uint32_t* __restrict__ tkeys,
                                                      const float* __restrict__ tvals,
-                                                     const float* __restrict__ derived, float* __restrict__ grad,
+                                                     const float* __restrict__ derived, float* __restrict__ out,
                                                      int32_t n) {
-    __shared__ float part[GATHER_SITES][9][NGRAD];
+    __shared__ float part[GATHER_SITES][9][S::N];
     __shared__ int found[GATHER_SITES][9];
     const int ls = threadIdx.x / 9, t = threadIdx.x % 9;
     const int site = blockIdx.x * GATHER_SITES + ls;
     if (ls < GATHER_SITES) {
-        float v[NGRAD];
+        float v[S::N];
 #pragma unroll
-        for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] = 0.0f;
+        for (int q2 = 0; q2 < S::N; ++q2) v[q2] = 0.0f;
         int hit = 0;
         if (site < n) {
             int hx, hy;
@@ -457,9 +543,9 @@ __global__ __launch_bounds__(256) void k_grad_gather(RegionGrid rg, const uint32
                 for (int pr = 0; pr < REGION_PROBES; ++pr) {
                     const uint32_t key = tkeys[base + pos];
                     if (key == (uint32_t)site) {
-                        const float* src = tvals + (base + pos) * NGRAD;
+                        const float* src = tvals + (base + pos) * S::N;
 #pragma unroll
-                        for (int q2 = 0; q2 < NGRAD; ++q2) v[q2] = src[q2];
+                        for (int q2 = 0; q2 < S::N; ++q2) v[q2] = src[q2];
                         hit = 1;
                         break;
                     }
@@ -469,25 +555,25 @@ __global__ __launch_bounds__(256) void k_grad_gather(RegionGrid rg, const uint32
             }
         }
 #pragma unroll
-        for (int q2 = 0; q2 < NGRAD; ++q2) part[ls][t][q2] = v[q2];
+        for (int q2 = 0; q2 < S::N; ++q2) part[ls][t][q2] = v[q2];
         found[ls][t] = hit;
     }
     __syncthreads();
     const int s2 = blockIdx.x * GATHER_SITES + (int)threadIdx.x;
     if (threadIdx.x < GATHER_SITES && s2 < n) {
         int any = 0;
-        float sum[NGRAD];
+        float sum[S::N];
 #pragma unroll
-        for (int q2 = 0; q2 < NGRAD; ++q2) sum[q2] = 0.0f;
+        for (int q2 = 0; q2 < S::N; ++q2) sum[q2] = 0.0f;
         for (int t2 = 0; t2 < 9; ++t2) {
             any |= found[threadIdx.x][t2];
 #pragma unroll
-            for (int q2 = 0; q2 < NGRAD; ++q2) sum[q2] += part[threadIdx.x][t2][q2];
+            for (int q2 = 0; q2 < S::N; ++q2) sum[q2] += part[threadIdx.x][t2][q2];
         }
         if (any) {
-            float* gr = grad + (size_t)s2 * REC;
+            float* gr = out + (size_t)s2 * S::STRIDE;
 #pragma unroll
-            for (int q2 = 0; q2 < NGRAD; ++q2) gr[q2] += sum[q2];
+            for (int q2 = 0; q2 < S::N; ++q2) gr[q2] += sum[q2];
         }
     }
 }
@@ -566,6 +652,14 @@ extern "C" size_t sad_render_bwd_workspace_bytes(int32_t h, int32_t w) {
 
 namespace sad {
 
+// The region tables in the caller's workspace.
+inline void region_tables(BwdArgs& b, void* workspace) {
+    b.rg = region_grid(b.p.h, b.p.w);
+    const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
+    b.tkeys = reinterpret_cast<uint32_t*>(workspace);
+    b.tvals = reinterpret_cast<float*>(b.tkeys + nreg * SLOTS);
+}
+
 // Argument checks of a backward pass over the list map topk, and its kernel
 // arguments.  Returns SAD_OK with b filled in, or the error status.
 inline int bwd_setup(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
@@ -585,27 +679,30 @@ inline int bwd_setup(const float* derived, int32_t n, int32_t h, int32_t w, cons
     b.p.grad = grad;
     b.p.loss = loss;
     b.p.image = image;
-    b.rg = region_grid(h, w);
-    const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
-    b.tkeys = reinterpret_cast<uint32_t*>(workspace);
-    b.tvals = reinterpret_cast<float*>(b.tkeys + nreg * SLOTS);
-    int e = 45;  // 2^E = 2^45 * (smallest power of two >= h*w)
+    b.out = grad;
+    region_tables(b, workspace);
+    int e = 45;  // 2^E = 2^45 * (smallest power of two >= h*w): the gradients carry a factor 1/(h w)
     while ((int64_t(1) << (e - 45)) < pix) ++e;
-    b.fix_scale_hi = ldexp(1.0, e - 32);
-    b.fix_inv = ldexp(1.0, -e);
+    for (int q = 0; q < NTERM_MAX; ++q) {
+        b.fix_scale_hi[q] = ldexp(1.0, e - 32);
+        b.fix_inv[q] = ldexp(1.0, -e);
+    }
     return SAD_OK;
 }
 
-int bwd_launch(const BwdArgs& b, void* stream) {
+template <class S>
+int region_launch(const BwdArgs& b, void* stream) {
     const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
     clear_error();
-    hipLaunchKernelGGL(k_render_bwd, dim3((unsigned)nreg), dim3(WAVE * REGION_WAVES), 0, as_stream(stream), b);
+    hipLaunchKernelGGL(k_render_bwd<S>, dim3((unsigned)nreg), dim3(WAVE * REGION_WAVES), 0, as_stream(stream), b);
     if (b.p.n > 0)
-        hipLaunchKernelGGL(k_grad_gather, dim3((unsigned)((b.p.n + GATHER_SITES - 1) / GATHER_SITES)),
+        hipLaunchKernelGGL(k_grad_gather<S>, dim3((unsigned)((b.p.n + GATHER_SITES - 1) / GATHER_SITES)),
                            dim3(GATHER_SITES * 9), 0, as_stream(stream), b.rg, b.tkeys, b.tvals, b.p.derived,
-                           b.p.grad, b.p.n);
+                           b.out, b.p.n);
     return launch_status();
 }
+
+int bwd_launch(const BwdArgs& b, void* stream) { return region_launch<GradSums>(b, stream); }
 
 }  // namespace sad
 
@@ -617,6 +714,40 @@ extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_
     if (st != SAD_OK) return st;
     if (int64_t(h) * w == 0) return SAD_OK;
     return bwd_launch(b, stream);
+}
+
+extern "C" int sad_site_stats(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
+                              const float* target, float* stats, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    int st = pix_common(derived, n, h, w, topk);
+    if (st != SAD_OK) return st;
+    const int64_t pix = int64_t(h) * w;
+    if (!array_ok(target, pix, 4) || !array_ok(stats, n, 16)) return SAD_EINVAL;
+    const int64_t sbytes = int64_t(n) * NSTAT * 4;
+    if (overlap(stats, sbytes, derived, int64_t(n) * REC * 4)) return SAD_EINVAL;
+    const size_t need = sad_render_bwd_workspace_bytes(h, w);
+    if (pix > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)) return SAD_EINVAL;
+    if (overlap(workspace, (int64_t)need, stats, sbytes) || overlap(workspace, (int64_t)need, target, pix * 12))
+        return SAD_EINVAL;
+    if (pix == 0) return SAD_OK;
+    BwdArgs b;
+    b.p = pix_args(derived, n, h, w, topk);
+    b.p.target = target;
+    b.out = stats;
+    region_tables(b, workspace);
+    // per-term fixed-point scales 2^E_q with |t| 2^E_q < 2^52 for the usual
+    // range of each term: weights <= 1, errors of colours in [0, 1] <= 3 (the
+    // removal delta <= 6), offsets from a site inside the image <= D (the
+    // smallest power of two >= max(h, w)); other terms go to float atomics
+    int lg = 0;
+    while ((int64_t(1) << lg) < std::max(h, w)) ++lg;
+    const int eq[NSTAT] = {52, 50, 49, 52 - lg, 52 - lg, 52 - 2 * lg, 52 - 2 * lg, 52 - 2 * lg};
+    for (int q = 0; q < NTERM_MAX; ++q) {
+        const int e = eq[q < NSTAT ? q : 0];
+        b.fix_scale_hi[q] = ldexp(1.0, e - 32);
+        b.fix_inv[q] = ldexp(1.0, -e);
+    }
+    return region_launch<StatSums>(b, stream);
 }
 
 extern "C" int sad_step_fused(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk_prev,

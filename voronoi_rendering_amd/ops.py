@@ -16,6 +16,7 @@ from . import _native
 
 K = 8
 REC = 12
+NSTAT = 8  # budget statistics per site
 EMPTY_I32 = -1
 
 
@@ -127,6 +128,27 @@ def render_bwd(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target
                                       _ptr(image), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(derived))
     _native.check("sad_render_bwd", st)
+
+
+def site_stats(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target: torch.Tensor,
+               stats: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Accumulate the per-site budget statistics ([n][8]: mass, energy,
+    removal delta, sum w dx, sum w dy, sum w dx^2, sum w dx dy, sum w dy^2)
+    into ``stats`` (zeros when not given) and return it."""
+    n = derived.shape[0]
+    _need(derived, "derived", torch.float32, (n, REC))
+    _need(topk, "topk", torch.int32, (h, w, K))
+    _need(target, "target", torch.float32, (h, w, 3))
+    if stats is None:
+        stats = torch.zeros((n, NSTAT), dtype=torch.float32, device=derived.device)
+    _need(stats, "stats", torch.float32, (n, NSTAT))
+    if workspace is None:
+        workspace = bwd_workspace(h, w, derived.device)
+    st = _native.lib().sad_site_stats(_ptr(derived), n, h, w, _ptr(topk), _ptr(target), _ptr(stats),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(derived))
+    _native.check("sad_site_stats", st)
+    return stats
 
 
 def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor,
