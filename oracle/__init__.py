@@ -59,6 +59,8 @@ def lib() -> C.CDLL:
         L.sadref_render_fwd.argtypes = [f32p, i32, i32, i32, u32p, f64p]
         L.sadref_render_bwd.argtypes = [f32p, i32, i32, i32, u32p, f32p, f64p, f64p, f64p, f64p]
         L.sadref_site_stats.argtypes = [f32p, i32, i32, i32, u32p, f32p, f64p, f64p]
+        L.sadref_jfa_seed.argtypes = [f32p, i32, i32, i32, u32p]
+        L.sadref_jfa_flood.argtypes = [f32p, i32, i32, i32, u32p, u32p, i32, i32]
         L.sadref_query_points.argtypes = [f32p, i32, i32, i32, u32p, f32p, i64, f64p]
         L.sadref_adam_step.argtypes = [f32p, f32p, f32p, f32p, i32, i32, i32, f32p,
                                        C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, f32p]
@@ -184,6 +186,60 @@ def propagate_schedule(derived: np.ndarray, h: int, w: int, prev: np.ndarray | N
     if cur is None:
         cur = empty_map(h, w)
     return cur
+
+
+JFA_K = 4
+
+
+def jfa_steps(h: int, w: int) -> list[int]:
+    """Jump steps of a JFA round: B/2, B/4, ..., 1 with B = 2^ceil(log2 max(h, w))."""
+    b = 1
+    while b < max(h, w):
+        b *= 2
+    out = []
+    s = b // 2
+    while s >= 1:
+        out.append(s)
+        s //= 2
+    return out
+
+
+def jfa_seed(derived: np.ndarray, h: int, w: int) -> np.ndarray:
+    """Seed pass of the JFA prepass (see sadref_jfa_seed): [h][w][4] u32."""
+    derived = _f32(derived).reshape(-1, REC)
+    out = np.empty((h, w, JFA_K), dtype=np.uint32)
+    lib().sadref_jfa_seed(_p(derived, C.c_float), derived.shape[0], h, w, _p(out, C.c_uint32))
+    return out
+
+
+def jfa_flood(derived: np.ndarray, h: int, w: int, prev: np.ndarray, step: int, out_width: int = JFA_K) -> np.ndarray:
+    """One flood pass (see sadref_jfa_flood): [h][w][out_width] u32."""
+    derived = _f32(derived).reshape(-1, REC)
+    prev = _u32(prev).reshape(h, w, JFA_K)
+    out = np.empty((h, w, out_width), dtype=np.uint32)
+    lib().sadref_jfa_flood(_p(derived, C.c_float), derived.shape[0], h, w, _p(prev, C.c_uint32),
+                           _p(out, C.c_uint32), step, out_width)
+    return out
+
+
+def full_refresh(derived: np.ndarray, h: int, w: int, seed: int, n_pass: int = 16, inject: int = 64) -> np.ndarray:
+    """The render protocol's list rebuild (Sec. 6.6): one JFA round (seed and
+    flood passes, the last one writing a top-K map), then n_pass propagation
+    passes on the warm-up schedule with pass indices 0, 1, ..."""
+    steps = jfa_steps(h, w)
+    cur = jfa_seed(derived, h, w)
+    for t, s in enumerate(steps):
+        cur = jfa_flood(derived, h, w, cur, s, K if t == len(steps) - 1 else JFA_K)
+    if not steps:  # a 1x1 image: the seed alone, widened
+        cur = np.concatenate([cur, np.full((h, w, K - JFA_K), 0xFFFFFFFF, np.uint32)], axis=-1)
+    strides = []
+    b = 1
+    while b < max(h, w):
+        b *= 2
+    lb = b.bit_length() - 1
+    for t in range(n_pass):
+        strides.append(max(1, b >> (min(t, max(lb - 1, 0)) + 1)))
+    return propagate_schedule(derived, h, w, cur, strides, seed, 0, inject)
 
 
 def render_fwd(derived: np.ndarray, h: int, w: int, topk: np.ndarray) -> np.ndarray:

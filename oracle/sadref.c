@@ -260,6 +260,73 @@ void sadref_propagate_pixels(const float *derived, int32_t n, int32_t h, int32_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* JFA prepass of a full refresh (Appendix B.3, "JFA prepass"; the render
+ * protocol of Sec. 6.6 runs one JFA round before 16 propagation passes),
+ * after the jump flooding of Rong and Tan (2006).  The prepass keeps JFA_K = 4
+ * ids per pixel, ranked at the pixel centre like the top-K lists.
+ *
+ * Seed: a usable site whose logit at the centre of the pixel holding its
+ * position (floor, clamped to the image) is a number claims that pixel; of
+ * several sites on one pixel the one ranking first there stays.
+ * jfa [h][w][4]: the seed id or NONE in slot 0, NONE in slots 1..3. */
+#define JFA_K 4
+
+void sadref_jfa_seed(const float *derived, int32_t n, int32_t h, int32_t w, uint32_t *jfa)
+{
+    size_t pix = (size_t)h * w;
+    for (size_t p = 0; p < pix * JFA_K; ++p) jfa[p] = NONE;
+    if (pix == 0) return;
+    float *best = (float *)malloc(sizeof(float) * pix);
+    for (int32_t i = 0; i < n; ++i) {
+        if (!site_usable(derived, n, (uint32_t)i)) continue;
+        const float *d = derived + (size_t)i * REC;
+        int32_t ci = (int32_t)fminf(fmaxf(floorf(d[0]), 0.0f), (float)(w - 1));
+        int32_t cj = (int32_t)fminf(fmaxf(floorf(d[1]), 0.0f), (float)(h - 1));
+        if (!(d[1] == d[1])) cj = 0;  /* a NaN y: the first row (its logit is NaN anyway) */
+        size_t p = (size_t)cj * w + ci;
+        float s = score_at(d, (float)ci + 0.5f, (float)cj + 0.5f);
+        if (isnan(s)) continue;
+        uint32_t cur = jfa[p * JFA_K];
+        if (cur == NONE || s > best[p] || (s == best[p] && (uint32_t)i < cur)) {
+            jfa[p * JFA_K] = (uint32_t)i;
+            best[p] = s;
+        }
+    }
+    free(best);
+}
+
+/* Flood pass with jump step `step`: every pixel keeps the JFA_K best distinct
+ * usable ids among the 4-lists of the pixels at (i + a step, j + b step),
+ * a, b in {-1, 0, 1}, that lie inside the image (its own list included),
+ * ranked at its own centre.  out_width 4 writes [h][w][4]; out_width 8 writes
+ * a top-K map [h][w][8] with slots 4..7 NONE (the start of the propagation
+ * passes). */
+void sadref_jfa_flood(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *prev, uint32_t *next,
+                      int32_t step, int32_t out_width)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t j = 0; j < h; ++j) {
+        cand_t c[9 * JFA_K];
+        uint32_t top[K];
+        for (int32_t i = 0; i < w; ++i) {
+            float px = (float)i + 0.5f, py = (float)j + 0.5f;
+            int nc = 0;
+            for (int b = -1; b <= 1; ++b) {
+                for (int a = -1; a <= 1; ++a) {
+                    int64_t ii = (int64_t)i + (int64_t)a * step, jj = (int64_t)j + (int64_t)b * step;
+                    if (ii < 0 || ii >= w || jj < 0 || jj >= h) continue;
+                    const uint32_t *l = prev + ((size_t)jj * w + (size_t)ii) * JFA_K;
+                    for (int k = 0; k < JFA_K; ++k) nc = add_cand(c, nc, derived, n, l[k], px, py);
+                }
+            }
+            topk_of(c, nc, top);  /* sorted, distinct: its first JFA_K entries are the JFA_K best */
+            uint32_t *o = next + ((size_t)j * w + i) * (size_t)out_width;
+            for (int k = 0; k < out_width; ++k) o[k] = k < JFA_K ? top[k] : NONE;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Soft additively weighted rendering (Sec. 4.2): softmax of the logits over
  * the pixel's list, then the weighted colour blend.  Entries that name no
  * usable site or whose float32 logit is not finite are skipped; an empty list

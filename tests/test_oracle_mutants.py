@@ -38,6 +38,10 @@ MUTANTS = [
     ("moment about the wrong axis", "double wk = e.w[k];\n                double dx = (double)px - (double)d[0], dy = (double)py - (double)d[1];",
      "double wk = e.w[k];\n                double dx = (double)px - (double)d[0], dy = (double)py - (double)d[0];"),
     ("cross moment missing the weight", "wk * dx * dy, wk * dy * dy};", "dx * dy, wk * dy * dy};"),
+    ("flood without the diagonal neighbours", "for (int a = -1; a <= 1; ++a) {",
+     "for (int a = -1; a <= 1; ++a) {\n                    if (a != 0 && b != 0) continue;"),
+    ("seed keeps the worst-ranked site", "if (cur == NONE || s > best[p] ||", "if (cur == NONE || s < best[p] ||"),
+    ("flood step only along x", "jj = (int64_t)j + (int64_t)b * step;", "jj = (int64_t)j + (int64_t)b;"),
 ]
 
 
