@@ -186,6 +186,61 @@ def encode_run(torch, synth, SadField, wl, tgt, iters: int) -> dict:
             "note": "setup, 16 warm-up passes and all iterations inside the wall clock"}
 
 
+# The pages' per-call times of the same protocol on an NVIDIA RTX 5090 at 1.0
+# bits per pixel (Table 8: full refresh = one JFA round + 16 propagation
+# passes + render; Table 9: the stages), in ms.  Context only: other
+# hardware, and site counts set by the pages' bit budget rather than these.
+PAGES_REFRESH_MS = {512: {"total": 1.100, "render": 0.015, "passes16": 0.728, "pass1": 0.053},
+                    1024: {"total": 4.614, "render": 0.034, "passes16": 2.568, "pass1": 0.168},
+                    2048: {"total": 26.539, "render": 0.132, "passes16": 16.009, "pass1": 1.006}}
+
+
+def refresh_timings(torch, synth, ops, SadField) -> dict:
+    """The render protocol from the sites alone at 512^2, 1024^2 and 2048^2
+    (site density of the 2048^2 workload: 25k, 100k, 400k sites): one JFA
+    round, 16 propagation passes, the render, and for comparison one pass;
+    HIP events on the launch stream, 10 warm-up + 30 timed calls, medians."""
+    import numpy as np
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for side, n in ((512, 25_000), (1024, 100_000), (2048, 400_000)):
+        p = torch.from_numpy(synth.sites(7000 + side, n, side, side, synth.WIDE_SCALES)).to(dev)
+        f = SadField(p, side, side, 5000 + side)
+        img = torch.empty((side, side, 3), dtype=torch.float32, device=dev)
+        steps = ops.jfa_steps(side, side)
+        strides16 = ops.jfa_strides(side, side, 16)
+        rec = []
+        for it in range(40):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            ev[0].record(stream)
+            f.refresh(0)  # the JFA round alone
+            ev[1].record(stream)
+            f.propagate(strides16)
+            ev[2].record(stream)
+            ops.render_fwd(f.derived, side, side, f.topk, img)
+            ev[3].record(stream)
+            f.sites_changed()
+            f.propagate([1])
+            ev[4].record(stream)
+            if it >= 10:
+                rec.append(ev)
+        torch.cuda.synchronize()
+        t = {k: [] for k in ("jfa_round", "passes16", "render", "pass1")}
+        for ev in rec:
+            for k, (a, b) in zip(t, ((0, 1), (1, 2), (2, 3), (3, 4))):
+                t[k].append(ev[a].elapsed_time(ev[b]))
+        med = {k: float(np.median(v)) for k, v in t.items()}
+        out[f"{side}x{side}_{n // 1000}k"] = {
+            "total_ms": round(med["jfa_round"] + med["passes16"] + med["render"], 4),
+            "jfa_round_ms": round(med["jfa_round"], 4), "jfa_passes": len(steps) + 1,
+            "passes16_ms": round(med["passes16"], 4), "render_ms": round(med["render"], 4),
+            "pass1_ms": round(med["pass1"], 4), "pages_rtx5090_ms": PAGES_REFRESH_MS[side]}
+        del f, p, img
+    return out
+
+
 def secondary(torch, synth, ops, SadField) -> dict:
     """The other workloads, timed briefly with inputs resident on the GPU (not
     the headline): the 2048x2048 / 400k-site step, a training iteration
@@ -258,6 +313,8 @@ def secondary(torch, synth, ops, SadField) -> dict:
     m = xy.shape[0]
     out["query_2e24_points"] = {"Mqueries_per_s": round(m / t / 1e6, 1), "ms": round(t * 1e3, 3),
                                 "GB_per_s_algorithmic": round(52 * m / t / 1e9, 1)}
+    del f, xy, rgb
+    out["full_refresh"] = refresh_timings(torch, synth, ops, SadField)
     return out
 
 

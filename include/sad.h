@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 2
+#define SAD_ABI_VERSION 3
 #define SAD_K 8
 #define SAD_SITE_STRIDE 12
 #define SAD_EMPTY 0xffffffffu
@@ -206,6 +206,30 @@ int sad_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, const 
  */
 int sad_site_stats(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
                    const float *target, float *stats, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * JFA prepass of a full list refresh (Appendix B.3, "JFA prepass"; the render
+ * protocol of Sec. 6.6 runs one JFA round, then propagation passes starting
+ * from the round's last output, then the render), after the jump flooding of
+ * Rong and Tan (2006).  A 4-list holds 4 site ids ranked at the pixel centre
+ * as the top-K lists are, EMPTY-padded.
+ *
+ * sad_jfa_seed: jfa [h][w][4] uint32 (16-byte aligned) is overwritten: the
+ * pixel holding a usable site's position (floor of x and y, clamped to the
+ * image) gets in slot 0 the site ranking first at its centre among the sites
+ * on it; every other slot is EMPTY.
+ *
+ * sad_jfa_flood: one flood pass with jump step `step` >= 1: every pixel gets
+ * the 4 best distinct usable ids of the 4-lists jfa_prev at (i + a step,
+ * j + b step), a, b in {-1, 0, 1}, inside the image (its own included).
+ * out_width 4 writes out as [h][w][4]; out_width 8 writes a top-K map
+ * [h][w][8] with slots 4..7 EMPTY, the start of the propagation passes.  A
+ * round runs the steps B/2, B/4, ..., 1 with B the smallest power of two
+ * >= max(h, w).  out must not overlap jfa_prev or derived.
+ */
+int sad_jfa_seed(const float *derived, int32_t n, int32_t h, int32_t w, uint32_t *jfa, void *stream);
+int sad_jfa_flood(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *jfa_prev, uint32_t *out,
+                  int32_t step, int32_t out_width, void *stream);
 
 /*
  * One training-iteration pass in one call: a propagation pass followed by

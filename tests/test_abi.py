@@ -27,7 +27,8 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     syms = declared_symbols()
     for name in ("sad_prepare_sites", "sad_propagate_topk", "sad_render_fwd", "sad_render_bwd",
-                 "sad_render_bwd_workspace_bytes", "sad_step_fused", "sad_site_stats",
+                 "sad_render_bwd_workspace_bytes", "sad_step_fused", "sad_site_stats", "sad_jfa_seed",
+                 "sad_jfa_flood",
                  "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version"):
         assert name in syms
 
@@ -41,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sad_abi_version() == 2
+    assert lib.sad_abi_version() == 3
     for st in (0, -1, -2, -3, 7):
         assert lib.sad_status_string(st)
 
@@ -164,3 +165,18 @@ def test_site_stats_rejects(lib):
     assert call(wsb=wsb - 1) == EINVAL
     assert call(stats=WS + 64) == EINVAL  # inside the workspace
     assert call(h=0, topk=None, tgt=None, ws=None) == 0  # empty image: nothing to do
+
+
+def test_jfa_rejects(lib):
+    assert lib.sad_jfa_seed(P, -1, 8, 8, P + 4096, None) == EINVAL
+    assert lib.sad_jfa_seed(P, 10, 8, 8, None, None) == EINVAL
+    assert lib.sad_jfa_seed(P, 10, 8, 8, P + 4100, None) == EINVAL  # misaligned
+    assert lib.sad_jfa_seed(P, 10, 8, 8, P + 64, None) == EINVAL  # over the site records
+    assert lib.sad_jfa_seed(P, 10, 0, 8, None, None) == 0  # empty image
+    f = lib.sad_jfa_flood
+    assert f(P, 10, 8, 8, P + 4096, P + 8192, 0, 4, None) == EINVAL  # step 0
+    assert f(P, 10, 8, 8, P + 4096, P + 8192, 1, 5, None) == EINVAL  # width
+    assert f(P, 10, 8, 8, None, P + 8192, 1, 4, None) == EINVAL
+    assert f(P, 10, 8, 8, P + 4096, P + 4096 + 512, 1, 8, None) == EINVAL  # out over the input
+    assert f(P, 10, 8, 8, P + 4096, P + 16, 1, 4, None) == EINVAL  # out over the site records
+    assert f(P, 10, 0, 8, None, None, 1, 4, None) == 0

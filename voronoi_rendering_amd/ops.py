@@ -151,6 +151,47 @@ def site_stats(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target
     return stats
 
 
+JFA_K = 4  # ids per pixel in the JFA prepass
+
+
+def jfa_steps(h: int, w: int) -> list[int]:
+    """Jump steps of a JFA round: B/2, B/4, ..., 1, B the smallest power of two >= max(h, w)."""
+    b = 1
+    while b < max(h, w):
+        b *= 2
+    steps, s = [], b // 2
+    while s >= 1:
+        steps.append(s)
+        s //= 2
+    return steps
+
+
+def jfa_seed(derived: torch.Tensor, h: int, w: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Seed pass of the JFA prepass into ``out`` ([h][w][4] int32)."""
+    n = derived.shape[0]
+    _need(derived, "derived", torch.float32, (n, REC))
+    if out is None:
+        out = torch.empty((h, w, JFA_K), dtype=torch.int32, device=derived.device)
+    _need(out, "out", torch.int32, (h, w, JFA_K))
+    _native.check("sad_jfa_seed", _native.lib().sad_jfa_seed(_ptr(derived), n, h, w, _ptr(out), _stream(derived)))
+    return out
+
+
+def jfa_flood(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor, step: int, out_width: int = JFA_K,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """One flood pass of the JFA prepass; ``out`` is [h][w][4], or with
+    out_width 8 a top-K map [h][w][8]."""
+    n = derived.shape[0]
+    _need(derived, "derived", torch.float32, (n, REC))
+    _need(prev, "prev", torch.int32, (h, w, JFA_K))
+    if out is None:
+        out = torch.empty((h, w, out_width), dtype=torch.int32, device=derived.device)
+    _need(out, "out", torch.int32, (h, w, out_width))
+    _native.check("sad_jfa_flood", _native.lib().sad_jfa_flood(_ptr(derived), n, h, w, _ptr(prev), _ptr(out),
+                                                                int(step), int(out_width), _stream(derived)))
+    return out
+
+
 def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor,
                target: torch.Tensor, grad: torch.Tensor, *, stride: int, seed: int, pass_index: int,
                inject: int = 64, prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None,

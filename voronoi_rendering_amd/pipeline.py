@@ -56,6 +56,7 @@ class SadField:
         self.pass_index = 0
         self.adam_t = 0
         self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+        self._jfa = None  # ping-pong 4-lists of the JFA prepass, made on first use
 
     @property
     def topk(self) -> torch.Tensor:
@@ -77,6 +78,29 @@ class SadField:
 
     def warm(self, n_pass: int) -> None:
         """Fill the map from scratch with the warm-up jump schedule."""
+        self.propagate(ops.jfa_strides(self.h, self.w, n_pass))
+
+    def refresh(self, n_pass: int = 16) -> None:
+        """Rebuild the map from the sites alone (the render protocol of Sec. 6.6):
+        one JFA round (seed, then flood passes B/2, ..., 1, the last one writing
+        the top-K map), then n_pass propagation passes on the warm-up schedule."""
+        steps = ops.jfa_steps(self.h, self.w)
+        if not steps:  # a 1x1 image: the seed alone
+            self.maps[self.cur].fill_(-1)
+            self.maps[self.cur][..., :ops.JFA_K] = ops.jfa_seed(self.derived, self.h, self.w)
+        else:
+            if self._jfa is None:
+                self._jfa = [torch.empty((self.h, self.w, ops.JFA_K), dtype=torch.int32, device=self.params.device)
+                             for _ in range(2)]
+            a, b = self._jfa
+            ops.jfa_seed(self.derived, self.h, self.w, a)
+            for t, s in enumerate(steps):
+                if t == len(steps) - 1:
+                    ops.jfa_flood(self.derived, self.h, self.w, a, s, ops.K, self.maps[self.cur])
+                else:
+                    ops.jfa_flood(self.derived, self.h, self.w, a, s, ops.JFA_K, b)
+                    a, b = b, a
+        self.scores_valid = False
         self.propagate(ops.jfa_strides(self.h, self.w, n_pass))
 
     def forward_backward(self, target: torch.Tensor, image: torch.Tensor | None = None) -> None:
