@@ -328,6 +328,8 @@ def main() -> int:
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads' timings")
     ap.add_argument("--cpu-all", action="store_true",
                     help="also time the oracle on one 2048x2048 step (adds about a minute)")
+    ap.add_argument("--refresh-only", action="store_true",
+                    help="only time the full refresh (JFA round + 16 passes + render) at 512^2, 1024^2, 2048^2")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -352,6 +354,9 @@ def main() -> int:
     from voronoi_rendering_amd import ops
     from voronoi_rendering_amd.pipeline import SadField
 
+    if args.refresh_only:
+        print(json.dumps({"full_refresh": refresh_timings(torch, synth, ops, SadField)}), flush=True)
+        return 0
     wl = synth.C2
     dev = torch.device("cuda", 0)
     params = torch.from_numpy(wl.make_sites()).to(dev)
