@@ -61,6 +61,9 @@ def lib() -> C.CDLL:
         L.sadref_site_stats.argtypes = [f32p, i32, i32, i32, u32p, f32p, f64p, f64p]
         L.sadref_jfa_seed.argtypes = [f32p, i32, i32, i32, u32p]
         L.sadref_jfa_flood.argtypes = [f32p, i32, i32, i32, u32p, u32p, i32, i32]
+        f32 = C.c_float
+        L.sadref_densify_prune.argtypes = [f32p, f32p, f32p, f32p, i32, i32, i32, f32p, f32p, i32, i32, f32, f32, f32,
+                                           f32, f32, C.POINTER(C.c_int32)]
         L.sadref_query_points.argtypes = [f32p, i32, i32, i32, u32p, f32p, i64, f64p]
         L.sadref_adam_step.argtypes = [f32p, f32p, f32p, f32p, i32, i32, i32, f32p,
                                        C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, f32p]
@@ -186,6 +189,25 @@ def propagate_schedule(derived: np.ndarray, h: int, w: int, prev: np.ndarray | N
     if cur is None:
         cur = empty_map(h, w)
     return cur
+
+
+def densify_prune(params: np.ndarray, m: np.ndarray, v: np.ndarray, derived: np.ndarray, h: int, w: int,
+                  stats: np.ndarray, target: np.ndarray, n_split: int, n_prune: int, alpha: float, min_mass: float,
+                  offset: float, r_scale: float, logtau_shift: float):
+    """Budget control (see sadref_densify_prune) on copies of the site
+    arrays: returns (params, m, v, derived, (pruned, split))."""
+    params = _f32(params).reshape(-1, REC).copy()
+    n = params.shape[0]
+    m = _f32(m).reshape(n, REC).copy()
+    v = _f32(v).reshape(n, REC).copy()
+    derived = _f32(derived).reshape(n, REC).copy()
+    stats = _f32(stats).reshape(n, 8)
+    target = _f32(target).reshape(h, w, 3)
+    done = (C.c_int32 * 2)()
+    lib().sadref_densify_prune(_p(params, C.c_float), _p(m, C.c_float), _p(v, C.c_float), _p(derived, C.c_float),
+                               n, h, w, _p(stats, C.c_float), _p(target, C.c_float), n_split, n_prune, alpha,
+                               min_mass, offset, r_scale, logtau_shift, done)
+    return params, m, v, derived, (int(done[0]), int(done[1]))
 
 
 JFA_K = 4

@@ -560,6 +560,161 @@ void sadref_site_stats(const float *derived, int32_t n, int32_t h, int32_t w, co
 }
 
 /* ------------------------------------------------------------------------ */
+/* Budget control: densify and prune (Sec. 4.5; Appendix B.5 "Densification
+ * scores", "Split kernel", "Pruning").  Inputs: the sites, their Adam
+ * moments and prepared records, the statistics of sadref_site_stats (as
+ * float32) and the target.  The pages leave the amounts open; they are
+ * arguments here.
+ *  1. Prune: the n_prune active sites with the lowest removal delta (a NaN
+ *     delta ranks last; ties: lower id first) are switched off, position
+ *     (-1, -1).
+ *  2. Split candidates: sites still active with mass >= min_mass and mass > 0,
+ *     ranked by the densification score energy / mass^alpha (in double;
+ *     ties: lower id first; a NaN score is not a candidate).
+ *  3. The i-th candidate is split into the i-th inactive slot (ascending index)
+ *     while both last and i < n_split.  Axis: the principal eigenvector of the
+ *     weighted covariance about the site (from the moments), sigma the square
+ *     root of its eigenvalue; when that is degenerate, the direction of the
+ *     Sobel gradient of the target (channels summed) at the site's pixel, or
+ *     (1, 0) when that is zero, with sigma the site's larger scale.  The two
+ *     children sit at position +- offset sigma axis (the parent's slot takes
+ *     +, clamped to the image), take the target colour of their pixels,
+ *     log tau - logtau_shift and r * r_scale, and keep theta and the scales;
+ *     both get zero Adam moments.
+ *  4. The prepared records of every touched site are rewritten.
+ * All geometry in float32, one rounding per operation in the written order.
+ * done[0] = sites pruned, done[1] = sites split. */
+typedef struct { double key; uint32_t id; } rank_t;
+
+static int rank_asc(const void *pa, const void *pb)
+{
+    const rank_t *a = (const rank_t *)pa, *b = (const rank_t *)pb;
+    if (a->key < b->key) return -1;
+    if (a->key > b->key) return 1;
+    return a->id < b->id ? -1 : (a->id > b->id);
+}
+
+static float target_sum(const float *target, int32_t h, int32_t w, int32_t i, int32_t j)
+{
+    i = i < 0 ? 0 : (i >= w ? w - 1 : i);
+    j = j < 0 ? 0 : (j >= h ? h - 1 : j);
+    const float *t = target + ((size_t)j * w + i) * 3;
+    return (t[0] + t[1]) + t[2];
+}
+
+static int32_t cell_of(float v, int32_t size)
+{
+    return (int32_t)fminf(fmaxf(floorf(v), 0.0f), (float)(size - 1));
+}
+
+void sadref_densify_prune(float *params, float *m, float *v, float *derived, int32_t n, int32_t h, int32_t w,
+                          const float *stats, const float *target, int32_t n_split, int32_t n_prune, float alpha,
+                          float min_mass, float offset, float r_scale, float logtau_shift, int32_t *done)
+{
+    rank_t *r = (rank_t *)malloc(sizeof(rank_t) * (size_t)(n > 0 ? n : 1));
+    uint32_t *slots = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
+    int32_t nr = 0, pruned = 0, split = 0;
+    /* 1. prune */
+    for (int32_t i = 0; i < n; ++i) {
+        if (!(params[(size_t)i * REC] >= 0.0f)) continue;
+        float dl = stats[(size_t)i * 8 + 2];
+        r[nr].key = isnan(dl) ? INFINITY : (double)dl;
+        r[nr].id = (uint32_t)i;
+        nr++;
+    }
+    qsort(r, (size_t)nr, sizeof(rank_t), rank_asc);
+    for (int32_t k = 0; k < nr && k < n_prune; ++k) {
+        float *p = params + (size_t)r[k].id * REC;
+        p[0] = -1.0f;
+        p[1] = -1.0f;
+        sadref_prepare_sites(p, 1, derived + (size_t)r[k].id * REC);
+        pruned++;
+    }
+    /* 2. candidates, best first (the key is the negated score) */
+    nr = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const float *st = stats + (size_t)i * 8;
+        if (!(params[(size_t)i * REC] >= 0.0f) || !(st[0] >= min_mass) || !(st[0] > 0.0f)) continue;
+        double score = (double)st[1] / pow((double)st[0], (double)alpha);
+        if (isnan(score)) continue;
+        r[nr].key = -score;
+        r[nr].id = (uint32_t)i;
+        nr++;
+    }
+    qsort(r, (size_t)nr, sizeof(rank_t), rank_asc);
+    /* 3. free slots, ascending */
+    int32_t nf = 0;
+    for (int32_t i = 0; i < n; ++i)
+        if (!(params[(size_t)i * REC] >= 0.0f)) slots[nf++] = (uint32_t)i;
+    for (int32_t k = 0; k < nr && k < nf && k < n_split; ++k) {
+        uint32_t pi = r[k].id, ci = slots[k];
+        float *pp = params + (size_t)pi * REC, *pc = params + (size_t)ci * REC;
+        const float *st = stats + (size_t)pi * 8;
+        const float *d = derived + (size_t)pi * REC;
+        /* axis from the covariance about the site */
+        float ms = st[0];
+        float mx = st[3] / ms, my = st[4] / ms;
+        float a = st[5] / ms - mx * mx, b = st[6] / ms - mx * my, c = st[7] / ms - my * my;
+        float half = (a - c) * 0.5f;
+        float lam = (a + c) * 0.5f + sqrtf(half * half + b * b);
+        float e1x = b, e1y = lam - a, e2x = lam - c, e2y = b;
+        float n1 = e1x * e1x + e1y * e1y, n2 = e2x * e2x + e2y * e2y;
+        float ex = n1 >= n2 ? e1x : e2x, ey = n1 >= n2 ? e1y : e2y, nn = n1 >= n2 ? n1 : n2;
+        float ux, uy, sigma;
+        if (lam > 0.0f && nn > 0.0f && isfinite(lam) && isfinite(nn)) {
+            float len = sqrtf(nn);
+            ux = ex / len;
+            uy = ey / len;
+            sigma = sqrtf(lam);
+        } else {
+            int32_t i0 = cell_of(d[0], w), j0 = cell_of(d[1], h);
+            float gx = (target_sum(target, h, w, i0 + 1, j0 - 1) + 2.0f * target_sum(target, h, w, i0 + 1, j0) +
+                        target_sum(target, h, w, i0 + 1, j0 + 1)) -
+                       (target_sum(target, h, w, i0 - 1, j0 - 1) + 2.0f * target_sum(target, h, w, i0 - 1, j0) +
+                        target_sum(target, h, w, i0 - 1, j0 + 1));
+            float gy = (target_sum(target, h, w, i0 - 1, j0 + 1) + 2.0f * target_sum(target, h, w, i0, j0 + 1) +
+                        target_sum(target, h, w, i0 + 1, j0 + 1)) -
+                       (target_sum(target, h, w, i0 - 1, j0 - 1) + 2.0f * target_sum(target, h, w, i0, j0 - 1) +
+                        target_sum(target, h, w, i0 + 1, j0 - 1));
+            float gl = sqrtf(gx * gx + gy * gy);
+            ux = gl > 0.0f ? gx / gl : 1.0f;
+            uy = gl > 0.0f ? gy / gl : 0.0f;
+            sigma = 1.0f / fminf(d[6], d[7]);
+        }
+        float dx = (offset * sigma) * ux, dy = (offset * sigma) * uy;
+        float x = pp[0], y = pp[1];
+        float pos[2][2] = {{fminf(fmaxf(x + dx, 0.0f), (float)w), fminf(fmaxf(y + dy, 0.0f), (float)h)},
+                           {fminf(fmaxf(x - dx, 0.0f), (float)w), fminf(fmaxf(y - dy, 0.0f), (float)h)}};
+        float base[REC];
+        for (int q = 0; q < REC; ++q) base[q] = pp[q];
+        for (int ch = 0; ch < 2; ++ch) {
+            float *o = ch == 0 ? pp : pc;
+            uint32_t oi = ch == 0 ? pi : ci;
+            for (int q = 0; q < REC; ++q) o[q] = base[q];
+            o[0] = pos[ch][0];
+            o[1] = pos[ch][1];
+            const float *t = target + ((size_t)cell_of(pos[ch][1], h) * w + cell_of(pos[ch][0], w)) * 3;
+            o[4] = t[0];
+            o[5] = t[1];
+            o[6] = t[2];
+            o[2] = base[2] - logtau_shift;
+            o[3] = base[3] * r_scale;
+            for (int q = 0; q < REC; ++q) {
+                m[(size_t)oi * REC + q] = 0.0f;
+                v[(size_t)oi * REC + q] = 0.0f;
+            }
+        }
+        sadref_prepare_sites(pp, 1, derived + (size_t)pi * REC);
+        sadref_prepare_sites(pc, 1, derived + (size_t)ci * REC);
+        split++;
+    }
+    done[0] = pruned;
+    done[1] = split;
+    free(r);
+    free(slots);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Adam (Kingma and Ba, ICLR 2015) on the float32 site buffer (Sec. 5:
  * per-parameter base learning rates, fixed betas and epsilon), then the
  * projection of Sec. 4.1 (positions clamped to the image).  lr[5] holds the

@@ -42,6 +42,12 @@ MUTANTS = [
      "for (int a = -1; a <= 1; ++a) {\n                    if (a != 0 && b != 0) continue;"),
     ("seed keeps the worst-ranked site", "if (cur == NONE || s > best[p] ||", "if (cur == NONE || s < best[p] ||"),
     ("flood step only along x", "jj = (int64_t)j + (int64_t)b * step;", "jj = (int64_t)j + (int64_t)b;"),
+    ("prune the highest removal deltas", "r[nr].key = isnan(dl) ? INFINITY : (double)dl;",
+     "r[nr].key = isnan(dl) ? INFINITY : -(double)dl;"),
+    ("split along the minor axis", "float lam = (a + c) * 0.5f + sqrtf(half * half + b * b);",
+     "float lam = (a + c) * 0.5f - sqrtf(half * half + b * b);"),
+    ("children keep the parent's colour", "o[4] = t[0];", "o[4] = base[4];"),
+    ("children keep their Adam moments", "m[(size_t)oi * REC + q] = 0.0f;", "(void)oi;"),
 ]
 
 
