@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 3
+#define SAD_ABI_VERSION 4
 #define SAD_K 8
 #define SAD_SITE_STRIDE 12
 #define SAD_EMPTY 0xffffffffu
@@ -206,6 +206,42 @@ int sad_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, const 
  */
 int sad_site_stats(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
                    const float *target, float *stats, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Budget control from the statistics of sad_site_stats (Sec. 4.5, "Adaptive
+ * Budget: Densify and Prune"; Appendix B.5, "Densification scores", "Split
+ * kernel", "Pruning").  In place on params, adam_m, adam_v and derived
+ * ([n][12] float32 each, the Adam moments as sad_adam_step keeps them):
+ *   1. the n_prune active sites with the lowest removal delta (stats[i][2];
+ *      NaN ranks last; ties: lower id first) are switched off: position
+ *      (-1, -1);
+ *   2. the sites still active with mass stats[i][0] >= min_mass and > 0 are
+ *      ranked by energy / mass^alpha (stats[i][1] / stats[i][0]^alpha in
+ *      double; best first, ties: lower id; NaN scores skipped); while k <
+ *      n_split and both lists last, the k-th is split into the k-th inactive
+ *      slot (ascending index): its two children sit at its position
+ *      +- offset sigma u (its own slot takes +; each clamped to [0, w] x
+ *      [0, h]), with u and sigma^2 the major eigenvector and eigenvalue of
+ *      the weighted covariance about the site (moments stats[i][3..7] over
+ *      the mass), or when those are degenerate u the direction of the Sobel
+ *      gradient of the target (channels summed) at the site's pixel ((1, 0)
+ *      when zero) and sigma the site's larger scale; the children take the
+ *      target colour at their pixels, log tau - logtau_shift, r * r_scale,
+ *      the parent's theta and scales, and zero Adam moments;
+ *   3. the prepared records of every changed site are rewritten.
+ * The geometry is float32, one rounding per operation in that order.
+ *   stats      [n][8] float32 (16-byte aligned) as sad_site_stats writes it
+ *   target     [h][w][3] float32
+ *   done       NULL, or a device int32[2]: the numbers of sites pruned and split
+ *   workspace  device scratch of sad_budget_workspace_bytes(n) bytes,
+ *              256-byte aligned, owned by the caller (the rankings' keys and
+ *              the radix sorts' storage)
+ */
+size_t sad_budget_workspace_bytes(int32_t n);
+int sad_densify_prune(float *params, float *adam_m, float *adam_v, float *derived, int32_t n, int32_t h, int32_t w,
+                      const float *stats, const float *target, int32_t n_split, int32_t n_prune, float alpha,
+                      float min_mass, float offset, float r_scale, float logtau_shift, int32_t *done,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * JFA prepass of a full list refresh (Appendix B.3, "JFA prepass"; the render

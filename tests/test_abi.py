@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     syms = declared_symbols()
     for name in ("sad_prepare_sites", "sad_propagate_topk", "sad_render_fwd", "sad_render_bwd",
                  "sad_render_bwd_workspace_bytes", "sad_step_fused", "sad_site_stats", "sad_jfa_seed",
-                 "sad_jfa_flood",
+                 "sad_jfa_flood", "sad_budget_workspace_bytes", "sad_densify_prune",
                  "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version"):
         assert name in syms
 
@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sad_abi_version() == 3
+    assert lib.sad_abi_version() == 4
     for st in (0, -1, -2, -3, 7):
         assert lib.sad_status_string(st)
 
@@ -180,3 +180,30 @@ def test_jfa_rejects(lib):
     assert f(P, 10, 8, 8, P + 4096, P + 4096 + 512, 1, 8, None) == EINVAL  # out over the input
     assert f(P, 10, 8, 8, P + 4096, P + 16, 1, 4, None) == EINVAL  # out over the site records
     assert f(P, 10, 0, 8, None, None, 1, 4, None) == 0
+
+
+def test_densify_prune_rejects(lib):
+    f = lib.sad_densify_prune
+    n = 10
+    wsb = lib.sad_budget_workspace_bytes(n)
+    WS = 1 << 30
+    ok = dict(p=P, m=P + 4096, v=P + 8192, d=P + 12288, n=n, h=8, w=8, st=P + 16384, t=P + 20480, ns=2, npr=1,
+              done=None, ws=WS, wsb=wsb)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["p"], a["m"], a["v"], a["d"], a["n"], a["h"], a["w"], a["st"], a["t"], a["ns"], a["npr"], 1.0,
+                 1.0, 0.5, 0.85, 0.1, a["done"], a["ws"], a["wsb"], None)
+
+    assert call(ns=-1) == EINVAL
+    assert call(npr=-1) == EINVAL
+    assert call(m=None) == EINVAL
+    assert call(st=P + 16384 + 4) == EINVAL  # misaligned
+    assert call(v=P + 4096 + 64) == EINVAL  # the moments overlap
+    assert call(h=0, t=None) == EINVAL  # sites but no target image
+    assert call(ws=None) == EINVAL
+    assert call(ws=WS + 16) == EINVAL  # workspace not 256-byte aligned
+    assert call(wsb=wsb - 1) == EINVAL
+    assert call(done=P + 2) == EINVAL
+    assert call(done=P + 8) == EINVAL  # inside the sites
+    assert call(n=0, ws=None, done=None) == 0  # no sites and no counts: nothing to launch

@@ -335,6 +335,104 @@ def test_site_stats_ragged(sad, ref, h, w, n):
     stats_vs_oracle(sad, ref, d, sad.prepare_sites(to_gpu(p)), h, w, m, tgt, f"{h}x{w}, n={n}")
 
 
+# ---------------------------------------------------------------- budget control
+
+def budget_case(ref, seed, n, h, w, stats=None, d=None, p=None):
+    rng = np.random.default_rng(seed)
+    if p is None:
+        p = synth.sites(seed, n, h, w)
+        p[rng.random(n) < 0.15, 0] = -1.0
+    m = rng.normal(size=p.shape).astype(np.float32)
+    v = rng.random(p.shape).astype(np.float32)
+    t = rng.random((h, w, 3)).astype(np.float32)
+    d = ref.prepare_sites(p) if d is None else d
+    if stats is None:
+        stats = np.zeros((n, 8), np.float32)
+        stats[:, 0] = rng.random(n) * 10
+        stats[:, 1] = rng.random(n) * 2
+        stats[:, 2] = rng.normal(size=n)
+        stats[:, 3:5] = rng.normal(size=(n, 2))
+        stats[:, 5] = stats[:, 7] = rng.random(n) * 20 + 5
+        stats[:, 6] = rng.normal(size=n)
+        stats[rng.random(n) < 0.05, 5:8] = 0.0  # degenerate covariance: the target's gradient decides
+    return p, m, v, d, stats, t
+
+
+def budget_vs_oracle(sad, ref, p, m, v, d, stats, t, h, w, label, **kw):
+    want = ref.densify_prune(p, m, v, d, h, w, stats, t, kw["n_split"], kw["n_prune"], kw["alpha"], kw["min_mass"],
+                             kw["offset"], kw["r_scale"], kw["logtau_shift"])
+    gp, gm, gv, gd = (to_gpu(x) for x in (p, m, v, d))
+    done = sad.densify_prune(gp, gm, gv, gd, h, w, to_gpu(stats), to_gpu(t), **kw)
+    for got, exp, name in zip((gp, gm, gv, gd), want[:4], ("params", "m", "v", "derived")):
+        got = to_np(got)
+        assert np.array_equal(got.view(np.uint32), exp.view(np.uint32)), \
+            f"{label}: {name} differs at sites {np.unique(np.argwhere(got != exp)[:, 0])[:8]}"
+    assert tuple(to_np(done)) == want[4], label
+
+
+@pytest.mark.parametrize("alpha", [0.0, 1.0, 0.7])
+def test_densify_prune_bit_exact(sad, ref, alpha):
+    h, w, n = 40, 52, 600
+    p, m, v, d, st, t = budget_case(ref, 31, n, h, w)
+    kw = dict(n_split=40, n_prune=25, alpha=alpha, min_mass=1.0, offset=0.5, r_scale=0.85, logtau_shift=0.1)
+    budget_vs_oracle(sad, ref, p, m, v, d, st, t, h, w, f"alpha {alpha}", **kw)
+
+
+def test_densify_prune_limits(sad, ref):
+    h, w, n = 17, 23, 80
+    p, m, v, d, st, t = budget_case(ref, 33, n, h, w)
+    # more splits than free slots, more prunes than active sites
+    for ns, npr in ((70, 0), (5, 200), (0, 0), (200, 10)):
+        kw = dict(n_split=ns, n_prune=npr, alpha=1.0, min_mass=0.5, offset=0.7, r_scale=0.9, logtau_shift=0.05)
+        budget_vs_oracle(sad, ref, p, m, v, d, st, t, h, w, f"split {ns} prune {npr}", **kw)
+
+
+def test_densify_prune_on_real_statistics(sad, ref, c2_state):
+    """The 768x512 / 50k-site map: statistics from the GPU, then the same
+    float32 statistics into both sides."""
+    wl, p, d, dg, m_ref, m_gpu = c2_state
+    tgt = wl.make_target()
+    stats = to_np(sad.site_stats(dg, wl.h, wl.w, m_gpu, to_gpu(tgt)))
+    p2 = p.copy()
+    p2[::50, 0] = -1.0  # free slots
+    d2 = ref.prepare_sites(p2)
+    _, m, v, _, _, _ = budget_case(ref, 35, wl.n, wl.h, wl.w, stats=stats, d=d2, p=p2)
+    kw = dict(n_split=800, n_prune=500, alpha=1.0, min_mass=1.0, offset=0.5, r_scale=0.85, logtau_shift=0.1)
+    budget_vs_oracle(sad, ref, p2, m, v, d2, stats, tgt, wl.h, wl.w, "768x512 statistics", **kw)
+
+
+def test_densify_prune_without_sites(sad):
+    e = torch.zeros((0, 12), dtype=torch.float32, device=dev())
+    done = sad.densify_prune(e, e.clone(), e.clone(), e.clone(), 8, 8, torch.zeros((0, 8), device=dev()),
+                             torch.zeros((8, 8, 3), device=dev()), n_split=3, n_prune=3)
+    assert tuple(to_np(done)) == (0, 0)
+
+
+def test_field_densify_prune_bookkeeping(sad, ref):
+    """SadField.densify_prune: statistics from the field's own map, then the
+    budget step; the active count moves by split - pruned, the prepared
+    records follow the sites, and the field keeps training."""
+    from voronoi_rendering_amd.pipeline import SadField
+
+    wl = synth.C1
+    p = wl.make_sites()
+    p[np.random.default_rng(2).random(wl.n) < 0.2, 0] = -1.0
+    f = SadField(to_gpu(p), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+    f.warm(16)
+    tgt = to_gpu(wl.make_target())
+    before = int((f.params[:, 0] >= 0).sum())
+    done = to_np(f.densify_prune(tgt, n_split=30, n_prune=12, min_mass=0.5))
+    after = to_np(f.params)
+    assert done[0] == 12 and 0 < done[1] <= 30
+    assert int((after[:, 0] >= 0).sum()) == before - done[0] + done[1]
+    assert np.array_equal(to_np(f.derived).view(np.uint32), ref.prepare_sites(after).view(np.uint32))
+    prev, first = map_to_np(f.topk), f.pass_index
+    f.propagate([4, 2, 1])
+    want = ref.propagate_schedule(ref.prepare_sites(after), wl.h, wl.w, prev, [4, 2, 1], wl.inject_seed, first,
+                                  wl.inject)
+    assert np.array_equal(map_to_np(f.topk), want)
+
+
 # ---------------------------------------------------------------- JFA prepass and full refresh
 
 def crowded_sites(seed, n, h, w):

@@ -80,6 +80,15 @@ class SadField:
         """Fill the map from scratch with the warm-up jump schedule."""
         self.propagate(ops.jfa_strides(self.h, self.w, n_pass))
 
+    def densify_prune(self, target: torch.Tensor, **budget) -> torch.Tensor:
+        """Budget control over the current map: the per-site statistics, then
+        prune and split (keyword arguments as ops.densify_prune).  Returns the
+        numbers pruned and split (device int32[2])."""
+        stats = ops.site_stats(self.derived, self.h, self.w, self.topk, target)
+        done = ops.densify_prune(self.params, self.m, self.v, self.derived, self.h, self.w, stats, target, **budget)
+        self.sites_changed()
+        return done
+
     def refresh(self, n_pass: int = 16) -> None:
         """Rebuild the map from the sites alone (the render protocol of Sec. 6.6):
         one JFA round (seed, then flood passes B/2, ..., 1, the last one writing
