@@ -241,11 +241,47 @@ def refresh_timings(torch, synth, ops, SadField) -> dict:
     return out
 
 
+def budget_timings(torch, synth, ops, SadField) -> dict:
+    """The budget step on the 768x512 / 50k-site training workload after the
+    warm-up passes: the statistics of the map, then prune and split 500 sites
+    each; every timed call starts from the same copy of the sites (the copy is
+    outside the events).  HIP events on the launch stream, 5 warm-up + 20
+    timed calls, median."""
+    import numpy as np
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    wl = synth.C3
+    f = SadField(torch.from_numpy(wl.make_sites()).to(dev), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+    tgt = torch.from_numpy(wl.make_target()).to(dev)
+    f.warm(wl.warm_passes)
+    stats = ops.site_stats(f.derived, wl.h, wl.w, f.topk, tgt)
+    ws = ops.budget_workspace(wl.n, dev)
+    done = torch.zeros(2, dtype=torch.int32, device=dev)
+    state = (f.params, f.m, f.v, f.derived)
+    saved = [x.clone() for x in state]
+    rec = []
+    for it in range(25):
+        for x, y in zip(state, saved):
+            x.copy_(y)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        ops.densify_prune(*state, wl.h, wl.w, stats, tgt, n_split=500, n_prune=500, workspace=ws, done=done)
+        ev[1].record(stream)
+        if it >= 5:
+            rec.append(ev)
+    torch.cuda.synchronize()
+    t = float(np.median([a.elapsed_time(b) for a, b in rec]))
+    pruned, split = (int(x) for x in done.cpu())
+    return {"us": round(t * 1e3, 2), "pruned": pruned, "split": split, "sites": wl.n,
+            "note": "2 stable radix sorts over 50k keys, a stable select and 4 small kernels; launch- and latency-bound"}
+
+
 def secondary(torch, synth, ops, SadField) -> dict:
     """The other workloads, timed briefly with inputs resident on the GPU (not
     the headline): the 2048x2048 / 400k-site step, a training iteration
-    (step + Adam, the 768x512 training workload), the Adam step alone and the
-    budget statistics pass, the 1,000-iteration encode, and 2^24
+    (step + Adam, the 768x512 training workload), the Adam step alone, the
+    budget statistics pass and the budget step, the 1,000-iteration encode, and 2^24
     random-access queries on a 768x512 / 50k-site map."""
     dev = torch.device("cuda", 0)
 
@@ -302,6 +338,7 @@ def secondary(torch, synth, ops, SadField) -> dict:
     out["site_stats_768x512_50k"] = {"us": round(t * 1e6, 2), "GB_per_s": round(stat_bytes / t / 1e9, 1),
                                      "algorithmic_bytes": stat_bytes}
     del f, stats, ws
+    out["densify_prune_768x512_50k"] = budget_timings(torch, synth, ops, SadField)
     out["encode_768x512_50k_1000_iterations"] = encode_run(torch, synth, SadField, wl, tgt, 1000)
     del tgt
     wl = synth.C5
@@ -330,6 +367,8 @@ def main() -> int:
                     help="also time the oracle on one 2048x2048 step (adds about a minute)")
     ap.add_argument("--refresh-only", action="store_true",
                     help="only time the full refresh (JFA round + 16 passes + render) at 512^2, 1024^2, 2048^2")
+    ap.add_argument("--budget-only", action="store_true",
+                    help="only time the budget step (statistics given; prune and split 500 of 50k sites)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -356,6 +395,9 @@ def main() -> int:
 
     if args.refresh_only:
         print(json.dumps({"full_refresh": refresh_timings(torch, synth, ops, SadField)}), flush=True)
+        return 0
+    if args.budget_only:
+        print(json.dumps({"densify_prune_768x512_50k": budget_timings(torch, synth, ops, SadField)}), flush=True)
         return 0
     wl = synth.C2
     dev = torch.device("cuda", 0)

@@ -5,6 +5,9 @@
 // The rankings are stable radix sorts of per-site keys (the pages sort
 // key-value pairs by radix): a float mapped to an unsigned integer of the
 // same order, with the site id as the value, so equal keys keep ascending ids.
+// Sites that do not take part get the largest key, so the ranked ones form a
+// prefix of the sorted keys and no counts are needed; the free slots come
+// from a stable select of the inactive ids.
 //   1. prune: the n_prune active sites with the lowest removal delta are
 //      switched off (position (-1, -1));
 //   2. split: the sites still active with enough mass, ranked by
@@ -39,8 +42,9 @@ struct BudgetArgs {
     uint32_t *pkey, *pkey_s, *pid, *pid_s;          // prune ranking
     unsigned long long *skey, *skey_s;              // split ranking
     uint32_t *sid, *sid_s;
-    uint32_t *fkey, *fkey_s, *fid, *fid_s;          // free slots
-    int32_t* count;                                 // [0] active, [1] candidates, [2] free
+    uint8_t* free_flag;                             // [n] 1 for an inactive site
+    uint32_t* slot;                                 // free slots, ascending
+    int32_t* n_free;                                // [1] the number of free slots
     void* cub;                                      // the sorts' temporary storage
 };
 
@@ -56,31 +60,32 @@ __device__ __forceinline__ unsigned long long ordered64(double s) {
 
 __device__ __forceinline__ bool active_site(const float* params, int i) { return params[(size_t)i * REC] >= 0.0f; }
 
-// one atomic per wavefront for a per-lane flag count
-__device__ __forceinline__ void count_lanes(bool flag, int32_t* counter) {
-    const uint64_t b = __ballot(flag);
-    if ((threadIdx.x & (WAVE - 1)) == 0 && b) atomicAdd(counter, (int32_t)__popcll(b));
-}
-
 __global__ void k_budget_clear(int32_t* p, int k) {
     if ((int)threadIdx.x < k) p[threadIdx.x] = 0;
 }
 
+constexpr uint32_t NO_KEY32 = 0xFFFFFFFFu;  // larger than any active site's key (a NaN delta maps to +inf)
+constexpr unsigned long long NO_KEY64 = ~0ull;
+
 __global__ __launch_bounds__(256) void k_budget_prune_keys(BudgetArgs a) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    const bool in = i < a.n;
-    const bool act = in && active_site(a.params, i);
-    if (in) {
-        const float dl = a.stats[(size_t)i * NSTAT_B + 2];
-        a.pkey[i] = act ? ordered32(dl == dl ? dl : __builtin_inff()) : 0xFFFFFFFFu;
-        a.pid[i] = (uint32_t)i;
+    if (i == 0 && a.done) {
+        a.done[0] = 0;
+        a.done[1] = 0;
     }
-    count_lanes(act, &a.count[0]);
+    if (i >= a.n) return;
+    const float dl = a.stats[(size_t)i * NSTAT_B + 2];
+    a.pkey[i] = active_site(a.params, i) ? ordered32(dl == dl ? dl : __builtin_inff()) : NO_KEY32;
+    a.pid[i] = (uint32_t)i;
 }
 
+// Thread k prunes the k-th ranked site; the ranked sites are a prefix of the
+// sorted keys, so the last thread that prunes knows how many did.
 __global__ __launch_bounds__(256) void k_budget_prune(BudgetArgs a) {
     const int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= a.n_prune || k >= a.count[0]) return;
+    const int last = min(a.n_prune, a.n) - 1;
+    if (k > last || a.pkey_s[k] == NO_KEY32) return;
+    if (a.done && (k == last || a.pkey_s[k + 1] == NO_KEY32)) a.done[0] = k + 1;
     const uint32_t s = a.pid_s[k];
     float* p = a.params + (size_t)s * REC;
     p[0] = -1.0f;
@@ -91,22 +96,16 @@ __global__ __launch_bounds__(256) void k_budget_prune(BudgetArgs a) {
 
 __global__ __launch_bounds__(256) void k_budget_split_keys(BudgetArgs a) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    const bool in = i < a.n;
-    const bool act = in && active_site(a.params, i);
-    bool cand = false;
-    if (in) {
-        const float* st = a.stats + (size_t)i * NSTAT_B;
-        const float mass = st[0];
-        cand = act && (mass >= a.min_mass) && (mass > 0.0f);
-        const double score = (double)st[1] / pow((double)mass, (double)a.alpha);
-        cand = cand && (score == score);
-        a.skey[i] = cand ? ~ordered64(score) : ~0ull;  // best first
-        a.sid[i] = (uint32_t)i;
-        a.fkey[i] = act ? 1u : 0u;  // free slots first
-        a.fid[i] = (uint32_t)i;
-    }
-    count_lanes(cand, &a.count[1]);
-    count_lanes(in && !act, &a.count[2]);
+    if (i >= a.n) return;
+    const bool act = active_site(a.params, i);
+    const float* st = a.stats + (size_t)i * NSTAT_B;
+    const float mass = st[0];
+    bool cand = act && (mass >= a.min_mass) && (mass > 0.0f);
+    const double score = (double)st[1] / pow((double)mass, (double)a.alpha);
+    cand = cand && (score == score);
+    a.skey[i] = cand ? ~ordered64(score) : NO_KEY64;  // best first; ~ordered64 of a number is never ~0
+    a.sid[i] = (uint32_t)i;
+    a.free_flag[i] = act ? 0 : 1;
 }
 
 __device__ __forceinline__ float target_sum(const float* target, int h, int w, int i, int j) {
@@ -120,10 +119,13 @@ __device__ __forceinline__ int cell_of(float v, int size) {
     return (int)fminf(fmaxf(floorf(v), 0.0f), (float)(size - 1));
 }
 
+// Thread k splits the k-th ranked candidate into the k-th free slot.
 __global__ __launch_bounds__(256) void k_budget_split(BudgetArgs a) {
     const int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= a.n_split || k >= a.count[1] || k >= a.count[2]) return;
-    const uint32_t pi = a.sid_s[k], ci = a.fid_s[k];
+    const int last = min(a.n_split, *a.n_free) - 1;
+    if (k > last || a.skey_s[k] == NO_KEY64) return;
+    if (a.done && (k == last || a.skey_s[k + 1] == NO_KEY64)) a.done[1] = k + 1;
+    const uint32_t pi = a.sid_s[k], ci = a.slot[k];
     float* pp = a.params + (size_t)pi * REC;
     float* pc = a.params + (size_t)ci * REC;
     const float* st = a.stats + (size_t)pi * NSTAT_B;
@@ -199,23 +201,17 @@ __global__ __launch_bounds__(256) void k_budget_split(BudgetArgs a) {
     }
 }
 
-__global__ void k_budget_done(BudgetArgs a) {
-    if (threadIdx.x == 0) {
-        a.done[0] = min(a.n_prune, a.count[0]);
-        a.done[1] = min(a.n_split, min(a.count[1], a.count[2]));
-    }
-}
-
 // Workspace layout for n sites; returns the total bytes (pointers filled when base != nullptr).
 inline size_t budget_layout(int32_t n, char* base, BudgetArgs* a, size_t* cub_bytes) {
     size_t cb_p = 0, cb_s = 0, cb_f = 0;
+    hipcub::CountingInputIterator<uint32_t> ids(0);
     (void)hipcub::DeviceRadixSort::SortPairs(nullptr, cb_p, (uint32_t*)nullptr, (uint32_t*)nullptr,
                                              (uint32_t*)nullptr, (uint32_t*)nullptr, n, 0, 32);
     (void)hipcub::DeviceRadixSort::SortPairs(nullptr, cb_s, (unsigned long long*)nullptr,
                                              (unsigned long long*)nullptr, (uint32_t*)nullptr, (uint32_t*)nullptr, n,
                                              0, 64);
-    (void)hipcub::DeviceRadixSort::SortPairs(nullptr, cb_f, (uint32_t*)nullptr, (uint32_t*)nullptr,
-                                             (uint32_t*)nullptr, (uint32_t*)nullptr, n, 0, 1);
+    (void)hipcub::DeviceSelect::Flagged(nullptr, cb_f, ids, (const uint8_t*)nullptr, (uint32_t*)nullptr,
+                                        (int32_t*)nullptr, n);
     const size_t cub = std::max(cb_p, std::max(cb_s, cb_f));
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -224,19 +220,19 @@ inline size_t budget_layout(int32_t n, char* base, BudgetArgs* a, size_t* cub_by
         return p;
     };
     const size_t n4 = (size_t)n * 4, n8 = (size_t)n * 8;
-    char* p[14];
+    char* p[12];
     p[0] = take(n4); p[1] = take(n4); p[2] = take(n4); p[3] = take(n4);
     p[4] = take(n8); p[5] = take(n8); p[6] = take(n4); p[7] = take(n4);
-    p[8] = take(n4); p[9] = take(n4); p[10] = take(n4); p[11] = take(n4);
-    p[12] = take(16);
-    p[13] = take(cub);
+    p[8] = take((size_t)n); p[9] = take(n4);
+    p[10] = take(16);
+    p[11] = take(cub);
     if (a) {
         a->pkey = (uint32_t*)p[0]; a->pkey_s = (uint32_t*)p[1]; a->pid = (uint32_t*)p[2]; a->pid_s = (uint32_t*)p[3];
         a->skey = (unsigned long long*)p[4]; a->skey_s = (unsigned long long*)p[5];
         a->sid = (uint32_t*)p[6]; a->sid_s = (uint32_t*)p[7];
-        a->fkey = (uint32_t*)p[8]; a->fkey_s = (uint32_t*)p[9]; a->fid = (uint32_t*)p[10]; a->fid_s = (uint32_t*)p[11];
-        a->count = (int32_t*)p[12];
-        a->cub = p[13];
+        a->free_flag = (uint8_t*)p[8]; a->slot = (uint32_t*)p[9];
+        a->n_free = (int32_t*)p[10];
+        a->cub = p[11];
     }
     if (cub_bytes) *cub_bytes = cub;
     return off;
@@ -299,7 +295,6 @@ extern "C" int sad_densify_prune(float* params, float* adam_m, float* adam_v, fl
     budget_layout(n, static_cast<char*>(workspace), &a, &cub);
     void* cub_tmp = a.cub;
     const unsigned g = (unsigned)((n + 255) / 256);
-    hipLaunchKernelGGL(k_budget_clear, dim3(1), dim3(64), 0, s, a.count, 3);
     hipLaunchKernelGGL(k_budget_prune_keys, dim3(g), dim3(256), 0, s, a);
     size_t tb = cub;
     if (hipcub::DeviceRadixSort::SortPairs(cub_tmp, tb, a.pkey, a.pkey_s, a.pid, a.pid_s, n, 0, 32, s) != hipSuccess)
@@ -311,10 +306,10 @@ extern "C" int sad_densify_prune(float* params, float* adam_m, float* adam_v, fl
     if (hipcub::DeviceRadixSort::SortPairs(cub_tmp, tb, a.skey, a.skey_s, a.sid, a.sid_s, n, 0, 64, s) != hipSuccess)
         return SAD_EHIP;
     tb = cub;
-    if (hipcub::DeviceRadixSort::SortPairs(cub_tmp, tb, a.fkey, a.fkey_s, a.fid, a.fid_s, n, 0, 1, s) != hipSuccess)
+    if (hipcub::DeviceSelect::Flagged(cub_tmp, tb, hipcub::CountingInputIterator<uint32_t>(0), a.free_flag, a.slot,
+                                      a.n_free, n, s) != hipSuccess)
         return SAD_EHIP;
     if (n_split > 0)
         hipLaunchKernelGGL(k_budget_split, dim3((unsigned)((std::min(n_split, n) + 255) / 256)), dim3(256), 0, s, a);
-    if (done) hipLaunchKernelGGL(k_budget_done, dim3(1), dim3(64), 0, s, a);
     return launch_status();
 }

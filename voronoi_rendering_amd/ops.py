@@ -151,21 +151,28 @@ def site_stats(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target
     return stats
 
 
+def budget_workspace(n: int, device) -> torch.Tensor:
+    """Scratch memory for sad_densify_prune with n sites."""
+    nb = int(_native.lib().sad_budget_workspace_bytes(int(n)))
+    return torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
+
+
 def densify_prune(params: torch.Tensor, m: torch.Tensor, v: torch.Tensor, derived: torch.Tensor, h: int, w: int,
                   stats: torch.Tensor, target: torch.Tensor, *, n_split: int, n_prune: int, alpha: float = 1.0,
                   min_mass: float = 1.0, offset: float = 0.5, r_scale: float = 0.85, logtau_shift: float = 0.1,
-                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+                  workspace: torch.Tensor | None = None, done: torch.Tensor | None = None) -> torch.Tensor:
     """Prune and split sites in place (see sad_densify_prune); returns the
-    numbers pruned and split as a device int32[2]."""
+    numbers pruned and split as a device int32[2] (``done`` when given)."""
     n = params.shape[0]
     for t, name in ((params, "params"), (m, "m"), (v, "v"), (derived, "derived")):
         _need(t, name, torch.float32, (n, REC))
     _need(stats, "stats", torch.float32, (n, NSTAT))
     _need(target, "target", torch.float32, (h, w, 3))
     if workspace is None:
-        nb = int(_native.lib().sad_budget_workspace_bytes(n))
-        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=params.device)
-    done = torch.zeros(2, dtype=torch.int32, device=params.device)
+        workspace = budget_workspace(n, params.device)
+    if done is None:
+        done = torch.zeros(2, dtype=torch.int32, device=params.device)
+    _need(done, "done", torch.int32, (2,))
     st = _native.lib().sad_densify_prune(_ptr(params), _ptr(m), _ptr(v), _ptr(derived), n, h, w, _ptr(stats),
                                          _ptr(target), int(n_split), int(n_prune), float(alpha), float(min_mass),
                                          float(offset), float(r_scale), float(logtau_shift), _ptr(done),
