@@ -64,6 +64,11 @@ def lib() -> C.CDLL:
         f32 = C.c_float
         L.sadref_densify_prune.argtypes = [f32p, f32p, f32p, f32p, i32, i32, i32, f32p, f32p, i32, i32, f32, f32, f32,
                                            f32, f32, C.POINTER(C.c_int32)]
+        L.sadref_grad_mag.argtypes = [f32p, i32, i32, f32p]
+        L.sadref_grad_units.argtypes = [C.c_float]
+        L.sadref_grad_units.restype = u64
+        L.sadref_init_sites.argtypes = [f32p, i32, i32, i32, C.c_float, u64, C.c_float, C.c_float, C.c_float, f32p,
+                                        f32p]
         L.sadref_query_points.argtypes = [f32p, i32, i32, i32, u32p, f32p, i64, f64p]
         L.sadref_adam_step.argtypes = [f32p, f32p, f32p, f32p, i32, i32, i32, f32p,
                                        C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, f32p]
@@ -211,6 +216,30 @@ def densify_prune(params: np.ndarray, m: np.ndarray, v: np.ndarray, derived: np.
 
 
 JFA_K = 4
+
+
+def grad_mag(target: np.ndarray, h: int, w: int) -> np.ndarray:
+    """float32 |grad I| per pixel ([h][w]; see sadref_grad_mag)."""
+    t = _f32(target).reshape(h, w, 3)
+    g = np.empty((h, w), np.float32)
+    lib().sadref_grad_mag(_p(t, C.c_float), h, w, _p(g, C.c_float))
+    return g
+
+
+def grad_units(g: float) -> int:
+    """The integer weight (units of 2^-24) the sampler gives a float32 gradient magnitude."""
+    return int(lib().sadref_grad_units(float(g)))
+
+
+def init_sites(target: np.ndarray, h: int, w: int, n: int, lam: float, seed: int, log_tau: float = 0.0,
+               r: float = 0.0, log_scale: float = 0.0):
+    """Gradient-weighted initialisation (see sadref_init_sites): returns (params, derived)."""
+    t = _f32(target).reshape(h, w, 3)
+    p = np.zeros((n, REC), np.float32)
+    d = np.zeros((n, REC), np.float32)
+    lib().sadref_init_sites(_p(t, C.c_float), h, w, n, lam, seed, log_tau, r, log_scale, _p(p, C.c_float),
+                            _p(d, C.c_float))
+    return p, d
 
 
 def jfa_steps(h: int, w: int) -> list[int]:

@@ -715,6 +715,106 @@ void sadref_densify_prune(float *params, float *m, float *v, float *derived, int
 }
 
 /* ------------------------------------------------------------------------ */
+/* Gradient-weighted initialisation (Sec. 4.4): sites are drawn from
+ *   P_init(x) = (1 - lambda) |grad I(x)| / sum |grad I| + lambda / (H W).
+ * |grad I(x)| is the 2-norm over the 3 channels and both directions of the
+ * 3x3 Sobel derivatives of the target (borders clamped), in float32:
+ *   gx_c = (I(i+1,j-1) + 2 I(i+1,j) + I(i+1,j+1)) - (I(i-1,j-1) + 2 I(i-1,j) + I(i-1,j+1))
+ *   gy_c = (I(i-1,j+1) + 2 I(i,j+1) + I(i+1,j+1)) - (I(i-1,j-1) + 2 I(i,j-1) + I(i+1,j-1))
+ *   g = sqrt(((gx_0^2 + gy_0^2) + (gx_1^2 + gy_1^2)) + (gx_2^2 + gy_2^2))
+ * To draw from the mixture exactly, g is taken in integer units of 2^-24
+ * (truncated, at most 2^15; NaN counts 0) and summed exactly in 64 bits.
+ * Site i uses SplitMix64 outputs z_k at counters 4 i + k:
+ *   z_0: uniform part when (z_0 >> 40) 2^-24 < lambda, or when every g is 0;
+ *   z_1: uniform part: pixel ((z_1 >> 32) H W) >> 32; gradient part: the
+ *        first pixel (row-major) whose inclusive prefix sum exceeds
+ *        t = floor(z_1 G / 2^64), G the total;
+ *   z_2, z_3: the position inside the pixel, i + (z_2 >> 40) 2^-24 and
+ *        j + (z_3 >> 40) 2^-24 (float32 sums).
+ * The record: that position, log tau, r, the target colour of the pixel,
+ * angle 0, both log scales log_scale, zero padding.  Records are prepared
+ * into derived as sadref_prepare_sites. */
+static float tpx(const float *t, int32_t h, int32_t w, int32_t i, int32_t j, int c)
+{
+    i = i < 0 ? 0 : (i >= w ? w - 1 : i);
+    j = j < 0 ? 0 : (j >= h ? h - 1 : j);
+    return t[((size_t)j * w + i) * 3 + c];
+}
+
+void sadref_grad_mag(const float *target, int32_t h, int32_t w, float *g)
+{
+    for (int32_t j = 0; j < h; ++j)
+        for (int32_t i = 0; i < w; ++i) {
+            float acc = 0.0f;
+            for (int c = 0; c < 3; ++c) {
+                float gx = (tpx(target, h, w, i + 1, j - 1, c) + 2.0f * tpx(target, h, w, i + 1, j, c) +
+                            tpx(target, h, w, i + 1, j + 1, c)) -
+                           (tpx(target, h, w, i - 1, j - 1, c) + 2.0f * tpx(target, h, w, i - 1, j, c) +
+                            tpx(target, h, w, i - 1, j + 1, c));
+                float gy = (tpx(target, h, w, i - 1, j + 1, c) + 2.0f * tpx(target, h, w, i, j + 1, c) +
+                            tpx(target, h, w, i + 1, j + 1, c)) -
+                           (tpx(target, h, w, i - 1, j - 1, c) + 2.0f * tpx(target, h, w, i, j - 1, c) +
+                            tpx(target, h, w, i + 1, j - 1, c));
+                float e = gx * gx + gy * gy;
+                acc = c == 0 ? e : acc + e;
+            }
+            g[(size_t)j * w + i] = sqrtf(acc);
+        }
+}
+
+uint64_t sadref_grad_units(float g)
+{
+    if (!(g == g)) return 0;
+    return (uint64_t)(fminf(g, 32768.0f) * 16777216.0f);
+}
+
+void sadref_init_sites(const float *target, int32_t h, int32_t w, int32_t n, float lambda, uint64_t seed,
+                       float log_tau, float r, float log_scale, float *params, float *derived)
+{
+    size_t pix = (size_t)h * (size_t)w;
+    float *g = (float *)malloc(sizeof(float) * (pix > 0 ? pix : 1));
+    uint64_t *cum = (uint64_t *)malloc(sizeof(uint64_t) * (pix > 0 ? pix : 1));
+    sadref_grad_mag(target, h, w, g);
+    uint64_t total = 0;
+    for (size_t x = 0; x < pix; ++x) {
+        total += sadref_grad_units(g[x]);
+        cum[x] = total;
+    }
+    for (int32_t s = 0; s < n; ++s) {
+        uint64_t z[4];
+        for (int k = 0; k < 4; ++k) z[k] = sadref_splitmix64(seed, 4u * (uint64_t)s + (uint64_t)k);
+        float u0 = (float)(z[0] >> 40) * 0x1p-24f;
+        size_t x;
+        if (u0 < lambda || total == 0) {
+            x = (size_t)(((z[1] >> 32) * (uint64_t)pix) >> 32);
+        } else {
+            uint64_t t = (uint64_t)(((unsigned __int128)z[1] * total) >> 64);
+            size_t lo = 0, hi = pix - 1; /* first x with cum[x] > t; cum[pix-1] = total > t */
+            while (lo < hi) {
+                size_t mid = lo + (hi - lo) / 2;
+                if (cum[mid] > t) hi = mid; else lo = mid + 1;
+            }
+            x = lo;
+        }
+        int32_t i = (int32_t)(x % (size_t)w), j = (int32_t)(x / (size_t)w);
+        float *p = params + (size_t)s * REC;
+        p[0] = (float)i + (float)(z[2] >> 40) * 0x1p-24f;
+        p[1] = (float)j + (float)(z[3] >> 40) * 0x1p-24f;
+        p[2] = log_tau;
+        p[3] = r;
+        for (int c = 0; c < 3; ++c) p[4 + c] = target[x * 3 + c];
+        p[7] = 0.0f;
+        p[8] = log_scale;
+        p[9] = log_scale;
+        p[10] = 0.0f;
+        p[11] = 0.0f;
+    }
+    sadref_prepare_sites(params, n, derived);
+    free(g);
+    free(cum);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Adam (Kingma and Ba, ICLR 2015) on the float32 site buffer (Sec. 5:
  * per-parameter base learning rates, fixed betas and epsilon), then the
  * projection of Sec. 4.1 (positions clamped to the image).  lr[5] holds the

@@ -48,6 +48,13 @@ MUTANTS = [
      "float lam = (a + c) * 0.5f - sqrtf(half * half + b * b);"),
     ("children keep the parent's colour", "o[4] = t[0];", "o[4] = base[4];"),
     ("children keep their Adam moments", "m[(size_t)oi * REC + q] = 0.0f;", "(void)oi;"),
+    ("Sobel centre weight 1", "float gx = (tpx(target, h, w, i + 1, j - 1, c) + 2.0f * tpx(target, h, w, i + 1, j, c) +",
+     "float gx = (tpx(target, h, w, i + 1, j - 1, c) + 1.0f * tpx(target, h, w, i + 1, j, c) +"),
+    ("mixture weights swapped", "if (u0 < lambda || total == 0) {", "if (u0 >= lambda || total == 0) {"),
+    ("inverse CDF off by one", "if (cum[mid] > t) hi = mid; else lo = mid + 1;",
+     "if (cum[mid] >= t) hi = mid; else lo = mid + 1;"),
+    ("init colour channels reversed", "for (int c = 0; c < 3; ++c) p[4 + c] = target[x * 3 + c];",
+     "for (int c = 0; c < 3; ++c) p[4 + c] = target[x * 3 + (2 - c)];"),
 ]
 
 
