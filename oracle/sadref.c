@@ -723,7 +723,8 @@ void sadref_densify_prune(float *params, float *m, float *v, float *derived, int
  *   gy_c = (I(i-1,j+1) + 2 I(i,j+1) + I(i+1,j+1)) - (I(i-1,j-1) + 2 I(i,j-1) + I(i+1,j-1))
  *   g = sqrt(((gx_0^2 + gy_0^2) + (gx_1^2 + gy_1^2)) + (gx_2^2 + gy_2^2))
  * To draw from the mixture exactly, g is taken in integer units of 2^-24
- * (truncated, at most 2^15; NaN counts 0) and summed exactly in 64 bits.
+ * (truncated, at most 2^8, so that 2^30 pixels still sum exactly in 64 bits;
+ * NaN counts 0).
  * Site i uses SplitMix64 outputs z_k at counters 4 i + k:
  *   z_0: uniform part when (z_0 >> 40) 2^-24 < lambda, or when every g is 0;
  *   z_1: uniform part: pixel ((z_1 >> 32) H W) >> 32; gradient part: the
@@ -765,7 +766,7 @@ void sadref_grad_mag(const float *target, int32_t h, int32_t w, float *g)
 uint64_t sadref_grad_units(float g)
 {
     if (!(g == g)) return 0;
-    return (uint64_t)(fminf(g, 32768.0f) * 16777216.0f);
+    return (uint64_t)(fminf(g, 256.0f) * 16777216.0f);
 }
 
 void sadref_init_sites(const float *target, int32_t h, int32_t w, int32_t n, float lambda, uint64_t seed,
