@@ -156,24 +156,35 @@ def cpu_other(include_2048: bool) -> dict:
     return out
 
 
-def encode_run(torch, synth, SadField, wl, tgt, iters: int) -> dict:
+INIT = {"lam": 0.3, "log_tau": 0.0, "r": 0.0, "log_scale": 0.7}  # encode from the gradient-weighted density
+
+
+def encode_run(torch, synth, SadField, wl, tgt, iters: int, init: dict | None = None) -> dict:
     """The training workload end to end: wall clock from the initial
-    parameters in device memory (site preparation, warm-up passes, then
-    ``iters`` iterations of propagate + forward + backward + Adam) to the last
-    kernel's end; then an untimed second run of the same iterations that
-    renders the fit at a few iterations for its PSNR against the target."""
-    p0 = torch.from_numpy(wl.make_sites()).to("cuda")
+    parameters in device memory (or, with ``init``, from the target alone:
+    the gradient-weighted draw of the sites is inside the clock), site
+    preparation, warm-up passes, then ``iters`` iterations of propagate +
+    forward + backward + Adam, to the last kernel's end; then an untimed
+    second run of the same iterations that renders the fit at a few
+    iterations for its PSNR against the target."""
     strides = list(wl.strides)
+
+    def start():
+        if init is not None:
+            return SadField.from_target(tgt, wl.n, seed=wl.inject_seed, inject=wl.inject, **init)
+        return SadField(p0.clone(), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+
+    p0 = torch.from_numpy(wl.make_sites()).to("cuda") if init is None else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    f = SadField(p0.clone(), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+    f = start()
     f.warm(wl.warm_passes)
     for _ in range(iters):
         f.train_iter(strides, tgt)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     del f
-    f = SadField(p0.clone(), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+    f = start()
     f.warm(wl.warm_passes)
     psnr = {}
     marks = {1, 10, 100, iters}
@@ -182,8 +193,11 @@ def encode_run(torch, synth, SadField, wl, tgt, iters: int) -> dict:
         if it in marks:  # the updated sites over the iteration's map
             mse = float(((f.render() - tgt) ** 2).mean())
             psnr[str(it)] = round(10.0 * math.log10(1.0 / mse), 3)
-    return {"s": round(wall, 4), "ms_per_iteration": round(wall / iters * 1e3, 4), "psnr_db_at_iteration": psnr,
-            "note": "setup, 16 warm-up passes and all iterations inside the wall clock"}
+    out = {"s": round(wall, 4), "ms_per_iteration": round(wall / iters * 1e3, 4), "psnr_db_at_iteration": psnr,
+           "note": "setup, 16 warm-up passes and all iterations inside the wall clock"}
+    if init is not None:
+        out["init"] = dict(init, note="sites drawn from the target's gradient-weighted density inside the clock")
+    return out
 
 
 # The pages' per-call times of the same protocol on an NVIDIA RTX 5090 at 1.0
@@ -281,7 +295,8 @@ def secondary(torch, synth, ops, SadField) -> dict:
     """The other workloads, timed briefly with inputs resident on the GPU (not
     the headline): the 2048x2048 / 400k-site step, a training iteration
     (step + Adam, the 768x512 training workload), the Adam step alone, the
-    budget statistics pass and the budget step, the 1,000-iteration encode, and 2^24
+    budget statistics pass and the budget step, the 1,000-iteration encode (from the
+    synthetic sites and from a gradient-weighted draw), the draw alone, and 2^24
     random-access queries on a 768x512 / 50k-site map."""
     dev = torch.device("cuda", 0)
 
@@ -340,6 +355,13 @@ def secondary(torch, synth, ops, SadField) -> dict:
     del f, stats, ws
     out["densify_prune_768x512_50k"] = budget_timings(torch, synth, ops, SadField)
     out["encode_768x512_50k_1000_iterations"] = encode_run(torch, synth, SadField, wl, tgt, 1000)
+    out["encode_768x512_50k_1000_iterations_gradient_init"] = encode_run(torch, synth, SadField, wl, tgt, 1000, INIT)
+    ws = ops.init_workspace(wl.h, wl.w, dev)
+    prm = torch.empty((wl.n, ops.REC), dtype=torch.float32, device=dev)
+    drv = torch.empty_like(prm)
+    t = per_call(lambda: ops.init_sites(tgt, wl.n, seed=7, params=prm, derived=drv, workspace=ws, **INIT), 20)
+    out["init_sites_768x512_50k"] = {"us": round(t * 1e6, 2)}
+    del ws, prm, drv
     del tgt
     wl = synth.C5
     f = SadField(torch.from_numpy(wl.make_sites()).to(dev), wl.h, wl.w, wl.inject_seed, inject=wl.inject)

@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 4
+#define SAD_ABI_VERSION 5
 #define SAD_K 8
 #define SAD_SITE_STRIDE 12
 #define SAD_EMPTY 0xffffffffu
@@ -242,6 +242,35 @@ int sad_densify_prune(float *params, float *adam_m, float *adam_v, float *derive
                       const float *stats, const float *target, int32_t n_split, int32_t n_prune, float alpha,
                       float min_mass, float offset, float r_scale, float logtau_shift, int32_t *done,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Gradient-weighted initialisation (Sec. 4.4): n sites drawn independently
+ * from P_init(x) = (1 - lambda) |grad I(x)| / sum |grad I| + lambda / (h w).
+ * |grad I| is the 2-norm over the 3 channels and both directions of the 3x3
+ * Sobel derivatives of the target (borders repeated), float32; it is taken in
+ * integer units of 2^-24 (truncated, capped at 2^8) and the inclusive prefix
+ * sum of those units, exact in 64 bits, is the CDF.  Site s uses the
+ * SplitMix64 outputs z_k for counters 4 s + k (same generator as the probes):
+ *   z_0: the uniform part when (z_0 >> 40) * 2^-24 < lambda or every unit is 0,
+ *   z_1: the pixel: ((z_1 >> 32) * h * w) >> 32 for the uniform part, else the
+ *        first pixel (row-major) whose prefix sum exceeds (z_1 * G) >> 64,
+ *        G the total,
+ *   z_2, z_3: x = i + (z_2 >> 40) * 2^-24 and y = j + (z_3 >> 40) * 2^-24
+ *        (float32 sums) inside that pixel (i, j).
+ * The record: (x, y, log_tau, r, the target colour of pixel (i, j), angle 0,
+ * log_scale, log_scale, 0, 0); derived is written as sad_prepare_sites would.
+ *   target     [h][w][3] float32
+ *   lambda     in [0, 1]
+ *   params, derived  [n][12] float32, written, 16-byte aligned
+ *   workspace  device scratch of sad_init_workspace_bytes(h, w) bytes, 256-byte
+ *              aligned, owned by the caller (the units, their prefix sums and
+ *              the scan's storage)
+ * n = 0 does nothing; n > 0 needs h, w > 0.  Results depend only on the inputs.
+ */
+size_t sad_init_workspace_bytes(int32_t h, int32_t w);
+int sad_init_sites(const float *target, int32_t h, int32_t w, int32_t n, float lambda, uint64_t seed, float log_tau,
+                   float r, float log_scale, float *params, float *derived, void *workspace, size_t workspace_bytes,
+                   void *stream);
 
 /*
  * JFA prepass of a full list refresh (Appendix B.3, "JFA prepass"; the render

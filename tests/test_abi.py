@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     syms = declared_symbols()
     for name in ("sad_prepare_sites", "sad_propagate_topk", "sad_render_fwd", "sad_render_bwd",
                  "sad_render_bwd_workspace_bytes", "sad_step_fused", "sad_site_stats", "sad_jfa_seed",
-                 "sad_jfa_flood", "sad_budget_workspace_bytes", "sad_densify_prune",
+                 "sad_jfa_flood", "sad_budget_workspace_bytes", "sad_densify_prune", "sad_init_workspace_bytes",
+                 "sad_init_sites",
                  "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version"):
         assert name in syms
 
@@ -42,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sad_abi_version() == 4
+    assert lib.sad_abi_version() == 5
     for st in (0, -1, -2, -3, 7):
         assert lib.sad_status_string(st)
 
@@ -207,3 +208,30 @@ def test_densify_prune_rejects(lib):
     assert call(done=P + 2) == EINVAL
     assert call(done=P + 8) == EINVAL  # inside the sites
     assert call(n=0, ws=None, done=None) == 0  # no sites and no counts: nothing to launch
+
+
+def test_init_sites_rejects(lib):
+    f = lib.sad_init_sites
+    h, w, n = 8, 8, 10
+    wsb = lib.sad_init_workspace_bytes(h, w)
+    assert wsb >= 2 * 8 * h * w
+    WS = 1 << 30
+    ok = dict(t=P, h=h, w=w, n=n, lam=0.5, p=P + 4096, d=P + 8192, ws=WS, wsb=wsb)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["t"], a["h"], a["w"], a["n"], a["lam"], 7, 0.0, 0.0, 0.0, a["p"], a["d"], a["ws"], a["wsb"], None)
+
+    assert call(lam=-0.1) == EINVAL
+    assert call(lam=1.5) == EINVAL
+    assert call(lam=float("nan")) == EINVAL
+    assert call(n=-1) == EINVAL
+    assert call(h=0) == EINVAL  # sites need pixels
+    assert call(t=None) == EINVAL
+    assert call(p=P + 4096 + 4) == EINVAL  # misaligned
+    assert call(d=P + 4096 + 16) == EINVAL  # overlaps params
+    assert call(p=P + 64) == EINVAL  # overlaps the target
+    assert call(ws=None) == EINVAL
+    assert call(ws=WS + 64) == EINVAL
+    assert call(wsb=wsb - 1) == EINVAL
+    assert call(n=0, t=None, ws=None) == 0  # nothing to draw

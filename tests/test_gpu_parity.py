@@ -433,6 +433,49 @@ def test_field_densify_prune_bookkeeping(sad, ref):
     assert np.array_equal(map_to_np(f.topk), want)
 
 
+# ---------------------------------------------------------------- initialisation
+
+def init_vs_oracle(sad, ref, t, n, lam, seed, label, **kw):
+    h, w = t.shape[:2]
+    want_p, want_d = ref.init_sites(t, h, w, n, lam, seed, **kw)
+    gp, gd = sad.init_sites(to_gpu(t), n, lam=lam, seed=seed, **kw)
+    for got, exp, name in ((gp, want_p, "params"), (gd, want_d, "derived")):
+        got = to_np(got)
+        assert np.array_equal(got.view(np.uint32), exp.view(np.uint32)), \
+            f"{label}: {name} differs at sites {np.unique(np.argwhere(got != exp)[:, 0])[:8]}"
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.25, 1.0])
+def test_init_sites_bit_exact(sad, ref, lam):
+    t = synth.target_polygons(5, 37, 53, n_poly=5).astype(np.float32)
+    init_vs_oracle(sad, ref, t, 3000, lam, 77, f"37x53 lambda {lam}", log_tau=0.5, r=0.25, log_scale=-0.3)
+
+
+def test_init_sites_768x512(sad, ref):
+    wl = synth.C3
+    say(f"[gpu] init {wl.w}x{wl.h}, n={wl.n}")
+    init_vs_oracle(sad, ref, wl.make_target(), wl.n, 0.3, wl.param_seed, "768x512 / 50k", log_scale=0.7)
+
+
+def test_init_sites_edge_cases(sad, ref):
+    init_vs_oracle(sad, ref, np.full((1, 1, 3), 0.2, np.float32), 5, 0.0, 1, "1x1")
+    init_vs_oracle(sad, ref, np.full((7, 11, 3), 0.4, np.float32), 500, 0.0, 2, "flat image")
+    t = np.zeros((10, 12, 3), np.float32)
+    t[4, 6, 0] = 2.0 ** -22
+    t[7, 2, 1] = 2.0 ** -23
+    init_vs_oracle(sad, ref, t, 2000, 0.0, 5, "a few gradient units")
+    t = np.random.default_rng(3).random((1, 300, 3)).astype(np.float32)
+    init_vs_oracle(sad, ref, t, 700, 0.5, 6, "one row")
+    t[0, 5, 2] = np.nan
+    t[0, 9, 0] = 1e6  # capped weight
+    init_vs_oracle(sad, ref, t, 700, 0.1, 8, "NaN and huge values")
+
+
+def test_init_sites_without_sites(sad):
+    p, d = sad.init_sites(torch.zeros((4, 4, 3), device=dev()), 0, lam=0.5, seed=1)
+    assert p.shape == (0, 12) and d.shape == (0, 12)
+
+
 # ---------------------------------------------------------------- JFA prepass and full refresh
 
 def crowded_sites(seed, n, h, w):

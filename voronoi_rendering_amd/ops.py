@@ -181,6 +181,37 @@ def densify_prune(params: torch.Tensor, m: torch.Tensor, v: torch.Tensor, derive
     return done
 
 
+def init_workspace(h: int, w: int, device) -> torch.Tensor:
+    """Scratch memory for sad_init_sites on an h x w target."""
+    nb = int(_native.lib().sad_init_workspace_bytes(int(h), int(w)))
+    return torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
+
+
+def init_sites(target: torch.Tensor, n: int, *, lam: float, seed: int, log_tau: float = 0.0, r: float = 0.0,
+               log_scale: float = 0.0, params: torch.Tensor | None = None, derived: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Gradient-weighted initialisation of n sites from the [h][w][3] target
+    (see sad_init_sites); returns (params, derived)."""
+    if target.dim() != 3 or target.shape[2] != 3:
+        raise ValueError(f"target must have shape (h, w, 3), got {tuple(target.shape)}")
+    h, w = int(target.shape[0]), int(target.shape[1])
+    _need(target, "target", torch.float32, (h, w, 3))
+    dev = target.device
+    if params is None:
+        params = torch.empty((n, REC), dtype=torch.float32, device=dev)
+    if derived is None:
+        derived = torch.empty((n, REC), dtype=torch.float32, device=dev)
+    _need(params, "params", torch.float32, (n, REC))
+    _need(derived, "derived", torch.float32, (n, REC))
+    if workspace is None:
+        workspace = init_workspace(h, w, dev)
+    st = _native.lib().sad_init_sites(_ptr(target), h, w, int(n), float(lam), int(seed) & (2 ** 64 - 1),
+                                      float(log_tau), float(r), float(log_scale), _ptr(params), _ptr(derived),
+                                      _ptr(workspace), workspace.numel(), _stream(target))
+    _native.check("sad_init_sites", st)
+    return params, derived
+
+
 JFA_K = 4  # ids per pixel in the JFA prepass
 
 

@@ -58,6 +58,15 @@ class SadField:
         self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
         self._jfa = None  # ping-pong 4-lists of the JFA prepass, made on first use
 
+    @classmethod
+    def from_target(cls, target: torch.Tensor, n: int, *, lam: float, seed: int, log_tau: float = 0.0,
+                    r: float = 0.0, log_scale: float = 0.0, **kw) -> "SadField":
+        """A field of n sites drawn from the gradient-weighted density of the
+        [h][w][3] target (Sec. 4.4; see ops.init_sites); ``seed`` also seeds
+        the probes."""
+        params, _ = ops.init_sites(target, n, lam=lam, seed=seed, log_tau=log_tau, r=r, log_scale=log_scale)
+        return cls(params, int(target.shape[0]), int(target.shape[1]), seed, **kw)
+
     @property
     def topk(self) -> torch.Tensor:
         return self.maps[self.cur]
