@@ -64,6 +64,15 @@ def lib() -> C.CDLL:
         f32 = C.c_float
         L.sadref_densify_prune.argtypes = [f32p, f32p, f32p, f32p, i32, i32, i32, f32p, f32p, i32, i32, f32, f32, f32,
                                            f32, f32, C.POINTER(C.c_int32)]
+        L.sadref_half_bits.argtypes = [C.c_float]
+        L.sadref_half_bits.restype = u32
+        L.sadref_half_value.argtypes = [u32]
+        L.sadref_half_value.restype = C.c_double
+        L.sadref_pack_sites.argtypes = [f32p, f32p, i32, i32, i32, u32p, f32p]
+        L.sadref_unpack_site.argtypes = [u32p, f32p, i32, i32, f64p]
+        L.sadref_packed_logit.argtypes = [f64p, C.c_double, C.c_double]
+        L.sadref_packed_logit.restype = C.c_double
+        L.sadref_query_packed.argtypes = [u32p, f32p, i32, i32, i32, u32p, f32p, i64, f64p]
         L.sadref_grad_mag.argtypes = [f32p, i32, i32, f32p]
         L.sadref_grad_units.argtypes = [C.c_float]
         L.sadref_grad_units.restype = u64
@@ -216,6 +225,51 @@ def densify_prune(params: np.ndarray, m: np.ndarray, v: np.ndarray, derived: np.
 
 
 JFA_K = 4
+
+
+def half_bits(f: float) -> int:
+    """float16 bits of a float32, rounded to nearest even (own conversion)."""
+    return int(lib().sadref_half_bits(float(f)))
+
+
+def half_value(bits: int) -> float:
+    return float(lib().sadref_half_value(int(bits)))
+
+
+def pack_sites(params: np.ndarray, derived: np.ndarray, h: int, w: int):
+    """Packed evaluation records (see sadref_pack_sites): ([n][4] uint32, qp float32[10])."""
+    p = _f32(params).reshape(-1, REC)
+    d = _f32(derived).reshape(-1, REC)
+    n = p.shape[0]
+    out = np.zeros((n, 4), np.uint32)
+    qp = np.zeros(10, np.float32)
+    lib().sadref_pack_sites(_p(p, C.c_float), _p(d, C.c_float), n, h, w, _p(out, C.c_uint32), _p(qp, C.c_float))
+    return out, qp
+
+
+def unpack_site(record: np.ndarray, qp: np.ndarray, h: int, w: int):
+    """(x, y, tau', r', c_r, c_g, c_b, theta, a) of one packed record in float64, or None if not usable."""
+    rec = _u32(record).reshape(4)
+    q = _f32(qp)
+    v = np.zeros(9, np.float64)
+    ok = lib().sadref_unpack_site(_p(rec, C.c_uint32), _p(q, C.c_float), h, w, _p(v, C.c_double))
+    return v if ok else None
+
+
+def packed_logit(values: np.ndarray, px: float, py: float) -> float:
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    return float(lib().sadref_packed_logit(_p(v, C.c_double), float(px), float(py)))
+
+
+def query_packed(packed: np.ndarray, qp: np.ndarray, h: int, w: int, topk: np.ndarray, xy: np.ndarray) -> np.ndarray:
+    pk = _u32(packed).reshape(-1, 4)
+    q = _f32(qp)
+    m = _u32(topk)
+    pts = _f32(xy).reshape(-1, 2)
+    out = np.zeros((pts.shape[0], 3), np.float64)
+    lib().sadref_query_packed(_p(pk, C.c_uint32), _p(q, C.c_float), pk.shape[0], h, w, _p(m, C.c_uint32),
+                              _p(pts, C.c_float), pts.shape[0], _p(out, C.c_double))
+    return out
 
 
 def grad_mag(target: np.ndarray, h: int, w: int) -> np.ndarray:

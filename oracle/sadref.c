@@ -715,6 +715,190 @@ void sadref_densify_prune(float *params, float *m, float *v, float *derived, int
 }
 
 /* ------------------------------------------------------------------------ */
+/* Packed evaluation records (Appendix B.2, "Packed storage for evaluation"):
+ * four 32-bit words per site,
+ *   w0: x and y as 15-bit UNORM of x / W and y / H (bits 0-14, 15-29), bit 31
+ *       set for a usable site (a site that is not usable packs to 0, 0, 0, 0),
+ *   w1: colour r, g, b as 11/11/10-bit UNORM over the image's range per channel,
+ *   w2: log tau' and r' as 16/16-bit UNORM over the image's ranges,
+ *   w3: the direction as a 16-bit UNORM angle code over [-pi, pi] (low half)
+ *       and the log-anisotropy a as float16 (high half).
+ * The pages' metric has determinant 1 (eigenvalues e^a, e^-a along the
+ * direction and across it).  The metric diag(s1^-2, s2^-2) in the rotated
+ * frame is that one scaled by 1 / (s1 s2), and a scale of the distance is
+ * absorbed by tau and r:
+ *   a = log s2 - log s1,  hs = (log s1 + log s2) / 2,
+ *   log tau' = log tau - hs,  r' = r exp(hs),
+ * giving the same logit -tau' (sqrt(e^a u^2 + e^-a v^2) - r') with
+ * (u, v) the offset in the rotated frame.
+ * Per-image parameters qp[10] = (min, max - min) of log tau', r', c_r, c_g,
+ * c_b over the usable sites (NaN values ignored; no values: 0, 0).
+ * Codes: q = rint(clamp(t, 0, 1) * (2^bits - 1)), t = (v - min) / scale
+ * (0 when scale is not positive), NaN t gives 0.  Arithmetic is float32 in
+ * the order written; exp is the correctly rounded float32 exponential; the
+ * angle is wrapped as theta - 2 pi_f rint(theta / (2 pi)_f) and coded from
+ * (wrapped + pi_f) / (2 pi)_f; float16 rounding is to nearest even. */
+#define TWO_PI_F 6.28318548f
+#define INV_TWO_PI_F 0.159154937f
+#define PI_F 3.14159274f
+#define SADREF_PI 3.14159265358979323846
+
+static uint32_t unorm_code(float t, uint32_t maxq)
+{
+    t = fminf(fmaxf(t, 0.0f), 1.0f); /* NaN becomes 0 */
+    return (uint32_t)rintf(t * (float)maxq);
+}
+
+uint32_t sadref_half_bits(float f)
+{
+    uint32_t sign = signbit(f) ? 0x8000u : 0u;
+    double a = fabs((double)f);
+    if (isnan(f)) return 0x7E00u;
+    if (a >= 65520.0) return sign | 0x7C00u; /* rounds to infinity */
+    if (a < 0x1p-14) return sign | (uint32_t)nearbyint(a * 0x1p24); /* steps of 2^-24; 1024 = smallest normal */
+    int e;
+    frexp(a, &e); /* a in [2^(e-1), 2^e) */
+    double ulp = ldexp(1.0, e - 11);
+    double r = nearbyint(a / ulp) * ulp;
+    frexp(r, &e);
+    double mant = r / ldexp(1.0, e - 1) - 1.0;
+    return sign | (uint32_t)((e - 1 + 15) << 10) | (uint32_t)nearbyint(mant * 1024.0);
+}
+
+double sadref_half_value(uint32_t hb)
+{
+    double sg = (hb & 0x8000u) ? -1.0 : 1.0;
+    uint32_t e = (hb >> 10) & 31u, m = hb & 1023u;
+    if (e == 0) return sg * ldexp((double)m, -24);
+    if (e == 31) return m ? NAN : sg * INFINITY;
+    return sg * ldexp((double)(1024u + m), (int)e - 25);
+}
+
+static void packed_values(const float *p, float v[5])
+{
+    float hs = 0.5f * (p[8] + p[9]);
+    v[0] = p[2] - hs;
+    v[1] = p[3] * sadref_exp_f32(hs);
+    v[2] = p[4];
+    v[3] = p[5];
+    v[4] = p[6];
+}
+
+void sadref_pack_sites(const float *params, const float *derived, int32_t n, int32_t h, int32_t w, uint32_t *packed,
+                       float *qp)
+{
+    float lo[5], hi[5];
+    for (int k = 0; k < 5; ++k) {
+        lo[k] = INFINITY;
+        hi[k] = -INFINITY;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        if (!site_usable(derived, n, (uint32_t)i)) continue;
+        float v[5];
+        packed_values(params + (size_t)i * REC, v);
+        for (int k = 0; k < 5; ++k)
+            if (v[k] == v[k]) {
+                lo[k] = fminf(lo[k], v[k]);
+                hi[k] = fmaxf(hi[k], v[k]);
+            }
+    }
+    for (int k = 0; k < 5; ++k) {
+        if (lo[k] > hi[k]) lo[k] = hi[k] = 0.0f;
+        qp[2 * k] = lo[k];
+        qp[2 * k + 1] = hi[k] - lo[k];
+    }
+    static const uint32_t maxq[5] = {65535u, 65535u, 2047u, 2047u, 1023u};
+    for (int32_t i = 0; i < n; ++i) {
+        uint32_t *o = packed + (size_t)i * 4;
+        if (!site_usable(derived, n, (uint32_t)i)) {
+            o[0] = o[1] = o[2] = o[3] = 0u;
+            continue;
+        }
+        const float *p = params + (size_t)i * REC;
+        float v[5];
+        uint32_t q[5];
+        packed_values(p, v);
+        for (int k = 0; k < 5; ++k) {
+            float sc = qp[2 * k + 1];
+            q[k] = unorm_code(sc > 0.0f ? (v[k] - qp[2 * k]) / sc : 0.0f, maxq[k]);
+        }
+        uint32_t qx = unorm_code(p[0] / (float)w, 32767u), qy = unorm_code(p[1] / (float)h, 32767u);
+        float th = p[7] - TWO_PI_F * rintf(p[7] * INV_TWO_PI_F);
+        uint32_t qt = unorm_code((th + PI_F) * INV_TWO_PI_F, 65535u);
+        o[0] = qx | (qy << 15) | 0x80000000u;
+        o[1] = q[2] | (q[3] << 11) | (q[4] << 22);
+        o[2] = q[0] | (q[1] << 16);
+        o[3] = qt | (sadref_half_bits(p[9] - p[8]) << 16);
+    }
+}
+
+/* The values a packed record stands for, in float64:
+ * out[9] = (x, y, tau', r', c_r, c_g, c_b, theta, a); returns 0 for a record
+ * without the usable bit. */
+int sadref_unpack_site(const uint32_t *o, const float *qp, int32_t h, int32_t w, double *out)
+{
+    if (!(o[0] >> 31)) return 0;
+    out[0] = (double)(o[0] & 32767u) / 32767.0 * (double)w;
+    out[1] = (double)((o[0] >> 15) & 32767u) / 32767.0 * (double)h;
+    out[2] = exp((double)qp[0] + (double)(o[2] & 65535u) / 65535.0 * (double)qp[1]);
+    out[3] = (double)qp[2] + (double)(o[2] >> 16) / 65535.0 * (double)qp[3];
+    out[4] = (double)qp[4] + (double)(o[1] & 2047u) / 2047.0 * (double)qp[5];
+    out[5] = (double)qp[6] + (double)((o[1] >> 11) & 2047u) / 2047.0 * (double)qp[7];
+    out[6] = (double)qp[8] + (double)(o[1] >> 22) / 1023.0 * (double)qp[9];
+    out[7] = (double)(o[3] & 65535u) / 65535.0 * (2.0 * SADREF_PI) - SADREF_PI;
+    out[8] = sadref_half_value(o[3] >> 16);
+    return 1;
+}
+
+double sadref_packed_logit(const double *v, double px, double py)
+{
+    double dx = px - v[0], dy = py - v[1];
+    double cs = cos(v[7]), sn = sin(v[7]);
+    double u = cs * dx + sn * dy, t = cs * dy - sn * dx;
+    return -v[2] * (sqrt(exp(v[8]) * u * u + exp(-v[8]) * t * t) - v[3]);
+}
+
+/* Random access from packed records: as sadref_query_points, with each list
+ * entry's site decoded from its packed record (float64); an id >= n or a
+ * record without the usable bit is skipped, as are non-finite logits. */
+void sadref_query_packed(const uint32_t *packed, const float *qp, int32_t n, int32_t h, int32_t w,
+                         const uint32_t *topk, const float *xy, int64_t m, double *rgb)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < m; ++t) {
+        float qx = xy[2 * t], qy = xy[2 * t + 1];
+        if (!isfinite(qx) || !isfinite(qy)) {
+            rgb[3 * t] = rgb[3 * t + 1] = rgb[3 * t + 2] = NAN;
+            continue;
+        }
+        double fx = floor((double)qx), fy = floor((double)qy);
+        int32_t i = fx < 0 ? 0 : (fx > (double)(w - 1) ? w - 1 : (int32_t)fx);
+        int32_t j = fy < 0 ? 0 : (fy > (double)(h - 1) ? h - 1 : (int32_t)fy);
+        const uint32_t *list = topk + ((size_t)j * w + i) * K;
+        double l[K], col[K][3], mx = -INFINITY;
+        int cnt = 0;
+        for (int k = 0; k < K; ++k) {
+            double v[9];
+            if (list[k] >= (uint32_t)n || !sadref_unpack_site(packed + (size_t)list[k] * 4, qp, h, w, v)) continue;
+            double s = sadref_packed_logit(v, (double)qx, (double)qy);
+            if (!isfinite(s)) continue;
+            l[cnt] = s;
+            for (int ch = 0; ch < 3; ++ch) col[cnt][ch] = v[4 + ch];
+            mx = fmax(mx, s);
+            cnt++;
+        }
+        double z = 0.0, c[3] = {0.0, 0.0, 0.0};
+        for (int k = 0; k < cnt; ++k) {
+            l[k] = exp(l[k] - mx);
+            z += l[k];
+        }
+        for (int k = 0; k < cnt; ++k)
+            for (int ch = 0; ch < 3; ++ch) c[ch] += l[k] / z * col[k][ch];
+        for (int ch = 0; ch < 3; ++ch) rgb[3 * t + ch] = c[ch];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Gradient-weighted initialisation (Sec. 4.4): sites are drawn from
  *   P_init(x) = (1 - lambda) |grad I(x)| / sum |grad I| + lambda / (H W).
  * |grad I(x)| is the 2-norm over the 3 channels and both directions of the

@@ -55,6 +55,15 @@ MUTANTS = [
      "if (cum[mid] >= t) hi = mid; else lo = mid + 1;"),
     ("init colour channels reversed", "for (int c = 0; c < 3; ++c) p[4 + c] = target[x * 3 + c];",
      "for (int c = 0; c < 3; ++c) p[4 + c] = target[x * 3 + (2 - c)];"),
+    ("packed anisotropy sign", "o[3] = qt | (sadref_half_bits(p[9] - p[8]) << 16);",
+     "o[3] = qt | (sadref_half_bits(p[8] - p[9]) << 16);"),
+    ("packed r without the scale", "v[1] = p[3] * sadref_exp_f32(hs);", "v[1] = p[3];"),
+    ("packed colour fields shifted", "o[1] = q[2] | (q[3] << 11) | (q[4] << 22);",
+     "o[1] = q[2] | (q[3] << 10) | (q[4] << 21);"),
+    ("packed angle decoded over half the circle",
+     "out[7] = (double)(o[3] & 65535u) / 65535.0 * (2.0 * SADREF_PI) - SADREF_PI;",
+     "out[7] = (double)(o[3] & 65535u) / 65535.0 * SADREF_PI - SADREF_PI;"),
+    ("packed half rounding truncates", "double r = nearbyint(a / ulp) * ulp;", "double r = floor(a / ulp) * ulp;"),
 ]
 
 
