@@ -732,7 +732,8 @@ void sadref_densify_prune(float *params, float *m, float *v, float *derived, int
  * giving the same logit -tau' (sqrt(e^a u^2 + e^-a v^2) - r') with
  * (u, v) the offset in the rotated frame.
  * Per-image parameters qp[10] = (min, max - min) of log tau', r', c_r, c_g,
- * c_b over the usable sites (NaN values ignored; no values: 0, 0).
+ * c_b over the usable sites (NaN values ignored, -0 taken as +0; no values:
+ * 0, 0).
  * Codes: q = rint(clamp(t, 0, 1) * (2^bits - 1)), t = (v - min) / scale
  * (0 when scale is not positive), NaN t gives 0.  Arithmetic is float32 in
  * the order written; exp is the correctly rounded float32 exponential; the
@@ -796,11 +797,11 @@ void sadref_pack_sites(const float *params, const float *derived, int32_t n, int
         if (!site_usable(derived, n, (uint32_t)i)) continue;
         float v[5];
         packed_values(params + (size_t)i * REC, v);
-        for (int k = 0; k < 5; ++k)
-            if (v[k] == v[k]) {
-                lo[k] = fminf(lo[k], v[k]);
-                hi[k] = fmaxf(hi[k], v[k]);
-            }
+        for (int k = 0; k < 5; ++k) {
+            float x = v[k] + 0.0f; /* -0 counts as +0, so the range is unique */
+            if (x < lo[k]) lo[k] = x;
+            if (x > hi[k]) hi[k] = x;
+        }
     }
     for (int k = 0; k < 5; ++k) {
         if (lo[k] > hi[k]) lo[k] = hi[k] = 0.0f;
