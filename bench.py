@@ -297,7 +297,8 @@ def secondary(torch, synth, ops, SadField) -> dict:
     (step + Adam, the 768x512 training workload), the Adam step alone, the
     budget statistics pass and the budget step, the 1,000-iteration encode (from the
     synthetic sites and from a gradient-weighted draw), the draw alone, and 2^24
-    random-access queries on a 768x512 / 50k-site map."""
+    random-access queries on a 768x512 / 50k-site map, from the float32 records
+    and from the packed ones."""
     dev = torch.device("cuda", 0)
 
     def per_call(fn, reps):
@@ -372,6 +373,14 @@ def secondary(torch, synth, ops, SadField) -> dict:
     m = xy.shape[0]
     out["query_2e24_points"] = {"Mqueries_per_s": round(m / t / 1e6, 1), "ms": round(t * 1e3, 3),
                                 "GB_per_s_algorithmic": round(52 * m / t / 1e9, 1)}
+    pk, qp = ops.pack_sites(f.params, f.derived, wl.h, wl.w)
+    tp = per_call(lambda: ops.pack_sites(f.params, f.derived, wl.h, wl.w, pk, qp), 20)
+    t = per_call(lambda: ops.query_packed(pk, qp, wl.h, wl.w, f.topk, xy, rgb), 5)
+    out["query_packed_2e24_points"] = {"Mqueries_per_s": round(m / t / 1e6, 1), "ms": round(t * 1e3, 3),
+                                       "GB_per_s_algorithmic": round(52 * m / t / 1e9, 1),
+                                       "pack_50k_us": round(tp * 1e6, 2),
+                                       "note": "16-byte packed records (Appendix B.2) instead of 48-byte ones"}
+    del pk, qp
     del f, xy, rgb
     out["full_refresh"] = refresh_timings(torch, synth, ops, SadField)
     return out

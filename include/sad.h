@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 5
+#define SAD_ABI_VERSION 6
 #define SAD_K 8
 #define SAD_SITE_STRIDE 12
 #define SAD_EMPTY 0xffffffffu
@@ -271,6 +271,36 @@ size_t sad_init_workspace_bytes(int32_t h, int32_t w);
 int sad_init_sites(const float *target, int32_t h, int32_t w, int32_t n, float lambda, uint64_t seed, float log_tau,
                    float r, float log_scale, float *params, float *derived, void *workspace, size_t workspace_bytes,
                    void *stream);
+
+/*
+ * Packed 16-byte evaluation records (Appendix B.2, "Packed storage for
+ * evaluation") and random access from them (Sec. 6.6).
+ * sad_pack_sites: packed [n][4] uint32 (16-byte aligned) receives one record
+ * per site: w0 = qx | qy << 15 | 1 << 31 with qx, qy the 15-bit UNORM codes of
+ * x / w and y / h; w1 = colour codes r | g << 11 | b << 22 (11/11/10 bits);
+ * w2 = log tau' code | r' code << 16; w3 = angle code | float16(a) << 16.
+ * The stored site is the determinant-1 form of the same logit:
+ * hs = 0.5 (log s1 + log s2), log tau' = log tau - hs, r' = r exp(hs)
+ * (correctly rounded float32 exp), a = log s2 - log s1 (float16, nearest
+ * even).  qparams float32[10] receives (min, max - min) of log tau', r', c_r,
+ * c_g, c_b over the usable sites (NaN ignored, -0 as +0; none: 0, 0); codes
+ * are rint(clamp(t, 0, 1) (2^bits - 1)) with t = (v - min) / (max - min) (0
+ * when the range is not positive); the angle code is that of
+ * (theta_w + pi_f) / (2 pi)_f, theta_w = theta - (2 pi)_f rint(theta / (2 pi)_f),
+ * all float32 in that order.  A site that is not usable (derived x < 0) packs
+ * to four zeros.  qparams is also the scratch of the range reduction, so it
+ * must not be read while the call runs.  n > 0 needs h, w > 0.
+ * sad_query_packed: as sad_query_points, with each list entry decoded from
+ * its record (value = min + code / (2^bits - 1) (max - min); x = qx w / 32767,
+ * y = qy h / 32767; angle = code 2 pi / 65535 - pi); entries with an id >= n or
+ * without the usable bit are skipped.  The offsets to the point are formed in
+ * float64; exp, sine and cosine use the GPU's hardware approximations, so
+ * results differ from exact decoding by a few float32 roundings of the logits.
+ */
+int sad_pack_sites(const float *params, const float *derived, int32_t n, int32_t h, int32_t w, uint32_t *packed,
+                   float *qparams, void *stream);
+int sad_query_packed(const uint32_t *packed, const float *qparams, int32_t n, int32_t h, int32_t w,
+                     const uint32_t *topk, const float *xy, int64_t m, float *rgb, void *stream);
 
 /*
  * JFA prepass of a full list refresh (Appendix B.3, "JFA prepass"; the render

@@ -52,6 +52,7 @@ def lib() -> C.CDLL:
         f32p, u32p, f64p, i64p = (C.POINTER(C.c_float), C.POINTER(C.c_uint32),
                                   C.POINTER(C.c_double), C.POINTER(C.c_int64))
         i32, u32, u64, i64 = C.c_int32, C.c_uint32, C.c_uint64, C.c_int64
+        i32p = C.POINTER(C.c_int32)
         L.sadref_prepare_sites.argtypes = [f32p, i32, f32p]
         L.sadref_brute_topk.argtypes = [f32p, i32, i32, i32, u32p]
         L.sadref_propagate.argtypes = [f32p, i32, i32, i32, u32p, u32p, i32, u64, u32, i32]
@@ -70,6 +71,7 @@ def lib() -> C.CDLL:
         L.sadref_half_value.restype = C.c_double
         L.sadref_pack_sites.argtypes = [f32p, f32p, i32, i32, i32, u32p, f32p]
         L.sadref_unpack_site.argtypes = [u32p, f32p, i32, i32, f64p]
+        L.sadref_unpack_sites.argtypes = [u32p, f32p, i32, i32, i32, f64p, i32p]
         L.sadref_packed_logit.argtypes = [f64p, C.c_double, C.c_double]
         L.sadref_packed_logit.restype = C.c_double
         L.sadref_query_packed.argtypes = [u32p, f32p, i32, i32, i32, u32p, f32p, i64, f64p]
@@ -254,6 +256,18 @@ def unpack_site(record: np.ndarray, qp: np.ndarray, h: int, w: int):
     v = np.zeros(9, np.float64)
     ok = lib().sadref_unpack_site(_p(rec, C.c_uint32), _p(q, C.c_float), h, w, _p(v, C.c_double))
     return v if ok else None
+
+
+def unpack_sites(packed: np.ndarray, qp: np.ndarray, h: int, w: int):
+    """All records decoded ([n][9] float64 as unpack_site; zeros where not usable) and the usable mask."""
+    pk = _u32(packed).reshape(-1, 4)
+    q = _f32(qp)
+    n = pk.shape[0]
+    out = np.zeros((n, 9), np.float64)
+    ok = np.zeros(n, np.int32)
+    lib().sadref_unpack_sites(_p(pk, C.c_uint32), _p(q, C.c_float), n, h, w, _p(out, C.c_double),
+                              _p(ok, C.c_int32))
+    return out, ok.astype(bool)
 
 
 def packed_logit(values: np.ndarray, px: float, py: float) -> float:

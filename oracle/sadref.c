@@ -851,6 +851,12 @@ int sadref_unpack_site(const uint32_t *o, const float *qp, int32_t h, int32_t w,
     return 1;
 }
 
+void sadref_unpack_sites(const uint32_t *packed, const float *qp, int32_t n, int32_t h, int32_t w, double *out,
+                         int32_t *usable)
+{
+    for (int32_t i = 0; i < n; ++i) usable[i] = sadref_unpack_site(packed + (size_t)i * 4, qp, h, w, out + (size_t)i * 9);
+}
+
 double sadref_packed_logit(const double *v, double px, double py)
 {
     double dx = px - v[0], dy = py - v[1];

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     for name in ("sad_prepare_sites", "sad_propagate_topk", "sad_render_fwd", "sad_render_bwd",
                  "sad_render_bwd_workspace_bytes", "sad_step_fused", "sad_site_stats", "sad_jfa_seed",
                  "sad_jfa_flood", "sad_budget_workspace_bytes", "sad_densify_prune", "sad_init_workspace_bytes",
-                 "sad_init_sites",
+                 "sad_init_sites", "sad_pack_sites", "sad_query_packed",
                  "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version"):
         assert name in syms
 
@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sad_abi_version() == 5
+    assert lib.sad_abi_version() == 6
     for st in (0, -1, -2, -3, 7):
         assert lib.sad_status_string(st)
 
@@ -235,3 +235,19 @@ def test_init_sites_rejects(lib):
     assert call(ws=WS + 64) == EINVAL
     assert call(wsb=wsb - 1) == EINVAL
     assert call(n=0, t=None, ws=None) == 0  # nothing to draw
+
+
+def test_packed_rejects(lib):
+    pk, q, m_ = lib.sad_pack_sites, lib.sad_query_packed, P + 65536
+    assert pk(P, P + 4096, -1, 8, 8, P + 8192, P + 12288, None) == EINVAL
+    assert pk(P, P + 4096, 10, 0, 8, P + 8192, P + 12288, None) == EINVAL  # positions need an image
+    assert pk(P, P + 4096, 10, 8, 8, P + 8, P + 12288, None) == EINVAL  # misaligned records
+    assert pk(P, P + 4096, 10, 8, 8, P + 4096 + 64, P + 12288, None) == EINVAL  # records over derived
+    assert pk(P, P + 4096, 10, 8, 8, P + 8192, None, None) == EINVAL
+    assert pk(P, P + 4096, 10, 8, 8, P + 8192, P + 8192 + 32, None) == EINVAL  # ranges inside the records
+    assert q(P, P + 4096, 10, 8, 8, P + 8192, m_, -1, m_ + 4096, None) == EINVAL
+    assert q(P, P + 4096, 10, 0, 8, P + 8192, m_, 5, m_ + 4096, None) == EINVAL  # points without lists
+    assert q(P, None, 10, 8, 8, P + 8192, m_, 5, m_ + 4096, None) == EINVAL
+    assert q(P, P + 4096, 10, 8, 8, P + 8192, m_ + 4, 5, m_ + 4096, None) == EINVAL  # misaligned points
+    assert q(P, P + 4096, 10, 8, 8, P + 8192, m_, 5, m_ + 8, None) == EINVAL  # colours over the points
+    assert q(P, P + 4096, 10, 8, 8, P + 8192, m_, 0, m_ + 4096, None) == 0  # no points

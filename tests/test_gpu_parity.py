@@ -476,6 +476,142 @@ def test_init_sites_without_sites(sad):
     assert p.shape == (0, 12) and d.shape == (0, 12)
 
 
+# ---------------------------------------------------------------- packed records
+
+def pack_vs_oracle(sad, ref, p, h, w, label):
+    d = ref.prepare_sites(p)
+    want_pk, want_qp = ref.pack_sites(p, d, h, w)
+    gpk, gqp = sad.pack_sites(to_gpu(p), to_gpu(d), h, w)
+    got_pk = to_np(gpk).view(np.uint32)
+    assert np.array_equal(to_np(gqp).view(np.uint32), want_qp.view(np.uint32)), f"{label}: ranges {to_np(gqp)} {want_qp}"
+    bad = np.argwhere(got_pk != want_pk)
+    assert len(bad) == 0, f"{label}: {len(bad)} words differ, first {bad[:4].tolist()}"
+    return d, want_pk, want_qp, gpk, gqp
+
+
+def packed_query_bound(ref, pk, qp, h, w, topk, xy):
+    """Per point, what float32 decoding may change in the colour: with the
+    float64 decode of each usable entry (tau, r, a, offset d, distance, logit),
+    dl_k = 2^-19 (|l_k| (1 + |log tau_k|) + tau_k (dist_k + |r_k| + e^(|a_k|/2) |d_k|))
+    covers the roundings of the offset, the range decode and the hardware exp,
+    sine and cosine; the softmax moves the colour by at most
+    2 max_k dl_k max_k |c_k - c|, plus the colour decode's rounding."""
+    v, ok = ref.unpack_sites(pk, qp, h, w)
+    n = len(ok)
+    xy = np.nan_to_num(xy, nan=0.0, posinf=0.0, neginf=0.0)  # non-finite points are NaN on both sides
+    i = np.clip(np.floor(xy[:, 0]), 0, w - 1).astype(int)
+    j = np.clip(np.floor(xy[:, 1]), 0, h - 1).astype(int)
+    ids = topk[j, i].astype(np.int64)  # [m][8]
+    use = (ids < n) & ok[np.minimum(ids, n - 1)]
+    e = v[np.minimum(ids, n - 1)]  # [m][8][9]
+    dx = xy[:, 0:1].astype(np.float64) - e[..., 0]
+    dy = xy[:, 1:2].astype(np.float64) - e[..., 1]
+    cs, sn = np.cos(e[..., 7]), np.sin(e[..., 7])
+    u, t = cs * dx + sn * dy, cs * dy - sn * dx
+    dist = np.sqrt(np.exp(e[..., 8]) * u * u + np.exp(-e[..., 8]) * t * t)
+    lg = -e[..., 2] * (dist - e[..., 3])
+    use &= np.isfinite(lg)
+    dl = 2.0 ** -19 * (np.abs(lg) * (1 + np.abs(np.log(e[..., 2]))) +
+                       e[..., 2] * (dist + np.abs(e[..., 3]) + np.exp(np.abs(e[..., 8]) / 2) * np.hypot(dx, dy)))
+    dl = np.where(use, dl, 0.0).max(1)
+    col = e[..., 4:7]
+    cmax = np.where(use[..., None], col, -np.inf).max(1)
+    cmin = np.where(use[..., None], col, np.inf).min(1)
+    spread = np.where(use.any(1)[:, None], cmax - cmin, 0.0)
+    return 2 * dl[:, None] * spread + 2.0 ** -20 * (1 + np.abs(col).max(axis=(1, 2)))[:, None]
+
+
+def query_packed_vs_oracle(sad, ref, pk, qp, gpk, gqp, h, w, topk_np, topk_gpu, xy, label):
+    want = ref.query_packed(pk, qp, h, w, topk_np, xy)
+    got = to_np(sad.query_packed(gpk, gqp, h, w, topk_gpu, to_gpu(xy)))
+    bound = packed_query_bound(ref, pk, qp, h, w, topk_np, xy)
+    fin = np.isfinite(want)
+    assert np.array_equal(fin, np.isfinite(got)), label
+    err = np.abs(got - want)[fin]
+    ratio = (np.abs(got - want) / bound)[fin]
+    say(f"[gpu] {label}: max |err| {err.max():.3g}, median {np.median(err):.3g}, max err/bound {ratio.max():.3g}")
+    assert (ratio <= 1.0).all(), f"{label}: {int((ratio > 1).sum())} values beyond the bound, worst {ratio.max():.3g}"
+    assert err.max() <= 1e-5, label  # and the query path's bar
+
+
+def test_pack_sites_bit_exact(sad, ref):
+    wl = synth.C1
+    p = wl.make_sites()
+    p[::7, 0] = -1.0
+    pack_vs_oracle(sad, ref, p, wl.h, wl.w, "64x64 / 256")
+    p = synth.sites(3, 5000, 37, 53, synth.WIDE_SCALES)
+    p[:, 7] = np.random.default_rng(4).uniform(-50, 50, 5000).astype(np.float32)  # wrapped angles
+    p[10, 4] = -0.0
+    p[11, 2] = np.nan  # ignored by the ranges, coded 0
+    pack_vs_oracle(sad, ref, p, 37, 53, "37x53 / 5000, wide angles, NaN")
+    p = synth.sites(5, 40, 9, 9)
+    p[:, 0] = -1.0
+    pack_vs_oracle(sad, ref, p, 9, 9, "no usable site")
+    pack_vs_oracle(sad, ref, np.zeros((0, 12), np.float32), 9, 9, "no sites")
+
+
+def test_query_packed_c1(sad, ref):
+    wl = synth.C1
+    p = wl.make_sites()
+    p[3, 0] = -1.0
+    d, pk, qp, gpk, gqp = pack_vs_oracle(sad, ref, p, wl.h, wl.w, "C1")
+    m = ref.brute_topk(d, wl.h, wl.w)
+    xy = synth.queries(21, 20000, wl.h, wl.w)
+    xy[:5] = [[np.nan, 1.0], [-3.0, 2.0], [70.0, 70.0], [0.0, 0.0], [64.0, 64.0]]
+    query_packed_vs_oracle(sad, ref, pk, qp, gpk, gqp, wl.h, wl.w, m, to_gpu(m), xy, "C1 queries")
+
+
+def test_query_packed_c5_sampled(sad, ref):
+    """The 768x512 / 50k-site map and 2^24 points in one call; sampled points
+    against the oracle."""
+    wl = synth.C5
+    p = wl.make_sites()
+    d, pk, qp, gpk, gqp = pack_vs_oracle(sad, ref, p, wl.h, wl.w, "C5 records")
+    dg = sad.prepare_sites(to_gpu(p))
+    m_gpu = gpu_schedule(sad, dg, wl.h, wl.w, synth.jfa_strides(wl.h, wl.w, wl.warm_passes), wl.inject_seed,
+                         wl.inject)
+    xy = wl.make_queries()
+    rgb = to_np(sad.query_packed(gpk, gqp, wl.h, wl.w, m_gpu, to_gpu(xy)))
+    pick = np.random.default_rng(8).choice(len(xy), 20000, replace=False)
+    mnp = map_to_np(m_gpu)
+    want = ref.query_packed(pk, qp, wl.h, wl.w, mnp, xy[pick])
+    bound = packed_query_bound(ref, pk, qp, wl.h, wl.w, mnp, xy[pick])
+    ratio = np.abs(rgb[pick] - want) / bound
+    say(f"[gpu] C5 packed: max |err| {np.abs(rgb[pick] - want).max():.3g}, max err/bound {ratio.max():.3g}")
+    assert (ratio <= 1.0).all() and np.abs(rgb[pick] - want).max() <= 1e-5
+
+
+def test_queries_past_one_launch(sad, ref):
+    """2^30 + 777 points (more than one launch's chunk) from both query paths
+    on a 64x64 map: sampled points, those around the chunk boundary and the
+    last ones against the oracle."""
+    wl = synth.C1
+    p = wl.make_sites()
+    d = ref.prepare_sites(p)
+    m_np = ref.brute_topk(d, wl.h, wl.w)
+    dg, mg = to_gpu(d), to_gpu(m_np)
+    pk, qp = ref.pack_sites(p, d, wl.h, wl.w)
+    gpk, gqp = to_gpu(pk), to_gpu(qp)
+    m = (1 << 30) + 777
+    say(f"[gpu] {m} points on the GPU")
+    g = torch.Generator(device=dev())
+    g.manual_seed(12)
+    xy = torch.rand((m, 2), generator=g, device=dev())
+    xy *= torch.tensor([wl.w, wl.h], dtype=torch.float32, device=dev())
+    rgb = torch.empty((m, 3), dtype=torch.float32, device=dev())
+    pick = np.concatenate([np.random.default_rng(3).integers(0, m, 3000), np.arange((1 << 30) - 50, m)])
+    pt = to_np(xy[torch.from_numpy(pick).to(dev())])
+    sad.query_points(dg, wl.h, wl.w, mg, xy, rgb)
+    got = to_np(rgb[torch.from_numpy(pick).to(dev())])
+    assert np.abs(got - ref.query_points(d, wl.h, wl.w, m_np, pt)).max() <= 1e-5
+    rgb.fill_(-1.0)
+    sad.query_packed(gpk, gqp, wl.h, wl.w, mg, xy, rgb)
+    got = to_np(rgb[torch.from_numpy(pick).to(dev())])
+    want = ref.query_packed(pk, qp, wl.h, wl.w, m_np, pt)
+    assert (np.abs(got - want) <= packed_query_bound(ref, pk, qp, wl.h, wl.w, m_np, pt)).all()
+    del xy, rgb
+
+
 # ---------------------------------------------------------------- JFA prepass and full refresh
 
 def crowded_sites(seed, n, h, w):

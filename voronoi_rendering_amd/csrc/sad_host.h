@@ -12,6 +12,7 @@ constexpr int64_t MAX_SITES = int64_t(1) << 30;
 constexpr int32_t MAX_SIDE = 1 << 15;
 constexpr int64_t MAX_TILES = int64_t(1) << 26;
 constexpr int64_t MAX_QUERIES = int64_t(1) << 40;
+constexpr int64_t QUERY_CHUNK = int64_t(1) << 30;  // points per query launch
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 

@@ -583,12 +583,12 @@ struct QueryArgs {
     const uint32_t* topk;
     const float* xy;
     float* rgb;
-    int64_t m;
+    int64_t m, base;  // points base .. m - 1 in this launch
     int32_t n, h, w;
 };
 
 __global__ __launch_bounds__(256) void k_query(QueryArgs a) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t = a.base + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= a.m) return;
     const float2 q = reinterpret_cast<const float2*>(a.xy)[t];
     float* o = a.rgb + t * 3;
@@ -798,6 +798,8 @@ extern "C" int sad_query_points(const float* derived, int32_t n, int32_t h, int3
     a.h = h;
     a.w = w;
     clear_error();
-    hipLaunchKernelGGL(k_query, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, as_stream(stream), a);
+    for (a.base = 0; a.base < m; a.base += QUERY_CHUNK)  // a dispatch holds fewer than 2^32 work-items
+        hipLaunchKernelGGL(k_query, dim3((unsigned)((std::min(QUERY_CHUNK, m - a.base) + 255) / 256)), dim3(256), 0,
+                           as_stream(stream), a);
     return launch_status();
 }

@@ -212,6 +212,46 @@ def init_sites(target: torch.Tensor, n: int, *, lam: float, seed: int, log_tau: 
     return params, derived
 
 
+NQP = 10  # per-image parameters of the packed records
+
+
+def pack_sites(params: torch.Tensor, derived: torch.Tensor, h: int, w: int, packed: torch.Tensor | None = None,
+               qparams: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Packed 16-byte evaluation records ([n][4] int32 holding uint32 words)
+    and their per-image parameters (float32[10]); see sad_pack_sites."""
+    n = params.shape[0]
+    _need(params, "params", torch.float32, (n, REC))
+    _need(derived, "derived", torch.float32, (n, REC))
+    if packed is None:
+        packed = torch.empty((n, 4), dtype=torch.int32, device=params.device)
+    if qparams is None:
+        qparams = torch.empty(NQP, dtype=torch.float32, device=params.device)
+    _need(packed, "packed", torch.int32, (n, 4))
+    _need(qparams, "qparams", torch.float32, (NQP,))
+    st = _native.lib().sad_pack_sites(_ptr(params), _ptr(derived), n, h, w, _ptr(packed), _ptr(qparams),
+                                      _stream(params))
+    _native.check("sad_pack_sites", st)
+    return packed, qparams
+
+
+def query_packed(packed: torch.Tensor, qparams: torch.Tensor, h: int, w: int, topk: torch.Tensor, xy: torch.Tensor,
+                 rgb: torch.Tensor | None = None) -> torch.Tensor:
+    """Colours at points [m][2] from packed records (see sad_query_packed)."""
+    n = packed.shape[0]
+    _need(packed, "packed", torch.int32, (n, 4))
+    _need(qparams, "qparams", torch.float32, (NQP,))
+    _need(topk, "topk", torch.int32, (h, w, K))
+    m = xy.shape[0]
+    _need(xy, "xy", torch.float32, (m, 2))
+    if rgb is None:
+        rgb = torch.empty((m, 3), dtype=torch.float32, device=xy.device)
+    _need(rgb, "rgb", torch.float32, (m, 3))
+    st = _native.lib().sad_query_packed(_ptr(packed), _ptr(qparams), n, h, w, _ptr(topk), _ptr(xy), m, _ptr(rgb),
+                                        _stream(xy))
+    _native.check("sad_query_packed", st)
+    return rgb
+
+
 JFA_K = 4  # ids per pixel in the JFA prepass
 
 
