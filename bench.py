@@ -159,19 +159,22 @@ def cpu_other(include_2048: bool) -> dict:
 INIT = {"lam": 0.3, "log_tau": 0.0, "r": 0.0, "log_scale": 0.7}  # encode from the gradient-weighted density
 
 
-def encode_run(torch, synth, SadField, wl, tgt, iters: int, init: dict | None = None) -> dict:
+def encode_run(torch, synth, SadField, wl, tgt, iters: int, init: dict | None = None, n0: int | None = None,
+               budget=None) -> dict:
     """The training workload end to end: wall clock from the initial
     parameters in device memory (or, with ``init``, from the target alone:
     the gradient-weighted draw of the sites is inside the clock), site
     preparation, warm-up passes, then ``iters`` iterations of propagate +
     forward + backward + Adam, to the last kernel's end; then an untimed
     second run of the same iterations that renders the fit at a few
-    iterations for its PSNR against the target."""
+    iterations for its PSNR against the target.  ``n0`` sites are drawn
+    (default: the workload's count) and ``budget`` is the fit's
+    budget-control schedule."""
     strides = list(wl.strides)
 
     def start():
         if init is not None:
-            return SadField.from_target(tgt, wl.n, seed=wl.inject_seed, inject=wl.inject, **init)
+            return SadField.from_target(tgt, n0 or wl.n, seed=wl.inject_seed, inject=wl.inject, **init)
         return SadField(p0.clone(), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
 
     p0 = torch.from_numpy(wl.make_sites()).to("cuda") if init is None else None
@@ -179,8 +182,7 @@ def encode_run(torch, synth, SadField, wl, tgt, iters: int, init: dict | None = 
     t0 = time.perf_counter()
     f = start()
     f.warm(wl.warm_passes)
-    for _ in range(iters):
-        f.train_iter(strides, tgt)
+    f.fit(tgt, iters, strides, budget)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     del f
@@ -190,13 +192,20 @@ def encode_run(torch, synth, SadField, wl, tgt, iters: int, init: dict | None = 
     marks = {1, 10, 100, iters}
     for it in range(1, iters + 1):
         f.train_iter(strides, tgt)
+        if budget is not None and budget.due(it):  # the same schedule, one iteration at a time
+            f.budget_step(tgt, budget)
         if it in marks:  # the updated sites over the iteration's map
             mse = float(((f.render() - tgt) ** 2).mean())
             psnr[str(it)] = round(10.0 * math.log10(1.0 / mse), 3)
     out = {"s": round(wall, 4), "ms_per_iteration": round(wall / iters * 1e3, 4), "psnr_db_at_iteration": psnr,
            "note": "setup, 16 warm-up passes and all iterations inside the wall clock"}
     if init is not None:
-        out["init"] = dict(init, note="sites drawn from the target's gradient-weighted density inside the clock")
+        out["init"] = dict(init, sites=n0 or wl.n,
+                           note="sites drawn from the target's gradient-weighted density inside the clock")
+    if budget is not None:
+        out["budget"] = {"every": budget.every, "start": budget.start, "stop": budget.stop, "n_split": budget.n_split,
+                         "n_prune": budget.n_prune, "refresh_passes": budget.refresh_passes,
+                         "final_sites": f.active_sites()}
     return out
 
 
@@ -357,6 +366,11 @@ def secondary(torch, synth, ops, SadField) -> dict:
     out["densify_prune_768x512_50k"] = budget_timings(torch, synth, ops, SadField)
     out["encode_768x512_50k_1000_iterations"] = encode_run(torch, synth, SadField, wl, tgt, 1000)
     out["encode_768x512_50k_1000_iterations_gradient_init"] = encode_run(torch, synth, SadField, wl, tgt, 1000, INIT)
+    from voronoi_rendering_amd.pipeline import BudgetSchedule
+
+    prune = BudgetSchedule(every=100, start=100, stop=800, n_prune=6250)  # 100k drawn, 50k left after iteration 800
+    out["encode_768x512_100k_to_50k_1000_iterations_budget"] = encode_run(torch, synth, SadField, wl, tgt, 1000, INIT,
+                                                                          100_000, prune)
     ws = ops.init_workspace(wl.h, wl.w, dev)
     prm = torch.empty((wl.n, ops.REC), dtype=torch.float32, device=dev)
     drv = torch.empty_like(prm)

@@ -433,6 +433,30 @@ def test_field_densify_prune_bookkeeping(sad, ref):
     assert np.array_equal(map_to_np(f.topk), want)
 
 
+def test_fit_with_budget_schedule(sad, ref):
+    """A fit from a gradient-weighted draw with scheduled budget steps: the
+    site count follows the schedule, prepared records follow the sites, every
+    list holds distinct usable ids only, and the error drops."""
+    from voronoi_rendering_amd.pipeline import BudgetSchedule, SadField
+
+    wl = synth.C1
+    tgt = to_gpu(wl.make_target())
+    f = SadField.from_target(tgt, 400, lam=0.3, seed=17, log_scale=0.5)
+    f.warm(16)
+    err0 = float(((f.render() - tgt) ** 2).mean())
+    sched = BudgetSchedule(every=5, start=5, stop=20, n_split=10, n_prune=50, min_mass=0.5)
+    f.fit(tgt, 25, [4, 2, 1], sched)
+    assert f.active_sites() == 400 - 4 * 50 + 4 * 10
+    p = to_np(f.params)
+    assert np.array_equal(to_np(f.derived).view(np.uint32), ref.prepare_sites(p).view(np.uint32))
+    m = map_to_np(f.topk)
+    usable = p[:, 0] >= 0
+    for row in m.reshape(-1, 8):
+        ids = row[row != 0xFFFFFFFF]
+        assert len(set(ids.tolist())) == len(ids) and usable[ids].all()
+    assert float(((f.render() - tgt) ** 2).mean()) < err0
+
+
 # ---------------------------------------------------------------- initialisation
 
 def init_vs_oracle(sad, ref, t, n, lam, seed, label, **kw):

@@ -33,6 +33,29 @@ def bias_corrections(beta1: float, beta2: float, t: int) -> tuple[float, float]:
 
 
 @dataclass
+class BudgetSchedule:
+    """When and how much budget control a fit runs (Sec. 4.5; the pages leave
+    the numbers open): at iterations start, start + every, ... up to stop, split
+    n_split and prune n_prune sites with the budget step's constants, then
+    rebuild the lists from the sites (a JFA round and refresh_passes
+    propagation passes), since the new sites are in no list yet."""
+    every: int = 100
+    start: int = 100
+    stop: int = 800
+    n_split: int = 0
+    n_prune: int = 0
+    alpha: float = 1.0
+    min_mass: float = 1.0
+    offset: float = 0.5
+    r_scale: float = 0.85
+    logtau_shift: float = 0.1
+    refresh_passes: int = 4
+
+    def due(self, it: int) -> bool:
+        return self.start <= it <= self.stop and (it - self.start) % self.every == 0
+
+
+@dataclass
 class SadField:
     params: torch.Tensor  # [n][12] float32 on the GPU
     h: int
@@ -150,6 +173,27 @@ class SadField:
     def train_iter(self, strides: Sequence[int], target: torch.Tensor, fused: bool = True) -> None:
         self.step(strides, target, fused)
         self.adam_step()
+
+    def fit(self, target: torch.Tensor, iters: int, strides: Sequence[int],
+            budget: BudgetSchedule | None = None) -> None:
+        """iters training iterations (propagation passes, forward, backward,
+        Adam), with budget control on the given schedule."""
+        for it in range(1, iters + 1):
+            self.train_iter(strides, target)
+            if budget is not None and budget.due(it):
+                self.budget_step(target, budget)
+
+    def budget_step(self, target: torch.Tensor, budget: BudgetSchedule) -> torch.Tensor:
+        """One scheduled budget step: statistics, prune and split, then the
+        lists rebuilt from the sites.  Returns the numbers pruned and split."""
+        done = self.densify_prune(target, n_split=budget.n_split, n_prune=budget.n_prune, alpha=budget.alpha,
+                                  min_mass=budget.min_mass, offset=budget.offset, r_scale=budget.r_scale,
+                                  logtau_shift=budget.logtau_shift)
+        self.refresh(budget.refresh_passes)
+        return done
+
+    def active_sites(self) -> int:
+        return int((self.params[:, 0] >= 0).sum())
 
     def render(self) -> torch.Tensor:
         return ops.render_fwd(self.derived, self.h, self.w, self.topk)
