@@ -51,10 +51,9 @@ def algorithmic_bytes(h: int, w: int, n: int, n_pass: int) -> dict:
 KERNEL_OF = {"propagate": "k_propagate", "render_bwd": "k_render_bwd"}
 
 
-def measured_traffic(kind: str):
-    """HBM bytes per launch of the kernel from the committed rocprofv3 counter
-    summary (scaled FETCH_SIZE + WRITE_SIZE), or None when the kernel's sources
-    changed since the counters were taken."""
+def counter_record(kind: str):
+    """The kernel's entry of the committed rocprofv3 counter summary, or None
+    when the kernel's sources changed since the counters were taken."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "hbm_counters_768x512.json")
@@ -64,11 +63,34 @@ def measured_traffic(kind: str):
         h = hashlib.sha256()
         for f in rec["sources"]:
             h.update(open(os.path.join(ROOT, f), "rb").read())
-        if h.hexdigest() != rec["source_sha256"]:
-            return None
-        return int(rec["bytes"])
+        return rec if h.hexdigest() == rec["source_sha256"] else None
     except (OSError, KeyError, ValueError):
         return None
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch of the kernel (scaled FETCH_SIZE + WRITE_SIZE), or None."""
+    rec = counter_record(kind)
+    return int(rec["bytes"]) if rec else None
+
+
+# Vector ALU issue peak without packed math: 256 CUs x 4 SIMDs, one wave64
+# instruction (64 lane-operations) per SIMD every 4 cycles, at 2.4 GHz.
+VALU_PEAK_T = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def valu_roofline(kind: str, seconds: float):
+    """Vector-ALU lane-operations per second of the kernel (instructions per
+    wavefront and wavefronts per launch from the counter summary, duration
+    measured live) against the issue peak, or None without valid counters."""
+    rec = counter_record(kind)
+    if not rec or "valu_insts_per_wave" not in rec:
+        return None
+    ops = rec["valu_insts_per_wave"] * rec["waves_per_dispatch"] * 64
+    ach = ops / seconds / 1e12
+    return {"bound": "alu", "achieved": round(ach, 2), "peak": round(VALU_PEAK_T, 2), "unit": "T lane-op/s",
+            "frac": round(ach / VALU_PEAK_T, 4), "valu_insts_per_wave": round(rec["valu_insts_per_wave"], 1),
+            "valu_busy_pct_counter": round(rec["valu_busy_pct"], 1), "kernel": kind}
 
 
 def cpu_baseline(wl, budget_s: float) -> dict:
@@ -560,6 +582,7 @@ def main() -> int:
         "kernel_timing": f"HIP events on the launch stream over {ev_steps} further steps of separate calls: one pair "
                          "around the step's passes (per-pass average), one around the backward (with the gather)",
         "roofline": roofline,
+        "valu_roofline": valu_roofline(dom, avg[dom]),
     }
     if not args.no_secondary:
         out["secondary"] = secondary(torch, synth, ops, SadField)
