@@ -222,20 +222,76 @@ def test_propagate_is_deterministic(sad, c2_state):
     assert torch.equal(a, b)
 
 
-def test_propagate_c4_full_map(sad, ref):
+@pytest.fixture(scope="module")
+def c4_state(sad, ref):
     """2048x2048, 400k sites: 16 warm-up passes and the step strides
-    16, 8, 4, 2, 1 give the oracle's map bit for bit."""
+    16, 8, 4, 2, 1 on both sides."""
     wl = synth.C4
     p = wl.make_sites()
     d = ref.prepare_sites(p)
     strides = synth.jfa_strides(wl.h, wl.w, wl.warm_passes) + list(wl.strides)
     dg = sad.prepare_sites(to_gpu(p))
-    m_gpu = map_to_np(gpu_schedule(sad, dg, wl.h, wl.w, strides, wl.inject_seed, wl.inject))
+    m_gpu = gpu_schedule(sad, dg, wl.h, wl.w, strides, wl.inject_seed, wl.inject)
     cur = None
     for t, s in enumerate(strides):
         cur = ref.propagate(d, wl.h, wl.w, cur, s, wl.inject_seed, t, wl.inject)
         say(f"[gpu] C4 oracle pass {t + 1}/{len(strides)} (stride {s})")
-    assert np.array_equal(m_gpu, cur), f"{(m_gpu != cur).any(-1).sum()} pixels differ"
+    return wl, d, dg, cur, m_gpu
+
+
+def test_propagate_c4_full_map(c4_state):
+    """The 2048x2048 map after warm-up and one step equals the oracle's bit for bit."""
+    wl, d, dg, m_ref, m_gpu = c4_state
+    got = map_to_np(m_gpu)
+    assert np.array_equal(got, m_ref), f"{(got != m_ref).any(-1).sum()} pixels differ"
+
+
+def test_render_c4(sad, ref, c4_state):
+    """Forward, loss and gradients at 2048x2048 / 400k sites (the densest
+    gradient scatter of the workloads)."""
+    wl, d, dg, m_ref, m_gpu = c4_state
+    tgt = wl.make_target()
+    g_ref, g_abs, loss_ref, img_ref = ref.render_bwd(d, wl.h, wl.w, m_ref, tgt)
+    grad = torch.zeros((wl.n, 12), dtype=torch.float32, device=dev())
+    loss = torch.zeros(1, dtype=torch.float32, device=dev())
+    img = torch.empty((wl.h, wl.w, 3), dtype=torch.float32, device=dev())
+    sad.render_bwd(dg, wl.h, wl.w, m_gpu, to_gpu(tgt), grad, loss, img)
+    assert_colour_close(to_np(img), img_ref, "C4 image")
+    assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
+    assert_grad_close(to_np(grad), g_ref, g_abs, "C4 gradients", m_ref, (wl.h, wl.w))
+
+
+def test_propagate_and_render_8192_sampled(sad, ref):
+    """8192x8192 (2^20 tiles) with 2M sites, some inactive: two passes from
+    the empty map (strides 64 and 1), 4,000 sampled pixels and the image's
+    corners and edges of each pass against the oracle run on the GPU's
+    previous map, then the render at those pixels."""
+    h = w = 8192
+    n = 2_000_000
+    p = synth.sites(77, n, h, w, synth.WIDE_SCALES)
+    p[::97, 0] = -1.0
+    say(f"[gpu] {w}x{h}, n={n}: preparing sites")
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p))
+    assert np.array_equal(to_np(dg).view(np.uint32), d.view(np.uint32))
+    rng = np.random.default_rng(5)
+    edge = [0, w - 1, (h - 1) * w, h * w - 1, 5 * w, 5 * w + w - 1, (h - 1) * w + 77]
+    pix = np.concatenate([rng.integers(0, h * w, 4000), edge]).astype(np.int64)
+    sel = torch.from_numpy(pix).to(dev())
+    cur = sad.empty_map(h, w, dev())
+    nxt = torch.empty_like(cur)
+    prev_np = None
+    for t, s in enumerate((64, 1)):
+        sad.propagate_topk(dg, h, w, cur, nxt, stride=s, seed=91, pass_index=t, inject=64)
+        got = to_np(nxt.view(-1, 8)[sel]).view(np.uint32)
+        want = ref.propagate_pixels(d, h, w, prev_np, s, 91, t, 64, pix)
+        assert np.array_equal(got, want), f"pass {t}: {(got != want).any(-1).sum()} sampled pixels differ"
+        say(f"[gpu] pass {t} (stride {s}) matches at {len(pix)} pixels")
+        prev_np = map_to_np(nxt)
+        cur, nxt = nxt, cur
+    xy = np.stack([pix % w + 0.5, pix // w + 0.5], 1).astype(np.float32)
+    got = to_np(sad.query_points(dg, h, w, cur, to_gpu(xy)))
+    assert np.abs(got - ref.query_points(d, h, w, prev_np, xy)).max() <= 1e-5
 
 
 # ---------------------------------------------------------------- render / backward
