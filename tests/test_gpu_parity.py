@@ -724,7 +724,8 @@ def test_jfa_seed_and_flood(sad, ref, h, w, n):
         assert np.array_equal(map_to_np(got), want), f"flood step {step} width {width}"
 
 
-@pytest.mark.parametrize("h,w,n", [(64, 64, 256), (512, 512, 25_000), (45, 131, 900), (1, 1, 3)])
+@pytest.mark.parametrize("h,w,n", [(64, 64, 256), (512, 512, 25_000), (45, 131, 900), (1, 1, 3),
+                                   (2048, 2048, 400_000)])
 def test_full_refresh_and_render(sad, ref, h, w, n):
     """One JFA round, 16 propagation passes and the render, from the sites alone."""
     from voronoi_rendering_amd.pipeline import SadField
