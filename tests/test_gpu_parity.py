@@ -434,6 +434,14 @@ def test_densify_prune_bit_exact(sad, ref, alpha):
     budget_vs_oracle(sad, ref, p, m, v, d, st, t, h, w, f"alpha {alpha}", **kw)
 
 
+def test_densify_prune_400k(sad, ref):
+    """400k sites on a 2048x2048 target: the sorts take their large-input path."""
+    h = w = 2048
+    p, m, v, d, st, t = budget_case(ref, 37, 400_000, h, w)
+    kw = dict(n_split=9000, n_prune=7000, alpha=0.5, min_mass=1.0, offset=0.5, r_scale=0.85, logtau_shift=0.1)
+    budget_vs_oracle(sad, ref, p, m, v, d, st, t, h, w, "400k sites", **kw)
+
+
 def test_densify_prune_limits(sad, ref):
     h, w, n = 17, 23, 80
     p, m, v, d, st, t = budget_case(ref, 33, n, h, w)
