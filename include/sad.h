@@ -22,7 +22,7 @@
  *     SAD_EINVAL       negative size, NULL pointer where data is needed,
  *                      misaligned pointer (arrays: 16 bytes), size limits
  *                      exceeded, aliasing that the call forbids
- *     SAD_EUNSUPPORTED a parameter outside what this build implements
+ *     SAD_EUNSUPPORTED a parameter outside what this library implements
  *                      (inject_per_tile > 64)
  *     SAD_EHIP         the HIP runtime refused the launch
  *   sad_status_string() names a status.

@@ -10,7 +10,7 @@ extern "C" const char* sad_status_string(int status) {
         case SAD_EINVAL:
             return "SAD_EINVAL: invalid argument (size, NULL or misaligned pointer, limit, aliasing)";
         case SAD_EUNSUPPORTED:
-            return "SAD_EUNSUPPORTED: parameter outside what this build implements";
+            return "SAD_EUNSUPPORTED: parameter outside what this library implements";
         case SAD_EHIP:
             return "SAD_EHIP: the HIP runtime refused the launch";
         default:
