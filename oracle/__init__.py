@@ -55,6 +55,7 @@ def lib() -> C.CDLL:
         i32p = C.POINTER(C.c_int32)
         L.sadref_prepare_sites.argtypes = [f32p, i32, f32p]
         L.sadref_brute_topk.argtypes = [f32p, i32, i32, i32, u32p]
+        L.sadref_brute_topk_pixels.argtypes = [f32p, i32, i32, i32, i64p, i64, u32p]
         L.sadref_propagate.argtypes = [f32p, i32, i32, i32, u32p, u32p, i32, u64, u32, i32]
         L.sadref_propagate_pixels.argtypes = [f32p, i32, i32, i32, u32p, i32, u64, u32, i32, i64p, i64, u32p]
         L.sadref_render_fwd.argtypes = [f32p, i32, i32, i32, u32p, f64p]
@@ -153,6 +154,16 @@ def brute_topk(derived: np.ndarray, h: int, w: int) -> np.ndarray:
     derived = _f32(derived).reshape(-1, REC)
     out = np.empty((h, w, K), dtype=np.uint32)
     lib().sadref_brute_topk(_p(derived, C.c_float), derived.shape[0], h, w, _p(out, C.c_uint32))
+    return out
+
+
+def brute_topk_pixels(derived: np.ndarray, h: int, w: int, pixels: np.ndarray) -> np.ndarray:
+    """Exact top-K lists ([m][8]) at the given flat pixel indices."""
+    derived = _f32(derived).reshape(-1, REC)
+    pixels = np.ascontiguousarray(pixels, dtype=np.int64)
+    out = np.empty((pixels.shape[0], K), np.uint32)
+    lib().sadref_brute_topk_pixels(_p(derived, C.c_float), derived.shape[0], h, w, _p(pixels, C.c_int64),
+                                   pixels.shape[0], _p(out, C.c_uint32))
     return out
 
 

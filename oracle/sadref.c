@@ -182,6 +182,26 @@ void sadref_brute_topk(const float *derived, int32_t n, int32_t h, int32_t w, ui
     }
 }
 
+/* The same exact top-K at chosen pixels only (flat indices j * w + i). */
+void sadref_brute_topk_pixels(const float *derived, int32_t n, int32_t h, int32_t w, const int64_t *pix,
+                              int64_t npix, uint32_t *out)
+{
+    (void)h;
+#pragma omp parallel
+    {
+        cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < npix; ++t) {
+            int32_t i = (int32_t)(pix[t] % w), j = (int32_t)(pix[t] / w);
+            float px = (float)i + 0.5f, py = (float)j + 0.5f;
+            int nc = 0;
+            for (int32_t s = 0; s < n; ++s) nc = add_cand(c, nc, derived, n, (uint32_t)s, px, py);
+            topk_of(c, nc, out + (size_t)t * K);
+        }
+        free(c);
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Stochastic injection (Sec. 4.3, global probe set G_t): J site ids per pass
  * per 8x8 pixel tile, the same ids for every pixel of the tile.  The ids come

@@ -67,6 +67,19 @@ def sites(seed: int, n: int, h: int, w: int, recipe: SiteRecipe = SMALL_SCALES) 
     return out
 
 
+def sites_unique_cells(seed: int, n: int, h: int, w: int, recipe: SiteRecipe = WIDE_SCALES) -> np.ndarray:
+    """Site records whose centres lie in n distinct pixels (drawn without
+    replacement) at uniform offsets inside them, the other values as sites()
+    draws them: the collision-free layout of the top-K convergence protocol."""
+    p = sites(seed, n, h, w, recipe)
+    rng = np.random.default_rng(seed + 1)
+    cells = rng.choice(h * w, n, replace=False)
+    off = rng.random((n, 2))
+    p[:, 0] = ((cells % w) + off[:, 0]).astype(np.float32)
+    p[:, 1] = ((cells // w) + off[:, 1]).astype(np.float32)
+    return p
+
+
 def target_polygons(seed: int, h: int, w: int, n_poly: int = 8) -> np.ndarray:
     """Linear colour ramp plus ``n_poly`` opaque convex polygons ([h][w][3] float32).
 

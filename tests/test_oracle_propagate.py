@@ -137,3 +137,15 @@ def test_inject_ids_counter_layout_and_range(ref):
     exp = ids.size / 16
     chi2 = ((hist - exp) ** 2 / exp).sum()
     assert chi2 < 45.0  # p ~ 1e-4 for 15 degrees of freedom
+
+
+def test_brute_force_at_chosen_pixels(ref):
+    """The sampled exact top-K equals the full one at those pixels (including
+    the image's last pixel and repeats)."""
+    h, w = 21, 34
+    p = synth.sites(8, 90, h, w)
+    p[::11, 0] = -1.0
+    d = ref.prepare_sites(p)
+    full = ref.brute_topk(d, h, w).reshape(-1, 8)
+    pix = np.concatenate([np.random.default_rng(2).integers(0, h * w, 50), [0, h * w - 1, 7, 7]])
+    assert np.array_equal(ref.brute_topk_pixels(d, h, w, pix), full[pix])
