@@ -422,6 +422,9 @@ def secondary(torch, synth, ops, SadField) -> dict:
     return out
 
 
+SETTLE_STEPS = 500  # untimed steps after the refresh, before the warm-up steps
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -471,10 +474,17 @@ def main() -> int:
     params = torch.from_numpy(wl.make_sites()).to(dev)
     target = torch.from_numpy(wl.make_target()).to(dev)
     f = SadField(params, wl.h, wl.w, wl.inject_seed, inject=wl.inject)
-    f.warm(wl.warm_passes)
+    strides = list(wl.strides)
+    # The map a long fit works on: the pages' full refresh (a JFA round and 16
+    # passes), then steps until the lists have settled (on these static sites
+    # they reach the exact top-8 everywhere; a step on settled lists is a few
+    # per cent slower than on fresh ones, whose neighbours are mostly listed).
+    f.refresh(16)
+    for _ in range(SETTLE_STEPS):
+        f.sites_changed()
+        f.step(strides, target, fused=True)
     torch.cuda.synchronize()
 
-    strides = list(wl.strides)
     stream = torch.cuda.current_stream(dev)
     ev = []  # (kind, start event, end event, launches between them)
 
@@ -575,6 +585,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": "C2: 768x512 RGB f32, 50,000 sites, K=8, strides 8,4,2,1, 64 injected per 8x8 "
                                "tile, forward+backward with loss",
+                   "map": f"full refresh (JFA round + 16 passes), then {SETTLE_STEPS} settling steps",
                    "pixels": pix, "sites": wl.n, "passes_per_step": len(strides), "parallelism": "single GPU"},
         "step_frac_of_hbm_roofline": round(ab["step"] / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_us": {k: round(v * 1e6, 3) for k, v in avg.items()},

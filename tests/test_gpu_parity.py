@@ -186,6 +186,40 @@ def test_propagate_c2_full_map(c2_state):
     assert np.array_equal(got, m_ref), f"{(got != m_ref).any(-1).sum()} pixels differ"
 
 
+def test_c2_map_quality(sad, ref):
+    """Quality of the 768x512 / 50k-site map (top-8 sets against brute force
+    on 1,024 random pixels): 16 passes from an empty map find few sites (a
+    site enters the lists only when a probe lands on it), the full refresh
+    about two thirds of the lists, and steps on the static sites settle the
+    lists to the exact top-8."""
+    from voronoi_rendering_amd.pipeline import SadField
+
+    wl = synth.C2
+    p = wl.make_sites()
+    d = ref.prepare_sites(p)
+    tgt = to_gpu(wl.make_target())
+    pix = np.random.default_rng(70).integers(0, wl.h * wl.w, 1024)
+    exact = np.sort(ref.brute_topk_pixels(d, wl.h, wl.w, pix), axis=1)
+    sel = torch.from_numpy(pix).to(dev())
+
+    def match(f):
+        got = np.sort(to_np(f.topk.view(-1, 8)[sel]).view(np.uint32), axis=1)
+        return float((got == exact).all(1).mean())
+
+    f = SadField(to_gpu(p), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+    f.warm(wl.warm_passes)
+    from_empty = match(f)
+    f.refresh(16)
+    refreshed = match(f)
+    for _ in range(500):
+        f.sites_changed()
+        f.step(list(wl.strides), tgt, fused=True)
+    settled = match(f)
+    say(f"[gpu] C2 exact match: 16 passes from empty {from_empty:.3f}, full refresh {refreshed:.3f}, "
+        f"+500 steps {settled:.3f}")
+    assert refreshed >= 0.5 and settled >= 0.99
+
+
 def test_propagate_with_score_maps(sad, ref, c2_state):
     """Passes chained through score maps (the previous pass's logits reused)
     give the oracle's lists bit for bit, and the score map holds exactly the
