@@ -155,7 +155,7 @@ constexpr int RT_X = 4, RT_Y = 2;  // tiles per region
 constexpr int REGION_W = RT_X * TILE, REGION_H = RT_Y * TILE;
 constexpr int REGION_WAVES = RT_X * RT_Y;
 constexpr int SLOTS = 256;
-constexpr int REGION_PROBES = 16;
+constexpr int REGION_PROBES = 32;
 constexpr int NGRAD = 10;
 constexpr int NSTAT = 8;
 constexpr int NTERM_MAX = 10;
