@@ -128,9 +128,11 @@ __global__ __launch_bounds__(256) void k_render_fwd(PixArgs a) {
 //
 // A workgroup covers one region of 2 x 4 tiles (16 rows x 32 columns of
 // pixels), one wavefront per tile.  Per-pixel gradient contributions are
-// summed in LDS per site (open addressing keyed by site id, multiplicative
-// hash, linear probing over at most REGION_PROBES slots, keys claimed by
-// compare-and-swap).
+// summed in LDS per site (open addressing keyed by site id: a multiplicative
+// hash picks the first slot and a second one an odd step, so a site's probe
+// sequence visits every slot and sequences of different sites do not run
+// together as linear probing's do when the table fills; at most REGION_PROBES
+// slots, keys claimed by compare-and-swap).
 //
 // The LDS sums are exact 64-bit fixed-point integers: a contribution t
 // becomes floor(t 2^E), 2^E = 2^45 * (the power of two >= h*w), so
@@ -171,6 +173,7 @@ __host__ __device__ inline RegionGrid region_grid(int32_t h, int32_t w) {
 }
 
 __device__ __forceinline__ uint32_t slot_hash(uint32_t id) { return (id * 2654435761u) >> 24; }  // 8 bits
+__device__ __forceinline__ uint32_t slot_step(uint32_t id) { return ((id * 0x85ebca6bu) >> 24) | 1u; }  // odd
 
 // home region of a site from its prepared position (same arithmetic in both kernels)
 __device__ __forceinline__ void home_region(float x, float y, RegionGrid rg, int& hx, int& hy) {
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
                 slot[k] = pos[k];
                 pend &= ~(1u << k);
             } else {
-                pos[k] = (pos[k] + 1) & (SLOTS - 1);
+                pos[k] = (pos[k] + (int)slot_step(ids[k])) & (SLOTS - 1);
             }
         }
     }
@@ -550,7 +553,7 @@ __global__ __launch_bounds__(256) void k_grad_gather(RegionGrid rg, const uint32
                         break;
                     }
                     if (key == EMPTY) break;
-                    pos = (pos + 1) & (SLOTS - 1);
+                    pos = (pos + slot_step((uint32_t)site)) & (SLOTS - 1);
                 }
             }
         }
