@@ -12,9 +12,13 @@
 //
 // Flood pass with step s: every pixel keeps the 4 best distinct usable ids of
 // the 4-lists at (i + a s, j + b s), a, b in {-1, 0, 1}, inside the image.
-// One wavefront per 8x8 tile; ids already in the pixel's list are not scored
-// again, and a wavefront skips a neighbour's scoring when no lane has a new id
-// in it.
+// One wavefront per 8x8 tile.  An id is not scored again when it is in the
+// pixel's list or in one of the two lists visited just before (in the order
+// centre, right, bottom-right, bottom, bottom-left, left, top-left, top,
+// top-right): such an id is in the list or has been beaten by 4 better ones,
+// and the 4th entry only improves.  About half of a pixel's 36 candidates
+// repeat; most repeats sit in those two lists.  A wavefront skips a
+// neighbour's scoring when no lane has a new id in it.
 #include "sad_device.h"
 #include "sad_host.h"
 
@@ -124,21 +128,36 @@ __global__ __launch_bounds__(WAVE* JFA_WAVES) void k_jfa_flood(JfaArgs a) {
     Top4 t;
     t.clear();
     if (n > 0) {
+        constexpr int ORDER[9] = {4, 5, 8, 7, 6, 3, 0, 1, 2};  // q = (a + 1) + 3 (b + 1)
+        uint32_t seen1[JFA_K], seen2[JFA_K];  // the ids of the last two lists visited
+#pragma unroll
+        for (int k = 0; k < JFA_K; ++k) seen1[k] = seen2[k] = EMPTY;
 #pragma unroll
         for (int q0 = 0; q0 < 9; ++q0) {
-            const int q = (q0 + 4) % 9;  // the pixel's own list first
+            const int q = ORDER[q0];
             const uint32_t v[JFA_K] = {nl[q].x, nl[q].y, nl[q].z, nl[q].w};
             bool fresh[JFA_K];
             bool any = false;
 #pragma unroll
             for (int k = 0; k < JFA_K; ++k) {
-                fresh[k] = ok[q] & (v[k] < n) & !t.has(v[k]);
+                const bool seen = (v[k] == seen1[0]) | (v[k] == seen1[1]) | (v[k] == seen1[2]) | (v[k] == seen1[3]) |
+                                  (v[k] == seen2[0]) | (v[k] == seen2[1]) | (v[k] == seen2[2]) | (v[k] == seen2[3]);
+                fresh[k] = ok[q] & (v[k] < n) & !t.has(v[k]) & !seen;
                 any |= fresh[k];
             }
-            if (!__any(any)) continue;
-            Geo g[JFA_K];
 #pragma unroll
-            for (int k = 0; k < JFA_K; ++k) g[k] = load_geo_clamped(a.derived, n, v[k]);
+            for (int k = 0; k < JFA_K; ++k) {
+                seen2[k] = seen1[k];
+                seen1[k] = ok[q] ? v[k] : EMPTY;  // a list outside the image was not considered
+            }
+            if (!__any(any)) continue;
+            Geo g[JFA_K];  // only lanes with a new id fetch its record
+#pragma unroll
+            for (int k = 0; k < JFA_K; ++k) {
+                g[k].g0 = make_float4(-1.0f, -1.0f, 0.0f, 0.0f);
+                g[k].g1 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (fresh[k]) g[k] = load_geo(a.derived, v[k]);  // fresh implies v[k] < n
+            }
 #pragma unroll
             for (int k = 0; k < JFA_K; ++k) {
                 const float s = usable_logit(g[k], v[k] < n, px, py);
