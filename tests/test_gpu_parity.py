@@ -220,6 +220,41 @@ def test_c2_map_quality(sad, ref):
     assert refreshed >= 0.5 and settled >= 0.99
 
 
+def test_bench_map_step(sad, ref):
+    """The launch configuration the bench times: the 768x512 / 50k-site map
+    built by the full refresh and settled by 500 steps, then one more step
+    (stride-8 pass with the logits recomputed, passes with score maps, the
+    backward): every pass and the gradients against the oracle run on the
+    GPU's map."""
+    from voronoi_rendering_amd.pipeline import SadField
+
+    wl = synth.C2
+    p = wl.make_sites()
+    d = ref.prepare_sites(p)
+    tgt_np = wl.make_target()
+    tgt = to_gpu(tgt_np)
+    f = SadField(to_gpu(p), wl.h, wl.w, wl.inject_seed, inject=wl.inject)
+    f.refresh(16)
+    for _ in range(500):
+        f.sites_changed()
+        f.step(list(wl.strides), tgt, fused=True)
+    f.sites_changed()
+    prev = map_to_np(f.topk)
+    for s in wl.strides:
+        first = f.pass_index
+        f.propagate([s])
+        want = ref.propagate(d, wl.h, wl.w, prev, s, wl.inject_seed, first, wl.inject)
+        got = map_to_np(f.topk)
+        assert np.array_equal(got, want), f"stride {s}: {(got != want).any(-1).sum()} pixels differ"
+        prev = want
+    g_ref, g_abs, loss_ref, _ = ref.render_bwd(d, wl.h, wl.w, prev, tgt_np)
+    grad = torch.zeros((wl.n, 12), dtype=torch.float32, device=dev())
+    loss = torch.zeros(1, dtype=torch.float32, device=dev())
+    sad.render_bwd(f.derived, wl.h, wl.w, f.topk, tgt, grad, loss, None)
+    assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
+    assert_grad_close(to_np(grad), g_ref, g_abs, "settled-map gradients", prev, (wl.h, wl.w))
+
+
 def test_propagate_with_score_maps(sad, ref, c2_state):
     """Passes chained through score maps (the previous pass's logits reused)
     give the oracle's lists bit for bit, and the score map holds exactly the
