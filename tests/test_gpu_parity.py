@@ -363,6 +363,42 @@ def test_propagate_and_render_8192_sampled(sad, ref):
     assert np.abs(got - ref.query_points(d, h, w, prev_np, xy)).max() <= 1e-5
 
 
+def test_calls_follow_the_current_stream(sad, ref):
+    """Every call enqueues on the caller's current stream: a side stream
+    (default priority) gives the same map and image as the default stream,
+    bit for bit, and the same loss and gradients up to the order of their
+    float atomics."""
+    wl = synth.C1
+    p = to_gpu(wl.make_sites())
+    tgt = to_gpu(wl.make_target())
+
+    def run():
+        d = sad.prepare_sites(p)
+        cur = sad.empty_map(wl.h, wl.w, dev())
+        nxt = torch.empty_like(cur)
+        for t, st in enumerate(wl.strides):
+            sad.propagate_topk(d, wl.h, wl.w, cur, nxt, stride=st, seed=wl.inject_seed, pass_index=t,
+                               inject=wl.inject)
+            cur, nxt = nxt, cur
+        grad = torch.zeros((wl.n, 12), dtype=torch.float32, device=dev())
+        loss = torch.zeros(1, dtype=torch.float32, device=dev())
+        img = torch.empty((wl.h, wl.w, 3), dtype=torch.float32, device=dev())
+        sad.render_bwd(d, wl.h, wl.w, cur, tgt, grad, loss, img)
+        return cur, img, loss, grad
+
+    base = [to_np(x) for x in run()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        out = run()
+    side.synchronize()
+    got = [to_np(x) for x in out]
+    for a, b in zip(base[:2], got[:2]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    np.testing.assert_allclose(got[2], base[2], rtol=1e-6)
+    np.testing.assert_allclose(got[3], base[3], rtol=1e-5, atol=1e-7 * np.abs(base[3]).max())
+
+
 # ---------------------------------------------------------------- render / backward
 
 def test_render_fwd_c1_c2(sad, ref, c2_state):
