@@ -48,7 +48,7 @@ def algorithmic_bytes(h: int, w: int, n: int, n_pass: int) -> dict:
     return {"propagate": prop, "render_bwd": bwd, "step": step}
 
 
-KERNEL_OF = {"propagate": "k_propagate", "render_bwd": "k_render_bwd"}
+KERNEL_OF = {"propagate": "k_propagate", "render_bwd": "k_backward"}
 
 
 def counter_record(kind: str):
@@ -388,7 +388,7 @@ def secondary(torch, synth, ops, SadField) -> dict:
     out["adam_step_50k"] = {"us": round(t * 1e6, 2), "GB_per_s": round(adam_bytes / t / 1e9, 1),
                             "algorithmic_bytes": adam_bytes}
     stats = torch.zeros((wl.n, ops.NSTAT), dtype=torch.float32, device=dev)
-    ws = ops.bwd_workspace(wl.h, wl.w, dev)
+    ws = ops.stats_workspace(wl.h, wl.w, dev)
     t = per_call(lambda: ops.site_stats(f.derived, wl.h, wl.w, f.topk, tgt, stats, ws), 20)
     stat_bytes = wl.h * wl.w * (32 + 12) + wl.n * (48 + 2 * 32)  # lists, target; records, stats read + written
     out["site_stats_768x512_50k"] = {"us": round(t * 1e6, 2), "GB_per_s": round(stat_bytes / t / 1e9, 1),

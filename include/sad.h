@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 6
+#define SAD_ABI_VERSION 7
 #define SAD_K 8
 #define SAD_SITE_STRIDE 12
 #define SAD_EMPTY 0xffffffffu
@@ -153,7 +153,8 @@ int sad_render_fwd(const float *derived, int32_t n, int32_t h, int32_t w, const 
                    void *stream);
 
 /*
- * Loss and hand-derived gradients (Sec. 6.1 loss; Appendix B.4).
+ * Loss and hand-derived gradients (Sec. 6.1 loss; Appendix B.4 "Per-pixel
+ * gradients").
  * L = sum over pixels and channels of (c - target)^2 / (h*w).
  * With g = 2 (c - target) / (h*w) and delta_k = w_k (g.c_i - g.c) for entry k
  * (site i), the gradient record of site i receives, summed over pixels:
@@ -163,25 +164,22 @@ int sad_render_fwd(const float *derived, int32_t n, int32_t h, int32_t w, const 
  *   x += -2 kappa (a cos/s1 - b sin/s2);  y += -2 kappa (a sin/s1 + b cos/s2);
  *   theta += 2 kappa a_r b_r (1/s1^2 - 1/s2^2);
  *   log_s1 += -2 kappa a^2;  log_s2 += -2 kappa b^2.
- * The per-pixel terms are summed per site on chip, then per site across
- * neighbouring image regions (Sec. 4.8 reduces gradients per tile for the
- * same reason); only sites with very wide footprints use float atomics.
+ * The logits are the float32 values of the formula above; the weights,
+ * blend, residual and terms are formed in float64 from them.  The terms are
+ * summed per site on chip over regions of 32 x 16 pixels (Sec. 4.8 reduces
+ * gradients per tile before any global atomic), then added to grad with one
+ * float atomic per (region, site, parameter).
  *   target     [h][w][3] float32, read
- *   grad       [n][12] float32, ACCUMULATED into (+=); the summation order,
- *              and so the last bits, vary from run to run; entries 10, 11
- *              are not touched
+ *   grad       [n][12] float32, ACCUMULATED into (+=); the order of the float
+ *              atomics, and so the last bits, vary from run to run; entries
+ *              10, 11 are not touched
  *   loss       NULL, or one float32 accumulated into (+= L)
  *   image      NULL, or [h][w][3] float32 written with the rendered colours
- *   workspace  device scratch of at least sad_render_bwd_workspace_bytes(h, w)
- *              bytes, 16-byte aligned, owned by the caller; its contents on
- *              entry do not matter and it must not be in use by another call
- *              at the same time
+ * grad, loss and image may overlap neither each other nor derived, topk or
+ * target.  The call needs no scratch memory.
  */
-size_t sad_render_bwd_workspace_bytes(int32_t h, int32_t w);
-
 int sad_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
-                   const float *target, float *grad, float *loss, float *image, void *workspace,
-                   size_t workspace_bytes, void *stream);
+                   const float *target, float *grad, float *loss, float *image, void *stream);
 
 /*
  * Per-site budget statistics over the map topk, the inputs of densification
@@ -199,11 +197,17 @@ int sad_render_bwd(const float *derived, int32_t n, int32_t h, int32_t w, const 
  *       weighted second moments about the site; their zeroth is the mass)
  *   target     [h][w][3] float32, read
  *   stats      [n][8] float32, 16-byte aligned, ACCUMULATED into (+=); the
- *              summation order, and so the last bits, may vary between runs
- *   workspace  as for sad_render_bwd (sad_render_bwd_workspace_bytes(h, w))
- * Sums per site are formed as in sad_render_bwd (per-region on-chip sums,
- * then one gather per site).
+ *              summation order, and so the last bits, may vary between runs;
+ *              may not overlap derived, topk or target
+ *   workspace  device scratch of at least sad_site_stats_workspace_bytes(h, w)
+ *              bytes, 16-byte aligned, owned by the caller; its contents on
+ *              entry do not matter; it may not overlap stats, derived, topk
+ *              or target, nor be in use by another call at the same time
+ * Sums per site are formed per region of 32 x 16 pixels on chip (exact
+ * fixed-point sums in LDS), written to the workspace, then gathered per site
+ * from the regions around the site's own.
  */
+size_t sad_site_stats_workspace_bytes(int32_t h, int32_t w);
 int sad_site_stats(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
                    const float *target, float *stats, void *workspace, size_t workspace_bytes, void *stream);
 
@@ -332,19 +336,19 @@ int sad_jfa_flood(const float *derived, int32_t n, int32_t h, int32_t w, const u
  * a training iteration, Sec. 6.6 / Table 9, then Sec. 4.8 / Appendix B.4).
  * Equivalent to sad_propagate_topk(derived, n, h, w, topk_prev, scores_prev,
  * topk_next, scores_next, stride, seed, pass_index, inject_per_tile) then
- * sad_render_bwd(derived, n, h, w, topk_next, target, grad, loss, image,
- * workspace, workspace_bytes): topk_next, scores_next and image are the same
- * bits; grad and loss differ only by summation order, as between two calls
- * of sad_render_bwd.  Every argument is checked before any work is enqueued,
- * so a rejected call leaves all buffers untouched.
+ * sad_render_bwd(derived, n, h, w, topk_next, target, grad, loss, image),
+ * and enqueued as those two launches: topk_next, scores_next and image are the
+ * same bits; grad and loss differ only by summation order, as between two
+ * calls of sad_render_bwd.  Every argument is checked before any work is
+ * enqueued, so a rejected call leaves all buffers untouched.
  * Arguments, formats and checks are those of the two calls; in addition
- * topk_next and scores_next must not overlap target, grad, loss, image,
- * workspace or derived.
+ * topk_next and scores_next must not overlap target, grad, loss, image or
+ * derived.
  */
 int sad_step_fused(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk_prev,
                    const float *scores_prev, uint32_t *topk_next, float *scores_next, int32_t stride, uint64_t seed,
                    uint32_t pass_index, int32_t inject_per_tile, const float *target, float *grad, float *loss,
-                   float *image, void *workspace, size_t workspace_bytes, void *stream);
+                   float *image, void *stream);
 
 /*
  * One Adam step (Kingma & Ba) on the site parameters (Sec. 5: per-parameter

@@ -27,7 +27,7 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     syms = declared_symbols()
     for name in ("sad_prepare_sites", "sad_propagate_topk", "sad_render_fwd", "sad_render_bwd",
-                 "sad_render_bwd_workspace_bytes", "sad_step_fused", "sad_site_stats", "sad_jfa_seed",
+                 "sad_site_stats_workspace_bytes", "sad_step_fused", "sad_site_stats", "sad_jfa_seed",
                  "sad_jfa_flood", "sad_budget_workspace_bytes", "sad_densify_prune", "sad_init_workspace_bytes",
                  "sad_init_sites", "sad_pack_sites", "sad_query_packed",
                  "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version"):
@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sad_abi_version() == 6
+    assert lib.sad_abi_version() == 7
     for st in (0, -1, -2, -3, 7):
         assert lib.sad_status_string(st)
 
@@ -92,14 +92,22 @@ def test_propagate_rejects(lib):
 def test_render_query_adam_reject(lib):
     assert lib.sad_render_fwd(P, 10, 8, 8, P + 4096, None, None) == EINVAL
     assert lib.sad_render_fwd(P, 10, -8, 8, P + 4096, P + 8192, None) == EINVAL
-    WS = 1 << 30
-    wsb = lib.sad_render_bwd_workspace_bytes(8, 8)
-    assert wsb > 0 and lib.sad_render_bwd_workspace_bytes(-1, 8) == 0
-    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, None, None, None, WS, wsb, None) == EINVAL
-    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P, None, None, WS, wsb, None) == EINVAL  # grad aliases
-    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P + 65536, P + 2, None, WS, wsb, None) == EINVAL
-    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P + 65536, None, None, None, wsb, None) == EINVAL
-    assert lib.sad_render_bwd(P, 10, 8, 8, P + 4096, P + 8192, P + 65536, None, None, WS, wsb - 1, None) == EINVAL
+    bwd = lib.sad_render_bwd
+    G, T, L = P + 65536, P + 8192, P + 131072  # grad, target, loss: apart
+    assert bwd(P, 10, 8, 8, P + 4096, T, None, None, None, None) == EINVAL  # no grad
+    assert bwd(P, 10, 8, 8, P + 4096, None, G, None, None, None) == EINVAL  # no target
+    assert bwd(P, 10, 8, 8, P + 4096, T, P, None, None, None) == EINVAL  # grad aliases derived
+    assert bwd(P, 10, 8, 8, P + 4096, T, P + 4096, None, None, None) == EINVAL  # grad over the lists
+    assert bwd(P, 10, 8, 8, P + 4096, T, T, None, None, None) == EINVAL  # grad over the target
+    assert bwd(P, 10, 8, 8, P + 4096, T, G, P + 2, None, None) == EINVAL  # loss misaligned
+    assert bwd(P, 10, 8, 8, P + 4096, T, G, T + 16, None, None) == EINVAL  # loss inside the target
+    assert bwd(P, 10, 8, 8, P + 4096, T, G, G + 64, None, None) == EINVAL  # loss inside grad
+    assert bwd(P, 10, 8, 8, P + 4096, T, G, None, P + 4096 + 32, None) == EINVAL  # image over the lists
+    assert bwd(P, 10, 8, 8, P + 4096, T, G, None, G + 16, None) == EINVAL  # image over grad
+    assert bwd(P, 10, 8, 8, P + 4096, T, G, L, L, None) == EINVAL  # image over the loss
+    assert bwd(P, 10, 8, 8, P + 4096, T, G, None, P + 2, None) == EINVAL  # image misaligned, over derived
+    assert bwd(P, -1, 8, 8, P + 4096, T, G, None, None, None) == EINVAL
+    assert bwd(P, 10, 0, 8, None, None, G, None, None, None) == 0  # empty image: nothing to do
     assert lib.sad_query_points(P, 10, 8, 8, P + 4096, P + 8192, -1, P + 65536, None) == EINVAL
     assert lib.sad_query_points(P, 10, 8, 8, P + 4096, P + 8196, 5, P + 65536, None) == EINVAL  # xy misaligned
     assert lib.sad_query_points(P, 10, 0, 8, P + 4096, P + 8192, 5, P + 65536, None) == EINVAL  # no lists
@@ -115,15 +123,13 @@ def test_render_query_adam_reject(lib):
 
 def test_step_fused_rejects(lib):
     f = lib.sad_step_fused
-    WS = 1 << 30
-    wsb = lib.sad_render_bwd_workspace_bytes(8, 8)
     ok = dict(derived=P, n=10, h=8, w=8, prev=None, sprev=None, nxt=P + 4096, snext=None, stride=1, seed=0, pi=0,
-              inj=64, tgt=P + 8192, grad=P + 65536, loss=None, img=None, ws=WS, wsb=wsb)
+              inj=64, tgt=P + 8192, grad=P + 65536, loss=None, img=None)
 
     def call(**kw):
         a = dict(ok, **kw)
         return f(a["derived"], a["n"], a["h"], a["w"], a["prev"], a["sprev"], a["nxt"], a["snext"], a["stride"],
-                 a["seed"], a["pi"], a["inj"], a["tgt"], a["grad"], a["loss"], a["img"], a["ws"], a["wsb"], None)
+                 a["seed"], a["pi"], a["inj"], a["tgt"], a["grad"], a["loss"], a["img"], None)
 
     # the checks of the propagation pass
     assert call(stride=0) == EINVAL
@@ -134,13 +140,11 @@ def test_step_fused_rejects(lib):
     assert call(tgt=None) == EINVAL
     assert call(grad=None) == EINVAL
     assert call(grad=P) == EINVAL  # aliases derived
-    assert call(ws=None) == EINVAL
-    assert call(wsb=wsb - 1) == EINVAL
     assert call(loss=P + 2) == EINVAL
+    assert call(loss=P + 8192 + 4) == EINVAL  # loss inside the target
     # the pass's outputs against everything else the step touches
     assert call(nxt=P + 8192) == EINVAL  # over the target
     assert call(snext=P + 65536) == EINVAL  # over the gradients
-    assert call(nxt=WS) == EINVAL  # over the workspace
     assert call(snext=P + 12288, img=P + 12288) == EINVAL  # image over the scores
     assert call(nxt=P + 16384, loss=P + 16384 + 64) == EINVAL  # loss inside the list map
     assert call(h=0, nxt=None, tgt=None) == 0  # empty image: nothing to do
@@ -149,7 +153,8 @@ def test_step_fused_rejects(lib):
 def test_site_stats_rejects(lib):
     f = lib.sad_site_stats
     WS = 1 << 30
-    wsb = lib.sad_render_bwd_workspace_bytes(8, 8)
+    wsb = lib.sad_site_stats_workspace_bytes(8, 8)
+    assert wsb > 0 and lib.sad_site_stats_workspace_bytes(-1, 8) == 0
     ok = dict(derived=P, n=10, h=8, w=8, topk=P + 4096, tgt=P + 8192, stats=P + 65536, ws=WS, wsb=wsb)
 
     def call(**kw):
@@ -165,6 +170,11 @@ def test_site_stats_rejects(lib):
     assert call(ws=None) == EINVAL
     assert call(wsb=wsb - 1) == EINVAL
     assert call(stats=WS + 64) == EINVAL  # inside the workspace
+    assert call(ws=P + 8192 + 64) == EINVAL  # workspace over the target
+    assert call(ws=P + 4096) == EINVAL  # workspace over the lists
+    assert call(ws=P) == EINVAL  # workspace over the site records
+    assert call(stats=P + 4096) == EINVAL  # statistics over the lists
+    assert call(stats=P + 8192) == EINVAL  # statistics over the target
     assert call(h=0, topk=None, tgt=None, ws=None) == 0  # empty image: nothing to do
 
 

@@ -252,7 +252,7 @@ def test_bench_map_step(sad, ref):
     loss = torch.zeros(1, dtype=torch.float32, device=dev())
     sad.render_bwd(f.derived, wl.h, wl.w, f.topk, tgt, grad, loss, None)
     assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
-    assert_grad_close(to_np(grad), g_ref, g_abs, "settled-map gradients", prev, (wl.h, wl.w))
+    assert_grad_close(to_np(grad), g_ref, "settled-map gradients")
 
 
 def test_propagate_with_score_maps(sad, ref, c2_state):
@@ -327,7 +327,7 @@ def test_render_c4(sad, ref, c4_state):
     sad.render_bwd(dg, wl.h, wl.w, m_gpu, to_gpu(tgt), grad, loss, img)
     assert_colour_close(to_np(img), img_ref, "C4 image")
     assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
-    assert_grad_close(to_np(grad), g_ref, g_abs, "C4 gradients", m_ref, (wl.h, wl.w))
+    assert_grad_close(to_np(grad), g_ref, "C4 gradients")
 
 
 def test_propagate_and_render_8192_sampled(sad, ref):
@@ -431,12 +431,11 @@ def test_render_bwd_c1(sad, ref):
     assert_colour_close(to_np(img), img_ref, "C1 image from backward")
     assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
     g = to_np(grad)
-    assert_grad_close(g, g_ref, g_abs, "C1 gradients", m, (wl.h, wl.w))
+    assert_grad_close(g, g_ref, "C1 gradients")
     assert np.all(g[:, 10:] == 0)
     # accumulation: a second call adds the same again
     sad.render_bwd(dg, wl.h, wl.w, to_gpu(m), to_gpu(tgt), grad, loss, None)
-    assert_grad_close(to_np(grad), 2 * g_ref, 2 * g_abs, "C1 gradients, accumulated twice", np.concatenate([m, m]),
-                      (wl.h, wl.w))
+    assert_grad_close(to_np(grad), 2 * g_ref, "C1 gradients, accumulated twice")
 
 
 def test_render_bwd_c2(sad, ref, c2_state):
@@ -447,7 +446,7 @@ def test_render_bwd_c2(sad, ref, c2_state):
     loss = torch.zeros(1, dtype=torch.float32, device=dev())
     sad.render_bwd(dg, wl.h, wl.w, m_gpu, to_gpu(tgt), grad, loss, None)
     assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
-    assert_grad_close(to_np(grad), g_ref, g_abs, "C2 gradients", m_ref, (wl.h, wl.w))
+    assert_grad_close(to_np(grad), g_ref, "C2 gradients")
 
 
 # ---------------------------------------------------------------- budget statistics
@@ -916,7 +915,7 @@ def fused_vs_oracle(sad, ref, d, dg, h, w, prev_np, prev_gpu, stride, seed, t, i
     assert np.array_equal(imf.view(np.uint32), imc.view(np.uint32)), f"{label}: images differ"
     assert_colour_close(imf, img_ref, f"{label} image")
     assert abs(lossf - loss_ref) <= 1e-5 * loss_ref
-    assert_grad_close(gf, g_ref, g_abs, f"{label} gradients", m1, (h, w))
+    assert_grad_close(gf, g_ref, f"{label} gradients")
     assert np.all(gf[:, 10:] == 0)
     return lf, sf
 

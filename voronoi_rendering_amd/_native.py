@@ -26,9 +26,9 @@ _SIGS = {
                                      C.c_void_p]),
     "sad_render_fwd": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p]),
-    "sad_render_bwd_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
     "sad_render_bwd": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
-                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "sad_site_stats_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
     "sad_site_stats": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "sad_budget_workspace_bytes": (C.c_size_t, [C.c_int32]),
@@ -47,8 +47,7 @@ _SIGS = {
                                 C.c_int32, C.c_void_p]),
     "sad_step_fused": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_void_p, C.c_int32, C.c_uint64, C.c_uint32, C.c_int32,
-                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
-                                 C.c_void_p]),
+                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "sad_adam_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                                 C.POINTER(C.c_float), C.c_float, C.c_float, C.c_float, C.c_float, C.c_float,
                                 C.c_void_p, C.c_void_p]),

@@ -1,16 +1,17 @@
-// sad_render.hip -- soft anisotropic Apollonius render (Sec. 4.2), its
-// backward pass with the per-site gradient reduction (Sec. 4.8, Appendix
-// B.4), and random-access queries (Sec. 6.6).
+// sad_render.hip -- soft anisotropic Apollonius render (Sec. 4.2), random-
+// access queries (Sec. 6.6) and the per-site budget statistics (Sec. 4.5,
+// Appendix B.5).
 //
 // The forward render uses the same mapping as the propagation pass: one
 // wavefront per 8x8 tile, 4 consecutive tiles per 256-thread workgroup.  The
-// backward works on regions of 2 x 4 tiles and reduces the per-site gradient
-// terms in two stages (described before k_render_bwd); queries take one
-// thread per point.
+// statistics work on regions of 2 x 4 tiles and reduce the per-site terms in
+// two stages (described before k_region_stats); queries take one thread per
+// point.
 #include <algorithm>
 #include <type_traits>
 
 #include "sad_propagate.h"
+#include "sad_region.h"
 
 namespace sad {
 
@@ -75,23 +76,6 @@ __device__ __forceinline__ void eval_point(const float* __restrict__ derived, ui
     }
 }
 
-// Rotate the 8 list entries left by r (0..7): entry k moves to (k - r) mod 8.
-__device__ __forceinline__ void rotate_list(uint4& l0, uint4& l1, int r) {
-    uint32_t v[K] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-#pragma unroll
-    for (int bit = 0; bit < 3; ++bit) {
-        const int sh = 1 << bit;
-        const bool on = (r >> bit) & 1;
-        uint32_t u[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) u[k] = on ? v[(k + sh) & (K - 1)] : v[k];
-#pragma unroll
-        for (int k = 0; k < K; ++k) v[k] = u[k];
-    }
-    l0 = make_uint4(v[0], v[1], v[2], v[3]);
-    l1 = make_uint4(v[4], v[5], v[6], v[7]);
-}
-
 struct PixArgs {
     const float* derived;
     const uint32_t* topk;
@@ -124,56 +108,32 @@ __global__ __launch_bounds__(256) void k_render_fwd(PixArgs a) {
     a.image[p * 3 + 2] = pe.c[2];
 }
 
-// ---------------------------------------------------------------- backward
+// ---------------------------------------------------------------- budget statistics
 //
-// A workgroup covers one region of 2 x 4 tiles (16 rows x 32 columns of
-// pixels), one wavefront per tile.  Per-pixel gradient contributions are
-// summed in LDS per site (open addressing keyed by site id: a multiplicative
-// hash picks the first slot and a second one an odd step, so a site's probe
-// sequence visits every slot and sequences of different sites do not run
-// together as linear probing's do when the table fills; at most REGION_PROBES
-// slots, keys claimed by compare-and-swap).
+// Per-site statistics of Sec. 4.5 / Appendix B.5 over the map.  A workgroup
+// covers one region (sad_region.h), one wavefront per tile; every listed site
+// claims a slot of the region's LDS table, its record is read into LDS once,
+// and each pixel's 8 statistics terms per entry are summed per slot.
 //
-// The LDS sums are exact 64-bit fixed-point integers: a contribution t
-// becomes floor(t 2^E), 2^E = 2^45 * (the power of two >= h*w), so
-// the resolution is 2^-45 of the 1/(h*w) scale every gradient carries, and
-// the integer adds are exact and independent of their order.  (LDS float
-// atomics are an order of magnitude slower than integer ones on this GPU.)
-// A contribution with |t 2^E| >= 2^53 (far outside the normal range) goes to
-// global memory as a float atomic instead, so a slot, which receives at most
-// one contribution per pixel of the region, never overflows.
+// The LDS sums are exact 64-bit fixed-point integers: a term t of column q
+// becomes floor(t 2^E_q) (2^E_q chosen per column from the range of its
+// terms), so the integer adds are exact and independent of their order.
+// (LDS float atomics are an order of magnitude slower than integer ones on
+// this GPU.)  A term with |t 2^E_q| >= 2^53 (far outside the column's range)
+// goes to global memory as a float atomic instead, so a slot, which receives
+// at most one term per pixel of the region, never overflows.
 //
-// The sums then leave the workgroup without device-wide float atomics, which
-// on a multi-die GPU are carried out at the memory side and cost far more
-// than the arithmetic: every site has a home region (the one containing its
-// position), the workgroup writes its table (keys at the same slots, the
-// summed values of the sites whose home is in the 3 x 3 regions around it) to
-// a workspace, and a second kernel gives every site the sum of its entries in
-// the 9 tables around its home (found by the same hash probing).  Sites
-// listed by a region outside that neighbourhood (very wide footprints) are
-// added with float atomics directly; their slot keeps a placeholder key so
-// probe chains stay intact.
-constexpr int RT_X = 4, RT_Y = 2;  // tiles per region
-constexpr int REGION_W = RT_X * TILE, REGION_H = RT_Y * TILE;
-constexpr int REGION_WAVES = RT_X * RT_Y;
-constexpr int SLOTS = 256;
-constexpr int REGION_PROBES = 32;
-constexpr int NGRAD = 10;
+// The sums then leave the workgroup without device-wide float atomics: every
+// site has a home region (the one containing its position), the workgroup
+// writes its table (keys at the same slots, the summed values of the sites
+// whose home is in the 3 x 3 regions around it) to a workspace, and a second
+// kernel gives every site the sum of its entries in the 9 tables around its
+// home (found by the same hash probing).  Sites listed by a region outside
+// that neighbourhood (very wide footprints) are added with float atomics
+// directly; their slot keeps a placeholder key so probe chains stay intact.
 constexpr int NSTAT = 8;
-constexpr int NTERM_MAX = 10;
 constexpr double FIX_LIMIT_HI = 0x1p21;  // |t 2^E| < 2^53, i.e. |t 2^(E-32)| < 2^21, goes to the fixed-point sums
 constexpr uint32_t PLACEHOLDER = 0xfffffffeu;
-
-struct RegionGrid {
-    int32_t rgx, rgy;
-};
-
-__host__ __device__ inline RegionGrid region_grid(int32_t h, int32_t w) {
-    return {(w + REGION_W - 1) / REGION_W, (h + REGION_H - 1) / REGION_H};
-}
-
-__device__ __forceinline__ uint32_t slot_hash(uint32_t id) { return (id * 2654435761u) >> 24; }  // 8 bits
-__device__ __forceinline__ uint32_t slot_step(uint32_t id) { return ((id * 0x85ebca6bu) >> 24) | 1u; }  // odd
 
 // home region of a site from its prepared position (same arithmetic in both kernels)
 __device__ __forceinline__ void home_region(float x, float y, RegionGrid rg, int& hx, int& hy) {
@@ -181,25 +141,14 @@ __device__ __forceinline__ void home_region(float x, float y, RegionGrid rg, int
     hy = min(max((int)floorf(y * (1.0f / REGION_H)), 0), rg.rgy - 1);
 }
 
-// What a region pass sums per site from every list entry: the loss
-// gradients (into grad [n][12]) or the budget statistics (into stats [n][8]).
-struct GradSums {
-    static constexpr int N = NGRAD;
-    static constexpr int STRIDE = REC;
-};
-struct StatSums {
-    static constexpr int N = NSTAT;
-    static constexpr int STRIDE = NSTAT;
-};
-
-struct BwdArgs {
+struct StatArgs {
     PixArgs p;
     RegionGrid rg;
-    uint32_t* tkeys;                  // [regions][SLOTS] site id, EMPTY or PLACEHOLDER
-    float* tvals;                     // [regions][SLOTS][N]
-    float* out;                       // [n][STRIDE], accumulated into
-    double fix_scale_hi[NTERM_MAX];   // per term: 2^(E_q - 32)
-    double fix_inv[NTERM_MAX];        // per term: 2^-E_q
+    uint32_t* tkeys;               // [regions][SLOTS] site id, EMPTY or PLACEHOLDER
+    float* tvals;                  // [regions][SLOTS][NSTAT]
+    float* out;                    // [n][NSTAT], accumulated into
+    double fix_scale_hi[NSTAT];    // per column: 2^(E_q - 32)
+    double fix_inv[NSTAT];         // per column: 2^-E_q
 };
 
 // The fixed-point value of a term t, given u = t 2^(E-32) (exact in double,
@@ -208,32 +157,28 @@ struct BwdArgs {
 // 0 <= f 2^32 < 2^32: hi is the upper word and floor(f 2^32) the lower.  f is
 // exact except for a tiny negative u, where f = 1 - |u| is rounded to double;
 // the lower word is then off by less than one unit (2^-E), within the
-// resolution of the sums.  (In float32 that rounding would cost up to 2^8
-// units, which the gradient tolerance does not cover.)
+// resolution of the sums.
 __device__ __forceinline__ unsigned long long to_fixed(double u) {
     const double hi = floor(u);
     const double lo = (u - hi) * 4294967296.0;
     return ((unsigned long long)(uint32_t)(int32_t)hi << 32) | (unsigned long long)(uint32_t)lo;
 }
 
-template <class S>
-__global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
-    constexpr bool GRAD = std::is_same_v<S, GradSums>;
+__global__ __launch_bounds__(WAVE* REGION_WAVES) void k_region_stats(StatArgs b) {
     __shared__ uint32_t keys[SLOTS];
     __shared__ float4 recs[SLOTS * 3];  // prepared record of the site in each slot
-    __shared__ unsigned long long acc[S::N * SLOTS];
-    __shared__ float wsum[REGION_WAVES];
+    __shared__ unsigned long long acc[NSTAT * SLOTS];
     const PixArgs& a = b.p;
     const uint32_t n = (uint32_t)a.n;
 
     for (int s = threadIdx.x; s < SLOTS; s += blockDim.x) keys[s] = EMPTY;
-    for (int s = threadIdx.x; s < S::N * SLOTS; s += blockDim.x) acc[s] = 0ull;
+    for (int s = threadIdx.x; s < NSTAT * SLOTS; s += blockDim.x) acc[s] = 0ull;
 
     const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
     const int reg = xcd_block(blockIdx.x, gridDim.x);
     const int rx = reg % b.rg.rgx, ry = reg / b.rg.rgx;
-    const int tx = rx * RT_X + (wv % RT_X), ty = ry * RT_Y + (wv / RT_X);
-    const int i = tx * TILE + (lane & (TILE - 1)), j = ty * TILE + (lane / TILE);
+    int i, j;
+    region_pixel(rx, ry, wv, lane, i, j);
     const bool inside = i < a.w && j < a.h;
     const size_t p = (size_t)j * a.w + i;
     const float px = (float)i + 0.5f, py = (float)j + 0.5f;
@@ -260,34 +205,9 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
     }
     __syncthreads();  // keys cleared
 
-    // 1. claim a slot for every listed site: all 8 probes of a lane go out
-    //    together, round by round, instead of one chain per entry
-    int slot[K], pos[K];
-    uint32_t pend = 0;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        slot[k] = -1;
-        pos[k] = (int)slot_hash(ids[k]);
-        if (ids[k] < n) pend |= 1u << k;
-    }
-    for (int round = 0; round < REGION_PROBES && __any(pend != 0); ++round) {
-        uint32_t cur[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) cur[k] = ((pend >> k) & 1) ? keys[pos[k]] : 0u;
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-            if (((pend >> k) & 1) && cur[k] == EMPTY) cur[k] = atomicCAS(&keys[pos[k]], EMPTY, ids[k]);
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            if (!((pend >> k) & 1)) continue;
-            if (cur[k] == EMPTY || cur[k] == ids[k]) {
-                slot[k] = pos[k];
-                pend &= ~(1u << k);
-            } else {
-                pos[k] = (pos[k] + (int)slot_step(ids[k])) & (SLOTS - 1);
-            }
-        }
-    }
+    // 1. a slot for every listed site
+    int slot[K];
+    claim_slots(keys, ids, n, slot);
     __syncthreads();
 
     // 2. every claimed site's record is read from memory once, into LDS
@@ -301,18 +221,15 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
     }
     __syncthreads();
 
-    // 3. forward and backward of the pixel, records from LDS.  When an entry
-    //    of some lane of the wavefront found no slot (its probe chain ran
-    //    out), the wavefront takes a copy of this code that reads such
-    //    records from memory; otherwise every record read is an LDS read
-    //    (one pointer that may point to either memory would make every read a
-    //    slower generic load).
+    // 3. the pixel's forward and statistics terms, records from LDS.  When an
+    //    entry of some lane of the wavefront found no slot (its probe chain
+    //    ran out), the wavefront takes a copy of this code that reads such
+    //    records from memory; otherwise every record read is an LDS read.
     // part q (0: x y tau r, 1: cos sin 1/s1 1/s2, 2: colour) of entry k's record
     bool slotted = true;
 #pragma unroll
     for (int k = 0; k < K; ++k) slotted &= (ids[k] >= n) | (slot[k] >= 0);
-    float lsum = 0.0f;
-    auto fwd_bwd = [&](auto lds_only) {
+    auto fwd_stats = [&](auto lds_only) {
         auto rec = [&](int k, int q) -> float4 {
             if constexpr (decltype(lds_only)::value)
                 return recs[(slot[k] >= 0 ? slot[k] : 0) * 3 + q];
@@ -345,7 +262,7 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
             z += e[k];
         }
         float c[3] = {0.f, 0.f, 0.f};
-        float cl[GRAD ? 1 : K][3];  // the entries' colours (statistics only)
+        float cl[K][3];  // the entries' colours
         if (z > 0.0f) {
             const float iz = 1.0f / z;
 #pragma unroll
@@ -356,130 +273,82 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
                 c[0] += e[k] * col.x;
                 c[1] += e[k] * col.y;
                 c[2] += e[k] * col.z;
-                if constexpr (!GRAD) {
-                    cl[k][0] = col.x;
-                    cl[k][1] = col.y;
-                    cl[k][2] = col.z;
-                }
+                cl[k][0] = col.x;
+                cl[k][1] = col.y;
+                cl[k][2] = col.z;
             }
         }
         // entry k's terms go to its slot's fixed-point sums, or to memory when
         // it has no slot or a term is outside the fixed-point range
-        auto add_terms = [&](int k, uint32_t id, const float (&t)[S::N]) {
+        auto add_terms = [&](int k, uint32_t id, const float (&t)[NSTAT]) {
 #pragma unroll
-            for (int q2 = 0; q2 < S::N; ++q2) {
+            for (int q2 = 0; q2 < NSTAT; ++q2) {
                 const double u = (double)t[q2] * b.fix_scale_hi[q2];
                 if (slot[k] >= 0 && fabs(u) < FIX_LIMIT_HI)
                     atomicAdd(&acc[q2 * SLOTS + slot[k]], to_fixed(u));
                 else
-                    unsafeAtomicAdd(&b.out[(size_t)id * S::STRIDE + q2], t[q2]);
+                    unsafeAtomicAdd(&b.out[(size_t)id * NSTAT + q2], t[q2]);
             }
         };
-        if constexpr (GRAD) {
-            float g[3];
+        // mass, energy, removal delta, moments about the site
+        float err = 0.0f;
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch) err += (c[ch] - tg[ch]) * (c[ch] - tg[ch]);
+        // c' of an entry (the blend of the other usable entries) from the
+        // normalised weights, which include the largest one (>= 1/8); for
+        // the entry holding the largest logit the others are re-weighted
+        // relative to the largest remaining logit, so that their blend
+        // survives even when their normalised weights underflow
+        int top = -1;
+#pragma unroll
+        for (int k = 0; k < K; ++k) top = (top < 0 && use[k] && l[k] == mx) ? k : top;
+        float m2 = -__builtin_inff();
+#pragma unroll
+        for (int k = 0; k < K; ++k) m2 = (use[k] && k != top) ? fmaxf(m2, l[k]) : m2;
+        float ct[3] = {0.f, 0.f, 0.f}, zt = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (!use[k] || k == top) continue;
+            const float ek = __expf(l[k] - m2);
+            zt += ek;
+            ct[0] += ek * cl[k][0];
+            ct[1] += ek * cl[k][1];
+            ct[2] += ek * cl[k][2];
+        }
+        const float izt = zt > 0.0f ? 1.0f / zt : 0.0f;  // no other entry: c' is black
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (!use[k]) continue;
+            float cp[3] = {0.f, 0.f, 0.f}, zk = 0.0f;
+#pragma unroll
+            for (int j2 = 0; j2 < K; ++j2) {
+                if (j2 == k || !use[j2]) continue;
+                zk += e[j2];
+                cp[0] += e[j2] * cl[j2][0];
+                cp[1] += e[j2] * cl[j2][1];
+                cp[2] += e[j2] * cl[j2][2];
+            }
+            const bool is_top = k == top;
+            const float izk = is_top ? izt : 1.0f / zk;
+            const float w = e[k];
+            // |c' - I|^2 - |c - I|^2 = (c' - c).(c' + c - 2I) with c' - c = w (c' - c_k)
+            float dl = 0.0f;
 #pragma unroll
             for (int ch = 0; ch < 3; ++ch) {
-                const float r = c[ch] - tg[ch];
-                lsum += r * r;
-                g[ch] = 2.0f * r * a.inv_p;
-                if (a.image) a.image[p * 3 + ch] = c[ch];
+                const float cpc = (is_top ? ct[ch] : cp[ch]) * izk;
+                dl += (cpc - cl[k][ch]) * (cpc + c[ch] - 2.0f * tg[ch]);
             }
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                if (!use[k]) continue;
-                const uint32_t id = ids[k];
-                const float w = e[k];
-                const float4 g0 = rec(k, 0), g1 = rec(k, 1), col = rec(k, 2);
-                const float tau = g0.z, cs = g1.x, sn = g1.y, is1 = g1.z, is2 = g1.w;
-                // g.(c_i - c): differences first, so a site coloured like the pixel
-                // does not lose its gradient to cancellation
-                const float delta = w * (g[0] * (col.x - c[0]) + g[1] * (col.y - c[1]) + g[2] * (col.z - c[2]));
-                float t[NGRAD];
-                t[4] = w * g[0];
-                t[5] = w * g[1];
-                t[6] = w * g[2];
-                t[2] = delta * l[k];
-                t[3] = tau * delta;
-                const float dx = px - g0.x, dy = py - g0.y;
-                const float ar = dx * cs + dy * sn, br = dy * cs - dx * sn;
-                const float aa = ar * is1, bb = br * is2;
-                const float q = aa * aa + bb * bb;
-                t[0] = t[1] = t[7] = t[8] = t[9] = 0.0f;
-                if (q > 0.0f) {
-                    const float kap2 = -tau * delta * __builtin_amdgcn_rsqf(q);  // 2 kappa
-                    t[0] = -kap2 * (aa * is1 * cs - bb * is2 * sn);
-                    t[1] = -kap2 * (aa * is1 * sn + bb * is2 * cs);
-                    t[7] = kap2 * ar * br * ((is1 - is2) * (is1 + is2));  // 1/s1^2 - 1/s2^2 without cancellation
-                    t[8] = -kap2 * aa * aa;
-                    t[9] = -kap2 * bb * bb;
-                }
-                add_terms(k, id, t);
-            }
-        } else {
-            // budget statistics: mass, energy, removal delta, moments about the site
-            float err = 0.0f;
-#pragma unroll
-            for (int ch = 0; ch < 3; ++ch) err += (c[ch] - tg[ch]) * (c[ch] - tg[ch]);
-            // c' of an entry (the blend of the other usable entries) from the
-            // normalised weights, which include the largest one (>= 1/8); for
-            // the entry holding the largest logit the others are re-weighted
-            // relative to the largest remaining logit, so that their blend
-            // survives even when their normalised weights underflow
-            int top = -1;
-#pragma unroll
-            for (int k = 0; k < K; ++k) top = (top < 0 && use[k] && l[k] == mx) ? k : top;
-            float m2 = -__builtin_inff();
-#pragma unroll
-            for (int k = 0; k < K; ++k) m2 = (use[k] && k != top) ? fmaxf(m2, l[k]) : m2;
-            float ct[3] = {0.f, 0.f, 0.f}, zt = 0.0f;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                if (!use[k] || k == top) continue;
-                const float ek = __expf(l[k] - m2);
-                zt += ek;
-                ct[0] += ek * cl[k][0];
-                ct[1] += ek * cl[k][1];
-                ct[2] += ek * cl[k][2];
-            }
-            const float izt = zt > 0.0f ? 1.0f / zt : 0.0f;  // no other entry: c' is black
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                if (!use[k]) continue;
-                float cp[3] = {0.f, 0.f, 0.f}, zk = 0.0f;
-#pragma unroll
-                for (int j2 = 0; j2 < K; ++j2) {
-                    if (j2 == k || !use[j2]) continue;
-                    zk += e[j2];
-                    cp[0] += e[j2] * cl[j2][0];
-                    cp[1] += e[j2] * cl[j2][1];
-                    cp[2] += e[j2] * cl[j2][2];
-                }
-                const bool is_top = k == top;
-                const float izk = is_top ? izt : 1.0f / zk;
-                const float w = e[k];
-                // |c' - I|^2 - |c - I|^2 = (c' - c).(c' + c - 2I) with c' - c = w (c' - c_k)
-                float dl = 0.0f;
-#pragma unroll
-                for (int ch = 0; ch < 3; ++ch) {
-                    const float cpc = (is_top ? ct[ch] : cp[ch]) * izk;
-                    dl += (cpc - cl[k][ch]) * (cpc + c[ch] - 2.0f * tg[ch]);
-                }
-                const float4 g0 = rec(k, 0);
-                const float dx = px - g0.x, dy = py - g0.y;
-                const float wdx = w * dx, wdy = w * dy;
-                const float t[NSTAT] = {w, w * err, w * dl, wdx, wdy, wdx * dx, wdx * dy, wdy * dy};
-                add_terms(k, ids[k], t);
-            }
+            const float4 g0 = rec(k, 0);
+            const float dx = px - g0.x, dy = py - g0.y;
+            const float wdx = w * dx, wdy = w * dy;
+            const float t[NSTAT] = {w, w * err, w * dl, wdx, wdy, wdx * dx, wdx * dy, wdy * dy};
+            add_terms(k, ids[k], t);
         }
     };
     if (__all(slotted))
-        fwd_bwd(std::true_type{});
+        fwd_stats(std::true_type{});
     else
-        fwd_bwd(std::false_type{});
-    if (a.loss) {
-        const float ws = wave_sum(lsum);
-        if (lane == 0) wsum[wv] = ws;
-    }
+        fwd_stats(std::false_type{});
     __syncthreads();
     // 4. publish the region's table
     const int region = reg;
@@ -487,54 +356,48 @@ __global__ __launch_bounds__(WAVE* REGION_WAVES) void k_render_bwd(BwdArgs b) {
         const uint32_t id = keys[s];
         uint32_t key = id;
         if (id != EMPTY) {
-            float v[S::N];
+            float v[NSTAT];
 #pragma unroll
-            for (int q2 = 0; q2 < S::N; ++q2) v[q2] = (float)((double)(long long)acc[q2 * SLOTS + s] * b.fix_inv[q2]);
+            for (int q2 = 0; q2 < NSTAT; ++q2) v[q2] = (float)((double)(long long)acc[q2 * SLOTS + s] * b.fix_inv[q2]);
             const float4 r0 = recs[s * 3 + 0];
             int hx, hy;
             home_region(r0.x, r0.y, b.rg, hx, hy);
             if (abs(hx - rx) <= 1 && abs(hy - ry) <= 1) {
-                float* dst = b.tvals + ((size_t)region * SLOTS + s) * S::N;
+                float* dst = b.tvals + ((size_t)region * SLOTS + s) * NSTAT;
 #pragma unroll
-                for (int q2 = 0; q2 < S::N; ++q2) dst[q2] = v[q2];
+                for (int q2 = 0; q2 < NSTAT; ++q2) dst[q2] = v[q2];
             } else {
                 key = PLACEHOLDER;
 #pragma unroll
-                for (int q2 = 0; q2 < S::N; ++q2) unsafeAtomicAdd(&b.out[(size_t)id * S::STRIDE + q2], v[q2]);
+                for (int q2 = 0; q2 < NSTAT; ++q2) unsafeAtomicAdd(&b.out[(size_t)id * NSTAT + q2], v[q2]);
             }
         }
         b.tkeys[(size_t)region * SLOTS + s] = key;
-    }
-    if (a.loss && threadIdx.x == 0) {
-        float tot = 0.0f;
-        for (int k = 0; k < REGION_WAVES; ++k) tot += wsum[k];
-        unsafeAtomicAdd(a.loss, tot * a.inv_p);
     }
 }
 
 // Every site gets the sum of its entries in the tables of the 3 x 3 regions
 // around its home region.  A workgroup takes GATHER_SITES sites with one thread
 // per (site, table): the thread finds the site in its table by the probing the
-// backward used (stopping at an empty slot or after REGION_PROBES slots) and
-// loads the entry; then one thread per site adds the 9 partial sums in a fixed
-// order to the site's output record (gradient or statistics).  One writer per
-// site, no atomics, and a result that does not depend on scheduling.  A site
-// found in no table is not touched.
+// statistics pass used (stopping at an empty slot or after REGION_PROBES
+// slots) and loads the entry; then one thread per site adds the 9 partial sums
+// in a fixed order to the site's output record.  One writer per site, no
+// atomics, and a result that does not depend on scheduling.  A site found in
+// no table is not touched.
 constexpr int GATHER_SITES = 28;  // 28 x 9 = 252 threads
 
-template <class S>
-__global__ __launch_bounds__(256) void k_grad_gather(RegionGrid rg, const uint32_t* __restrict__ tkeys,
-                                                     const float* __restrict__ tvals,
-                                                     const float* __restrict__ derived, float* __restrict__ out,
-                                                     int32_t n) {
-    __shared__ float part[GATHER_SITES][9][S::N];
+__global__ __launch_bounds__(256) void k_stats_gather(RegionGrid rg, const uint32_t* __restrict__ tkeys,
+                                                      const float* __restrict__ tvals,
+                                                      const float* __restrict__ derived, float* __restrict__ out,
+                                                      int32_t n) {
+    __shared__ float part[GATHER_SITES][9][NSTAT];
     __shared__ int found[GATHER_SITES][9];
     const int ls = threadIdx.x / 9, t = threadIdx.x % 9;
     const int site = blockIdx.x * GATHER_SITES + ls;
     if (ls < GATHER_SITES) {
-        float v[S::N];
+        float v[NSTAT];
 #pragma unroll
-        for (int q2 = 0; q2 < S::N; ++q2) v[q2] = 0.0f;
+        for (int q2 = 0; q2 < NSTAT; ++q2) v[q2] = 0.0f;
         int hit = 0;
         if (site < n) {
             int hx, hy;
@@ -546,9 +409,9 @@ __global__ __launch_bounds__(256) void k_grad_gather(RegionGrid rg, const uint32
                 for (int pr = 0; pr < REGION_PROBES; ++pr) {
                     const uint32_t key = tkeys[base + pos];
                     if (key == (uint32_t)site) {
-                        const float* src = tvals + (base + pos) * S::N;
+                        const float* src = tvals + (base + pos) * NSTAT;
 #pragma unroll
-                        for (int q2 = 0; q2 < S::N; ++q2) v[q2] = src[q2];
+                        for (int q2 = 0; q2 < NSTAT; ++q2) v[q2] = src[q2];
                         hit = 1;
                         break;
                     }
@@ -558,25 +421,25 @@ __global__ __launch_bounds__(256) void k_grad_gather(RegionGrid rg, const uint32
             }
         }
 #pragma unroll
-        for (int q2 = 0; q2 < S::N; ++q2) part[ls][t][q2] = v[q2];
+        for (int q2 = 0; q2 < NSTAT; ++q2) part[ls][t][q2] = v[q2];
         found[ls][t] = hit;
     }
     __syncthreads();
     const int s2 = blockIdx.x * GATHER_SITES + (int)threadIdx.x;
     if (threadIdx.x < GATHER_SITES && s2 < n) {
         int any = 0;
-        float sum[S::N];
+        float sum[NSTAT];
 #pragma unroll
-        for (int q2 = 0; q2 < S::N; ++q2) sum[q2] = 0.0f;
+        for (int q2 = 0; q2 < NSTAT; ++q2) sum[q2] = 0.0f;
         for (int t2 = 0; t2 < 9; ++t2) {
             any |= found[threadIdx.x][t2];
 #pragma unroll
-            for (int q2 = 0; q2 < S::N; ++q2) sum[q2] += part[threadIdx.x][t2][q2];
+            for (int q2 = 0; q2 < NSTAT; ++q2) sum[q2] += part[threadIdx.x][t2][q2];
         }
         if (any) {
-            float* gr = out + (size_t)s2 * S::STRIDE;
+            float* gr = out + (size_t)s2 * NSTAT;
 #pragma unroll
-            for (int q2 = 0; q2 < S::N; ++q2) gr[q2] += sum[q2];
+            for (int q2 = 0; q2 < NSTAT; ++q2) gr[q2] += sum[q2];
         }
     }
 }
@@ -647,76 +510,10 @@ extern "C" int sad_render_fwd(const float* derived, int32_t n, int32_t h, int32_
     return launch_status();
 }
 
-extern "C" size_t sad_render_bwd_workspace_bytes(int32_t h, int32_t w) {
+extern "C" size_t sad_site_stats_workspace_bytes(int32_t h, int32_t w) {
     if (!image_ok(h, w)) return 0;
     const RegionGrid rg = region_grid(h, w);
-    return (size_t)rg.rgx * rg.rgy * SLOTS * (sizeof(uint32_t) + NGRAD * sizeof(float));
-}
-
-namespace sad {
-
-// The region tables in the caller's workspace.
-inline void region_tables(BwdArgs& b, void* workspace) {
-    b.rg = region_grid(b.p.h, b.p.w);
-    const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
-    b.tkeys = reinterpret_cast<uint32_t*>(workspace);
-    b.tvals = reinterpret_cast<float*>(b.tkeys + nreg * SLOTS);
-}
-
-// Argument checks of a backward pass over the list map topk, and its kernel
-// arguments.  Returns SAD_OK with b filled in, or the error status.
-inline int bwd_setup(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
-                     const float* target, float* grad, float* loss, float* image, void* workspace,
-                     size_t workspace_bytes, BwdArgs& b) {
-    int st = pix_common(derived, n, h, w, topk);
-    if (st != SAD_OK) return st;
-    const int64_t pix = int64_t(h) * w;
-    if (!array_ok(target, pix, 4) || !array_ok(grad, n, 16)) return SAD_EINVAL;
-    if ((loss && !aligned(loss, 4)) || (image && !aligned(image, 4))) return SAD_EINVAL;
-    if (overlap(grad, int64_t(n) * REC * 4, derived, int64_t(n) * REC * 4)) return SAD_EINVAL;
-    const size_t need = sad_render_bwd_workspace_bytes(h, w);
-    if (pix > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)) return SAD_EINVAL;
-    if (overlap(workspace, (int64_t)need, grad, int64_t(n) * REC * 4)) return SAD_EINVAL;
-    b.p = pix_args(derived, n, h, w, topk);
-    b.p.target = target;
-    b.p.grad = grad;
-    b.p.loss = loss;
-    b.p.image = image;
-    b.out = grad;
-    region_tables(b, workspace);
-    int e = 45;  // 2^E = 2^45 * (smallest power of two >= h*w): the gradients carry a factor 1/(h w)
-    while ((int64_t(1) << (e - 45)) < pix) ++e;
-    for (int q = 0; q < NTERM_MAX; ++q) {
-        b.fix_scale_hi[q] = ldexp(1.0, e - 32);
-        b.fix_inv[q] = ldexp(1.0, -e);
-    }
-    return SAD_OK;
-}
-
-template <class S>
-int region_launch(const BwdArgs& b, void* stream) {
-    const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
-    clear_error();
-    hipLaunchKernelGGL(k_render_bwd<S>, dim3((unsigned)nreg), dim3(WAVE * REGION_WAVES), 0, as_stream(stream), b);
-    if (b.p.n > 0)
-        hipLaunchKernelGGL(k_grad_gather<S>, dim3((unsigned)((b.p.n + GATHER_SITES - 1) / GATHER_SITES)),
-                           dim3(GATHER_SITES * 9), 0, as_stream(stream), b.rg, b.tkeys, b.tvals, b.p.derived,
-                           b.out, b.p.n);
-    return launch_status();
-}
-
-int bwd_launch(const BwdArgs& b, void* stream) { return region_launch<GradSums>(b, stream); }
-
-}  // namespace sad
-
-extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
-                              const float* target, float* grad, float* loss, float* image, void* workspace,
-                              size_t workspace_bytes, void* stream) {
-    BwdArgs b;
-    const int st = bwd_setup(derived, n, h, w, topk, target, grad, loss, image, workspace, workspace_bytes, b);
-    if (st != SAD_OK) return st;
-    if (int64_t(h) * w == 0) return SAD_OK;
-    return bwd_launch(b, stream);
+    return (size_t)rg.rgx * rg.rgy * SLOTS * (sizeof(uint32_t) + NSTAT * sizeof(float));
 }
 
 extern "C" int sad_site_stats(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
@@ -727,60 +524,41 @@ extern "C" int sad_site_stats(const float* derived, int32_t n, int32_t h, int32_
     const int64_t pix = int64_t(h) * w;
     if (!array_ok(target, pix, 4) || !array_ok(stats, n, 16)) return SAD_EINVAL;
     const int64_t sbytes = int64_t(n) * NSTAT * 4;
-    if (overlap(stats, sbytes, derived, int64_t(n) * REC * 4)) return SAD_EINVAL;
-    const size_t need = sad_render_bwd_workspace_bytes(h, w);
-    if (pix > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)) return SAD_EINVAL;
-    if (overlap(workspace, (int64_t)need, stats, sbytes) || overlap(workspace, (int64_t)need, target, pix * 12))
+    if (overlap(stats, sbytes, derived, int64_t(n) * REC * 4) || overlap(stats, sbytes, topk, pix * K * 4) ||
+        overlap(stats, sbytes, target, pix * 12))
         return SAD_EINVAL;
+    const size_t need = sad_site_stats_workspace_bytes(h, w);
+    if (pix > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)) return SAD_EINVAL;
+    const void* reads[4] = {stats, target, topk, derived};
+    const int64_t rbytes[4] = {sbytes, pix * 12, pix * K * 4, int64_t(n) * REC * 4};
+    for (int q = 0; q < 4; ++q)
+        if (overlap(workspace, (int64_t)need, reads[q], rbytes[q])) return SAD_EINVAL;
     if (pix == 0) return SAD_OK;
-    BwdArgs b;
+    StatArgs b;
     b.p = pix_args(derived, n, h, w, topk);
     b.p.target = target;
     b.out = stats;
-    region_tables(b, workspace);
-    // per-term fixed-point scales 2^E_q with |t| 2^E_q < 2^52 for the usual
+    b.rg = region_grid(h, w);
+    const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
+    b.tkeys = reinterpret_cast<uint32_t*>(workspace);
+    b.tvals = reinterpret_cast<float*>(b.tkeys + nreg * SLOTS);
+    // per-column fixed-point scales 2^E_q with |t| 2^E_q < 2^52 for the usual
     // range of each term: weights <= 1, errors of colours in [0, 1] <= 3 (the
     // removal delta <= 6), offsets from a site inside the image <= D (the
     // smallest power of two >= max(h, w)); other terms go to float atomics
     int lg = 0;
     while ((int64_t(1) << lg) < std::max(h, w)) ++lg;
     const int eq[NSTAT] = {52, 50, 49, 52 - lg, 52 - lg, 52 - 2 * lg, 52 - 2 * lg, 52 - 2 * lg};
-    for (int q = 0; q < NTERM_MAX; ++q) {
-        const int e = eq[q < NSTAT ? q : 0];
-        b.fix_scale_hi[q] = ldexp(1.0, e - 32);
-        b.fix_inv[q] = ldexp(1.0, -e);
+    for (int q = 0; q < NSTAT; ++q) {
+        b.fix_scale_hi[q] = ldexp(1.0, eq[q] - 32);
+        b.fix_inv[q] = ldexp(1.0, -eq[q]);
     }
-    return region_launch<StatSums>(b, stream);
-}
-
-extern "C" int sad_step_fused(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk_prev,
-                              const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride,
-                              uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, const float* target,
-                              float* grad, float* loss, float* image, void* workspace, size_t workspace_bytes,
-                              void* stream) {
-    PropArgs pa;
-    int st = prop_setup(derived, n, h, w, topk_prev, scores_prev, topk_next, scores_next, stride, seed, pass_index,
-                        inject_per_tile, pa);
-    if (st != SAD_OK) return st;
-    BwdArgs b;
-    st = bwd_setup(derived, n, h, w, topk_next, target, grad, loss, image, workspace, workspace_bytes, b);
-    if (st != SAD_OK) return st;
-    // the pass's outputs must not share memory with anything else the step reads or writes
-    const int64_t pix = int64_t(h) * w, mbytes = pix * K * 4, gbytes = int64_t(n) * REC * 4;
-    const size_t need = sad_render_bwd_workspace_bytes(h, w);
-    const void* outs[2] = {topk_next, scores_next};
-    const void* others[6] = {target, grad, loss, image, workspace, derived};
-    const int64_t obytes[6] = {pix * 12, gbytes, 4, pix * 12, (int64_t)need, gbytes};
-    for (int o = 0; o < 2; ++o)
-        for (int q = 0; q < 6; ++q)
-            if (overlap(outs[o], mbytes, others[q], obytes[q])) return SAD_EINVAL;
-    if (pix == 0) return SAD_OK;
-    // every check has passed: the pass, then the backward over its lists, in
-    // stream order
-    st = sad_propagate_topk(derived, n, h, w, topk_prev, scores_prev, topk_next, scores_next, stride, seed, pass_index,
-                            inject_per_tile, stream);
-    if (st != SAD_OK) return st;
-    return bwd_launch(b, stream);
+    clear_error();
+    hipLaunchKernelGGL(k_region_stats, dim3((unsigned)nreg), dim3(WAVE * REGION_WAVES), 0, as_stream(stream), b);
+    if (n > 0)
+        hipLaunchKernelGGL(k_stats_gather, dim3((unsigned)((n + GATHER_SITES - 1) / GATHER_SITES)),
+                           dim3(GATHER_SITES * 9), 0, as_stream(stream), b.rg, b.tkeys, b.tvals, derived, stats, n);
+    return launch_status();
 }
 
 extern "C" int sad_query_points(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,

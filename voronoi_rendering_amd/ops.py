@@ -96,10 +96,10 @@ def render_fwd(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, image:
 _workspaces: dict = {}
 
 
-def bwd_workspace(h: int, w: int, device) -> torch.Tensor:
-    """A per-device scratch buffer for render_bwd, grown on demand and reused.
+def stats_workspace(h: int, w: int, device) -> torch.Tensor:
+    """A per-device scratch buffer for site_stats, grown on demand and reused.
     Calls that share it must be ordered (one stream, or explicit waits)."""
-    need = int(_native.lib().sad_render_bwd_workspace_bytes(h, w))
+    need = int(_native.lib().sad_site_stats_workspace_bytes(h, w))
     dev = torch.device(device)
     ws = _workspaces.get(dev)
     if ws is None or ws.numel() < need:
@@ -109,8 +109,7 @@ def bwd_workspace(h: int, w: int, device) -> torch.Tensor:
 
 
 def render_bwd(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target: torch.Tensor, grad: torch.Tensor,
-               loss: torch.Tensor | None = None, image: torch.Tensor | None = None,
-               workspace: torch.Tensor | None = None) -> None:
+               loss: torch.Tensor | None = None, image: torch.Tensor | None = None) -> None:
     """Accumulate the loss gradient into ``grad`` ([n][12]); optionally add the
     loss into ``loss`` (one float32) and write the rendered image."""
     n = derived.shape[0]
@@ -122,11 +121,8 @@ def render_bwd(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target
         _need(loss, "loss", torch.float32, (1,))
     if image is not None:
         _need(image, "image", torch.float32, (h, w, 3))
-    if workspace is None:
-        workspace = bwd_workspace(h, w, derived.device)
     st = _native.lib().sad_render_bwd(_ptr(derived), n, h, w, _ptr(topk), _ptr(target), _ptr(grad), _ptr(loss),
-                                      _ptr(image), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                      _stream(derived))
+                                      _ptr(image), _stream(derived))
     _native.check("sad_render_bwd", st)
 
 
@@ -143,7 +139,7 @@ def site_stats(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target
         stats = torch.zeros((n, NSTAT), dtype=torch.float32, device=derived.device)
     _need(stats, "stats", torch.float32, (n, NSTAT))
     if workspace is None:
-        workspace = bwd_workspace(h, w, derived.device)
+        workspace = stats_workspace(h, w, derived.device)
     st = _native.lib().sad_site_stats(_ptr(derived), n, h, w, _ptr(topk), _ptr(target), _ptr(stats),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(derived))
@@ -296,10 +292,9 @@ def jfa_flood(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor, step: i
 def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor,
                target: torch.Tensor, grad: torch.Tensor, *, stride: int, seed: int, pass_index: int,
                inject: int = 64, prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None,
-               loss: torch.Tensor | None = None, image: torch.Tensor | None = None,
-               workspace: torch.Tensor | None = None) -> torch.Tensor:
+               loss: torch.Tensor | None = None, image: torch.Tensor | None = None) -> torch.Tensor:
     """propagate_topk(...) into ``out`` followed by render_bwd over ``out``, in
-    one call (the new lists feed the backward directly)."""
+    one call (both launches checked before either is enqueued)."""
     n = derived.shape[0]
     _need(derived, "derived", torch.float32, (n, REC))
     if prev is not None:
@@ -315,13 +310,10 @@ def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None,
         _need(loss, "loss", torch.float32, (1,))
     if image is not None:
         _need(image, "image", torch.float32, (h, w, 3))
-    if workspace is None:
-        workspace = bwd_workspace(h, w, derived.device)
     st = _native.lib().sad_step_fused(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
                                       _ptr(out_scores), int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF,
                                       int(pass_index) & 0xFFFFFFFF, int(inject), _ptr(target), _ptr(grad),
-                                      _ptr(loss), _ptr(image), _ptr(workspace),
-                                      workspace.numel() * workspace.element_size(), _stream(derived))
+                                      _ptr(loss), _ptr(image), _stream(derived))
     _native.check("sad_step_fused", st)
     return out
 
