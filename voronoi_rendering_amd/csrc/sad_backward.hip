@@ -36,17 +36,10 @@
 namespace sad {
 
 constexpr int PIECE = 10;  // entries of one site per phase-B lane
-constexpr int MAX_PIECES = (REGION_PIX * K + PIECE - 1) / PIECE + SLOTS;
 constexpr int BWD_THREADS = WAVE * REGION_WAVES;
-static_assert(SLOTS == 4 * WAVE, "one wavefront plans the pieces, 4 slots per lane");
-static_assert(REGION_PIX * K < (1 << 13) && PIECE < 16 && SLOTS <= 256, "piece table packing");
-
-// What phase B needs of a pixel: the largest logit, 1/Z, dL/dc (float32,
-// formed in float64) and dL/dc . c (float64, c the blended colour).
-struct PixState {
-    float m, g0, g1, g2;
-    double iz, gc;
-};
+constexpr int SLOT_WAVES = SLOTS / WAVE;  // wavefronts that plan the buckets, one slot per lane
+static_assert(SLOTS % WAVE == 0 && SLOT_WAVES <= REGION_WAVES, "slot planning layout");
+static_assert(SLOTS <= 256, "slots are packed in 8 bits");
 
 struct BwdArgs {
     const float* derived;
@@ -60,44 +53,48 @@ struct BwdArgs {
     double inv_p;  // 1 / (h w)
 };
 
-// Site geometry for the gradient terms, in float64.
+// Site values for the gradient terms, in float64: geometry, and
+// (1/s1^2 - 1/s2^2) formed without cancellation.
 struct SiteD {
-    double x, y, tau, cs, sn, is1, is2;
+    double x, y, tau, cs, sn, is1, is2, dsq;
 };
 
 __device__ __forceinline__ SiteD site_d(float4 g0, float4 g1) {
-    return {(double)g0.x, (double)g0.y, (double)g0.z, (double)g1.x, (double)g1.y, (double)g1.z, (double)g1.w};
+    const double is1 = (double)g1.z, is2 = (double)g1.w;
+    return {(double)g0.x, (double)g0.y, (double)g0.z, (double)g1.x, (double)g1.y, is1, is2, (is1 - is2) * (is1 + is2)};
 }
 
-// The 10 terms of one list entry (Appendix B.4), in the gradient record's
-// order (x, y, log tau, r, colour, theta, log s1, log s2): (px, py) the pixel
-// centre, l the entry's float32 logit, w its weight, delta = dL/dl =
-// w (g.c_i - g.c) and g = dL/dc.  With 2 kappa = -tau delta / sqrt(q):
-// x: -2 kappa (a cos/s1 - b sin/s2), y: -2 kappa (a sin/s1 + b cos/s2),
-// theta: 2 kappa a_r b_r (1/s1^2 - 1/s2^2), log s_k: -2 kappa a^2, -2 kappa
-// b^2; at q = 0 (the pixel centre on the site) these are 0.
-__device__ __forceinline__ void entry_terms(const SiteD& s, double px, double py, float l, double w, double delta,
-                                            const float (&g)[3], double (&t)[NGRAD]) {
-    t[4] = w * (double)g[0];
-    t[5] = w * (double)g[1];
-    t[6] = w * (double)g[2];
-    t[2] = delta * (double)l;
-    t[3] = s.tau * delta;
+// Add the 10 terms of one list entry (Appendix B.4) to sum, in the gradient
+// record's order (x, y, log tau, r, colour, theta, log s1, log s2): (px, py)
+// the pixel centre, l the entry's float32 logit, w its weight, delta = dL/dl
+// = w (g.c_i - g.c) and g = dL/dc.  With a_r = dx cos + dy sin, b_r = dy cos
+// - dx sin, a = a_r/s1, b = b_r/s2, q = a^2 + b^2 and u = tau delta / sqrt(q)
+// (= -2 kappa): x: u (a cos/s1 - b sin/s2), y: u (a sin/s1 + b cos/s2),
+// theta: -u a_r b_r (1/s1^2 - 1/s2^2), log s1: u a^2, log s2: u b^2; at q = 0
+// (the pixel centre on the site) u is taken as 0.  Written with shared
+// factors and fused multiply-adds, all in float64.
+__device__ __forceinline__ void add_entry_terms(const SiteD& s, double px, double py, float l, double w,
+                                                double delta, const double (&g)[3], double (&sum)[NGRAD]) {
+    sum[4] = fma(w, g[0], sum[4]);
+    sum[5] = fma(w, g[1], sum[5]);
+    sum[6] = fma(w, g[2], sum[6]);
+    sum[2] = fma(delta, (double)l, sum[2]);
+    sum[3] = fma(s.tau, delta, sum[3]);
     const double dx = px - s.x, dy = py - s.y;
-    const double ar = dx * s.cs + dy * s.sn, br = dy * s.cs - dx * s.sn;
-    const double aa = ar * s.is1, bb = br * s.is2;
-    const double q = aa * aa + bb * bb;
-    t[0] = t[1] = t[7] = t[8] = t[9] = 0.0;
-    if (q > 0.0) {
-        const float qf = (float)q;
-        const double rs = qf >= 0x1p-100f ? (double)__builtin_amdgcn_rsqf(qf) : 1.0 / __builtin_sqrt(q);
-        const double kap2 = -s.tau * delta * rs;  // 2 kappa
-        t[0] = -kap2 * (aa * s.is1 * s.cs - bb * s.is2 * s.sn);
-        t[1] = -kap2 * (aa * s.is1 * s.sn + bb * s.is2 * s.cs);
-        t[7] = kap2 * ar * br * ((s.is1 - s.is2) * (s.is1 + s.is2));  // 1/s1^2 - 1/s2^2 without cancellation
-        t[8] = -kap2 * aa * aa;
-        t[9] = -kap2 * bb * bb;
-    }
+    const double ar = fma(dx, s.cs, dy * s.sn), br = fma(dy, s.cs, -(dx * s.sn));
+    const double a = ar * s.is1, b = br * s.is2;
+    const double q = fma(a, a, b * b);
+    // 1/sqrt(q): the hardware estimate refined by one Newton step
+    const double r0 = __builtin_amdgcn_rsq(q);
+    const double rs = q > 0.0 ? r0 * fma(-0.5 * q, r0 * r0, 1.5) : 0.0;
+    const double u = s.tau * delta * rs;
+    const double ua = u * a, ub = u * b;
+    const double A = ua * s.is1, B = ub * s.is2;
+    sum[0] = fma(A, s.cs, fma(-B, s.sn, sum[0]));
+    sum[1] = fma(A, s.sn, fma(B, s.cs, sum[1]));
+    sum[7] = fma(-(u * s.dsq), ar * br, sum[7]);
+    sum[8] = fma(ua, a, sum[8]);
+    sum[9] = fma(ub, b, sum[9]);
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {
@@ -106,53 +103,77 @@ __device__ __forceinline__ double wave_sum_d(double v) {
     return v;
 }
 
-// One wavefront turns the per-slot entry counts into bucket starts (in
-// place) and cuts every bucket into ceil(count / PIECE) pieces of nearly
-// equal length; ptab receives start | length << 13 | slot << 17 per piece,
-// *npieces their number.
-__device__ __forceinline__ void plan_pieces(uint32_t* cnt, uint32_t* ptab, uint32_t* npieces, int lane) {
-    uint32_t c[4], pcs[4], sc = 0, sp = 0;
+// A lane's slot and position in the slot's bucket for list entry k, packed as
+// slot | position << 8 (NOSLOT when the entry has no slot).
+constexpr uint32_t NOSLOT = 0xFFFFFFFFu;
+
+// Claim a slot of the region's table for every id < n of the lane's list
+// (the probing of claim_slots): slot16[k / 2] holds entry k's slot in its
+// k-th 16-bit half, 0xFFFF when the entry has no slot.  Branch-free: every
+// round reads the probed slot of all 8 entries (a read of one address by many
+// lanes is a broadcast), and compare-and-swaps only where a lane saw an
+// empty slot; the other lanes of that instruction aim it at their own word of
+// `mine` (which never holds EMPTY), so the instruction neither branches nor
+// touches the table for them.
+__device__ __forceinline__ void claim(uint32_t* keys, uint32_t* mine, const uint32_t (&ids)[K], uint32_t n,
+                                      uint32_t (&slot16)[K / 2]) {
+    uint32_t pos[K], pend = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        c[q] = cnt[4 * lane + q];
-        pcs[q] = (c[q] + PIECE - 1) / PIECE;
-        sc += c[q];
-        sp += pcs[q];
+    for (int k = 0; k < K; ++k) {
+        pos[k] = slot_hash(ids[k]);
+        pend |= (ids[k] < n ? 1u : 0u) << k;
     }
-    uint32_t isc = sc, isp = sp;  // inclusive prefix sums over the lanes
+    for (int round = 0; round < REGION_PROBES && __any(pend != 0); ++round) {
+        uint32_t cur[K];
 #pragma unroll
-    for (int off = 1; off < WAVE; off <<= 1) {
-        const uint32_t u = __shfl_up(isc, off, WAVE), v = __shfl_up(isp, off, WAVE);
-        if (lane >= off) {
-            isc += u;
-            isp += v;
+        for (int k = 0; k < K; ++k) cur[k] = keys[pos[k]];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const bool take = ((pend >> k) & 1) && cur[k] == EMPTY;
+            const uint32_t got = atomicCAS(take ? &keys[pos[k]] : mine, EMPTY, ids[k]);
+            cur[k] = take ? got : cur[k];
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const bool live = (pend >> k) & 1;
+            const bool hit = (cur[k] == EMPTY) | (cur[k] == ids[k]);  // claimed now, or before
+            pend &= ~((live && hit ? 1u : 0u) << k);
+            pos[k] = live && !hit ? (pos[k] + slot_step(ids[k])) & (SLOTS - 1) : pos[k];
         }
     }
-    uint32_t b0 = isc - sc, pb = isp - sp;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t s = 4 * lane + q;
-        cnt[s] = b0;
-        uint32_t st = b0;
-        for (uint32_t k = 0; k < pcs[q]; ++k) {
-            const uint32_t len = c[q] / pcs[q] + (k < c[q] % pcs[q] ? 1u : 0u);
-            ptab[pb + k] = st | (len << 13) | (s << 17);
-            st += len;
-        }
-        b0 += c[q];
-        pb += pcs[q];
+    for (int k = 0; k < K; k += 2) {
+        const uint32_t s0 = (ids[k] < n && !((pend >> k) & 1)) ? pos[k] : 0xFFFFu;
+        const uint32_t s1 = (ids[k + 1] < n && !((pend >> (k + 1)) & 1)) ? pos[k + 1] : 0xFFFFu;
+        slot16[k / 2] = s0 | (s1 << 16);
     }
-    if (lane == WAVE - 1) *npieces = isp;
 }
 
-__global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void k_backward(BwdArgs a) {
+__device__ __forceinline__ int slot_of(const uint32_t (&slot16)[K / 2], int k) {
+    const uint32_t v = (k & 1) ? slot16[k / 2] >> 16 : slot16[k / 2] & 0xFFFFu;
+    return v == 0xFFFFu ? -1 : (int)v;
+}
+
+__global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void k_backward(BwdArgs a) {
     __shared__ uint32_t keys[SLOTS];
-    __shared__ float4 recs[SLOTS * 3];       // prepared record of the site in each slot
-    __shared__ uint32_t cnt[SLOTS];          // entries per slot, then the slot's first position in `order`
-    __shared__ uint32_t ptab[MAX_PIECES];
+    __shared__ uint32_t cnt[SLOTS];          // entries per slot
+    __shared__ uint32_t bstart[SLOTS];       // the slot's first position in `order`
+    __shared__ uint32_t pstart[SLOTS];       // the slot's first piece
+    __shared__ uint32_t wtot[SLOT_WAVES][2]; // entries and pieces of each planning wavefront's slots
+    __shared__ uint32_t mine[BWD_THREADS];   // one word per lane that never holds EMPTY (see claim)
     __shared__ uint16_t order[REGION_PIX * K];  // pixels of the region's entries, grouped by slot
-    __shared__ PixState ps[REGION_PIX];
-    __shared__ double acc[NGRAD * SLOTS];    // per term and slot
+    // what phase B needs of each pixel: the largest logit, dL/dc (float32,
+    // formed in float64), 1/Z and dL/dc . c (float64, c the blended colour)
+    __shared__ float ps_m[REGION_PIX];
+    __shared__ float ps_g[REGION_PIX][3];
+    __shared__ double ps_iz[REGION_PIX];
+    __shared__ double ps_gc[REGION_PIX];
+    // the claimed sites' records during the forward, then the per-slot sums
+    // of phase B
+    __shared__ __attribute__((aligned(16))) double shared_sums[SLOTS * NGRAD];
+    static_assert(sizeof(float4) * 3 * SLOTS <= sizeof(double) * SLOTS * NGRAD, "records fit where the sums go");
+    float4* recs = reinterpret_cast<float4*>(shared_sums);  // [SLOTS][3]
+    double* acc = shared_sums;                              // [SLOTS][NGRAD]
     __shared__ double wsum[REGION_WAVES];
     __shared__ uint32_t npieces;
 
@@ -170,12 +191,12 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(4))
         keys[s] = EMPTY;
         cnt[s] = 0;
     }
-    for (int s = tid; s < NGRAD * SLOTS; s += BWD_THREADS) acc[s] = 0.0;
+    mine[tid] = 0;
 
     // The pixel's list, each lane starting at its own offset (anti-diagonal of
-    // the tile) so that neighbouring pixels listing the same sites claim and
-    // count different slots at each step.
-    const int rot = (lane + (lane >> 3)) & (K - 1);
+    // the tile), so that neighbouring pixels listing the same site at the same
+    // rank claim and count it in different instructions (same-address LDS
+    // atomics of one instruction are serialised).
     uint32_t ids[K];
     float tg[3] = {0.f, 0.f, 0.f};
     {
@@ -188,22 +209,34 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(4))
             tg[1] = a.target[p * 3 + 1];
             tg[2] = a.target[p * 3 + 2];
         }
-        rotate_list(l0, l1, rot);
-        ids[0] = l0.x; ids[1] = l0.y; ids[2] = l0.z; ids[3] = l0.w;
-        ids[4] = l1.x; ids[5] = l1.y; ids[6] = l1.z; ids[7] = l1.w;
+        // rotate left by (lane + lane / 8) mod 8 in three selects per entry;
+        // the empty asm after each stage keeps the compiler from merging the
+        // stages into an 8-way select per entry
+        uint32_t v[K] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const int rot = (lane + (lane >> 3)) & (K - 1);
+#pragma unroll
+        for (int bit = 0; bit < 3; ++bit) {
+            const bool on = (rot >> bit) & 1;
+            uint32_t u[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) u[k] = on ? v[(k + (1 << bit)) & (K - 1)] : v[k];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                v[k] = u[k];
+                asm volatile("" : "+v"(v[k]));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) ids[k] = v[k];
     }
     __syncthreads();  // table cleared
 
-    // A1. slots, and each entry's position in its slot's bucket
-    int slot[K];
-    claim_slots(keys, ids, n, slot);
-    uint32_t pos[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) pos[k] = slot[k] >= 0 ? atomicAdd(&cnt[slot[k]], 1u) : 0u;
+    // A1. a slot for every listed site
+    uint32_t slot16[K / 2];
+    claim(keys, &mine[tid], ids, n, slot16);
     __syncthreads();
 
-    // A2. every claimed site's record read from memory once, into LDS; the
-    //     first wavefront plans the pieces meanwhile
+    // A2. every claimed site's record is read from memory once, into LDS
     for (int s = tid; s < SLOTS; s += BWD_THREADS) {
         const uint32_t id = keys[s];
         if (id == EMPTY) continue;
@@ -212,102 +245,173 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(4))
         recs[s * 3 + 1] = r[1];
         recs[s * 3 + 2] = r[2];
     }
-    if (wv == 0) plan_pieces(cnt, ptab, &npieces, lane);
     __syncthreads();
 
-    // A3. the pixel's forward.  When an entry of some lane of the wavefront
-    //     found no slot (its probe chain ran out), the wavefront takes a copy
-    //     of this code that reads such records from memory and sends their
-    //     terms to memory directly; otherwise every record read is an LDS
-    //     read (one pointer that may point to either memory would make every
-    //     read a slower generic load).
+    // A3. the pixel's forward: float32 logits, their exponentials, then in
+    //     float64 the normaliser, the blend, the residual and dL/dc.  When an
+    //     entry of some lane of the wavefront found no slot, the wavefront
+    //     takes a copy of this code that reads such records from memory;
+    //     otherwise every record read is an LDS read (one pointer that may
+    //     point to either memory would make every read a slower generic load).
     bool slotted = true;
 #pragma unroll
-    for (int k = 0; k < K; ++k) slotted &= (ids[k] >= n) | (slot[k] >= 0);
+    for (int k = 0; k < K; ++k) slotted &= (ids[k] >= n) | (slot_of(slot16, k) >= 0);
     double lsum = 0.0;
     auto forward = [&](auto lds_only) {
         // part q (0: x y tau r, 1: cos sin 1/s1 1/s2, 2: colour) of entry k's record
         auto rec = [&](int k, int q) -> float4 {
+            const int sk = slot_of(slot16, k);
             if constexpr (decltype(lds_only)::value)
-                return recs[(slot[k] >= 0 ? slot[k] : 0) * 3 + q];
+                return recs[(sk >= 0 ? sk : 0) * 3 + q];
             else
-                return slot[k] >= 0 ? recs[slot[k] * 3 + q]
-                                    : reinterpret_cast<const float4*>(a.derived + (size_t)ids[k] * REC)[q];
+                return sk >= 0 ? recs[sk * 3 + q] : reinterpret_cast<const float4*>(a.derived + (size_t)ids[k] * REC)[q];
         };
         float l[K], e[K];
-        bool use[K];
         float mx = -__builtin_inff();
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            use[k] = false;
-            l[k] = 0.0f;
+            l[k] = __builtin_nanf("");
             if (ids[k] >= n) continue;
             Geo g;
             g.g0 = rec(k, 0);
             g.g1 = rec(k, 1);
             const float s = usable_logit(g, true, px, py);
             if (!finitef(s)) continue;
-            use[k] = true;
             l[k] = s;
             mx = fmaxf(mx, s);
         }
         double z = 0.0;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            e[k] = use[k] ? __expf(l[k] - mx) : 0.0f;
+            e[k] = finitef(l[k]) ? __expf(l[k] - mx) : 0.0f;
             z += (double)e[k];
         }
         const double iz = z > 0.0 ? 1.0 / z : 0.0;
         double c[3] = {0.0, 0.0, 0.0};
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            if (!use[k]) continue;
+            if (!finitef(l[k])) continue;
             const double wk = (double)e[k] * iz;
             const float4 col = rec(k, 2);
-            c[0] += wk * (double)col.x;
-            c[1] += wk * (double)col.y;
-            c[2] += wk * (double)col.z;
+            c[0] = fma(wk, (double)col.x, c[0]);
+            c[1] = fma(wk, (double)col.y, c[1]);
+            c[2] = fma(wk, (double)col.z, c[2]);
         }
         float g[3];
         double gc = 0.0;
 #pragma unroll
         for (int ch = 0; ch < 3; ++ch) {
             const double r = c[ch] - (double)tg[ch];
-            lsum += r * r;
+            lsum = fma(r, r, lsum);
             g[ch] = (float)(2.0 * r * a.inv_p);
-            gc += (double)g[ch] * c[ch];
+            gc = fma((double)g[ch], c[ch], gc);
         }
         if (inside && a.image) {
             a.image[p * 3 + 0] = (float)c[0];
             a.image[p * 3 + 1] = (float)c[1];
             a.image[p * 3 + 2] = (float)c[2];
         }
-        ps[tid] = PixState{mx == -__builtin_inff() ? 0.0f : mx, g[0], g[1], g[2], iz, gc};
-        if constexpr (!decltype(lds_only)::value) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                if (!use[k] || slot[k] >= 0) continue;
-                const float4 g0 = rec(k, 0), g1 = rec(k, 1), col = rec(k, 2);
-                const double wk = (double)e[k] * iz;
-                const double delta =
-                    wk * ((double)g[0] * (double)col.x + (double)g[1] * (double)col.y + (double)g[2] * (double)col.z - gc);
-                double t[NGRAD];
-                entry_terms(site_d(g0, g1), (double)px, (double)py, l[k], wk, delta, g, t);
-#pragma unroll
-                for (int q = 0; q < NGRAD; ++q) unsafeAtomicAdd(&a.grad[(size_t)ids[k] * REC + q], (float)t[q]);
-            }
-        }
+        ps_m[tid] = mx == -__builtin_inff() ? 0.0f : mx;
+        ps_g[tid][0] = g[0];
+        ps_g[tid][1] = g[1];
+        ps_g[tid][2] = g[2];
+        ps_iz[tid] = iz;
+        ps_gc[tid] = gc;
     };
     if (__all(slotted))
         forward(std::true_type{});
     else
         forward(std::false_type{});
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-        if (slot[k] >= 0) order[cnt[slot[k]] + pos[k]] = (uint16_t)tid;
     if (a.loss) {
         const double ws = wave_sum_d(lsum);
         if (lane == 0) wsum[wv] = ws;
+    }
+    // each entry's position in its slot's bucket (slots without a site
+    // count in the lane's own word)
+    uint32_t sp[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int sk = slot_of(slot16, k);
+        const uint32_t c = atomicAdd(sk >= 0 ? &cnt[sk] : &mine[tid], 1u);
+        sp[k] = sk >= 0 ? (uint32_t)sk | (c << 8) : NOSLOT;
+    }
+    __syncthreads();  // counts complete; records no longer read
+
+    // A4. buckets and pieces: each of the first SLOT_WAVES wavefronts scans
+    //     the entry counts of its slots (one per lane) and their piece counts
+    //     (ceil(count / PIECE)); the others clear the per-slot sums (where
+    //     the records were)
+    uint32_t my_c = 0, my_pc = 0, ex_c = 0, ex_pc = 0;
+    if (wv < SLOT_WAVES) {
+        my_c = cnt[tid];
+        my_pc = (my_c + PIECE - 1) / PIECE;
+        uint32_t ic = my_c, ip = my_pc;  // inclusive scans over the wavefront
+#pragma unroll
+        for (int off = 1; off < WAVE; off <<= 1) {
+            const uint32_t u = __shfl_up(ic, off, WAVE), v = __shfl_up(ip, off, WAVE);
+            if (lane >= off) {
+                ic += u;
+                ip += v;
+            }
+        }
+        ex_c = ic - my_c;
+        ex_pc = ip - my_pc;
+        if (lane == WAVE - 1) {
+            wtot[wv][0] = ic;
+            wtot[wv][1] = ip;
+        }
+    } else {
+        for (int s = tid - SLOT_WAVES * WAVE; s < NGRAD * SLOTS; s += BWD_THREADS - SLOT_WAVES * WAVE) acc[s] = 0.0;
+    }
+    __syncthreads();  // wavefront totals
+    if (wv < SLOT_WAVES) {
+        uint32_t bc = 0, bp = 0, tc = 0, tp = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < SLOT_WAVES; ++w2) {
+            bc += w2 < wv ? wtot[w2][0] : 0u;
+            bp += w2 < wv ? wtot[w2][1] : 0u;
+            tp += wtot[w2][1];
+            tc += wtot[w2][0];
+        }
+        bstart[tid] = bc + ex_c;
+        pstart[tid] = bp + ex_pc;
+        if (tid == 0) npieces = tp;
+        (void)tc;
+    }
+    __syncthreads();  // buckets planned
+
+    // A5. counting sort: the pixel's index into the bucket of each entry.
+    //     Entries without a slot (the region lists more sites than its table
+    //     holds; rare) send their terms to memory directly.
+    uint32_t lone = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (sp[k] != NOSLOT)
+            order[bstart[sp[k] & 0xFFu] + (sp[k] >> 8)] = (uint16_t)tid;
+        else if (ids[k] < n)
+            lone |= 1u << k;
+    }
+    if (lone) {
+        const double g[3] = {(double)ps_g[tid][0], (double)ps_g[tid][1], (double)ps_g[tid][2]};
+        for (; lone; lone &= lone - 1) {
+            const int k = __builtin_ctz(lone);
+            uint32_t id = ids[0];
+#pragma unroll
+            for (int kk = 1; kk < K; ++kk) id = k == kk ? ids[kk] : id;
+            const Geo gk = load_geo(a.derived, id);
+            const float l = usable_logit(gk, true, px, py);
+            if (!finitef(l)) continue;
+            const float4 col = reinterpret_cast<const float4*>(a.derived + (size_t)id * REC)[2];
+            const double wk = (double)__expf(l - ps_m[tid]) * ps_iz[tid];
+            const double delta =
+                wk * (fma(g[0], (double)col.x, fma(g[1], (double)col.y, g[2] * (double)col.z)) - ps_gc[tid]);
+            double t[NGRAD];
+#pragma unroll
+            for (int q = 0; q < NGRAD; ++q) t[q] = 0.0;
+            add_entry_terms(site_d(gk.g0, gk.g1), (double)px, (double)py, l, wk, delta, g, t);
+#pragma unroll
+            for (int q = 0; q < NGRAD; ++q) unsafeAtomicAdd(&a.grad[(size_t)id * REC + q], (float)t[q]);
+        }
     }
     __syncthreads();
 
@@ -317,43 +421,45 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(4))
     for (uint32_t base = 0; base < np; base += BWD_THREADS) {
         const uint32_t pc = base + (uint32_t)(lane * REGION_WAVES + wv);
         if (pc >= np) continue;
-        const uint32_t pe = ptab[pc];
-        const int start = (int)(pe & 0x1FFFu), len = (int)((pe >> 13) & 0xFu), s = (int)(pe >> 17);
-        Geo geo;
-        geo.g0 = recs[s * 3 + 0];
-        geo.g1 = recs[s * 3 + 1];
-        const float4 col = recs[s * 3 + 2];
+        // the piece's slot: the last slot whose first piece is <= pc (slots
+        // without entries have no pieces and are passed over)
+        int s = 0;
+#pragma unroll
+        for (int half = SLOTS / 2; half >= 1; half >>= 1) s = pstart[s + half] <= pc ? s + half : s;
+        const uint32_t kp = pc - pstart[s];
+        const int start = (int)(bstart[s] + kp * PIECE);
+        const int len = (int)min((uint32_t)PIECE, cnt[s] - kp * PIECE);
+        const uint32_t id = keys[s];
+        const Geo geo = load_geo(a.derived, id);
+        const float4 col = reinterpret_cast<const float4*>(a.derived + (size_t)id * REC)[2];
         const SiteD sd = site_d(geo.g0, geo.g1);
+        const double cr = (double)col.x, cg = (double)col.y, cb = (double)col.z;
         const bool active = geo.g0.x >= 0.0f;  // a claimed id is < n; an inactive site has x < 0
         double sum[NGRAD];
 #pragma unroll
         for (int q = 0; q < NGRAD; ++q) sum[q] = 0.0;
         for (int it = 0; it < len; ++it) {
             const int pp = order[start + it];
-            const PixState st = ps[pp];
             int pi, pj;
             region_pixel(rx, ry, pp / WAVE, pp & (WAVE - 1), pi, pj);
             const float fx = (float)pi + 0.5f, fy = (float)pj + 0.5f;
             const float l = logit(geo, fx, fy);
             if (!(active & finitef(l))) continue;  // unusable entries take no part (as in the forward)
-            const double wk = (double)__expf(l - st.m) * st.iz;
-            const float g[3] = {st.g0, st.g1, st.g2};
-            const double delta =
-                wk * ((double)g[0] * (double)col.x + (double)g[1] * (double)col.y + (double)g[2] * (double)col.z - st.gc);
-            double t[NGRAD];
-            entry_terms(sd, (double)fx, (double)fy, l, wk, delta, g, t);
-#pragma unroll
-            for (int q = 0; q < NGRAD; ++q) sum[q] += t[q];
+            const double wk = (double)__expf(l - ps_m[pp]) * ps_iz[pp];
+            const double g[3] = {(double)ps_g[pp][0], (double)ps_g[pp][1], (double)ps_g[pp][2]};
+            const double delta = wk * (fma(g[0], cr, fma(g[1], cg, g[2] * cb)) - ps_gc[pp]);
+            add_entry_terms(sd, (double)fx, (double)fy, l, wk, delta, g, sum);
         }
 #pragma unroll
-        for (int q = 0; q < NGRAD; ++q) atomicAdd(&acc[q * SLOTS + s], sum[q]);
+        for (int q = 0; q < NGRAD; ++q) atomicAdd(&acc[s * NGRAD + q], sum[q]);
     }
     __syncthreads();
 
     // C. the region's per-site sums leave the workgroup: one float atomic per
-    //    (site, term)
+    //    (site, term), a site's 10 terms from consecutive lanes (one or two
+    //    cache lines per site instead of one per lane)
     for (int pr = tid; pr < NGRAD * SLOTS; pr += BWD_THREADS) {
-        const int q = pr / SLOTS, s = pr % SLOTS;
+        const int s = pr / NGRAD, q = pr % NGRAD;
         const uint32_t id = keys[s];
         if (id == EMPTY) continue;
         const double v = acc[pr];
