@@ -212,6 +212,24 @@ int sad_site_stats(const float *derived, int32_t n, int32_t h, int32_t w, const 
                    const float *target, float *stats, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sad_site_stats without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, outputs and checks as sad_site_stats;
+ * the region tables live in a device array of the library,
+ * SAD_STATS_SCRATCH_BYTES per GPU, held from the library's load until the
+ * process ends (its address on a GPU is looked up on the first call made
+ * with that GPU current).  The call allocates nothing.
+ * Limit: sad_site_stats_workspace_bytes(h, w) <= SAD_STATS_SCRATCH_BYTES,
+ * i.e. ceil(w / 32) * ceil(h / 16) <= 4551 regions (1920 x 1080 and 2048 x
+ * 1024 fit; 2048 x 2048 does not); larger images return SAD_EUNSUPPORTED.
+ * Calls on one GPU share the array: calls that overlap on one GPU (on
+ * streams without ordering between them) race.
+ */
+#define SAD_STATS_SCRATCH_BYTES (40u << 20)
+int sad_site_stats_noalloc(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk,
+                           const float *target, float *stats, void *stream);
+
+/*
  * Budget control from the statistics of sad_site_stats (Sec. 4.5, "Adaptive
  * Budget: Densify and Prune"; Appendix B.5, "Densification scores", "Split
  * kernel", "Pruning").  In place on params, adam_m, adam_v and derived

@@ -178,6 +178,17 @@ def test_site_stats_rejects(lib):
     assert call(h=0, topk=None, tgt=None, ws=None) == 0  # empty image: nothing to do
 
 
+def test_site_stats_noalloc_rejects(lib):
+    """The allocation-free statistics refuse what sad_site_stats refuses, and
+    images whose region tables exceed the library's array (checked before any
+    GPU call)."""
+    f = lib.sad_site_stats_noalloc
+    assert f(P, 10, 2048, 2048, P + 4096, P + 8192, P + 65536, None) == EUNSUP
+    assert f(P, 10, 1 << 15, 1 << 15, P + 4096, P + 8192, P + 65536, None) == EUNSUP
+    assert f(P, 10, -1, 8, P + 4096, P + 8192, P + 65536, None) == EINVAL
+    assert lib.sad_site_stats_workspace_bytes(1080, 1920) <= 40 << 20 < lib.sad_site_stats_workspace_bytes(2048, 2048)
+
+
 def test_jfa_rejects(lib):
     assert lib.sad_jfa_seed(P, -1, 8, 8, P + 4096, None) == EINVAL
     assert lib.sad_jfa_seed(P, 10, 8, 8, None, None) == EINVAL

@@ -29,6 +29,8 @@ _SIGS = {
     "sad_render_bwd": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "sad_site_stats_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
+    "sad_site_stats_noalloc": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                         C.c_void_p, C.c_void_p]),
     "sad_site_stats": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "sad_budget_workspace_bytes": (C.c_size_t, [C.c_int32]),

@@ -8,6 +8,7 @@
 // two stages (described before k_region_stats); queries take one thread per
 // point.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "sad_propagate.h"
@@ -559,6 +560,55 @@ extern "C" int sad_site_stats(const float* derived, int32_t n, int32_t h, int32_
         hipLaunchKernelGGL(k_stats_gather, dim3((unsigned)((n + GATHER_SITES - 1) / GATHER_SITES)),
                            dim3(GATHER_SITES * 9), 0, as_stream(stream), b.rg, b.tkeys, b.tvals, derived, stats, n);
     return launch_status();
+}
+
+// ---------------------------------------------------------------- statistics without allocation
+//
+// sad_site_stats_noalloc: the statistics with their region tables in a
+// file-scope device array instead of a caller's workspace, for callers that
+// cannot allocate.  Every GPU the library runs on holds its own copy of the
+// array (SAD_STATS_SCRATCH_BYTES) from the library's load until the process
+// ends.  In host code `stats_scratch` names a host-side stand-in, not device
+// memory: its device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and only that address is
+// passed to kernels.  Calls on one GPU share the array, so calls that overlap
+// on one GPU (different streams, no ordering) race.
+namespace {
+
+static __device__ __align__(256) unsigned char stats_scratch[SAD_STATS_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void* scratch_addr[MAX_DEVICES];  // device address of stats_scratch per device, once resolved
+
+// The current device's address of stats_scratch, resolved on its first use.
+int scratch_for_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SAD_EHIP;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(stats_scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return SAD_EHIP;
+        }
+        scratch_addr[dev] = p;
+    }
+    *out = scratch_addr[dev];
+    return SAD_OK;
+}
+
+}  // namespace
+
+extern "C" int sad_site_stats_noalloc(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
+                                      const float* target, float* stats, void* stream) {
+    if (!image_ok(h, w)) return SAD_EINVAL;
+    if (sad_site_stats_workspace_bytes(h, w) > (size_t)SAD_STATS_SCRATCH_BYTES) return SAD_EUNSUPPORTED;
+    if (int64_t(h) * w == 0) return sad_site_stats(derived, n, h, w, topk, target, stats, nullptr, 0, stream);
+    void* scratch = nullptr;
+    const int st = scratch_for_current_device(&scratch);
+    if (st != SAD_OK) return st;
+    return sad_site_stats(derived, n, h, w, topk, target, stats, scratch, SAD_STATS_SCRATCH_BYTES, stream);
 }
 
 extern "C" int sad_query_points(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,

@@ -147,6 +147,21 @@ def site_stats(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target
     return stats
 
 
+def site_stats_noalloc(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, target: torch.Tensor,
+                       stats: torch.Tensor) -> torch.Tensor:
+    """site_stats with the library's own device scratch (no workspace, no
+    allocation); ``stats`` must be given.  Calls on one GPU must not overlap."""
+    n = derived.shape[0]
+    _need(derived, "derived", torch.float32, (n, REC))
+    _need(topk, "topk", torch.int32, (h, w, K))
+    _need(target, "target", torch.float32, (h, w, 3))
+    _need(stats, "stats", torch.float32, (n, NSTAT))
+    st = _native.lib().sad_site_stats_noalloc(_ptr(derived), n, h, w, _ptr(topk), _ptr(target), _ptr(stats),
+                                              _stream(derived))
+    _native.check("sad_site_stats_noalloc", st)
+    return stats
+
+
 def budget_workspace(n: int, device) -> torch.Tensor:
     """Scratch memory for sad_densify_prune with n sites."""
     nb = int(_native.lib().sad_budget_workspace_bytes(int(n)))
