@@ -354,11 +354,14 @@ int sad_jfa_flood(const float *derived, int32_t n, int32_t h, int32_t w, const u
  * a training iteration, Sec. 6.6 / Table 9, then Sec. 4.8 / Appendix B.4).
  * Equivalent to sad_propagate_topk(derived, n, h, w, topk_prev, scores_prev,
  * topk_next, scores_next, stride, seed, pass_index, inject_per_tile) then
- * sad_render_bwd(derived, n, h, w, topk_next, target, grad, loss, image),
- * and enqueued as those two launches: topk_next, scores_next and image are the
- * same bits; grad and loss differ only by summation order, as between two
- * calls of sad_render_bwd.  Every argument is checked before any work is
- * enqueued, so a rejected call leaves all buffers untouched.
+ * sad_render_bwd(derived, n, h, w, topk_next, target, grad, loss, image):
+ * topk_next, scores_next and image are the same bits; grad and loss differ
+ * only by summation order, as between two calls of sad_render_bwd.  One
+ * kernel does both: each workgroup runs the pass on a region of 32 x 16
+ * pixels and the backward starts from the lists and float32 logits the pass
+ * left in registers (no list is read back, no logit evaluated again).  Every
+ * argument is checked before any work is enqueued, so a rejected call leaves
+ * all buffers untouched.
  * Arguments, formats and checks are those of the two calls; in addition
  * topk_next and scores_next must not overlap target, grad, loss, image or
  * derived.

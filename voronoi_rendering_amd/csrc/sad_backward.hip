@@ -154,91 +154,84 @@ __device__ __forceinline__ int slot_of(const uint32_t (&slot16)[K / 2], int k) {
     return v == 0xFFFFu ? -1 : (int)v;
 }
 
-__global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void k_backward(BwdArgs a) {
-    __shared__ uint32_t keys[SLOTS];
-    __shared__ uint32_t cnt[SLOTS];          // entries per slot
-    __shared__ uint32_t bstart[SLOTS];       // the slot's first position in `order`
-    __shared__ uint32_t pstart[SLOTS];       // the slot's first piece
-    __shared__ uint32_t wtot[SLOT_WAVES][2]; // entries and pieces of each planning wavefront's slots
-    __shared__ uint32_t mine[BWD_THREADS];   // one word per lane that never holds EMPTY (see claim)
-    __shared__ uint16_t order[REGION_PIX * K];  // pixels of the region's entries, grouped by slot
+// The backward's LDS.
+struct BwdLds {
+    uint32_t keys[SLOTS];
+    uint32_t cnt[SLOTS];            // entries per slot
+    uint32_t bstart[SLOTS];         // the slot's first position in `order`
+    uint32_t pstart[SLOTS];         // the slot's first piece
+    uint32_t wtot[SLOT_WAVES][2];   // entries and pieces of each planning wavefront's slots
+    uint32_t mine[BWD_THREADS];     // one word per lane that never holds EMPTY (see claim)
+    uint16_t order[REGION_PIX * K];  // pixels of the region's entries, grouped by slot
     // what phase B needs of each pixel: the largest logit, dL/dc (float32,
     // formed in float64), 1/Z and dL/dc . c (float64, c the blended colour)
-    __shared__ float ps_m[REGION_PIX];
-    __shared__ float ps_g[REGION_PIX][3];
-    __shared__ double ps_iz[REGION_PIX];
-    __shared__ double ps_gc[REGION_PIX];
+    float ps_m[REGION_PIX];
+    float ps_g[REGION_PIX][3];
+    double ps_iz[REGION_PIX];
+    double ps_gc[REGION_PIX];
     // the claimed sites' records during the forward, then the per-slot sums
     // of phase B
-    __shared__ __attribute__((aligned(16))) double shared_sums[SLOTS * NGRAD];
-    static_assert(sizeof(float4) * 3 * SLOTS <= sizeof(double) * SLOTS * NGRAD, "records fit where the sums go");
-    float4* recs = reinterpret_cast<float4*>(shared_sums);  // [SLOTS][3]
-    double* acc = shared_sums;                              // [SLOTS][NGRAD]
-    __shared__ double wsum[REGION_WAVES];
-    __shared__ uint32_t npieces;
+    __attribute__((aligned(16))) double shared_sums[SLOTS * NGRAD];
+    double wsum[REGION_WAVES];
+    uint32_t npieces;
+};
+static_assert(sizeof(float4) * 3 * SLOTS <= sizeof(double) * SLOTS * NGRAD, "records fit where the sums go");
 
+// Rotate the lane's 8 entries left by (lane + lane / 8) mod 8 (anti-diagonal
+// of the tile), so that neighbouring pixels listing the same site at the same
+// rank claim and count it in different instructions (same-address LDS atomics
+// of one instruction are serialised).  Three selects per entry; the empty asm
+// after each stage keeps the compiler from merging the stages into an 8-way
+// select per entry.
+template <class T>
+struct Row8 {
+    T v[K];
+};
+
+template <class T>
+__device__ __forceinline__ Row8<T> rotate_lane(Row8<T> r, int lane) {
+    const int rot = (lane + (lane >> 3)) & (K - 1);
+#pragma unroll
+    for (int bit = 0; bit < 3; ++bit) {
+        const bool on = (rot >> bit) & 1;
+        T u[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) u[k] = on ? r.v[(k + (1 << bit)) & (K - 1)] : r.v[k];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            r.v[k] = u[k];
+            asm volatile("" : "+v"(r.v[k]));
+        }
+    }
+    return r;
+}
+
+// The backward of one region, from each lane's list (ids, in any order) and
+// target colour; with GIVEN_LOGITS, given[k] is entry k's float32 logit at
+// the pixel (as the propagation pass computed it) and the forward does not
+// evaluate it again.  The table of L must be cleared (keys EMPTY, cnt 0,
+// mine 0) and a barrier passed before the call.
+template <bool GIVEN_LOGITS>
+__device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int rx, int ry, uint32_t (&ids)[K],
+                                                const float (&given)[K], const float (&tg)[3]) {
     const uint32_t n = (uint32_t)a.n;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
-    const int reg = xcd_block(blockIdx.x, gridDim.x);
-    const int rx = reg % a.rg.rgx, ry = reg / a.rg.rgx;
     int i, j;
     region_pixel(rx, ry, wv, lane, i, j);
     const bool inside = i < a.w && j < a.h;
     const size_t p = (size_t)j * a.w + i;
     const float px = (float)i + 0.5f, py = (float)j + 0.5f;
-
-    for (int s = tid; s < SLOTS; s += BWD_THREADS) {
-        keys[s] = EMPTY;
-        cnt[s] = 0;
-    }
-    mine[tid] = 0;
-
-    // The pixel's list, each lane starting at its own offset (anti-diagonal of
-    // the tile), so that neighbouring pixels listing the same site at the same
-    // rank claim and count it in different instructions (same-address LDS
-    // atomics of one instruction are serialised).
-    uint32_t ids[K];
-    float tg[3] = {0.f, 0.f, 0.f};
-    {
-        uint4 l0 = make_uint4(EMPTY, EMPTY, EMPTY, EMPTY), l1 = l0;
-        if (inside) {
-            const uint4* l = reinterpret_cast<const uint4*>(a.topk + p * K);
-            l0 = l[0];
-            l1 = l[1];
-            tg[0] = a.target[p * 3 + 0];
-            tg[1] = a.target[p * 3 + 1];
-            tg[2] = a.target[p * 3 + 2];
-        }
-        // rotate left by (lane + lane / 8) mod 8 in three selects per entry;
-        // the empty asm after each stage keeps the compiler from merging the
-        // stages into an 8-way select per entry
-        uint32_t v[K] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const int rot = (lane + (lane >> 3)) & (K - 1);
-#pragma unroll
-        for (int bit = 0; bit < 3; ++bit) {
-            const bool on = (rot >> bit) & 1;
-            uint32_t u[K];
-#pragma unroll
-            for (int k = 0; k < K; ++k) u[k] = on ? v[(k + (1 << bit)) & (K - 1)] : v[k];
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                v[k] = u[k];
-                asm volatile("" : "+v"(v[k]));
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < K; ++k) ids[k] = v[k];
-    }
-    __syncthreads();  // table cleared
+    float4* recs = reinterpret_cast<float4*>(L.shared_sums);  // [SLOTS][3]
+    double* acc = L.shared_sums;                              // [SLOTS][NGRAD]
 
     // A1. a slot for every listed site
     uint32_t slot16[K / 2];
-    claim(keys, &mine[tid], ids, n, slot16);
+    claim(L.keys, &L.mine[tid], ids, n, slot16);
     __syncthreads();
 
     // A2. every claimed site's record is read from memory once, into LDS
     for (int s = tid; s < SLOTS; s += BWD_THREADS) {
-        const uint32_t id = keys[s];
+        const uint32_t id = L.keys[s];
         if (id == EMPTY) continue;
         const float4* r = reinterpret_cast<const float4*>(a.derived + (size_t)id * REC);
         recs[s * 3 + 0] = r[0];
@@ -272,10 +265,15 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
         for (int k = 0; k < K; ++k) {
             l[k] = __builtin_nanf("");
             if (ids[k] >= n) continue;
-            Geo g;
-            g.g0 = rec(k, 0);
-            g.g1 = rec(k, 1);
-            const float s = usable_logit(g, true, px, py);
+            float s;
+            if constexpr (GIVEN_LOGITS) {
+                s = given[k];  // the pass's own float32 logit of the entry
+            } else {
+                Geo g;
+                g.g0 = rec(k, 0);
+                g.g1 = rec(k, 1);
+                s = usable_logit(g, true, px, py);
+            }
             if (!finitef(s)) continue;
             l[k] = s;
             mx = fmaxf(mx, s);
@@ -311,12 +309,12 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
             a.image[p * 3 + 1] = (float)c[1];
             a.image[p * 3 + 2] = (float)c[2];
         }
-        ps_m[tid] = mx == -__builtin_inff() ? 0.0f : mx;
-        ps_g[tid][0] = g[0];
-        ps_g[tid][1] = g[1];
-        ps_g[tid][2] = g[2];
-        ps_iz[tid] = iz;
-        ps_gc[tid] = gc;
+        L.ps_m[tid] = mx == -__builtin_inff() ? 0.0f : mx;
+        L.ps_g[tid][0] = g[0];
+        L.ps_g[tid][1] = g[1];
+        L.ps_g[tid][2] = g[2];
+        L.ps_iz[tid] = iz;
+        L.ps_gc[tid] = gc;
     };
     if (__all(slotted))
         forward(std::true_type{});
@@ -324,7 +322,7 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
         forward(std::false_type{});
     if (a.loss) {
         const double ws = wave_sum_d(lsum);
-        if (lane == 0) wsum[wv] = ws;
+        if (lane == 0) L.wsum[wv] = ws;
     }
     // each entry's position in its slot's bucket (slots without a site
     // count in the lane's own word)
@@ -332,7 +330,7 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int sk = slot_of(slot16, k);
-        const uint32_t c = atomicAdd(sk >= 0 ? &cnt[sk] : &mine[tid], 1u);
+        const uint32_t c = atomicAdd(sk >= 0 ? &L.cnt[sk] : &L.mine[tid], 1u);
         sp[k] = sk >= 0 ? (uint32_t)sk | (c << 8) : NOSLOT;
     }
     __syncthreads();  // counts complete; records no longer read
@@ -343,7 +341,7 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
     //     the records were)
     uint32_t my_c = 0, my_pc = 0, ex_c = 0, ex_pc = 0;
     if (wv < SLOT_WAVES) {
-        my_c = cnt[tid];
+        my_c = L.cnt[tid];
         my_pc = (my_c + PIECE - 1) / PIECE;
         uint32_t ic = my_c, ip = my_pc;  // inclusive scans over the wavefront
 #pragma unroll
@@ -357,8 +355,8 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
         ex_c = ic - my_c;
         ex_pc = ip - my_pc;
         if (lane == WAVE - 1) {
-            wtot[wv][0] = ic;
-            wtot[wv][1] = ip;
+            L.wtot[wv][0] = ic;
+            L.wtot[wv][1] = ip;
         }
     } else {
         for (int s = tid - SLOT_WAVES * WAVE; s < NGRAD * SLOTS; s += BWD_THREADS - SLOT_WAVES * WAVE) acc[s] = 0.0;
@@ -368,14 +366,14 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
         uint32_t bc = 0, bp = 0, tc = 0, tp = 0;
 #pragma unroll
         for (int w2 = 0; w2 < SLOT_WAVES; ++w2) {
-            bc += w2 < wv ? wtot[w2][0] : 0u;
-            bp += w2 < wv ? wtot[w2][1] : 0u;
-            tp += wtot[w2][1];
-            tc += wtot[w2][0];
+            bc += w2 < wv ? L.wtot[w2][0] : 0u;
+            bp += w2 < wv ? L.wtot[w2][1] : 0u;
+            tp += L.wtot[w2][1];
+            tc += L.wtot[w2][0];
         }
-        bstart[tid] = bc + ex_c;
-        pstart[tid] = bp + ex_pc;
-        if (tid == 0) npieces = tp;
+        L.bstart[tid] = bc + ex_c;
+        L.pstart[tid] = bp + ex_pc;
+        if (tid == 0) L.npieces = tp;
         (void)tc;
     }
     __syncthreads();  // buckets planned
@@ -387,12 +385,12 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         if (sp[k] != NOSLOT)
-            order[bstart[sp[k] & 0xFFu] + (sp[k] >> 8)] = (uint16_t)tid;
+            L.order[L.bstart[sp[k] & 0xFFu] + (sp[k] >> 8)] = (uint16_t)tid;
         else if (ids[k] < n)
             lone |= 1u << k;
     }
     if (lone) {
-        const double g[3] = {(double)ps_g[tid][0], (double)ps_g[tid][1], (double)ps_g[tid][2]};
+        const double g[3] = {(double)L.ps_g[tid][0], (double)L.ps_g[tid][1], (double)L.ps_g[tid][2]};
         for (; lone; lone &= lone - 1) {
             const int k = __builtin_ctz(lone);
             uint32_t id = ids[0];
@@ -402,9 +400,9 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
             const float l = usable_logit(gk, true, px, py);
             if (!finitef(l)) continue;
             const float4 col = reinterpret_cast<const float4*>(a.derived + (size_t)id * REC)[2];
-            const double wk = (double)__expf(l - ps_m[tid]) * ps_iz[tid];
+            const double wk = (double)__expf(l - L.ps_m[tid]) * L.ps_iz[tid];
             const double delta =
-                wk * (fma(g[0], (double)col.x, fma(g[1], (double)col.y, g[2] * (double)col.z)) - ps_gc[tid]);
+                wk * (fma(g[0], (double)col.x, fma(g[1], (double)col.y, g[2] * (double)col.z)) - L.ps_gc[tid]);
             double t[NGRAD];
 #pragma unroll
             for (int q = 0; q < NGRAD; ++q) t[q] = 0.0;
@@ -417,7 +415,7 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
 
     // B. one piece per lane: a site's entries, pieces dealt across the
     //    wavefronts in turn
-    const uint32_t np = npieces;
+    const uint32_t np = L.npieces;
     for (uint32_t base = 0; base < np; base += BWD_THREADS) {
         const uint32_t pc = base + (uint32_t)(lane * REGION_WAVES + wv);
         if (pc >= np) continue;
@@ -425,11 +423,11 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
         // without entries have no pieces and are passed over)
         int s = 0;
 #pragma unroll
-        for (int half = SLOTS / 2; half >= 1; half >>= 1) s = pstart[s + half] <= pc ? s + half : s;
-        const uint32_t kp = pc - pstart[s];
-        const int start = (int)(bstart[s] + kp * PIECE);
-        const int len = (int)min((uint32_t)PIECE, cnt[s] - kp * PIECE);
-        const uint32_t id = keys[s];
+        for (int half = SLOTS / 2; half >= 1; half >>= 1) s = L.pstart[s + half] <= pc ? s + half : s;
+        const uint32_t kp = pc - L.pstart[s];
+        const int start = (int)(L.bstart[s] + kp * PIECE);
+        const int len = (int)min((uint32_t)PIECE, L.cnt[s] - kp * PIECE);
+        const uint32_t id = L.keys[s];
         const Geo geo = load_geo(a.derived, id);
         const float4 col = reinterpret_cast<const float4*>(a.derived + (size_t)id * REC)[2];
         const SiteD sd = site_d(geo.g0, geo.g1);
@@ -439,15 +437,15 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
 #pragma unroll
         for (int q = 0; q < NGRAD; ++q) sum[q] = 0.0;
         for (int it = 0; it < len; ++it) {
-            const int pp = order[start + it];
+            const int pp = L.order[start + it];
             int pi, pj;
             region_pixel(rx, ry, pp / WAVE, pp & (WAVE - 1), pi, pj);
             const float fx = (float)pi + 0.5f, fy = (float)pj + 0.5f;
             const float l = logit(geo, fx, fy);
             if (!(active & finitef(l))) continue;  // unusable entries take no part (as in the forward)
-            const double wk = (double)__expf(l - ps_m[pp]) * ps_iz[pp];
-            const double g[3] = {(double)ps_g[pp][0], (double)ps_g[pp][1], (double)ps_g[pp][2]};
-            const double delta = wk * (fma(g[0], cr, fma(g[1], cg, g[2] * cb)) - ps_gc[pp]);
+            const double wk = (double)__expf(l - L.ps_m[pp]) * L.ps_iz[pp];
+            const double g[3] = {(double)L.ps_g[pp][0], (double)L.ps_g[pp][1], (double)L.ps_g[pp][2]};
+            const double delta = wk * (fma(g[0], cr, fma(g[1], cg, g[2] * cb)) - L.ps_gc[pp]);
             add_entry_terms(sd, (double)fx, (double)fy, l, wk, delta, g, sum);
         }
 #pragma unroll
@@ -460,16 +458,122 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
     //    cache lines per site instead of one per lane)
     for (int pr = tid; pr < NGRAD * SLOTS; pr += BWD_THREADS) {
         const int s = pr / NGRAD, q = pr % NGRAD;
-        const uint32_t id = keys[s];
+        const uint32_t id = L.keys[s];
         if (id == EMPTY) continue;
         const double v = acc[pr];
         if (v != 0.0) unsafeAtomicAdd(&a.grad[(size_t)id * REC + q], (float)v);
     }
     if (a.loss && tid == 0) {
         double tot = 0.0;
-        for (int k = 0; k < REGION_WAVES; ++k) tot += wsum[k];
+        for (int k = 0; k < REGION_WAVES; ++k) tot += L.wsum[k];
         unsafeAtomicAdd(a.loss, (float)(tot * a.inv_p));
     }
+}
+
+__global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void k_backward(BwdArgs a) {
+    __shared__ BwdLds L;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
+    const int reg = xcd_block(blockIdx.x, gridDim.x);
+    const int rx = reg % a.rg.rgx, ry = reg / a.rg.rgx;
+    int i, j;
+    region_pixel(rx, ry, wv, lane, i, j);
+    const bool inside = i < a.w && j < a.h;
+    const size_t p = (size_t)j * a.w + i;
+
+    for (int s = tid; s < SLOTS; s += BWD_THREADS) {
+        L.keys[s] = EMPTY;
+        L.cnt[s] = 0;
+    }
+    L.mine[tid] = 0;
+
+    uint32_t ids[K];
+    float tg[3] = {0.f, 0.f, 0.f};
+    {
+        uint4 l0 = make_uint4(EMPTY, EMPTY, EMPTY, EMPTY), l1 = l0;
+        if (inside) {
+            const uint4* l = reinterpret_cast<const uint4*>(a.topk + p * K);
+            l0 = l[0];
+            l1 = l[1];
+            tg[0] = a.target[p * 3 + 0];
+            tg[1] = a.target[p * 3 + 1];
+            tg[2] = a.target[p * 3 + 2];
+        }
+        const Row8<uint32_t> r = rotate_lane(Row8<uint32_t>{{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w}}, lane);
+#pragma unroll
+        for (int k = 0; k < K; ++k) ids[k] = r.v[k];
+    }
+    __syncthreads();  // table cleared
+    const float none[K] = {};
+    backward_region<false>(a, L, rx, ry, ids, none, tg);
+}
+
+// The propagation pass's LDS for the eight wavefronts of a region.
+template <bool SMALL_IDS>
+struct PassLds {
+    QueueId<SMALL_IDS> queue[REGION_WAVES][QCAP][WAVE];
+    float qscore[REGION_WAVES][QCAP][WAVE];
+};
+
+// A training iteration's last propagation pass and the backward over its
+// lists in one kernel (Sec. 6.6 / Table 9 one-pass update, then Sec. 4.8 /
+// Appendix B.4).  A workgroup takes one region: each wavefront runs the pass
+// on its tile of the region (propagate_tile: the next lists and logits are
+// written as by sad_propagate_topk), keeps the tile's new lists with their
+// float32 logits in registers, and after a barrier the region's backward
+// starts from them in the same LDS: no list is read back and no logit of the
+// forward is evaluated again, and regions start their backward while others
+// still run their pass.
+template <bool SMALL_IDS>
+__global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(SMALL_IDS ? 6 : 1)))
+void k_step_last(PropArgs pa, BwdArgs a) {
+    __shared__ union {
+        PassLds<SMALL_IDS> pass;
+        BwdLds bwd;
+    } lds;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int reg = xcd_block(blockIdx.x, gridDim.x);
+    const int rx = reg % a.rg.rgx, ry = reg / a.rg.rgx;
+    const int tx = rx * RT_X + wv % RT_X, ty = ry * RT_Y + wv / RT_X;
+    TopK t;
+    t.clear();
+    if (tx < pa.tiles_x && ty * pa.tiles_x + tx < pa.n_tiles)  // uniform per wavefront
+        propagate_tile<SMALL_IDS>(pa, ty * pa.tiles_x + tx, lds.pass.queue[wv], lds.pass.qscore[wv], t);
+    int i, j;
+    region_pixel(rx, ry, wv, lane, i, j);  // the pixel the pass just listed
+    float tg[3] = {0.f, 0.f, 0.f};
+    if (i < a.w && j < a.h) {
+        const size_t p = (size_t)j * a.w + i;
+        tg[0] = a.target[p * 3 + 0];
+        tg[1] = a.target[p * 3 + 1];
+        tg[2] = a.target[p * 3 + 2];
+    }
+    uint32_t ids[K];
+    float lg[K];
+    {
+        Row8<uint32_t> ri;
+        Row8<float> rl;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            ri.v[k] = t.id[k];
+            rl.v[k] = t.s[k];
+        }
+        ri = rotate_lane(ri, lane);
+        rl = rotate_lane(rl, lane);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            ids[k] = ri.v[k];
+            lg[k] = rl.v[k];
+        }
+    }
+    __syncthreads();  // the pass's queues are no longer read
+    for (int s = tid; s < SLOTS; s += BWD_THREADS) {
+        lds.bwd.keys[s] = EMPTY;
+        lds.bwd.cnt[s] = 0;
+    }
+    lds.bwd.mine[tid] = 0;
+    __syncthreads();  // table cleared
+    backward_region<true>(a, lds.bwd, rx, ry, ids, lg, tg);
 }
 
 // Argument checks of a backward pass over the list map topk, and its kernel
@@ -547,10 +651,12 @@ extern "C" int sad_step_fused(const float* derived, int32_t n, int32_t h, int32_
         for (int q = 0; q < 5; ++q)
             if (overlap(outs[o], mbytes, others[q], obytes[q])) return SAD_EINVAL;
     if (pix == 0) return SAD_OK;
-    // every check has passed: the pass, then the backward over its lists, in
-    // stream order
-    st = sad_propagate_topk(derived, n, h, w, topk_prev, scores_prev, topk_next, scores_next, stride, seed, pass_index,
-                            inject_per_tile, stream);
-    if (st != SAD_OK) return st;
-    return bwd_launch(b, stream);
+    // every check has passed: one kernel, one workgroup per backward region
+    const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
+    clear_error();
+    if (pa.n <= SMALL_IDS_MAX)
+        hipLaunchKernelGGL(k_step_last<true>, dim3((unsigned)nreg), dim3(BWD_THREADS), 0, as_stream(stream), pa, b);
+    else
+        hipLaunchKernelGGL(k_step_last<false>, dim3((unsigned)nreg), dim3(BWD_THREADS), 0, as_stream(stream), pa, b);
+    return launch_status();
 }
