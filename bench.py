@@ -41,16 +41,19 @@ def algorithmic_bytes(h: int, w: int, n: int, n_pass: int) -> dict:
     render_bwd: read list (32 B) + target (12 B) per pixel, read the 48-byte
                 prepared record and read-modify-write the 40-byte gradient
                 record (80 B) per site.
+    step_last:  the last pass and the backward in one kernel: read + write
+                the list (64 B) + the target (12 B) per pixel, 128 B per site.
     step:       the whole step with the last list handed from the pass to the
                 backward: 64 B per pixel per pass + the target + 128 B per site."""
     p = h * w
     prop = 64 * p
     bwd = p * (32 + 12) + n * (48 + 80)
+    last = p * (64 + 12) + n * 128
     step = n_pass * 64 * p + 12 * p + n * 128
-    return {"propagate": prop, "render_bwd": bwd, "step": step}
+    return {"propagate": prop, "render_bwd": bwd, "step_last": last, "step": step}
 
 
-KERNEL_OF = {"propagate": "k_propagate", "render_bwd": "k_backward"}
+KERNEL_OF = {"propagate": "k_propagate", "render_bwd": "k_backward", "step_last": "k_step_last"}
 
 
 def counter_record(kind: str):
@@ -76,15 +79,21 @@ def measured_traffic(kind: str):
     return int(rec["bytes"]) if rec else None
 
 
-# Vector ALU issue peak without packed math: 256 CUs x 4 SIMDs, one wave64
-# instruction (64 lane-operations) per SIMD every 4 cycles, at 2.4 GHz.
-VALU_PEAK_T = 256 * 4 * 16 * 2.4e9 / 1e12
+# Vector ALU issue peak: the published fp32 vector peak (157.3 TFLOP/s, an FMA
+# counted as two flops) in lane-operations: 256 CUs x 4 SIMDs x 32 lanes per
+# clock at 2.4 GHz, i.e. a wave64 fp32 instruction every 2 cycles per SIMD.  A
+# kernel of nothing but independent v_fma_f32 reaches about 51 T of it on the
+# MI355X (its clock under that load reads about 2.1 GHz).
+VALU_PEAK_T = 157.3 / 2
 
 
 def valu_roofline(kind: str, seconds: float):
     """Vector-ALU lane-operations per second of the kernel (instructions per
     wavefront and wavefronts per launch from the counter summary, duration
-    measured live) against the issue peak, or None without valid counters."""
+    measured live) against the issue peak, or None without valid counters.
+    Every VALU instruction counts as 64 lane-operations (float64 and
+    transcendental instructions take longer to issue, so for a kernel with
+    many of them the fraction understates how busy the ALU is)."""
     rec = counter_record(kind)
     if not rec or "valu_insts_per_wave" not in rec:
         return None
@@ -506,17 +515,18 @@ def main() -> int:
         if not record:
             f.step(strides, target, fused=True)
             return
-        # the same kernels as separate calls: one event pair around the
-        # step's passes (their average is the per-pass duration; an event pair
-        # per launch would add its own gaps) and one around the backward
+        # the same launches as the timed steps: one event pair around the
+        # step's first passes (their average is the per-pass duration; an
+        # event pair per launch would add its own gaps) and one around the
+        # last pass and the backward (one kernel)
         a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         a.record(stream)
-        f.propagate(strides)
+        f.propagate(strides[:-1])
         b.record(stream)
-        f.forward_backward(target)
+        f.step(strides[-1:], target, fused=True)
         c.record(stream)
-        ev.append(("propagate", a, b, len(strides)))
-        ev.append(("render_bwd", b, c, 1))
+        ev.append(("propagate", a, b, len(strides) - 1))
+        ev.append(("step_last", b, c, 1))
 
     for _ in range(args.warmup):
         step(False)
@@ -546,10 +556,19 @@ def main() -> int:
             f.propagate([s_])
             b.record(stream)
             evs.append((s_, a, b))
+        # the backward alone (its own kernel, as sad_render_bwd runs it)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         f.forward_backward(target)
+        b.record(stream)
+        evs.append(("bwd", a, b))
     torch.cuda.synchronize()
+    bwd_alone = []
     for s_, a, b in evs:
-        by_stride[s_].append(a.elapsed_time(b) * 1e3)
+        if s_ == "bwd":
+            bwd_alone.append(a.elapsed_time(b) * 1e3)
+        else:
+            by_stride[s_].append(a.elapsed_time(b) * 1e3)
     # a plain device copy of 256 MiB: the bandwidth this machine's HBM reaches
     src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -601,8 +620,10 @@ def main() -> int:
         "step_frac_of_hbm_roofline": round(ab["step"] / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_us": {k: round(v * 1e6, 3) for k, v in avg.items()},
         "pass_us_by_stride": {str(k): round(float(np.median(v)), 3) for k, v in by_stride.items()},
-        "kernel_timing": f"HIP events on the launch stream over {ev_steps} further steps of separate calls: one pair "
-                         "around the step's passes (per-pass average), one around the backward",
+        "render_bwd_alone_us": round(float(np.median(bwd_alone)), 3),
+        "kernel_timing": f"HIP events on the launch stream over {ev_steps} further steps of the timed launches: one "
+                         "pair around the step's first passes (per-pass average), one around the last pass + backward "
+                         "kernel; per-stride passes and the backward alone (sad_render_bwd) from one pair per launch",
         "roofline": roofline,
         "valu_roofline": valu_roofline(dom, avg[dom]),
     }

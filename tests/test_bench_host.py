@@ -25,6 +25,8 @@ def test_algorithmic_bytes_of_the_step():
     assert ab["propagate"] == 64 * pix
     # four passes of lists, the target, and per site the record read and the gradient read and written
     assert ab["step"] == pix * (64 * 4 + 12) + 50_000 * (48 + 80)
+    # the last pass and the backward in one kernel: lists read and written, the target, 128 B per site
+    assert ab["step_last"] == pix * (64 + 12) + 50_000 * 128
 
 
 def test_counter_summary_matches_the_sources():
@@ -36,7 +38,11 @@ def test_counter_summary_matches_the_sources():
     assert rec["waves_per_dispatch"] == 6144 and rec["valu_insts_per_wave"] > 0
     assert bench.measured_traffic("propagate") == int(rec["bytes"])
     v = bench.valu_roofline("propagate", 25e-6)
-    assert v["bound"] == "alu" and abs(v["peak"] - 39.32) < 0.01 and 0 < v["frac"] < 1
+    # the fp32 vector peak, 157.3 TFLOP/s, in lane-operations (an FMA is two flops)
+    assert v["bound"] == "alu" and abs(v["peak"] - 78.65) < 0.01 and 0 < v["frac"] < 1
+    for kind in ("step_last", "render_bwd"):
+        r = bench.counter_record(kind)
+        assert r is not None and r["waves_per_dispatch"] == 6144 and r["bytes"] > 0
 
 
 def test_profiles_are_short_text():
