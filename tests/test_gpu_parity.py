@@ -1004,8 +1004,9 @@ def test_step_fused_without_sites(sad, ref):
 
 def test_pipeline_step_fused_equals_separate_calls(sad, ref):
     """SadField.step with the fused call and with separate calls give the same
-    lists and score maps, and gradients within the tolerance, over three
-    steps of the 64x64 workload from an empty map."""
+    lists and gradients within the tolerance, over three steps of the 64x64
+    workload from an empty map (the fused step keeps no logits of its last
+    pass, so the next step recomputes them; the lists do not change)."""
     from voronoi_rendering_amd.pipeline import SadField
 
     wl = synth.C1
@@ -1017,7 +1018,7 @@ def test_pipeline_step_fused_equals_separate_calls(sad, ref):
             f.step([4, 2, 1], tgt, fused=fused)
     a, b = fields
     assert torch.equal(a.topk, b.topk)
-    assert torch.equal(a.scores[a.cur], b.scores[b.cur])
+    assert not a.scores_valid and b.scores_valid
     # the same kernels either way; terms that go to float atomics (very large
     # ones) may be summed in another order
     ga, gb = to_np(a.grad).astype(np.float64), to_np(b.grad).astype(np.float64)

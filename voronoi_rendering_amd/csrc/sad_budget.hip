@@ -18,7 +18,9 @@
 // The geometry is float32, one rounding per operation in the written order.
 #include <algorithm>
 
-#include <hipcub/hipcub.hpp>
+#include <rocprim/device/device_radix_sort.hpp>
+#include <rocprim/device/device_select.hpp>
+#include <rocprim/iterator/counting_iterator.hpp>
 
 #include "sad_device.h"
 #include "sad_host.h"
@@ -201,17 +203,22 @@ __global__ __launch_bounds__(256) void k_budget_split(BudgetArgs a) {
     }
 }
 
+// rocPRIM's device radix sort: below its merge-sort limit (the default) it
+// sorts blocks and merges them; a limit of 0 takes its onesweep path (one
+// histogram, then one scatter kernel per 8-bit digit) at every size.
+constexpr size_t SORT_MERGE_LIMIT = 1024 * 1024;
+using SortConfig = rocprim::radix_sort_config<rocprim::default_config, rocprim::default_config,
+                                              rocprim::default_config, SORT_MERGE_LIMIT>;
+
 // Workspace layout for n sites; returns the total bytes (pointers filled when base != nullptr).
 inline size_t budget_layout(int32_t n, char* base, BudgetArgs* a, size_t* cub_bytes) {
     size_t cb_p = 0, cb_s = 0, cb_f = 0;
-    hipcub::CountingInputIterator<uint32_t> ids(0);
-    (void)hipcub::DeviceRadixSort::SortPairs(nullptr, cb_p, (uint32_t*)nullptr, (uint32_t*)nullptr,
-                                             (uint32_t*)nullptr, (uint32_t*)nullptr, n, 0, 32);
-    (void)hipcub::DeviceRadixSort::SortPairs(nullptr, cb_s, (unsigned long long*)nullptr,
-                                             (unsigned long long*)nullptr, (uint32_t*)nullptr, (uint32_t*)nullptr, n,
-                                             0, 64);
-    (void)hipcub::DeviceSelect::Flagged(nullptr, cb_f, ids, (const uint8_t*)nullptr, (uint32_t*)nullptr,
-                                        (int32_t*)nullptr, n);
+    (void)rocprim::radix_sort_pairs<SortConfig>(nullptr, cb_p, (uint32_t*)nullptr, (uint32_t*)nullptr,
+                                                (uint32_t*)nullptr, (uint32_t*)nullptr, (size_t)n, 0, 32);
+    (void)rocprim::radix_sort_pairs<SortConfig>(nullptr, cb_s, (unsigned long long*)nullptr, (unsigned long long*)nullptr,
+                                                (uint32_t*)nullptr, (uint32_t*)nullptr, (size_t)n, 0, 64);
+    (void)rocprim::select(nullptr, cb_f, rocprim::counting_iterator<uint32_t>(0), (const uint8_t*)nullptr,
+                          (uint32_t*)nullptr, (int32_t*)nullptr, (size_t)n);
     const size_t cub = std::max(cb_p, std::max(cb_s, cb_f));
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -297,17 +304,19 @@ extern "C" int sad_densify_prune(float* params, float* adam_m, float* adam_v, fl
     const unsigned g = (unsigned)((n + 255) / 256);
     hipLaunchKernelGGL(k_budget_prune_keys, dim3(g), dim3(256), 0, s, a);
     size_t tb = cub;
-    if (hipcub::DeviceRadixSort::SortPairs(cub_tmp, tb, a.pkey, a.pkey_s, a.pid, a.pid_s, n, 0, 32, s) != hipSuccess)
+    if (rocprim::radix_sort_pairs<SortConfig>(cub_tmp, tb, a.pkey, a.pkey_s, a.pid, a.pid_s, (size_t)n, 0, 32, s) !=
+        hipSuccess)
         return SAD_EHIP;
     if (n_prune > 0)
         hipLaunchKernelGGL(k_budget_prune, dim3((unsigned)((std::min(n_prune, n) + 255) / 256)), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_budget_split_keys, dim3(g), dim3(256), 0, s, a);
     tb = cub;
-    if (hipcub::DeviceRadixSort::SortPairs(cub_tmp, tb, a.skey, a.skey_s, a.sid, a.sid_s, n, 0, 64, s) != hipSuccess)
+    if (rocprim::radix_sort_pairs<SortConfig>(cub_tmp, tb, a.skey, a.skey_s, a.sid, a.sid_s, (size_t)n, 0, 64, s) !=
+        hipSuccess)
         return SAD_EHIP;
     tb = cub;
-    if (hipcub::DeviceSelect::Flagged(cub_tmp, tb, hipcub::CountingInputIterator<uint32_t>(0), a.free_flag, a.slot,
-                                      a.n_free, n, s) != hipSuccess)
+    if (rocprim::select(cub_tmp, tb, rocprim::counting_iterator<uint32_t>(0), a.free_flag, a.slot, a.n_free, (size_t)n,
+                        s) != hipSuccess)
         return SAD_EHIP;
     if (n_split > 0)
         hipLaunchKernelGGL(k_budget_split, dim3((unsigned)((std::min(n_split, n) + 255) / 256)), dim3(256), 0, s, a);

@@ -12,7 +12,7 @@
 // prefix sum above floor(z G / 2^64) for the gradient part), k = 2, 3 the
 // offsets inside the pixel.  A site starts there with the target colour of
 // its pixel, the given log tau, r and log scale (both axes) and angle 0.
-#include <hipcub/hipcub.hpp>
+#include <rocprim/device/device_scan.hpp>
 
 #include "sad_device.h"
 #include "sad_host.h"
@@ -101,7 +101,8 @@ __global__ __launch_bounds__(256) void k_init_sample(InitArgs a) {
 // Workspace: units [pix] u64, cdf [pix] u64, the scan's temporary storage.
 inline size_t init_layout(int64_t pix, char* base, uint64_t** units, uint64_t** cdf, void** tmp, size_t* tmp_bytes) {
     size_t tb = 0;
-    (void)hipcub::DeviceScan::InclusiveSum(nullptr, tb, (const uint64_t*)nullptr, (uint64_t*)nullptr, (int)pix);
+    (void)rocprim::inclusive_scan(nullptr, tb, (const uint64_t*)nullptr, (uint64_t*)nullptr, (size_t)pix,
+                                  rocprim::plus<uint64_t>());
     size_t off = 0;
     auto take = [&](size_t bytes) {
         char* p = base ? base + off : nullptr;
@@ -151,7 +152,8 @@ extern "C" int sad_init_sites(const float* target, int32_t h, int32_t w, int32_t
     clear_error();
     hipLaunchKernelGGL(k_init_units, dim3((unsigned)((w + INIT_BX - 1) / INIT_BX), (unsigned)((h + INIT_BY - 1) / INIT_BY)),
                        dim3(INIT_BX * INIT_BY), 0, s, target, h, w, units);
-    if (hipcub::DeviceScan::InclusiveSum(tmp, tb, units, cdf, (int)pix, s) != hipSuccess) return SAD_EHIP;
+    if (rocprim::inclusive_scan(tmp, tb, units, cdf, (size_t)pix, rocprim::plus<uint64_t>(), s) != hipSuccess)
+        return SAD_EHIP;
     InitArgs a;
     a.target = target;
     a.cdf = cdf;

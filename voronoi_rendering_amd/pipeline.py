@@ -155,13 +155,15 @@ class SadField:
             self.forward_backward(target)
             return
         self.propagate(strides[:-1])
+        # The last pass's logits are not kept: a training iteration rewrites the
+        # sites next, so the following pass recomputes them anyway.
         ops.step_fused(self.derived, self.h, self.w, self.maps[self.cur], self.maps[1 - self.cur], target, self.grad,
                        stride=int(strides[-1]), seed=self.seed, pass_index=self.pass_index, inject=self.inject,
-                       prev_scores=self.scores[self.cur] if self.scores_valid else None,
-                       out_scores=self.scores[1 - self.cur], loss=self.loss)
+                       prev_scores=self.scores[self.cur] if self.scores_valid else None, out_scores=None,
+                       loss=self.loss)
         self.cur = 1 - self.cur
         self.pass_index += 1
-        self.scores_valid = True
+        self.scores_valid = False
 
     def adam_step(self) -> None:
         self.adam_t += 1
