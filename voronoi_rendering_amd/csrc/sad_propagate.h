@@ -78,6 +78,47 @@ __device__ __forceinline__ bool probe_may_enter(const Geo& g, float thr, float b
     return !boundable | !(ub < thr);  // values of an unboundable site are not used
 }
 
+// A cheap screen in front of the exact logit of a queued neighbour id: false
+// only when the float32 logit `logit(g, px, py)` of the site is certainly
+// below ts, the logit of the list's 8th entry, so that the site cannot rank
+// before that entry; true for an inactive-site test that passes and for
+// anything non-finite.  On a settled map almost every queued id is such a
+// clear loser, and the screen costs about half of the exact evaluation (no
+// correctly rounded square root, fused multiply-adds).
+//
+// It evaluates l' = tau (r - s') with a' = fma(dx, cos, dy sin) / s1,
+// b' = fma(dy, cos, -(dx sin)) / s2, q' = fma(a', a', b'^2) and s' the
+// hardware square root of q' (within 1 ulp of the correctly rounded one for
+// normal q'), and passes unless l' + M < ts for
+//     M = tau (2^-20 (T + 2 (s' + |r|)) + 2^-60),  T = (|dx| + |dy|)(1/s1 + 1/s2).
+// Why M bounds |l - l'|, with u = 2^-24, D = |dx| + |dy| and (A, B) the
+// rotated, scaled offset in real arithmetic on the same float32 inputs
+// (|cos|, |sin| <= 1): both evaluations form a and b within (2u + u^2) D / s_i
+// + u |a| (resp. |b|) of A and B, so the two vectors (a, b) lie within
+// 2.01 u T + 1.42 u |(a, b)| of (A, B); the squares and their sum scale the
+// squared norm by at most 1 + 2u + u^2, i.e. the root by 1 + 1.01 u; the
+// correctly rounded root adds u sqrt(q), the hardware one 2u sqrt(q'), so the
+// two roots differ by at most 4.02 u T + 8.5 u S (S the larger root).  The
+// subtraction of r adds u |d| + u |d'| <= 2u (S + |r|)(1 + u), and the product
+// with tau one rounding u |l| <= u tau (S + |r|)(1 + u) on each side, so
+// |l - l'| <= tau u (4.02 T + 12.6 S + 4.1 |r|), which M (16 u T + 32 u s'
+// + 32 u |r|) exceeds with room for the roundings of M and of l' + M (a
+// rounded sum below the float ts implies the exact sum below it).  The last
+// term of M covers roots of subnormal q, where the hardware root is only
+// absolutely close (sqrt of 2^-126 is 2^-63).
+__device__ __forceinline__ bool may_rank_before(const Geo& g, float px, float py, float ts) {
+    const float dx = px - g.g0.x, dy = py - g.g0.y;
+    const float a = __builtin_fmaf(dx, g.g1.x, dy * g.g1.y) * g.g1.z;
+    const float b = __builtin_fmaf(dy, g.g1.x, -(dx * g.g1.y)) * g.g1.w;
+    const float q = __builtin_fmaf(a, a, b * b);
+    const float s = __builtin_amdgcn_sqrtf(q);
+    const float tau = g.g0.z, r = g.g0.w;
+    const float l = tau * (r - s);
+    const float T = (fabsf(dx) + fabsf(dy)) * (g.g1.z + g.g1.w);
+    const float M = tau * __builtin_fmaf(0x1p-20f, __builtin_fmaf(2.0f, s + fabsf(r), T), 0x1p-60f);
+    return (g.g0.x >= 0.0f) & !(l + M < ts);
+}
+
 // compare-exchange for the sorting network: entry i ends up ranking before j
 __device__ __forceinline__ void cex(TopK& t, int i, int j) {
     bool sw = ranks_before(t.s[j], t.id[j], t.s[i], t.id[i]);
@@ -296,6 +337,8 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
         // not divide QCAP): its rows are clamped for the read (the value is
         // then not used) and its slots past cnt write nothing, so that a
         // column whose every id passes is not written past its end.
+        // Each batch is first screened (may_rank_before); the exact logits
+        // are evaluated only when some lane holds an id the screen lets pass.
         const float ts = t.s[K - 1];
         const uint32_t ti = t.id[K - 1];
         int ns = 0;
@@ -307,15 +350,23 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
             Geo qg[QBATCH];
 #pragma unroll
             for (int b = 0; b < QBATCH; ++b) qg[b] = load_geo_clamped(a.derived, n, v[b]);
+            bool maybe[QBATCH], any_maybe = false;
 #pragma unroll
             for (int b = 0; b < QBATCH; ++b) {
-                const float sc = usable_logit(qg[b], v[b] < n, px, py);
-                const bool pass = (sc == sc) & ranks_before(sc, v[b], ts, ti);  // false past cnt
-                if (it + b < cnt) {  // then ns <= it + b < cnt <= QCAP
-                    queue[ns][lane] = (QueueId<SMALL_IDS>)v[b];  // a passing id is < n
-                    qscore[ns][lane] = sc;
+                maybe[b] = (it + b < cnt) & may_rank_before(qg[b], px, py, ts);  // queued ids are < n
+                any_maybe |= maybe[b];
+            }
+            if (__any(any_maybe)) {
+#pragma unroll
+                for (int b = 0; b < QBATCH; ++b) {
+                    const float sc = usable_logit(qg[b], v[b] < n, px, py);
+                    const bool pass = maybe[b] & (sc == sc) & ranks_before(sc, v[b], ts, ti);  // false past cnt
+                    if (it + b < cnt) {  // then ns <= it + b < cnt <= QCAP
+                        queue[ns][lane] = (QueueId<SMALL_IDS>)v[b];  // a passing id is < n
+                        qscore[ns][lane] = sc;
+                    }
+                    ns += pass ? 1 : 0;
                 }
-                ns += pass ? 1 : 0;
             }
         }
         // insert the survivors
