@@ -141,6 +141,36 @@ def test_propagate_full_neighbour_queue(sad, ref, n):
         assert np.array_equal(got, want), f"stride {stride}: {np.argwhere(got != want)[:5]}"
 
 
+@pytest.mark.parametrize("n", [1500, 70000])
+def test_propagate_extreme_sites(sad, ref, n):
+    """Sites far outside the workloads' ranges, where the screen of queued
+    ids (an approximate logit and an error bound) has the least room: scales
+    from e^-6 to e^8 px per axis (anisotropy up to e^14), tau from e^-6 to
+    e^6, r from -5 to 20, a tenth of the sites a thousand image widths away,
+    some at the pixel centres.  Eight passes from the oracle's warm map, each
+    bit for bit; both id widths."""
+    h, w = 60, 90
+    rec = synth.SiteRecipe(ls_lo=-6.0, ls_hi=8.0, r_lo=-5.0, r_hi=20.0, logtau_lo=-6.0, logtau_hi=6.0)
+    p = synth.sites(4242 + n, n, h, w, rec)
+    rng = np.random.default_rng(n)
+    far = rng.random(n) < 0.1
+    p[far, 0] *= np.float32(1000.0)
+    p[far, 1] *= np.float32(1000.0)
+    centred = rng.random(n) < 0.05
+    p[centred, 0] = np.floor(p[centred, 0] % w) + np.float32(0.5)
+    p[centred, 1] = np.floor(p[centred, 1] % h) + np.float32(0.5)
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p))
+    m = ref.propagate_schedule(d, h, w, None, synth.jfa_strides(h, w, 12), 31, 0, 64)
+    cur = to_gpu(m)
+    for t, stride in enumerate((8, 4, 2, 1, 1, 3, 2, 1)):
+        want = ref.propagate(d, h, w, m, stride, 31, 12 + t, 64)
+        got_t = sad.propagate_topk(dg, h, w, cur, stride=stride, seed=31, pass_index=12 + t, inject=64)
+        got = map_to_np(got_t)
+        assert np.array_equal(got, want), f"pass {t} stride {stride}: {np.argwhere(got != want)[:5]}"
+        m, cur = want, got_t
+
+
 @pytest.mark.parametrize("n", [65535, 65536])
 def test_propagate_at_the_16_bit_id_boundary(sad, ref, n):
     """Site counts on both sides of the packed 16-bit membership test, with
