@@ -12,12 +12,14 @@ resident in GPU memory when the timed region starts.
 
 The first pass of each step recomputes the logits of the pixels' previous
 lists (as after an Adam update); the following passes reuse the logits the
-previous pass wrote.
+previous pass wrote.  The passes before the last hand their lists on with
+16-bit ids (every id of the 50,000 fits), the last pass writes 32-bit ids.
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events in up to 50
-further steps made of separate calls (the same kernels as the fused call), on
-the stream the kernels run on (torch's current stream): one event pair around
-a step's passes, one around its backward.
+further steps made of the same launches, on the stream the kernels run on
+(torch's current stream): one event pair around a step's first passes, one
+around its last pass + backward kernel.  The per-stride figures time single
+passes on 32-bit maps, and the standalone backward, one event pair each.
 """
 from __future__ import annotations
 
@@ -521,9 +523,7 @@ def main() -> int:
         # last pass and the backward (one kernel)
         a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         a.record(stream)
-        f.propagate(strides[:-1])
-        b.record(stream)
-        f.step(strides[-1:], target, fused=True)
+        f.step(strides, target, fused=True, before_last=lambda: b.record(stream))
         c.record(stream)
         ev.append(("propagate", a, b, len(strides) - 1))
         ev.append(("step_last", b, c, 1))
@@ -623,7 +623,8 @@ def main() -> int:
         "render_bwd_alone_us": round(float(np.median(bwd_alone)), 3),
         "kernel_timing": f"HIP events on the launch stream over {ev_steps} further steps of the timed launches: one "
                          "pair around the step's first passes (per-pass average), one around the last pass + backward "
-                         "kernel; per-stride passes and the backward alone (sad_render_bwd) from one pair per launch",
+                         "kernel; per-stride passes (32-bit maps) and the backward alone (sad_render_bwd) from one pair "
+                         "per launch",
         "roofline": roofline,
         "valu_roofline": valu_roofline(dom, avg[dom]),
     }

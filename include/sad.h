@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 7
+#define SAD_ABI_VERSION 8
 #define SAD_K 8
 #define SAD_SITE_STRIDE 12
 #define SAD_EMPTY 0xffffffffu
@@ -140,6 +140,27 @@ int sad_prepare_sites(const float *params, int32_t n, float *derived, void *stre
 int sad_propagate_topk(const float *derived, int32_t n, int32_t h, int32_t w, const uint32_t *topk_prev,
                        const float *scores_prev, uint32_t *topk_next, float *scores_next, int32_t stride,
                        uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, void *stream);
+
+/*
+ * sad_propagate_topk with a choice of id width for each map (the same pass of
+ * Sec. 4.3): prev_bits and next_bits are 16 or 32, the width of topk_prev's
+ * and topk_next's ids.  A map of width 16 is [h][w][8] uint16 (16 bytes per
+ * pixel) with the empty slot 0xffff; it needs n <= 65535 (SAD_EUNSUPPORTED
+ * otherwise), so that every usable id is below 0xffff.  The lists are those
+ * sad_propagate_topk writes, id for id (0xffff where it writes 0xffffffff), and
+ * an input id at or above n is dropped as there.  Within a training step the
+ * passes can hand their lists on at width 16, beside their score maps: a pass
+ * then moves 48 instead of 64 bytes per pixel each way.
+ *   topk_prev    NULL, or a map of width prev_bits (16-byte aligned)
+ *   topk_next    a map of width next_bits, written
+ *   prev_bits, next_bits  16 or 32 (SAD_EINVAL otherwise)
+ * Other arguments and checks as sad_propagate_topk (overlaps are checked on
+ * each map's own size).
+ */
+int sad_propagate_topk_widths(const float *derived, int32_t n, int32_t h, int32_t w, const void *topk_prev,
+                              int32_t prev_bits, const float *scores_prev, void *topk_next, int32_t next_bits,
+                              float *scores_next, int32_t stride, uint64_t seed, uint32_t pass_index,
+                              int32_t inject_per_tile, void *stream);
 
 /*
  * Soft additively weighted render (Sec. 4.2): per pixel, the softmax of the
@@ -370,6 +391,17 @@ int sad_step_fused(const float *derived, int32_t n, int32_t h, int32_t w, const 
                    const float *scores_prev, uint32_t *topk_next, float *scores_next, int32_t stride, uint64_t seed,
                    uint32_t pass_index, int32_t inject_per_tile, const float *target, float *grad, float *loss,
                    float *image, void *stream);
+
+/*
+ * sad_step_fused reading a previous map of width prev_bits (16 or 32, as
+ * sad_propagate_topk_widths; width 16 needs n <= 65535): the last pass of a
+ * step whose earlier passes handed their lists on at width 16.  topk_next is
+ * written with 32-bit ids, as sad_step_fused writes it.
+ */
+int sad_step_fused_widths(const float *derived, int32_t n, int32_t h, int32_t w, const void *topk_prev,
+                          int32_t prev_bits, const float *scores_prev, uint32_t *topk_next, float *scores_next,
+                          int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject_per_tile,
+                          const float *target, float *grad, float *loss, float *image, void *stream);
 
 /*
  * One Adam step (Kingma & Ba) on the site parameters (Sec. 5: per-parameter

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
                  "sad_site_stats_workspace_bytes", "sad_step_fused", "sad_site_stats", "sad_jfa_seed",
                  "sad_jfa_flood", "sad_budget_workspace_bytes", "sad_densify_prune", "sad_init_workspace_bytes",
                  "sad_init_sites", "sad_pack_sites", "sad_query_packed",
-                 "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version"):
+                 "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version",
+                 "sad_propagate_topk_widths", "sad_step_fused_widths"):
         assert name in syms
 
 
@@ -43,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sad_abi_version() == 7
+    assert lib.sad_abi_version() == 8
     for st in (0, -1, -2, -3, 7):
         assert lib.sad_status_string(st)
 
@@ -87,6 +88,35 @@ def test_propagate_rejects(lib):
     assert call(snext=P + 4096) == EINVAL  # the two outputs alias
     assert call(snext=P + 65540) == EINVAL  # misaligned scores
     assert call(h=0, nxt=None) == 0  # empty image
+
+
+def test_propagate_widths_rejects(lib):
+    """The id-width variant: widths other than 16 and 32, 16-bit maps with
+    more than 65,535 sites, and overlaps measured on each map's own size (a
+    16-bit map of 8x8 pixels is 1 KiB)."""
+    f = lib.sad_propagate_topk_widths
+    ok = dict(derived=P, n=10, h=8, w=8, prev=P + 65536, pb=16, sprev=None, nxt=P + 4096, nb=16, snext=None, stride=1,
+              seed=0, pi=0, inj=64)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["derived"], a["n"], a["h"], a["w"], a["prev"], a["pb"], a["sprev"], a["nxt"], a["nb"], a["snext"],
+                 a["stride"], a["seed"], a["pi"], a["inj"], None)
+
+    assert call(pb=8) == EINVAL
+    assert call(nb=64) == EINVAL
+    assert call(pb=0, prev=None) == EINVAL  # the width is checked even without a previous map
+    assert call(n=65536) == EUNSUP  # 16-bit ids need n <= 65535
+    assert call(n=65536, nb=32) == EUNSUP
+    assert call(prev=P + 4096 + 1008) == EINVAL  # 16-bit maps overlap in their last 16 bytes
+    assert call(nxt=P + 4100) == EINVAL  # misaligned
+    assert call(sprev=P + 8192, snext=P + 8192 + 2032) == EINVAL  # score maps overlap (2 KiB each)
+    assert call(snext=P + 4096 + 512) == EINVAL  # next scores inside the next map
+    g = lib.sad_step_fused_widths
+    G, T = P + (1 << 20), P + (2 << 20)  # grad and target, apart from everything
+    assert g(P, 65536, 8, 8, P + 65536, 16, None, P + 4096, None, 1, 0, 0, 64, T, G, None, None, None) == EUNSUP
+    assert g(P, 10, 8, 8, P + 65536, 24, None, P + 4096, None, 1, 0, 0, 64, T, G, None, None, None) == EINVAL
+    assert g(P, 10, 8, 8, P + 65536, 16, None, P + 4096, None, 1, 0, 0, 64, T, None, None, None, None) == EINVAL
 
 
 def test_render_query_adam_reject(lib):

@@ -1055,6 +1055,86 @@ def test_pipeline_step_fused_equals_separate_calls(sad, ref):
     assert np.all(np.abs(ga - gb) <= 1e-5 * np.abs(gb) + 1e-6 * np.abs(gb).max(axis=0))
 
 
+def map16_to_np(t: torch.Tensor) -> np.ndarray:
+    """A 16-bit-id map read back as 32-bit ids (0xffff -> 0xffffffff)."""
+    m = t.cpu().numpy().view(np.uint16).astype(np.uint32)
+    m[m == 0xFFFF] = 0xFFFFFFFF
+    return m
+
+
+def map16_from_np(m: np.ndarray) -> torch.Tensor:
+    """32-bit ids (all below 0xffff or 0xffffffff) as a 16-bit-id map on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(m.astype(np.uint16)).view(np.int16)).to(dev())
+
+
+@pytest.mark.parametrize("h,w,n", [(64, 64, 256), (13, 29, 300), (67, 72, 1000), (37, 70, 65535)])
+def test_propagate_16bit_maps(sad, ref, h, w, n):
+    """Passes that read and write 16-bit-id maps (every combination of the two
+    widths, with and without score maps) give the oracle's lists, id for id,
+    and the same score maps as the 32-bit passes; from an empty map, through
+    the warm-up schedule and a step's strides, up to the 16-bit limit of
+    65,535 sites (the last id 65,534 next to the empty slot 0xffff)."""
+    p = synth.sites(300 + n, n, h, w)
+    if n >= 10:
+        p[3, 0] = -1.0  # an inactive site
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p))
+    strides = list(synth.jfa_strides(h, w, 6)) + [8, 4, 2, 1, 1]
+    m = None
+    prev32 = prev16 = None
+    sc_prev = None
+    for t, s_ in enumerate(strides):
+        want = ref.propagate(d, h, w, m, s_, 17, t, 64)
+        out16 = torch.empty((h, w, 8), dtype=torch.int16, device=dev())
+        out32 = torch.empty((h, w, 8), dtype=torch.int32, device=dev())
+        sc16 = torch.empty((h, w, 8), dtype=torch.float32, device=dev())
+        sc32 = torch.empty((h, w, 8), dtype=torch.float32, device=dev())
+        # 16 -> 16 (or empty -> 16) with score maps; 16 -> 32 without; 32 -> 16 with the 32-bit scores
+        sad.propagate_topk(dg, h, w, prev16, out16, stride=s_, seed=17, pass_index=t, inject=64,
+                           prev_scores=sc_prev, out_scores=sc16)
+        sad.propagate_topk(dg, h, w, prev16, out32, stride=s_, seed=17, pass_index=t, inject=64)
+        got16, got32 = map16_to_np(out16), map_to_np(out32)
+        assert np.array_equal(got16, want), f"pass {t} 16->16: {np.argwhere(got16 != want)[:4]}"
+        assert np.array_equal(got32, want), f"pass {t} 16->32"
+        if prev32 is not None:
+            o = torch.empty((h, w, 8), dtype=torch.int16, device=dev())
+            sad.propagate_topk(dg, h, w, prev32, o, stride=s_, seed=17, pass_index=t, inject=64,
+                               out_scores=sc32)
+            assert np.array_equal(map16_to_np(o), want), f"pass {t} 32->16"
+            assert np.array_equal(to_np(sc32).view(np.uint32), to_np(sc16).view(np.uint32)), f"pass {t} scores"
+        m, prev16, prev32, sc_prev = want, out16, out32, sc16
+
+
+def test_step_fused_from_16bit_map(sad, ref, c2_state):
+    """The fused last pass + backward reading a 16-bit-id map (and its score
+    map) on the 768x512 map: the oracle's lists, loss and gradients, and the
+    same lists, image and score map as the call that reads the 32-bit map."""
+    wl, p, d, dg, m_ref, m_gpu = c2_state
+    h, w = wl.h, wl.w
+    tgt = wl.make_target()
+    prev16 = map16_from_np(m_ref)
+    assert np.array_equal(map16_to_np(prev16), m_ref)
+    m1 = ref.propagate(d, h, w, m_ref, 1, wl.inject_seed, 702, wl.inject)
+    g_ref, _, loss_ref, img_ref = ref.render_bwd(d, h, w, m1, tgt)
+    res = []
+    for prev in (prev16, m_gpu):
+        out = torch.empty((h, w, 8), dtype=torch.int32, device=dev())
+        osc = torch.empty((h, w, 8), dtype=torch.float32, device=dev())
+        grad = torch.zeros((wl.n, 12), dtype=torch.float32, device=dev())
+        loss = torch.zeros(1, dtype=torch.float32, device=dev())
+        img = torch.empty((h, w, 3), dtype=torch.float32, device=dev())
+        sad.step_fused(dg, h, w, prev, out, to_gpu(tgt), grad, stride=1, seed=wl.inject_seed, pass_index=702,
+                       inject=wl.inject, out_scores=osc, loss=loss, image=img)
+        res.append((map_to_np(out), to_np(osc), to_np(grad), loss.item(), to_np(img)))
+    (l16, s16, g16, loss16, i16), (l32, s32, _, _, i32) = res
+    assert np.array_equal(l16, m1) and np.array_equal(l16, l32)
+    assert np.array_equal(s16.view(np.uint32), s32.view(np.uint32))
+    assert np.array_equal(i16.view(np.uint32), i32.view(np.uint32))
+    assert_colour_close(i16, img_ref, "fused from 16-bit image")
+    assert abs(loss16 - loss_ref) <= 1e-5 * loss_ref
+    assert_grad_close(g16, g_ref, "fused from 16-bit gradients")
+
+
 # ---------------------------------------------------------------- Adam
 
 def test_adam_bit_exact(sad, ref):

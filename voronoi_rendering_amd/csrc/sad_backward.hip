@@ -523,7 +523,7 @@ struct PassLds {
 // starts from them in the same LDS: no list is read back and no logit of the
 // forward is evaluated again, and regions start their backward while others
 // still run their pass.
-template <bool SMALL_IDS>
+template <bool SMALL_IDS, bool PREV16>
 __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(SMALL_IDS ? 6 : 1)))
 void k_step_last(PropArgs pa, BwdArgs a) {
     __shared__ union {
@@ -538,7 +538,8 @@ void k_step_last(PropArgs pa, BwdArgs a) {
     TopK t;
     t.clear();
     if (tx < pa.tiles_x && ty * pa.tiles_x + tx < pa.n_tiles)  // uniform per wavefront
-        propagate_tile<SMALL_IDS>(pa, ty * pa.tiles_x + tx, lds.pass.queue[wv], lds.pass.qscore[wv], t);
+        propagate_tile<SMALL_IDS, PREV16, false>(pa, ty * pa.tiles_x + tx, lds.pass.queue[wv], lds.pass.qscore[wv],
+                                                 t);
     int i, j;
     region_pixel(rx, ry, wv, lane, i, j);  // the pixel the pass just listed
     float tg[3] = {0.f, 0.f, 0.f};
@@ -631,13 +632,15 @@ extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_
     return bwd_launch(b, stream);
 }
 
-extern "C" int sad_step_fused(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk_prev,
-                              const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride,
-                              uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, const float* target,
-                              float* grad, float* loss, float* image, void* stream) {
+// Checks and launch of the fused last pass + backward (prev_bits: the id
+// width of topk_prev; the new lists are written with 32-bit ids).
+static int step_fused(const float* derived, int32_t n, int32_t h, int32_t w, const void* topk_prev, int32_t prev_bits,
+                      const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride, uint64_t seed,
+                      uint32_t pass_index, int32_t inject_per_tile, const float* target, float* grad, float* loss,
+                      float* image, void* stream) {
     PropArgs pa;
-    int st = prop_setup(derived, n, h, w, topk_prev, scores_prev, topk_next, scores_next, stride, seed, pass_index,
-                        inject_per_tile, pa);
+    int st = prop_setup(derived, n, h, w, topk_prev, prev_bits, scores_prev, topk_next, 32, scores_next, stride, seed,
+                        pass_index, inject_per_tile, pa);
     if (st != SAD_OK) return st;
     BwdArgs b;
     st = bwd_setup(derived, n, h, w, topk_next, target, grad, loss, image, b);
@@ -653,10 +656,30 @@ extern "C" int sad_step_fused(const float* derived, int32_t n, int32_t h, int32_
     if (pix == 0) return SAD_OK;
     // every check has passed: one kernel, one workgroup per backward region
     const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
+    const hipStream_t s = as_stream(stream);
     clear_error();
-    if (pa.n <= SMALL_IDS_MAX)
-        hipLaunchKernelGGL(k_step_last<true>, dim3((unsigned)nreg), dim3(BWD_THREADS), 0, as_stream(stream), pa, b);
+    if (pa.n > SMALL_IDS_MAX)
+        hipLaunchKernelGGL((k_step_last<false, false>), dim3((unsigned)nreg), dim3(BWD_THREADS), 0, s, pa, b);
+    else if (pa.prev16)
+        hipLaunchKernelGGL((k_step_last<true, true>), dim3((unsigned)nreg), dim3(BWD_THREADS), 0, s, pa, b);
     else
-        hipLaunchKernelGGL(k_step_last<false>, dim3((unsigned)nreg), dim3(BWD_THREADS), 0, as_stream(stream), pa, b);
+        hipLaunchKernelGGL((k_step_last<true, false>), dim3((unsigned)nreg), dim3(BWD_THREADS), 0, s, pa, b);
     return launch_status();
+}
+
+extern "C" int sad_step_fused(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk_prev,
+                              const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride,
+                              uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, const float* target,
+                              float* grad, float* loss, float* image, void* stream) {
+    return step_fused(derived, n, h, w, topk_prev, 32, scores_prev, topk_next, scores_next, stride, seed, pass_index,
+                      inject_per_tile, target, grad, loss, image, stream);
+}
+
+extern "C" int sad_step_fused_widths(const float* derived, int32_t n, int32_t h, int32_t w, const void* topk_prev,
+                                     int32_t prev_bits, const float* scores_prev, uint32_t* topk_next,
+                                     float* scores_next, int32_t stride, uint64_t seed, uint32_t pass_index,
+                                     int32_t inject_per_tile, const float* target, float* grad, float* loss,
+                                     float* image, void* stream) {
+    return step_fused(derived, n, h, w, topk_prev, prev_bits, scores_prev, topk_next, scores_next, stride, seed,
+                      pass_index, inject_per_tile, target, grad, loss, image, stream);
 }

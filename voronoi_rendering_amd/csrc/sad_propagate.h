@@ -38,9 +38,11 @@ namespace sad {
 
 struct PropArgs {
     const float* derived;
-    const uint32_t* prev;
+    const uint32_t* prev;      // the previous map with 32-bit ids, or
+    const uint16_t* prev16;    // with 16-bit ids (at most one of the two; neither: an empty map)
     const float* prev_scores;  // nullable: logits of prev's entries under derived
-    uint32_t* next;
+    uint32_t* next;            // the next map with 32-bit ids, or
+    uint16_t* next16;          // with 16-bit ids (exactly one of the two)
     float* next_scores;        // nullable: logits of next's entries are written here
     uint64_t seed;
     int32_t n, h, w, stride, inject, tiles_x, n_tiles;
@@ -185,9 +187,15 @@ using QueueId = std::conditional_t<SMALL_IDS, uint16_t, uint32_t>;
 // workgroup barrier inside.  SMALL_IDS requires a.n <= SMALL_IDS_MAX; the
 // neighbour lists are then held as packed 16-bit pairs and queued as 16-bit
 // ids, which leaves registers and LDS for more wavefronts per compute unit.
-template <bool SMALL_IDS>
+// PREV16 / NEXT16 (SMALL_IDS only): the previous / next map holds 16-bit ids
+// (a.prev16 / a.next16, 16 bytes per pixel, the empty slot 0xffff).  A
+// 16-bit list is read as the packed pairs the neighbour lists use anyway,
+// and its 0xffff slots, being >= n, are dropped like any unusable id.
+template <bool SMALL_IDS, bool PREV16 = false, bool NEXT16 = false>
 __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, QueueId<SMALL_IDS> (*queue)[WAVE],
                                                float (*qscore)[WAVE], TopK& t) {
+    static_assert(SMALL_IDS || !(PREV16 || NEXT16), "16-bit maps hold 16-bit ids");
+    const bool has_prev = PREV16 ? a.prev16 != nullptr : a.prev != nullptr;  // uniform
     constexpr int NW = SMALL_IDS ? K / 2 : K;  // registers per neighbour list
     const int lane = threadIdx.x & (WAVE - 1);
     const int tx = tile % a.tiles_x, ty = tile / a.tiles_x;
@@ -196,7 +204,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
     const bool inside = (i < a.w) & (j < a.h);
     const float px = (float)i + 0.5f, py = (float)j + 0.5f;
     const uint32_t n = (uint32_t)a.n;
-    const bool have_prev = inside && a.prev;
+    const bool have_prev = inside && has_prev;
 
     // Issue every independent load first: the pixel's list, the 4 neighbour
     // lists and this lane's probe site.  Every list load reads a pixel inside
@@ -207,12 +215,22 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
     uint32_t nbr[4][NW];  // ids, or pack16 pairs of ids
     bool nb_ok[4];
     const int nb[4][2] = {{a.stride, 0}, {-a.stride, 0}, {0, a.stride}, {0, -a.stride}};
-    if (a.prev) {  // uniform
+    if (has_prev) {  // uniform
         const size_t pc = (size_t)min(j, a.h - 1) * a.w + min(i, a.w - 1);
-        const uint4* l = reinterpret_cast<const uint4*>(a.prev + pc * K);
-        const uint4 l0 = l[0], l1 = l[1];
-        own[0] = l0.x; own[1] = l0.y; own[2] = l0.z; own[3] = l0.w;
-        own[4] = l1.x; own[5] = l1.y; own[6] = l1.z; own[7] = l1.w;
+        if constexpr (PREV16) {
+            const uint4 l = *reinterpret_cast<const uint4*>(a.prev16 + pc * K);
+            const uint32_t pr[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+            for (int k = 0; k < K / 2; ++k) {
+                own[2 * k] = pr[k] & 0xFFFFu;
+                own[2 * k + 1] = pr[k] >> 16;
+            }
+        } else {
+            const uint4* l = reinterpret_cast<const uint4*>(a.prev + pc * K);
+            const uint4 l0 = l[0], l1 = l[1];
+            own[0] = l0.x; own[1] = l0.y; own[2] = l0.z; own[3] = l0.w;
+            own[4] = l1.x; own[5] = l1.y; own[6] = l1.z; own[7] = l1.w;
+        }
         if (a.prev_scores) {
             const float4* ls = reinterpret_cast<const float4*>(a.prev_scores + pc * K);
             const float4 s0 = ls[0], s1 = ls[1];
@@ -224,6 +242,11 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
             const int ii = i + nb[q][0], jj = j + nb[q][1];
             nb_ok[q] = inside & (ii >= 0) & (ii < a.w) & (jj >= 0) & (jj < a.h);
             const size_t pq = (size_t)min(max(jj, 0), a.h - 1) * a.w + min(max(ii, 0), a.w - 1);
+            if constexpr (PREV16) {
+                const uint4 m = *reinterpret_cast<const uint4*>(a.prev16 + pq * K);
+                nbr[q][0] = m.x; nbr[q][1] = m.y; nbr[q][2] = m.z; nbr[q][3] = m.w;
+                continue;
+            }
             const uint4* m = reinterpret_cast<const uint4*>(a.prev + pq * K);
             const uint4 m0 = m[0], m1 = m[1];
             if constexpr (SMALL_IDS) {
@@ -414,9 +437,16 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
     }
 
     if (inside) {
-        uint4* o = reinterpret_cast<uint4*>(a.next + ((size_t)j * a.w + i) * K);
-        o[0] = make_uint4(t.id[0], t.id[1], t.id[2], t.id[3]);
-        o[1] = make_uint4(t.id[4], t.id[5], t.id[6], t.id[7]);
+        if constexpr (NEXT16) {
+            // ids < n <= 0xFFFF keep their value; EMPTY saturates to 0xffff
+            *reinterpret_cast<uint4*>(a.next16 + ((size_t)j * a.w + i) * K) =
+                make_uint4(pack16(t.id[0], t.id[1]), pack16(t.id[2], t.id[3]), pack16(t.id[4], t.id[5]),
+                           pack16(t.id[6], t.id[7]));
+        } else {
+            uint4* o = reinterpret_cast<uint4*>(a.next + ((size_t)j * a.w + i) * K);
+            o[0] = make_uint4(t.id[0], t.id[1], t.id[2], t.id[3]);
+            o[1] = make_uint4(t.id[4], t.id[5], t.id[6], t.id[7]);
+        }
         if (a.next_scores) {
             float4* os = reinterpret_cast<float4*>(a.next_scores + ((size_t)j * a.w + i) * K);
             os[0] = make_float4(t.s[0], t.s[1], t.s[2], t.s[3]);
@@ -428,31 +458,39 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
 // Argument checks of a propagation pass (shared by the entry points that run
 // one) and its kernel arguments.  Returns SAD_OK with a filled in, or the
 // error status.
-inline int prop_setup(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk_prev,
-                      const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride,
-                      uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, PropArgs& a) {
+inline int prop_setup(const float* derived, int32_t n, int32_t h, int32_t w, const void* topk_prev,
+                      int32_t prev_bits, const float* scores_prev, void* topk_next, int32_t next_bits,
+                      float* scores_next, int32_t stride, uint64_t seed, uint32_t pass_index,
+                      int32_t inject_per_tile, PropArgs& a) {
     if (!sites_ok(n) || !image_ok(h, w) || stride < 1 || inject_per_tile < 0) return SAD_EINVAL;
+    if ((prev_bits != 16 && prev_bits != 32) || (next_bits != 16 && next_bits != 32)) return SAD_EINVAL;
     if (inject_per_tile > SAD_MAX_INJECT) return SAD_EUNSUPPORTED;
+    // a 16-bit map needs every usable id below 0xffff, its empty slot
+    if ((prev_bits == 16 || next_bits == 16) && n > SMALL_IDS_MAX) return SAD_EUNSUPPORTED;
     const int64_t pix = int64_t(h) * w;
-    const int64_t mbytes = pix * K * 4;
+    const int64_t pbytes = pix * K * (prev_bits / 8), nbytes = pix * K * (next_bits / 8), sbytes = pix * K * 4;
     if (!array_ok(derived, n, 16) || !array_ok(topk_next, pix, 16)) return SAD_EINVAL;
     if ((topk_prev && !aligned(topk_prev, 16)) || (scores_prev && !aligned(scores_prev, 16)) ||
         (scores_next && !aligned(scores_next, 16)))
         return SAD_EINVAL;
     if (scores_prev && !topk_prev) return SAD_EINVAL;
     const void* outs[2] = {topk_next, scores_next};
+    const int64_t obytes[2] = {nbytes, sbytes};
     const void* ins[2] = {topk_prev, scores_prev};
+    const int64_t ibytes[2] = {pbytes, sbytes};
     for (int o = 0; o < 2; ++o)
         for (int q = 0; q < 2; ++q)
-            if (overlap(outs[o], mbytes, ins[q], mbytes)) return SAD_EINVAL;
-    if (overlap(topk_next, mbytes, scores_next, mbytes) || overlap(topk_prev, mbytes, scores_prev, mbytes))
+            if (overlap(outs[o], obytes[o], ins[q], ibytes[q])) return SAD_EINVAL;
+    if (overlap(topk_next, nbytes, scores_next, sbytes) || overlap(topk_prev, pbytes, scores_prev, sbytes))
         return SAD_EINVAL;
     const int64_t ntiles = int64_t(tiles_x(w)) * tiles_y(h);
     if (ntiles > MAX_TILES) return SAD_EINVAL;
     a.derived = derived;
-    a.prev = topk_prev;
+    a.prev = prev_bits == 32 ? static_cast<const uint32_t*>(topk_prev) : nullptr;
+    a.prev16 = prev_bits == 16 ? static_cast<const uint16_t*>(topk_prev) : nullptr;
     a.prev_scores = scores_prev;
-    a.next = topk_next;
+    a.next = next_bits == 32 ? static_cast<uint32_t*>(topk_next) : nullptr;
+    a.next16 = next_bits == 16 ? static_cast<uint16_t*>(topk_next) : nullptr;
     a.next_scores = scores_next;
     a.seed = seed;
     a.n = n;

@@ -3,7 +3,9 @@
 PyTorch only provides device memory and the current stream: every wrapper
 checks shapes, dtypes and devices, passes raw pointers to libsad.so, and the
 work runs in the HIP kernels.  Top-K maps are torch.int32 tensors holding the
-uint32 site ids bit for bit (empty slot 0xffffffff reads as -1).
+uint32 site ids bit for bit (empty slot 0xffffffff reads as -1); the passes
+also take torch.int16 maps holding uint16 ids (empty slot 0xffff, read as -1)
+when there are at most 65,535 sites.
 """
 from __future__ import annotations
 
@@ -56,27 +58,41 @@ def empty_map(h: int, w: int, device="cuda") -> torch.Tensor:
     return torch.full((h, w, K), EMPTY_I32, dtype=torch.int32, device=device)
 
 
+def _map_bits(t: torch.Tensor, name: str, h: int, w: int) -> int:
+    """Id width of a top-K map tensor: int32 holds 32-bit ids, int16 16-bit ids."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.int16:
+        _need(t, name, torch.int16, (h, w, K))
+        return 16
+    _need(t, name, torch.int32, (h, w, K))
+    return 32
+
+
 def propagate_topk(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor | None = None,
                    *, stride: int, seed: int, pass_index: int, inject: int = 64,
                    prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None) -> torch.Tensor:
     """One propagation pass.  ``prev_scores`` (optional) must hold the logits of
     ``prev``'s entries under ``derived`` as a previous pass wrote them to its
-    ``out_scores``; pass it only while the sites are unchanged."""
+    ``out_scores``; pass it only while the sites are unchanged.  ``prev`` and
+    ``out`` may be int16 maps (16-bit ids, sad_propagate_topk_widths)."""
     n = derived.shape[0]
     _need(derived, "derived", torch.float32, (n, REC))
-    if prev is not None:
-        _need(prev, "prev", torch.int32, (h, w, K))
+    pbits = _map_bits(prev, "prev", h, w) if prev is not None else 32
     if prev_scores is not None:
         _need(prev_scores, "prev_scores", torch.float32, (h, w, K))
     if out is None:
         out = torch.empty((h, w, K), dtype=torch.int32, device=derived.device)
-    _need(out, "out", torch.int32, (h, w, K))
+    obits = _map_bits(out, "out", h, w)
     if out_scores is not None:
         _need(out_scores, "out_scores", torch.float32, (h, w, K))
-    st = _native.lib().sad_propagate_topk(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
-                                          _ptr(out_scores), int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF,
-                                          int(pass_index) & 0xFFFFFFFF, int(inject), _stream(derived))
-    _native.check("sad_propagate_topk", st)
+    tail = (int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF, int(pass_index) & 0xFFFFFFFF, int(inject), _stream(derived))
+    if pbits == 32 and obits == 32:
+        st = _native.lib().sad_propagate_topk(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
+                                              _ptr(out_scores), *tail)
+        _native.check("sad_propagate_topk", st)
+    else:
+        st = _native.lib().sad_propagate_topk_widths(_ptr(derived), n, h, w, _ptr(prev), pbits, _ptr(prev_scores),
+                                                     _ptr(out), obits, _ptr(out_scores), *tail)
+        _native.check("sad_propagate_topk_widths", st)
     return out
 
 
@@ -309,11 +325,11 @@ def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None,
                inject: int = 64, prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None,
                loss: torch.Tensor | None = None, image: torch.Tensor | None = None) -> torch.Tensor:
     """propagate_topk(...) into ``out`` followed by render_bwd over ``out``, in
-    one call (both launches checked before either is enqueued)."""
+    one call (both launches checked before either is enqueued).  ``prev`` may
+    be an int16 map (16-bit ids); ``out`` has 32-bit ids."""
     n = derived.shape[0]
     _need(derived, "derived", torch.float32, (n, REC))
-    if prev is not None:
-        _need(prev, "prev", torch.int32, (h, w, K))
+    pbits = _map_bits(prev, "prev", h, w) if prev is not None else 32
     if prev_scores is not None:
         _need(prev_scores, "prev_scores", torch.float32, (h, w, K))
     _need(out, "out", torch.int32, (h, w, K))
@@ -325,11 +341,16 @@ def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None,
         _need(loss, "loss", torch.float32, (1,))
     if image is not None:
         _need(image, "image", torch.float32, (h, w, 3))
-    st = _native.lib().sad_step_fused(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
-                                      _ptr(out_scores), int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF,
-                                      int(pass_index) & 0xFFFFFFFF, int(inject), _ptr(target), _ptr(grad),
-                                      _ptr(loss), _ptr(image), _stream(derived))
-    _native.check("sad_step_fused", st)
+    tail = (int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF, int(pass_index) & 0xFFFFFFFF, int(inject), _ptr(target),
+            _ptr(grad), _ptr(loss), _ptr(image), _stream(derived))
+    if pbits == 32:
+        st = _native.lib().sad_step_fused(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
+                                          _ptr(out_scores), *tail)
+        _native.check("sad_step_fused", st)
+    else:
+        st = _native.lib().sad_step_fused_widths(_ptr(derived), n, h, w, _ptr(prev), pbits, _ptr(prev_scores),
+                                                 _ptr(out), _ptr(out_scores), *tail)
+        _native.check("sad_step_fused_widths", st)
     return out
 
 

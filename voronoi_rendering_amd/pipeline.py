@@ -9,7 +9,7 @@ because a pass only reads the previous map.
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import Sequence
+from typing import Callable, Sequence
 
 import torch
 
@@ -75,6 +75,9 @@ class SadField:
         # logits of each map's entries, valid while the sites do not change
         self.scores = [torch.empty((self.h, self.w, ops.K), dtype=torch.float32, device=dev) for _ in range(2)]
         self.scores_valid = False
+        # 16-bit-id maps through which a step's passes hand on their lists
+        # (made on first use; only when every id fits in 16 bits)
+        self.maps16 = None
         self.cur = 0
         self.pass_index = 0
         self.adam_t = 0
@@ -147,20 +150,41 @@ class SadField:
     def forward_backward(self, target: torch.Tensor, image: torch.Tensor | None = None) -> None:
         ops.render_bwd(self.derived, self.h, self.w, self.topk, target, self.grad, self.loss, image)
 
-    def step(self, strides: Sequence[int], target: torch.Tensor, fused: bool = True) -> None:
+    def step(self, strides: Sequence[int], target: torch.Tensor, fused: bool = True,
+             before_last: Callable[[], None] | None = None) -> None:
         """Propagation passes + forward + backward (gradients accumulate).  With
-        ``fused`` the last pass and the backward run as one call."""
+        ``fused`` the last pass and the backward run as one call, and
+        ``before_last`` (if given) is called between the enqueueing of the other
+        passes and of that call (a place for timing events)."""
         if not fused or len(strides) == 0:
             self.propagate(strides)
             self.forward_backward(target)
             return
-        self.propagate(strides[:-1])
+        if self.params.shape[0] > 0xFFFF or len(strides) < 2:
+            self.propagate(strides[:-1])
+            prev, prev_scores = self.maps[self.cur], self.scores[self.cur] if self.scores_valid else None
+        else:
+            # the passes before the last hand their lists on with 16-bit ids
+            # (48 instead of 64 bytes per pixel each way with the logits)
+            if self.maps16 is None:
+                self.maps16 = [torch.empty((self.h, self.w, ops.K), dtype=torch.int16, device=self.params.device)
+                               for _ in range(2)]
+            prev, sc = self.maps[self.cur], self.cur
+            prev_scores = self.scores[sc] if self.scores_valid else None
+            for k, s in enumerate(strides[:-1]):
+                out = self.maps16[k % 2]
+                ops.propagate_topk(self.derived, self.h, self.w, prev, out, stride=int(s), seed=self.seed,
+                                   pass_index=self.pass_index, inject=self.inject, prev_scores=prev_scores,
+                                   out_scores=self.scores[1 - sc])
+                prev, sc, prev_scores = out, 1 - sc, self.scores[1 - sc]
+                self.pass_index += 1
+        if before_last is not None:
+            before_last()
         # The last pass's logits are not kept: a training iteration rewrites the
         # sites next, so the following pass recomputes them anyway.
-        ops.step_fused(self.derived, self.h, self.w, self.maps[self.cur], self.maps[1 - self.cur], target, self.grad,
+        ops.step_fused(self.derived, self.h, self.w, prev, self.maps[1 - self.cur], target, self.grad,
                        stride=int(strides[-1]), seed=self.seed, pass_index=self.pass_index, inject=self.inject,
-                       prev_scores=self.scores[self.cur] if self.scores_valid else None, out_scores=None,
-                       loss=self.loss)
+                       prev_scores=prev_scores, out_scores=None, loss=self.loss)
         self.cur = 1 - self.cur
         self.pass_index += 1
         self.scores_valid = False
