@@ -142,25 +142,34 @@ int sad_propagate_topk(const float *derived, int32_t n, int32_t h, int32_t w, co
                        uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, void *stream);
 
 /*
- * sad_propagate_topk with a choice of id width for each map (the same pass of
- * Sec. 4.3): prev_bits and next_bits are 16 or 32, the width of topk_prev's
- * and topk_next's ids.  A map of width 16 is [h][w][8] uint16 (16 bytes per
- * pixel) with the empty slot 0xffff; it needs n <= 65535 (SAD_EUNSUPPORTED
+ * sad_propagate_topk with a choice of id width for each map and a shorter
+ * form of the logits handed from pass to pass (the same pass of Sec. 4.3).
+ * prev_bits and next_bits are 16 or 32, the width of topk_prev's and
+ * topk_next's ids.  A map of width 16 is [h][w][8] uint16 (16 bytes per pixel)
+ * with the empty slot 0xffff; it needs n <= 65535 (SAD_EUNSUPPORTED
  * otherwise), so that every usable id is below 0xffff.  The lists are those
  * sad_propagate_topk writes, id for id (0xffff where it writes 0xffffffff), and
- * an input id at or above n is dropped as there.  Within a training step the
- * passes can hand their lists on at width 16, beside their score maps: a pass
- * then moves 48 instead of 64 bytes per pixel each way.
- *   topk_prev    NULL, or a map of width prev_bits (16-byte aligned)
- *   topk_next    a map of width next_bits, written
- *   prev_bits, next_bits  16 or 32 (SAD_EINVAL otherwise)
- * Other arguments and checks as sad_propagate_topk (overlaps are checked on
- * each map's own size).
+ * an input id at or above n is dropped as there.
+ *   thr_prev   NULL, or [h][w] float32: the logit of each previous list's 8th
+ *              entry (-inf where the list is shorter), as written to thr_next
+ *              by the pass that produced topk_prev with the same prepared
+ *              sites (so that its lists hold usable ids in ranking order).
+ *              Not together with scores_prev; requires topk_prev.  The pass
+ *              then evaluates a pixel's other logits only if it inserts a
+ *              candidate (on settled lists almost never) or scores_next is
+ *              requested: it reads 4 instead of 32 bytes of logits per pixel.
+ *              Thresholds made before the sites changed give wrong lists.
+ *   thr_next   NULL, or [h][w] float32 written with the logit of each new
+ *              list's 8th entry (-inf where it is shorter).
+ * Within a training step the passes can hand their lists on at width 16 with
+ * their thresholds: a pass then moves 20 instead of 64 bytes per pixel each
+ * way.  Other arguments and checks as sad_propagate_topk; no two of the six
+ * maps may overlap (each measured on its own size).
  */
 int sad_propagate_topk_widths(const float *derived, int32_t n, int32_t h, int32_t w, const void *topk_prev,
-                              int32_t prev_bits, const float *scores_prev, void *topk_next, int32_t next_bits,
-                              float *scores_next, int32_t stride, uint64_t seed, uint32_t pass_index,
-                              int32_t inject_per_tile, void *stream);
+                              int32_t prev_bits, const float *scores_prev, const float *thr_prev, void *topk_next,
+                              int32_t next_bits, float *scores_next, float *thr_next, int32_t stride, uint64_t seed,
+                              uint32_t pass_index, int32_t inject_per_tile, void *stream);
 
 /*
  * Soft additively weighted render (Sec. 4.2): per pixel, the softmax of the
@@ -394,14 +403,20 @@ int sad_step_fused(const float *derived, int32_t n, int32_t h, int32_t w, const 
 
 /*
  * sad_step_fused reading a previous map of width prev_bits (16 or 32, as
- * sad_propagate_topk_widths; width 16 needs n <= 65535): the last pass of a
- * step whose earlier passes handed their lists on at width 16.  topk_next is
- * written with 32-bit ids, as sad_step_fused writes it.
+ * sad_propagate_topk_widths; width 16 needs n <= 65535) and optionally only
+ * its lists' 8th logits (thr_prev, as there; not with scores_prev): the last
+ * pass of a step whose earlier passes handed their lists on in that form.
+ * topk_next is written with 32-bit ids, as sad_step_fused writes it.  With
+ * thr_prev the backward evaluates the pixels' logits from the site records it
+ * stages anyway, rather than taking them from the pass.  In addition to the
+ * checks of sad_step_fused, grad, loss and image must not overlap topk_prev,
+ * scores_prev or thr_prev.
  */
 int sad_step_fused_widths(const float *derived, int32_t n, int32_t h, int32_t w, const void *topk_prev,
-                          int32_t prev_bits, const float *scores_prev, uint32_t *topk_next, float *scores_next,
-                          int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject_per_tile,
-                          const float *target, float *grad, float *loss, float *image, void *stream);
+                          int32_t prev_bits, const float *scores_prev, const float *thr_prev, uint32_t *topk_next,
+                          float *scores_next, int32_t stride, uint64_t seed, uint32_t pass_index,
+                          int32_t inject_per_tile, const float *target, float *grad, float *loss, float *image,
+                          void *stream);
 
 /*
  * One Adam step (Kingma & Ba) on the site parameters (Sec. 5: per-parameter

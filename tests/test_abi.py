@@ -91,17 +91,19 @@ def test_propagate_rejects(lib):
 
 
 def test_propagate_widths_rejects(lib):
-    """The id-width variant: widths other than 16 and 32, 16-bit maps with
-    more than 65,535 sites, and overlaps measured on each map's own size (a
-    16-bit map of 8x8 pixels is 1 KiB)."""
+    """The variant with id widths and 8th-logit maps: widths other than 16
+    and 32, 16-bit maps with more than 65,535 sites, threshold maps without a
+    previous map or together with a score map, and overlaps measured on each
+    map's own size (for 8x8 pixels a 16-bit map is 1 KiB, a threshold map
+    256 bytes)."""
     f = lib.sad_propagate_topk_widths
-    ok = dict(derived=P, n=10, h=8, w=8, prev=P + 65536, pb=16, sprev=None, nxt=P + 4096, nb=16, snext=None, stride=1,
-              seed=0, pi=0, inj=64)
+    ok = dict(derived=P, n=10, h=8, w=8, prev=P + 65536, pb=16, sprev=None, tprev=None, nxt=P + 4096, nb=16,
+              snext=None, tnext=None, stride=1, seed=0, pi=0, inj=64)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["derived"], a["n"], a["h"], a["w"], a["prev"], a["pb"], a["sprev"], a["nxt"], a["nb"], a["snext"],
-                 a["stride"], a["seed"], a["pi"], a["inj"], None)
+        return f(a["derived"], a["n"], a["h"], a["w"], a["prev"], a["pb"], a["sprev"], a["tprev"], a["nxt"], a["nb"],
+                 a["snext"], a["tnext"], a["stride"], a["seed"], a["pi"], a["inj"], None)
 
     assert call(pb=8) == EINVAL
     assert call(nb=64) == EINVAL
@@ -112,11 +114,26 @@ def test_propagate_widths_rejects(lib):
     assert call(nxt=P + 4100) == EINVAL  # misaligned
     assert call(sprev=P + 8192, snext=P + 8192 + 2032) == EINVAL  # score maps overlap (2 KiB each)
     assert call(snext=P + 4096 + 512) == EINVAL  # next scores inside the next map
+    assert call(tprev=P + 8192, prev=None) == EINVAL  # thresholds without a previous map
+    assert call(tprev=P + 8192, sprev=P + 12288) == EINVAL  # thresholds and scores together
+    assert call(tprev=P + 8194) == EINVAL  # misaligned thresholds
+    assert call(tprev=P + 8192, tnext=P + 8192 + 252) == EINVAL  # threshold maps overlap (256 bytes each)
+    assert call(tnext=P + 65536 + 1020) == EINVAL  # next thresholds over the previous map
+    assert call(tprev=P + 4096 + 1000) == EINVAL  # previous thresholds over the next map
     g = lib.sad_step_fused_widths
     G, T = P + (1 << 20), P + (2 << 20)  # grad and target, apart from everything
-    assert g(P, 65536, 8, 8, P + 65536, 16, None, P + 4096, None, 1, 0, 0, 64, T, G, None, None, None) == EUNSUP
-    assert g(P, 10, 8, 8, P + 65536, 24, None, P + 4096, None, 1, 0, 0, 64, T, G, None, None, None) == EINVAL
-    assert g(P, 10, 8, 8, P + 65536, 16, None, P + 4096, None, 1, 0, 0, 64, T, None, None, None, None) == EINVAL
+
+    def fused(**kw):
+        a = dict(dict(prev=P + 65536, pb=16, tprev=None, nxt=P + 4096, n=10, grad=G, loss=None, image=None), **kw)
+        return g(P, a["n"], 8, 8, a["prev"], a["pb"], None, a["tprev"], a["nxt"], None, 1, 0, 0, 64, T, a["grad"],
+                 a["loss"], a["image"], None)
+
+    assert fused(n=65536) == EUNSUP
+    assert fused(pb=24) == EINVAL
+    assert fused(grad=None) == EINVAL
+    assert fused(grad=P + 65536) == EINVAL  # gradients over the previous map
+    assert fused(tprev=P + 8192, loss=P + 8192 + 8) == EINVAL  # loss inside the thresholds
+    assert fused(image=P + 65536 + 512) == EINVAL  # image over the previous map
 
 
 def test_render_query_adam_reject(lib):

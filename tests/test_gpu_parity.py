@@ -1105,6 +1105,81 @@ def test_propagate_16bit_maps(sad, ref, h, w, n):
         m, prev16, prev32, sc_prev = want, out16, out32, sc16
 
 
+def eighth_logits(ref, d, m):
+    """The oracle's logit of each list's 8th entry (-inf where it is empty)."""
+    h, w = m.shape[:2]
+    out = np.full((h, w), -np.inf, dtype=np.float32)
+    for j in range(h):
+        for i in range(w):
+            if m[j, i, 7] != 0xFFFFFFFF:
+                out[j, i] = ref.score(d, int(m[j, i, 7]), i + 0.5, j + 0.5)
+    return out
+
+
+@pytest.mark.parametrize("h,w,n,bits", [(64, 64, 256, 16), (29, 45, 400, 32), (40, 40, 3000, 16)])
+def test_propagate_thresholds(sad, ref, h, w, n, bits):
+    """Passes that hand on only each list's 8th logit: from an empty map
+    through the warm-up schedule (lists fill up, so most lanes insert and
+    evaluate their other logits) and a step's strides, every pass gives the
+    oracle's lists and 8th logits bit for bit, and asked for all logits it
+    writes the score map the full pass writes."""
+    p = synth.sites(500 + n, n, h, w)
+    p[5, 0] = -1.0  # an inactive site
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p))
+    dt = torch.int16 if bits == 16 else torch.int32
+    strides = list(synth.jfa_strides(h, w, 5)) + [8, 4, 2, 1, 3, 1]
+    m, prev, thr = None, None, None
+    for t, s_ in enumerate(strides):
+        want = ref.propagate(d, h, w, m, s_, 23, t, 64)
+        out = torch.empty((h, w, 8), dtype=dt, device=dev())
+        out_thr = torch.empty((h, w), dtype=torch.float32, device=dev())
+        sad.propagate_topk(dg, h, w, prev, out, stride=s_, seed=23, pass_index=t, inject=64, prev_thr=thr,
+                           out_thr=out_thr)
+        got = map16_to_np(out) if bits == 16 else map_to_np(out)
+        assert np.array_equal(got, want), f"pass {t}: {np.argwhere(got != want)[:4]}"
+        assert np.array_equal(to_np(out_thr).view(np.uint32), eighth_logits(ref, d, want).view(np.uint32)), t
+        if thr is not None:
+            # all logits asked for: the lanes that did not insert evaluate theirs too
+            full = torch.empty((h, w, 8), dtype=dt, device=dev())
+            sc = torch.empty((h, w, 8), dtype=torch.float32, device=dev())
+            sad.propagate_topk(dg, h, w, prev, full, stride=s_, seed=23, pass_index=t, inject=64, prev_thr=thr,
+                               out_scores=sc)
+            ref_sc = torch.empty((h, w, 8), dtype=torch.float32, device=dev())
+            sad.propagate_topk(dg, h, w, to_gpu(m), torch.empty((h, w, 8), dtype=torch.int32, device=dev()),
+                               stride=s_, seed=23, pass_index=t, inject=64, out_scores=ref_sc)
+            assert np.array_equal(to_np(sc).view(np.uint32), to_np(ref_sc).view(np.uint32)), f"pass {t} scores"
+        m, prev, thr = want, out, out_thr
+
+
+def test_step_fused_from_thresholds(sad, ref):
+    """The fused last pass + backward from a 16-bit map with only its 8th
+    logits, on lists still filling (64x64 workload after 6 passes from empty,
+    most lanes insert) and on the settled 768x512-like density at 96x128: the
+    oracle's lists, loss and gradients (the backward takes the logits from
+    the site records it stages)."""
+    for (h, w, n, npass) in ((64, 64, 256, 6), (96, 128, 1500, 14)):
+        p = synth.sites(700 + n, n, h, w, synth.WIDE_SCALES)
+        d = ref.prepare_sites(p)
+        dg = sad.prepare_sites(to_gpu(p))
+        strides = synth.jfa_strides(h, w, npass)
+        m = ref.propagate_schedule(d, h, w, None, strides, 41, 0, 64)
+        thr = torch.from_numpy(eighth_logits(ref, d, m)).to(dev())
+        m1 = ref.propagate(d, h, w, m, 1, 41, npass, 64)
+        tgt = synth.target_noise_edges(710 + n, h, w)
+        g_ref, _, loss_ref, img_ref = ref.render_bwd(d, h, w, m1, tgt)
+        out = torch.empty((h, w, 8), dtype=torch.int32, device=dev())
+        grad = torch.zeros((n, 12), dtype=torch.float32, device=dev())
+        loss = torch.zeros(1, dtype=torch.float32, device=dev())
+        img = torch.empty((h, w, 3), dtype=torch.float32, device=dev())
+        sad.step_fused(dg, h, w, map16_from_np(m), out, to_gpu(tgt), grad, stride=1, seed=41, pass_index=npass,
+                       inject=64, loss=loss, image=img, prev_thr=thr)
+        assert np.array_equal(map_to_np(out), m1), f"{h}x{w}: lists"
+        assert_colour_close(to_np(img), img_ref, f"{h}x{w} image")
+        assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
+        assert_grad_close(to_np(grad), g_ref, f"{h}x{w} gradients from thresholds")
+
+
 def test_step_fused_from_16bit_map(sad, ref, c2_state):
     """The fused last pass + backward reading a 16-bit-id map (and its score
     map) on the 768x512 map: the oracle's lists, loss and gradients, and the

@@ -523,7 +523,7 @@ struct PassLds {
 // starts from them in the same LDS: no list is read back and no logit of the
 // forward is evaluated again, and regions start their backward while others
 // still run their pass.
-template <bool SMALL_IDS, bool PREV16>
+template <bool SMALL_IDS, bool PREV16, bool THR_IN>
 __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(SMALL_IDS ? 6 : 1)))
 void k_step_last(PropArgs pa, BwdArgs a) {
     __shared__ union {
@@ -538,8 +538,8 @@ void k_step_last(PropArgs pa, BwdArgs a) {
     TopK t;
     t.clear();
     if (tx < pa.tiles_x && ty * pa.tiles_x + tx < pa.n_tiles)  // uniform per wavefront
-        propagate_tile<SMALL_IDS, PREV16, false>(pa, ty * pa.tiles_x + tx, lds.pass.queue[wv], lds.pass.qscore[wv],
-                                                 t);
+        propagate_tile<SMALL_IDS, PREV16, false, THR_IN>(pa, ty * pa.tiles_x + tx, lds.pass.queue[wv],
+                                                         lds.pass.qscore[wv], t);
     int i, j;
     region_pixel(rx, ry, wv, lane, i, j);  // the pixel the pass just listed
     float tg[3] = {0.f, 0.f, 0.f};
@@ -574,7 +574,10 @@ void k_step_last(PropArgs pa, BwdArgs a) {
     }
     lds.bwd.mine[tid] = 0;
     __syncthreads();  // table cleared
-    backward_region<true>(a, lds.bwd, rx, ry, ids, lg, tg);
+    // with only the 8th logits given (THR_IN) the lanes' other logits are not
+    // all known: the forward evaluates them from the site records it stages
+    // in LDS (the same float32 values)
+    backward_region<!THR_IN>(a, lds.bwd, rx, ry, ids, lg, tg);
 }
 
 // Argument checks of a backward pass over the list map topk, and its kernel
@@ -635,12 +638,12 @@ extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_
 // Checks and launch of the fused last pass + backward (prev_bits: the id
 // width of topk_prev; the new lists are written with 32-bit ids).
 static int step_fused(const float* derived, int32_t n, int32_t h, int32_t w, const void* topk_prev, int32_t prev_bits,
-                      const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride, uint64_t seed,
-                      uint32_t pass_index, int32_t inject_per_tile, const float* target, float* grad, float* loss,
-                      float* image, void* stream) {
+                      const float* scores_prev, const float* thr_prev, uint32_t* topk_next, float* scores_next,
+                      int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, const float* target,
+                      float* grad, float* loss, float* image, void* stream) {
     PropArgs pa;
-    int st = prop_setup(derived, n, h, w, topk_prev, prev_bits, scores_prev, topk_next, 32, scores_next, stride, seed,
-                        pass_index, inject_per_tile, pa);
+    int st = prop_setup(derived, n, h, w, topk_prev, prev_bits, scores_prev, thr_prev, topk_next, 32, scores_next,
+                        nullptr, stride, seed, pass_index, inject_per_tile, pa);
     if (st != SAD_OK) return st;
     BwdArgs b;
     st = bwd_setup(derived, n, h, w, topk_next, target, grad, loss, image, b);
@@ -653,17 +656,37 @@ static int step_fused(const float* derived, int32_t n, int32_t h, int32_t w, con
     for (int o = 0; o < 2; ++o)
         for (int q = 0; q < 5; ++q)
             if (overlap(outs[o], mbytes, others[q], obytes[q])) return SAD_EINVAL;
+    // nor may the backward's outputs share memory with the pass's inputs
+    const void* bouts[3] = {grad, loss, image};
+    const int64_t bbytes[3] = {gbytes, 4, pix * 12};
+    const void* pins[3] = {topk_prev, scores_prev, thr_prev};
+    const int64_t pbytes[3] = {pix * K * (prev_bits / 8), pix * K * 4, pix * 4};
+    for (int o = 0; o < 3; ++o)
+        for (int q = 0; q < 3; ++q)
+            if (overlap(bouts[o], bbytes[o], pins[q], pbytes[q])) return SAD_EINVAL;
     if (pix == 0) return SAD_OK;
     // every check has passed: one kernel, one workgroup per backward region
     const size_t nreg = (size_t)b.rg.rgx * b.rg.rgy;
     const hipStream_t s = as_stream(stream);
     clear_error();
-    if (pa.n > SMALL_IDS_MAX)
-        hipLaunchKernelGGL((k_step_last<false, false>), dim3((unsigned)nreg), dim3(BWD_THREADS), 0, s, pa, b);
-    else if (pa.prev16)
-        hipLaunchKernelGGL((k_step_last<true, true>), dim3((unsigned)nreg), dim3(BWD_THREADS), 0, s, pa, b);
-    else
-        hipLaunchKernelGGL((k_step_last<true, false>), dim3((unsigned)nreg), dim3(BWD_THREADS), 0, s, pa, b);
+    const dim3 grid((unsigned)nreg), block(BWD_THREADS);
+    const bool thr = pa.prev_thr != nullptr;
+    if (pa.n > SMALL_IDS_MAX) {
+        if (thr)
+            hipLaunchKernelGGL((k_step_last<false, false, true>), grid, block, 0, s, pa, b);
+        else
+            hipLaunchKernelGGL((k_step_last<false, false, false>), grid, block, 0, s, pa, b);
+    } else if (pa.prev16) {
+        if (thr)
+            hipLaunchKernelGGL((k_step_last<true, true, true>), grid, block, 0, s, pa, b);
+        else
+            hipLaunchKernelGGL((k_step_last<true, true, false>), grid, block, 0, s, pa, b);
+    } else {
+        if (thr)
+            hipLaunchKernelGGL((k_step_last<true, false, true>), grid, block, 0, s, pa, b);
+        else
+            hipLaunchKernelGGL((k_step_last<true, false, false>), grid, block, 0, s, pa, b);
+    }
     return launch_status();
 }
 
@@ -671,15 +694,15 @@ extern "C" int sad_step_fused(const float* derived, int32_t n, int32_t h, int32_
                               const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride,
                               uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, const float* target,
                               float* grad, float* loss, float* image, void* stream) {
-    return step_fused(derived, n, h, w, topk_prev, 32, scores_prev, topk_next, scores_next, stride, seed, pass_index,
-                      inject_per_tile, target, grad, loss, image, stream);
+    return step_fused(derived, n, h, w, topk_prev, 32, scores_prev, nullptr, topk_next, scores_next, stride, seed,
+                      pass_index, inject_per_tile, target, grad, loss, image, stream);
 }
 
 extern "C" int sad_step_fused_widths(const float* derived, int32_t n, int32_t h, int32_t w, const void* topk_prev,
-                                     int32_t prev_bits, const float* scores_prev, uint32_t* topk_next,
-                                     float* scores_next, int32_t stride, uint64_t seed, uint32_t pass_index,
-                                     int32_t inject_per_tile, const float* target, float* grad, float* loss,
-                                     float* image, void* stream) {
-    return step_fused(derived, n, h, w, topk_prev, prev_bits, scores_prev, topk_next, scores_next, stride, seed,
-                      pass_index, inject_per_tile, target, grad, loss, image, stream);
+                                     int32_t prev_bits, const float* scores_prev, const float* thr_prev,
+                                     uint32_t* topk_next, float* scores_next, int32_t stride, uint64_t seed,
+                                     uint32_t pass_index, int32_t inject_per_tile, const float* target, float* grad,
+                                     float* loss, float* image, void* stream) {
+    return step_fused(derived, n, h, w, topk_prev, prev_bits, scores_prev, thr_prev, topk_next, scores_next, stride,
+                      seed, pass_index, inject_per_tile, target, grad, loss, image, stream);
 }

@@ -41,9 +41,11 @@ struct PropArgs {
     const uint32_t* prev;      // the previous map with 32-bit ids, or
     const uint16_t* prev16;    // with 16-bit ids (at most one of the two; neither: an empty map)
     const float* prev_scores;  // nullable: logits of prev's entries under derived
+    const float* prev_thr;     // nullable (not with prev_scores): the logit of each prev list's 8th entry
     uint32_t* next;            // the next map with 32-bit ids, or
     uint16_t* next16;          // with 16-bit ids (exactly one of the two)
     float* next_scores;        // nullable: logits of next's entries are written here
+    float* next_thr;           // nullable: the logit of each next list's 8th entry is written here
     uint64_t seed;
     int32_t n, h, w, stride, inject, tiles_x, n_tiles;
     uint32_t pass_index;
@@ -191,9 +193,18 @@ using QueueId = std::conditional_t<SMALL_IDS, uint16_t, uint32_t>;
 // (a.prev16 / a.next16, 16 bytes per pixel, the empty slot 0xffff).  A
 // 16-bit list is read as the packed pairs the neighbour lists use anyway,
 // and its 0xffff slots, being >= n, are dropped like any unusable id.
-template <bool SMALL_IDS, bool PREV16 = false, bool NEXT16 = false>
+// THR_IN: the previous lists come with only their 8th entry's logit
+// (a.prev_thr), written by a pass over the same sites, so that they hold
+// usable ids in ranking order.  A lane then knows the one logit the screen
+// and the ranking against the 8th entry use; the other seven are evaluated
+// (materialize) only when the lane is about to insert a candidate or the
+// caller asks for all logits, so that a pass on settled lists (almost no
+// insertions) reads 4 instead of 32 bytes of logits per pixel.  *lazy (when
+// given) receives whether the lane's logits other than the 8th are still
+// unknown when the pass ends.
+template <bool SMALL_IDS, bool PREV16 = false, bool NEXT16 = false, bool THR_IN = false>
 __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, QueueId<SMALL_IDS> (*queue)[WAVE],
-                                               float (*qscore)[WAVE], TopK& t) {
+                                               float (*qscore)[WAVE], TopK& t, bool* lazy_out = nullptr) {
     static_assert(SMALL_IDS || !(PREV16 || NEXT16), "16-bit maps hold 16-bit ids");
     const bool has_prev = PREV16 ? a.prev16 != nullptr : a.prev != nullptr;  // uniform
     constexpr int NW = SMALL_IDS ? K / 2 : K;  // registers per neighbour list
@@ -231,7 +242,9 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
             own[0] = l0.x; own[1] = l0.y; own[2] = l0.z; own[3] = l0.w;
             own[4] = l1.x; own[5] = l1.y; own[6] = l1.z; own[7] = l1.w;
         }
-        if (a.prev_scores) {
+        if constexpr (THR_IN) {
+            own_s[K - 1] = a.prev_thr[pc];
+        } else if (a.prev_scores) {
             const float4* ls = reinterpret_cast<const float4*>(a.prev_scores + pc * K);
             const float4 s0 = ls[0], s1 = ls[1];
             own_s[0] = s0.x; own_s[1] = s0.y; own_s[2] = s0.z; own_s[3] = s0.w;
@@ -275,7 +288,14 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
     // 1. the pixel's previous list, in ranking order (its logits come from the
     //    caller's score map when the sites have not changed since it was made)
     t.clear();
-    if (a.prev_scores) {
+    bool lazy = false;  // THR_IN: the lane's logits other than the 8th are not evaluated yet
+    if constexpr (THR_IN) {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (have_prev & (own[k] < n)) t.id[k] = own[k];
+        if (have_prev & (own[K - 1] < n)) t.s[K - 1] = own_s[K - 1];
+        lazy = have_prev & (own[0] < n);
+    } else if (a.prev_scores) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             if (have_prev & (own[k] < n) & (own_s[k] == own_s[k])) {
@@ -300,10 +320,35 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
             }
         }
     }
+    // the logits of the lanes in `need` that are still unknown (THR_IN), in
+    // the list's order: the same float32 values the pass that wrote the list
+    // evaluated
+    auto materialize = [&](bool need) {
+        if constexpr (THR_IN) {
+            need &= lazy;
+            if (__any(need)) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    Geo og[K / 2];
+#pragma unroll
+                    for (int k = 0; k < K / 2; ++k)
+                        og[k] = load_geo_clamped(a.derived, n, need ? t.id[half * 4 + k] : EMPTY);
+#pragma unroll
+                    for (int k = 0; k < K / 2; ++k) {
+                        const int kk = half * 4 + k;
+                        const float s = usable_logit(og[k], t.id[kk] < n, px, py);
+                        t.s[kk] = need & (t.id[kk] < n) ? s : t.s[kk];
+                    }
+                }
+                lazy &= !need;
+            }
+        }
+    };
     bool ordered = true;
 #pragma unroll
     for (int k = 0; k < K - 1; ++k)
         ordered &= ranks_before(t.s[k], t.id[k], t.s[k + 1], t.id[k + 1]) | (t.id[k + 1] == EMPTY);
+    if (THR_IN) ordered = true;  // lists a pass wrote over the same sites are in order
     if (!__all(ordered)) {
         sort8(t);
         // a malformed previous list may repeat an id: rebuild such lists by insertion
@@ -393,6 +438,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
             }
         }
         // insert the survivors
+        materialize(ns > 0);
         for (int u = 0; __any(u < ns); ++u) {
             const bool live = u < ns;
             const uint32_t v = live ? (uint32_t)queue[u][lane] : EMPTY;
@@ -432,7 +478,12 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
             g.g1.w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pg.g1.w), q));
             const float s = logit(g, px, py);  // a survivor is an active site (checked above)
             const bool ok = inside & (s == s);
-            if (__any(ok & ranks_before(s, id, t.s[K - 1], t.id[K - 1]))) t.insert_if(s, id, ok);
+            // a candidate that does not rank before the 8th entry leaves the list as it is
+            const bool beats = ok & ranks_before(s, id, t.s[K - 1], t.id[K - 1]);
+            if (__any(beats)) {
+                materialize(beats);
+                t.insert_if(s, id, beats);
+            }
         }
     }
 
@@ -447,21 +498,26 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
             o[0] = make_uint4(t.id[0], t.id[1], t.id[2], t.id[3]);
             o[1] = make_uint4(t.id[4], t.id[5], t.id[6], t.id[7]);
         }
+        if (a.next_thr) a.next_thr[(size_t)j * a.w + i] = t.s[K - 1];
+    }
+    if (a.next_scores) materialize(true);  // uniform; a no-op unless THR_IN
+    if (inside) {
         if (a.next_scores) {
             float4* os = reinterpret_cast<float4*>(a.next_scores + ((size_t)j * a.w + i) * K);
             os[0] = make_float4(t.s[0], t.s[1], t.s[2], t.s[3]);
             os[1] = make_float4(t.s[4], t.s[5], t.s[6], t.s[7]);
         }
     }
+    if (lazy_out) *lazy_out = lazy;
 }
 
 // Argument checks of a propagation pass (shared by the entry points that run
 // one) and its kernel arguments.  Returns SAD_OK with a filled in, or the
 // error status.
 inline int prop_setup(const float* derived, int32_t n, int32_t h, int32_t w, const void* topk_prev,
-                      int32_t prev_bits, const float* scores_prev, void* topk_next, int32_t next_bits,
-                      float* scores_next, int32_t stride, uint64_t seed, uint32_t pass_index,
-                      int32_t inject_per_tile, PropArgs& a) {
+                      int32_t prev_bits, const float* scores_prev, const float* thr_prev, void* topk_next,
+                      int32_t next_bits, float* scores_next, float* thr_next, int32_t stride, uint64_t seed,
+                      uint32_t pass_index, int32_t inject_per_tile, PropArgs& a) {
     if (!sites_ok(n) || !image_ok(h, w) || stride < 1 || inject_per_tile < 0) return SAD_EINVAL;
     if ((prev_bits != 16 && prev_bits != 32) || (next_bits != 16 && next_bits != 32)) return SAD_EINVAL;
     if (inject_per_tile > SAD_MAX_INJECT) return SAD_EUNSUPPORTED;
@@ -473,25 +529,32 @@ inline int prop_setup(const float* derived, int32_t n, int32_t h, int32_t w, con
     if ((topk_prev && !aligned(topk_prev, 16)) || (scores_prev && !aligned(scores_prev, 16)) ||
         (scores_next && !aligned(scores_next, 16)))
         return SAD_EINVAL;
-    if (scores_prev && !topk_prev) return SAD_EINVAL;
-    const void* outs[2] = {topk_next, scores_next};
-    const int64_t obytes[2] = {nbytes, sbytes};
-    const void* ins[2] = {topk_prev, scores_prev};
-    const int64_t ibytes[2] = {pbytes, sbytes};
-    for (int o = 0; o < 2; ++o)
-        for (int q = 0; q < 2; ++q)
+    if ((scores_prev || thr_prev) && !topk_prev) return SAD_EINVAL;
+    if (scores_prev && thr_prev) return SAD_EINVAL;
+    if ((thr_prev && !aligned(thr_prev, 4)) || (thr_next && !aligned(thr_next, 4))) return SAD_EINVAL;
+    const int64_t tbytes = pix * 4;
+    const void* outs[3] = {topk_next, scores_next, thr_next};
+    const int64_t obytes[3] = {nbytes, sbytes, tbytes};
+    const void* ins[3] = {topk_prev, scores_prev, thr_prev};
+    const int64_t ibytes[3] = {pbytes, sbytes, tbytes};
+    for (int o = 0; o < 3; ++o) {
+        for (int q = 0; q < 3; ++q)
             if (overlap(outs[o], obytes[o], ins[q], ibytes[q])) return SAD_EINVAL;
-    if (overlap(topk_next, nbytes, scores_next, sbytes) || overlap(topk_prev, pbytes, scores_prev, sbytes))
-        return SAD_EINVAL;
+        for (int q = o + 1; q < 3; ++q)
+            if (overlap(outs[o], obytes[o], outs[q], obytes[q]) || overlap(ins[o], ibytes[o], ins[q], ibytes[q]))
+                return SAD_EINVAL;
+    }
     const int64_t ntiles = int64_t(tiles_x(w)) * tiles_y(h);
     if (ntiles > MAX_TILES) return SAD_EINVAL;
     a.derived = derived;
     a.prev = prev_bits == 32 ? static_cast<const uint32_t*>(topk_prev) : nullptr;
     a.prev16 = prev_bits == 16 ? static_cast<const uint16_t*>(topk_prev) : nullptr;
     a.prev_scores = scores_prev;
+    a.prev_thr = thr_prev;
     a.next = next_bits == 32 ? static_cast<uint32_t*>(topk_next) : nullptr;
     a.next16 = next_bits == 16 ? static_cast<uint16_t*>(topk_next) : nullptr;
     a.next_scores = scores_next;
+    a.next_thr = thr_next;
     a.seed = seed;
     a.n = n;
     a.h = h;

@@ -8,7 +8,7 @@ namespace sad {
 
 constexpr int WAVES_PER_WG = 4;
 
-template <bool SMALL_IDS, bool PREV16, bool NEXT16>
+template <bool SMALL_IDS, bool PREV16, bool NEXT16, bool THR_IN>
 __global__ __launch_bounds__(WAVE* WAVES_PER_WG) __attribute__((amdgpu_waves_per_eu(SMALL_IDS ? 6 : 1)))
 void k_propagate(PropArgs a) {
     __shared__ QueueId<SMALL_IDS> queue[WAVES_PER_WG][QCAP][WAVE];  // queued ids, then survivors' ids
@@ -17,7 +17,7 @@ void k_propagate(PropArgs a) {
     const int tile = xcd_block(blockIdx.x, gridDim.x) * WAVES_PER_WG + wv;
     if (tile >= a.n_tiles) return;  // uniform per wavefront
     TopK t;
-    propagate_tile<SMALL_IDS, PREV16, NEXT16>(a, tile, queue[wv], qscore[wv], t);
+    propagate_tile<SMALL_IDS, PREV16, NEXT16, THR_IN>(a, tile, queue[wv], qscore[wv], t);
 }
 
 // Launch the pass on checked arguments.
@@ -26,17 +26,31 @@ inline int prop_launch(const PropArgs& a, void* stream) {
     clear_error();
     const dim3 grid((unsigned)((a.n_tiles + WAVES_PER_WG - 1) / WAVES_PER_WG)), block(WAVE * WAVES_PER_WG);
     const hipStream_t s = as_stream(stream);
-    const bool p16 = a.prev16 != nullptr, n16 = a.next16 != nullptr;
-    if (a.n > SMALL_IDS_MAX)
-        hipLaunchKernelGGL((k_propagate<false, false, false>), grid, block, 0, s, a);
-    else if (p16 && n16)
-        hipLaunchKernelGGL((k_propagate<true, true, true>), grid, block, 0, s, a);
-    else if (p16)
-        hipLaunchKernelGGL((k_propagate<true, true, false>), grid, block, 0, s, a);
-    else if (n16)
-        hipLaunchKernelGGL((k_propagate<true, false, true>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((k_propagate<true, false, false>), grid, block, 0, s, a);
+    const bool p16 = a.prev16 != nullptr, n16 = a.next16 != nullptr, thr = a.prev_thr != nullptr;
+    if (a.n > SMALL_IDS_MAX) {
+        if (thr)
+            hipLaunchKernelGGL((k_propagate<false, false, false, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((k_propagate<false, false, false, false>), grid, block, 0, s, a);
+    } else if (thr) {
+        if (p16 && n16)
+            hipLaunchKernelGGL((k_propagate<true, true, true, true>), grid, block, 0, s, a);
+        else if (p16)
+            hipLaunchKernelGGL((k_propagate<true, true, false, true>), grid, block, 0, s, a);
+        else if (n16)
+            hipLaunchKernelGGL((k_propagate<true, false, true, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((k_propagate<true, false, false, true>), grid, block, 0, s, a);
+    } else {
+        if (p16 && n16)
+            hipLaunchKernelGGL((k_propagate<true, true, true, false>), grid, block, 0, s, a);
+        else if (p16)
+            hipLaunchKernelGGL((k_propagate<true, true, false, false>), grid, block, 0, s, a);
+        else if (n16)
+            hipLaunchKernelGGL((k_propagate<true, false, true, false>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((k_propagate<true, false, false, false>), grid, block, 0, s, a);
+    }
     return launch_status();
 }
 
@@ -48,19 +62,20 @@ extern "C" int sad_propagate_topk(const float* derived, int32_t n, int32_t h, in
                                   const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride,
                                   uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, void* stream) {
     PropArgs a;
-    const int st = prop_setup(derived, n, h, w, topk_prev, 32, scores_prev, topk_next, 32, scores_next, stride, seed,
-                              pass_index, inject_per_tile, a);
+    const int st = prop_setup(derived, n, h, w, topk_prev, 32, scores_prev, nullptr, topk_next, 32, scores_next,
+                              nullptr, stride, seed, pass_index, inject_per_tile, a);
     if (st != SAD_OK) return st;
     return prop_launch(a, stream);
 }
 
 extern "C" int sad_propagate_topk_widths(const float* derived, int32_t n, int32_t h, int32_t w, const void* topk_prev,
-                                         int32_t prev_bits, const float* scores_prev, void* topk_next,
-                                         int32_t next_bits, float* scores_next, int32_t stride, uint64_t seed,
-                                         uint32_t pass_index, int32_t inject_per_tile, void* stream) {
+                                         int32_t prev_bits, const float* scores_prev, const float* thr_prev,
+                                         void* topk_next, int32_t next_bits, float* scores_next, float* thr_next,
+                                         int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject_per_tile,
+                                         void* stream) {
     PropArgs a;
-    const int st = prop_setup(derived, n, h, w, topk_prev, prev_bits, scores_prev, topk_next, next_bits, scores_next,
-                              stride, seed, pass_index, inject_per_tile, a);
+    const int st = prop_setup(derived, n, h, w, topk_prev, prev_bits, scores_prev, thr_prev, topk_next, next_bits,
+                              scores_next, thr_next, stride, seed, pass_index, inject_per_tile, a);
     if (st != SAD_OK) return st;
     return prop_launch(a, stream);
 }

@@ -69,11 +69,14 @@ def _map_bits(t: torch.Tensor, name: str, h: int, w: int) -> int:
 
 def propagate_topk(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor | None = None,
                    *, stride: int, seed: int, pass_index: int, inject: int = 64,
-                   prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None) -> torch.Tensor:
+                   prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None,
+                   prev_thr: torch.Tensor | None = None, out_thr: torch.Tensor | None = None) -> torch.Tensor:
     """One propagation pass.  ``prev_scores`` (optional) must hold the logits of
     ``prev``'s entries under ``derived`` as a previous pass wrote them to its
     ``out_scores``; pass it only while the sites are unchanged.  ``prev`` and
-    ``out`` may be int16 maps (16-bit ids, sad_propagate_topk_widths)."""
+    ``out`` may be int16 maps (16-bit ids), and ``prev_thr`` / ``out_thr``
+    ([h][w] float32) hand on only each list's 8th logit instead
+    (sad_propagate_topk_widths)."""
     n = derived.shape[0]
     _need(derived, "derived", torch.float32, (n, REC))
     pbits = _map_bits(prev, "prev", h, w) if prev is not None else 32
@@ -84,14 +87,18 @@ def propagate_topk(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | N
     obits = _map_bits(out, "out", h, w)
     if out_scores is not None:
         _need(out_scores, "out_scores", torch.float32, (h, w, K))
+    for t, name in ((prev_thr, "prev_thr"), (out_thr, "out_thr")):
+        if t is not None:
+            _need(t, name, torch.float32, (h, w))
     tail = (int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF, int(pass_index) & 0xFFFFFFFF, int(inject), _stream(derived))
-    if pbits == 32 and obits == 32:
+    if pbits == 32 and obits == 32 and prev_thr is None and out_thr is None:
         st = _native.lib().sad_propagate_topk(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
                                               _ptr(out_scores), *tail)
         _native.check("sad_propagate_topk", st)
     else:
         st = _native.lib().sad_propagate_topk_widths(_ptr(derived), n, h, w, _ptr(prev), pbits, _ptr(prev_scores),
-                                                     _ptr(out), obits, _ptr(out_scores), *tail)
+                                                     _ptr(prev_thr), _ptr(out), obits, _ptr(out_scores),
+                                                     _ptr(out_thr), *tail)
         _native.check("sad_propagate_topk_widths", st)
     return out
 
@@ -323,10 +330,12 @@ def jfa_flood(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor, step: i
 def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor,
                target: torch.Tensor, grad: torch.Tensor, *, stride: int, seed: int, pass_index: int,
                inject: int = 64, prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None,
-               loss: torch.Tensor | None = None, image: torch.Tensor | None = None) -> torch.Tensor:
+               loss: torch.Tensor | None = None, image: torch.Tensor | None = None,
+               prev_thr: torch.Tensor | None = None) -> torch.Tensor:
     """propagate_topk(...) into ``out`` followed by render_bwd over ``out``, in
     one call (both launches checked before either is enqueued).  ``prev`` may
-    be an int16 map (16-bit ids); ``out`` has 32-bit ids."""
+    be an int16 map (16-bit ids) and come with ``prev_thr`` (each list's 8th
+    logit) instead of ``prev_scores``; ``out`` has 32-bit ids."""
     n = derived.shape[0]
     _need(derived, "derived", torch.float32, (n, REC))
     pbits = _map_bits(prev, "prev", h, w) if prev is not None else 32
@@ -343,13 +352,15 @@ def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None,
         _need(image, "image", torch.float32, (h, w, 3))
     tail = (int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF, int(pass_index) & 0xFFFFFFFF, int(inject), _ptr(target),
             _ptr(grad), _ptr(loss), _ptr(image), _stream(derived))
-    if pbits == 32:
+    if prev_thr is not None:
+        _need(prev_thr, "prev_thr", torch.float32, (h, w))
+    if pbits == 32 and prev_thr is None:
         st = _native.lib().sad_step_fused(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
                                           _ptr(out_scores), *tail)
         _native.check("sad_step_fused", st)
     else:
         st = _native.lib().sad_step_fused_widths(_ptr(derived), n, h, w, _ptr(prev), pbits, _ptr(prev_scores),
-                                                 _ptr(out), _ptr(out_scores), *tail)
+                                                 _ptr(prev_thr), _ptr(out), _ptr(out_scores), *tail)
         _native.check("sad_step_fused_widths", st)
     return out
 

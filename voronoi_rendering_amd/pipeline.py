@@ -75,9 +75,10 @@ class SadField:
         # logits of each map's entries, valid while the sites do not change
         self.scores = [torch.empty((self.h, self.w, ops.K), dtype=torch.float32, device=dev) for _ in range(2)]
         self.scores_valid = False
-        # 16-bit-id maps through which a step's passes hand on their lists
-        # (made on first use; only when every id fits in 16 bits)
+        # 16-bit-id maps and 8th-logit maps through which a step's passes hand
+        # on their lists (made on first use; only when every id fits in 16 bits)
         self.maps16 = None
+        self.thr = None
         self.cur = 0
         self.pass_index = 0
         self.adam_t = 0
@@ -162,21 +163,23 @@ class SadField:
             return
         if self.params.shape[0] > 0xFFFF or len(strides) < 2:
             self.propagate(strides[:-1])
-            prev, prev_scores = self.maps[self.cur], self.scores[self.cur] if self.scores_valid else None
+            prev, prev_thr = self.maps[self.cur], None
+            prev_scores = self.scores[self.cur] if self.scores_valid else None
         else:
-            # the passes before the last hand their lists on with 16-bit ids
-            # (48 instead of 64 bytes per pixel each way with the logits)
+            # the passes before the last hand their lists on with 16-bit ids and
+            # only each list's 8th logit (20 instead of 64 bytes per pixel each way)
             if self.maps16 is None:
-                self.maps16 = [torch.empty((self.h, self.w, ops.K), dtype=torch.int16, device=self.params.device)
-                               for _ in range(2)]
-            prev, sc = self.maps[self.cur], self.cur
-            prev_scores = self.scores[sc] if self.scores_valid else None
+                dev = self.params.device
+                self.maps16 = [torch.empty((self.h, self.w, ops.K), dtype=torch.int16, device=dev) for _ in range(2)]
+                self.thr = [torch.empty((self.h, self.w), dtype=torch.float32, device=dev) for _ in range(2)]
+            prev, prev_thr = self.maps[self.cur], None
+            prev_scores = self.scores[self.cur] if self.scores_valid else None
             for k, s in enumerate(strides[:-1]):
-                out = self.maps16[k % 2]
+                out, out_thr = self.maps16[k % 2], self.thr[k % 2]
                 ops.propagate_topk(self.derived, self.h, self.w, prev, out, stride=int(s), seed=self.seed,
                                    pass_index=self.pass_index, inject=self.inject, prev_scores=prev_scores,
-                                   out_scores=self.scores[1 - sc])
-                prev, sc, prev_scores = out, 1 - sc, self.scores[1 - sc]
+                                   prev_thr=prev_thr, out_thr=out_thr)
+                prev, prev_scores, prev_thr = out, None, out_thr
                 self.pass_index += 1
         if before_last is not None:
             before_last()
@@ -184,7 +187,7 @@ class SadField:
         # sites next, so the following pass recomputes them anyway.
         ops.step_fused(self.derived, self.h, self.w, prev, self.maps[1 - self.cur], target, self.grad,
                        stride=int(strides[-1]), seed=self.seed, pass_index=self.pass_index, inject=self.inject,
-                       prev_scores=prev_scores, out_scores=None, loss=self.loss)
+                       prev_scores=prev_scores, out_scores=None, loss=self.loss, prev_thr=prev_thr)
         self.cur = 1 - self.cur
         self.pass_index += 1
         self.scores_valid = False
