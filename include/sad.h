@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 8
+#define SAD_ABI_VERSION 9
 #define SAD_K 8
 #define SAD_SITE_STRIDE 12
 #define SAD_EMPTY 0xffffffffu
@@ -142,14 +142,18 @@ int sad_propagate_topk(const float *derived, int32_t n, int32_t h, int32_t w, co
                        uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, void *stream);
 
 /*
- * sad_propagate_topk with a choice of id width for each map and a shorter
- * form of the logits handed from pass to pass (the same pass of Sec. 4.3).
- * prev_bits and next_bits are 16 or 32, the width of topk_prev's and
- * topk_next's ids.  A map of width 16 is [h][w][8] uint16 (16 bytes per pixel)
- * with the empty slot 0xffff; it needs n <= 65535 (SAD_EUNSUPPORTED
- * otherwise), so that every usable id is below 0xffff.  The lists are those
- * sad_propagate_topk writes, id for id (0xffff where it writes 0xffffffff), and
- * an input id at or above n is dropped as there.
+ * The maps a propagation pass (Sec. 4.3) reads and writes, for
+ * sad_propagate_pass and sad_step_fused_pass: sad_propagate_topk's four, with
+ * a choice of id width for each list map and two shorter forms of what passes
+ * hand on to each other within a training step.
+ *   topk_prev, scores_prev, topk_next, scores_next   as sad_propagate_topk
+ *   prev_bits, next_bits   16 or 32, the width of topk_prev's and topk_next's
+ *              ids.  A map of width 16 is [h][w][8] uint16 (16 bytes per
+ *              pixel) with the empty slot 0xffff; it needs n <= 65535
+ *              (SAD_EUNSUPPORTED otherwise), so that every usable id is below
+ *              0xffff.  The lists are those of width 32, id for id (0xffff
+ *              where that map holds 0xffffffff); an input id at or above n is
+ *              dropped as there.
  *   thr_prev   NULL, or [h][w] float32: the logit of each previous list's 8th
  *              entry (-inf where the list is shorter), as written to thr_next
  *              by the pass that produced topk_prev with the same prepared
@@ -161,15 +165,41 @@ int sad_propagate_topk(const float *derived, int32_t n, int32_t h, int32_t w, co
  *              Thresholds made before the sites changed give wrong lists.
  *   thr_next   NULL, or [h][w] float32 written with the logit of each new
  *              list's 8th entry (-inf where it is shorter).
- * Within a training step the passes can hand their lists on at width 16 with
- * their thresholds: a pass then moves 20 instead of 64 bytes per pixel each
- * way.  Other arguments and checks as sad_propagate_topk; no two of the six
- * maps may overlap (each measured on its own size).
+ *   probe_prev NULL, or [n][4] float32 (16-byte aligned): the sites' probe
+ *              records as written to probe_next from the same prepared sites.
+ *              The pass then decides which of a tile's probe ids can enter
+ *              any of its lists from these 16-byte records instead of the
+ *              48-byte prepared ones; the lists are the same.  Records made
+ *              before the sites changed give wrong lists.
+ *   probe_next NULL, or [n][4] float32 (16-byte aligned) written with every
+ *              site's probe record: (x, y, tau m, tau r) of its prepared
+ *              record, m the smaller inverse scale, or (x, y, 0, +inf) for a
+ *              site whose bound is not kept (non-finite values, tau <= 0,
+ *              scales more than 1024 apart).  Not written for an empty image.
+ * No two of these buffers and derived may overlap (each measured on its own
+ * size).  Within a training step the passes after the first can hand
+ * their lists on at width 16 with their thresholds and read the first pass's
+ * probe records: a pass then moves 20 instead of 64 bytes per pixel each way.
  */
-int sad_propagate_topk_widths(const float *derived, int32_t n, int32_t h, int32_t w, const void *topk_prev,
-                              int32_t prev_bits, const float *scores_prev, const float *thr_prev, void *topk_next,
-                              int32_t next_bits, float *scores_next, float *thr_next, int32_t stride, uint64_t seed,
-                              uint32_t pass_index, int32_t inject_per_tile, void *stream);
+typedef struct sad_pass_maps {
+    const void *topk_prev;
+    const float *scores_prev;
+    const float *thr_prev;
+    const float *probe_prev;
+    void *topk_next;
+    float *scores_next;
+    float *thr_next;
+    float *probe_next;
+    int32_t prev_bits;
+    int32_t next_bits;
+} sad_pass_maps;
+
+/*
+ * sad_propagate_topk on the maps of a sad_pass_maps (maps: a HOST pointer,
+ * read during the call).  Other arguments and checks as sad_propagate_topk.
+ */
+int sad_propagate_pass(const float *derived, int32_t n, int32_t h, int32_t w, const sad_pass_maps *maps,
+                       int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, void *stream);
 
 /*
  * Soft additively weighted render (Sec. 4.2): per pixel, the softmax of the
@@ -402,21 +432,19 @@ int sad_step_fused(const float *derived, int32_t n, int32_t h, int32_t w, const 
                    float *image, void *stream);
 
 /*
- * sad_step_fused reading a previous map of width prev_bits (16 or 32, as
- * sad_propagate_topk_widths; width 16 needs n <= 65535) and optionally only
- * its lists' 8th logits (thr_prev, as there; not with scores_prev): the last
- * pass of a step whose earlier passes handed their lists on in that form.
- * topk_next is written with 32-bit ids, as sad_step_fused writes it.  With
- * thr_prev the backward evaluates the pixels' logits from the site records it
- * stages anyway, rather than taking them from the pass.  In addition to the
- * checks of sad_step_fused, grad, loss and image must not overlap topk_prev,
- * scores_prev or thr_prev.
+ * sad_step_fused on the maps of a sad_pass_maps (maps: a HOST pointer, read
+ * during the call): the last pass of a step whose earlier passes handed their
+ * lists on at width 16, with thresholds or probe records.  The pass writes
+ * 32-bit ids (next_bits = 32) and no thresholds or probe records (thr_next
+ * and probe_next NULL; SAD_EINVAL otherwise).  With thr_prev the backward
+ * evaluates the pixels' logits from the site records it stages anyway,
+ * rather than taking them from the pass.  In addition to the checks of
+ * sad_step_fused, grad, loss and image must not overlap topk_prev,
+ * scores_prev, thr_prev or probe_prev.
  */
-int sad_step_fused_widths(const float *derived, int32_t n, int32_t h, int32_t w, const void *topk_prev,
-                          int32_t prev_bits, const float *scores_prev, const float *thr_prev, uint32_t *topk_next,
-                          float *scores_next, int32_t stride, uint64_t seed, uint32_t pass_index,
-                          int32_t inject_per_tile, const float *target, float *grad, float *loss, float *image,
-                          void *stream);
+int sad_step_fused_pass(const float *derived, int32_t n, int32_t h, int32_t w, const sad_pass_maps *maps,
+                        int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject_per_tile,
+                        const float *target, float *grad, float *loss, float *image, void *stream);
 
 /*
  * One Adam step (Kingma & Ba) on the site parameters (Sec. 5: per-parameter

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
                  "sad_jfa_flood", "sad_budget_workspace_bytes", "sad_densify_prune", "sad_init_workspace_bytes",
                  "sad_init_sites", "sad_pack_sites", "sad_query_packed",
                  "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version",
-                 "sad_propagate_topk_widths", "sad_step_fused_widths"):
+                 "sad_propagate_pass", "sad_step_fused_pass"):
         assert name in syms
 
 
@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sad_abi_version() == 8
+    assert lib.sad_abi_version() == 9
     for st in (0, -1, -2, -3, 7):
         assert lib.sad_status_string(st)
 
@@ -90,50 +90,69 @@ def test_propagate_rejects(lib):
     assert call(h=0, nxt=None) == 0  # empty image
 
 
-def test_propagate_widths_rejects(lib):
-    """The variant with id widths and 8th-logit maps: widths other than 16
-    and 32, 16-bit maps with more than 65,535 sites, threshold maps without a
-    previous map or together with a score map, and overlaps measured on each
-    map's own size (for 8x8 pixels a 16-bit map is 1 KiB, a threshold map
-    256 bytes)."""
-    f = lib.sad_propagate_topk_widths
-    ok = dict(derived=P, n=10, h=8, w=8, prev=P + 65536, pb=16, sprev=None, tprev=None, nxt=P + 4096, nb=16,
-              snext=None, tnext=None, stride=1, seed=0, pi=0, inj=64)
+def test_propagate_pass_rejects(lib):
+    """The pass on a sad_pass_maps: widths other than 16 and 32, 16-bit maps
+    with more than 65,535 sites, threshold maps without a previous map or
+    together with a score map, misaligned probe records, and overlaps
+    measured on each buffer's own size (for 8x8 pixels a 16-bit map is 1 KiB,
+    a threshold map 256 bytes; 10 sites' probe records are 160 bytes, their
+    prepared records 480)."""
+    from voronoi_rendering_amd._native import PassMaps
 
-    def call(**kw):
-        a = dict(ok, **kw)
-        return f(a["derived"], a["n"], a["h"], a["w"], a["prev"], a["pb"], a["sprev"], a["tprev"], a["nxt"], a["nb"],
-                 a["snext"], a["tnext"], a["stride"], a["seed"], a["pi"], a["inj"], None)
+    f = lib.sad_propagate_pass
+    base = dict(topk_prev=P + 65536, prev_bits=16, topk_next=P + 4096, next_bits=16)
 
-    assert call(pb=8) == EINVAL
-    assert call(nb=64) == EINVAL
-    assert call(pb=0, prev=None) == EINVAL  # the width is checked even without a previous map
+    def call(n=10, **kw):
+        m = PassMaps(**dict(base, **kw))
+        return f(P, n, 8, 8, C.byref(m), 1, 0, 0, 64, None)
+
+    assert f(P, 10, 8, 8, None, 1, 0, 0, 64, None) == EINVAL  # no maps
+    assert call(prev_bits=8) == EINVAL
+    assert call(next_bits=64) == EINVAL
+    assert call(prev_bits=0, topk_prev=None) == EINVAL  # the width is checked even without a previous map
     assert call(n=65536) == EUNSUP  # 16-bit ids need n <= 65535
-    assert call(n=65536, nb=32) == EUNSUP
-    assert call(prev=P + 4096 + 1008) == EINVAL  # 16-bit maps overlap in their last 16 bytes
-    assert call(nxt=P + 4100) == EINVAL  # misaligned
-    assert call(sprev=P + 8192, snext=P + 8192 + 2032) == EINVAL  # score maps overlap (2 KiB each)
-    assert call(snext=P + 4096 + 512) == EINVAL  # next scores inside the next map
-    assert call(tprev=P + 8192, prev=None) == EINVAL  # thresholds without a previous map
-    assert call(tprev=P + 8192, sprev=P + 12288) == EINVAL  # thresholds and scores together
-    assert call(tprev=P + 8194) == EINVAL  # misaligned thresholds
-    assert call(tprev=P + 8192, tnext=P + 8192 + 252) == EINVAL  # threshold maps overlap (256 bytes each)
-    assert call(tnext=P + 65536 + 1020) == EINVAL  # next thresholds over the previous map
-    assert call(tprev=P + 4096 + 1000) == EINVAL  # previous thresholds over the next map
-    g = lib.sad_step_fused_widths
+    assert call(n=65536, next_bits=32) == EUNSUP
+    assert call(topk_prev=P + 4096 + 1008) == EINVAL  # 16-bit maps overlap in their last 16 bytes
+    assert call(topk_next=P + 4100) == EINVAL  # misaligned
+    assert call(topk_next=None) == EINVAL
+    assert call(scores_prev=P + 8192, scores_next=P + 8192 + 2032) == EINVAL  # score maps overlap (2 KiB each)
+    assert call(scores_next=P + 4096 + 512) == EINVAL  # next scores inside the next map
+    assert call(thr_prev=P + 8192, topk_prev=None) == EINVAL  # thresholds without a previous map
+    assert call(scores_prev=P + 8192, topk_prev=None) == EINVAL  # scores without a previous map
+    assert call(thr_prev=P + 8192, scores_prev=P + 12288) == EINVAL  # thresholds and scores together
+    assert call(thr_prev=P + 8194) == EINVAL  # misaligned thresholds
+    assert call(thr_prev=P + 8192, thr_next=P + 8192 + 252) == EINVAL  # threshold maps overlap (256 bytes each)
+    assert call(thr_next=P + 65536 + 1020) == EINVAL  # next thresholds over the previous map
+    assert call(thr_prev=P + 4096 + 1000) == EINVAL  # previous thresholds over the next map
+    assert call(probe_prev=P + 8200) == EINVAL  # misaligned probe records
+    assert call(probe_next=P + 8200) == EINVAL
+    assert call(probe_next=P + 464) == EINVAL  # probe records over the prepared records
+    assert call(probe_prev=P + 8192, probe_next=P + 8192 + 144) == EINVAL  # the two record arrays overlap
+    assert call(probe_next=P + 65536 + 1008) == EINVAL  # records over the previous map
+    assert call(probe_next=P + 4096 + 1008) == EINVAL  # records over the next map
+    assert call(probe_prev=P + 4096 + 1008) == EINVAL  # previous records over the next map
+    assert call(probe_prev=P + 320) == EINVAL  # previous records over the prepared records
+    assert call(probe_prev=P + 65536 + 512) == EINVAL  # previous records over the previous map
+    g = lib.sad_step_fused_pass
     G, T = P + (1 << 20), P + (2 << 20)  # grad and target, apart from everything
+    fbase = dict(topk_prev=P + 65536, prev_bits=16, topk_next=P + 4096, next_bits=32)
 
-    def fused(**kw):
-        a = dict(dict(prev=P + 65536, pb=16, tprev=None, nxt=P + 4096, n=10, grad=G, loss=None, image=None), **kw)
-        return g(P, a["n"], 8, 8, a["prev"], a["pb"], None, a["tprev"], a["nxt"], None, 1, 0, 0, 64, T, a["grad"],
-                 a["loss"], a["image"], None)
+    def fused(n=10, grad=G, loss=None, image=None, **kw):
+        m = PassMaps(**dict(fbase, **kw))
+        return g(P, n, 8, 8, C.byref(m), 1, 0, 0, 64, T, grad, loss, image, None)
 
+    assert g(P, 10, 8, 8, None, 1, 0, 0, 64, T, G, None, None, None) == EINVAL  # no maps
     assert fused(n=65536) == EUNSUP
-    assert fused(pb=24) == EINVAL
+    assert fused(prev_bits=24) == EINVAL
+    assert fused(next_bits=16) == EINVAL  # the fused pass writes 32-bit lists
+    assert fused(thr_next=P + 8192) == EINVAL  # and no thresholds
+    assert fused(probe_next=P + 8192) == EINVAL  # or probe records
     assert fused(grad=None) == EINVAL
     assert fused(grad=P + 65536) == EINVAL  # gradients over the previous map
-    assert fused(tprev=P + 8192, loss=P + 8192 + 8) == EINVAL  # loss inside the thresholds
+    assert fused(thr_prev=P + 8192, loss=P + 8192 + 8) == EINVAL  # loss inside the thresholds
     assert fused(image=P + 65536 + 512) == EINVAL  # image over the previous map
+    assert fused(probe_prev=P + 8192, loss=P + 8192 + 152) == EINVAL  # loss inside the probe records
+    assert fused(probe_prev=G + 48) == EINVAL  # gradients over the probe records
 
 
 def test_render_query_adam_reject(lib):

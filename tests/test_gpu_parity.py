@@ -253,9 +253,9 @@ def test_c2_map_quality(sad, ref):
 def test_bench_map_step(sad, ref):
     """The launch configuration the bench times: the 768x512 / 50k-site map
     built by the full refresh and settled by 500 steps, then one more step
-    (stride-8 pass with the logits recomputed, passes with score maps, the
-    backward): every pass and the gradients against the oracle run on the
-    GPU's map."""
+    as the bench runs it, then one pass by pass (stride-8 pass with the logits
+    recomputed, passes with score maps, the backward): the lists and the
+    gradients against the oracle run on the GPU's map."""
     from voronoi_rendering_amd.pipeline import SadField
 
     wl = synth.C2
@@ -268,8 +268,24 @@ def test_bench_map_step(sad, ref):
     for _ in range(500):
         f.sites_changed()
         f.step(list(wl.strides), tgt, fused=True)
+    # the step as the bench runs it (16-bit hand-off, thresholds, probe
+    # records, the fused last pass): each pass's lists are the oracle's, so
+    # the last map must be the oracle's chain, and the gradients its backward's
     f.sites_changed()
     prev = map_to_np(f.topk)
+    first = f.pass_index
+    f.grad.zero_()
+    f.loss.zero_()
+    f.step(list(wl.strides), tgt, fused=True)
+    for k, s in enumerate(wl.strides):
+        prev = ref.propagate(d, wl.h, wl.w, prev, s, wl.inject_seed, first + k, wl.inject)
+    got = map_to_np(f.topk)
+    assert np.array_equal(got, prev), f"step: {(got != prev).any(-1).sum()} pixels differ"
+    g_ref, _, loss_ref, _ = ref.render_bwd(d, wl.h, wl.w, prev, tgt_np)
+    assert abs(f.loss.item() - loss_ref) <= 1e-5 * loss_ref
+    assert_grad_close(to_np(f.grad), g_ref, "step gradients")
+    # then pass by pass on 32-bit maps with score maps
+    f.sites_changed()
     for s in wl.strides:
         first = f.pass_index
         f.propagate([s])
@@ -1178,6 +1194,91 @@ def test_step_fused_from_thresholds(sad, ref):
         assert_colour_close(to_np(img), img_ref, f"{h}x{w} image")
         assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
         assert_grad_close(to_np(grad), g_ref, f"{h}x{w} gradients from thresholds")
+
+
+def probe_records_np(d: np.ndarray) -> np.ndarray:
+    """The probe records the pass writes, restated from the prepared records
+    (x, y, tau, r, cos, sin, 1/s1, 1/s2, ...): (x, y, tau m, tau r) in
+    float32 with m the smaller inverse scale, or (x, y, 0, inf) where the
+    bound is not kept (non-finite values, tau <= 0, m <= 0, scales more than
+    1024 apart)."""
+    x, y, tau, r = d[:, 0], d[:, 1], d[:, 2], d[:, 3]
+    m, M = np.minimum(d[:, 6], d[:, 7]), np.maximum(d[:, 6], d[:, 7])
+    with np.errstate(all="ignore"):
+        ok = (np.isfinite(x) & np.isfinite(y) & np.isfinite(tau) & np.isfinite(r) & np.isfinite(M) & (tau > 0)
+              & (m > 0) & (M <= np.float32(1024) * m))
+        out = np.stack([x, y, np.where(ok, tau * m, np.float32(0)), np.where(ok, tau * r, np.float32(np.inf))], 1)
+    return out.astype(np.float32)
+
+
+@pytest.mark.parametrize("n,bits", [(300, 16), (3000, 32), (3000, 16)])
+def test_propagate_probe_records(sad, ref, n, bits):
+    """Passes that cull their probes from the sites' 16-byte probe records:
+    the first pass writes them (checked against their definition), and from
+    there every pass of a chain through strides 8 ... 1 and back gives the
+    oracle's lists bit for bit, on sites far outside the workloads' ranges
+    (anisotropy up to e^14, where records carry no bound, a tenth of the sites
+    far away, inactive sites); with 16-bit maps and thresholds as a step hands
+    them on, or 32-bit maps."""
+    h, w = 60, 90
+    rec = synth.SiteRecipe(ls_lo=-6.0, ls_hi=8.0, r_lo=-5.0, r_hi=20.0, logtau_lo=-6.0, logtau_hi=6.0)
+    p = synth.sites(5151 + n, n, h, w, rec)
+    rng = np.random.default_rng(n + bits)
+    far = rng.random(n) < 0.1
+    p[far, 0] *= np.float32(1000.0)
+    p[far, 1] *= np.float32(1000.0)
+    p[rng.random(n) < 0.05, 0] = -1.0  # inactive
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p))
+    m = ref.propagate_schedule(d, h, w, None, synth.jfa_strides(h, w, 12), 37, 0, 64)
+    probe = torch.empty((n, 4), dtype=torch.float32, device=dev())
+    dt = torch.int16 if bits == 16 else torch.int32
+    prev = map16_from_np(m) if bits == 16 else to_gpu(m)
+    thr = None
+    for t, stride in enumerate((8, 4, 2, 1, 1, 3, 2, 1)):
+        want = ref.propagate(d, h, w, m, stride, 37, 12 + t, 64)
+        out = torch.empty((h, w, 8), dtype=dt, device=dev())
+        out_thr = torch.empty((h, w), dtype=torch.float32, device=dev()) if bits == 16 else None
+        sad.propagate_topk(dg, h, w, prev, out, stride=stride, seed=37, pass_index=12 + t, inject=64,
+                           prev_thr=thr, out_thr=out_thr, prev_probe=probe if t > 0 else None,
+                           out_probe=probe if t == 0 else None)
+        if t == 0:
+            got_rec, want_rec = to_np(probe), probe_records_np(to_np(dg))
+            assert np.array_equal(got_rec.view(np.uint32), want_rec.view(np.uint32)), \
+                np.argwhere(got_rec.view(np.uint32) != want_rec.view(np.uint32))[:4]
+            assert (got_rec[:, 3] == np.inf).any() and (got_rec[:, 3] < np.inf).any()
+        got = map16_to_np(out) if bits == 16 else map_to_np(out)
+        assert np.array_equal(got, want), f"pass {t} stride {stride}: {np.argwhere(got != want)[:4]}"
+        m, prev, thr = want, out, out_thr
+
+
+def test_step_fused_from_probe_records(sad, ref):
+    """The fused last pass + backward culling its probes from the probe
+    records a pass wrote, from a 16-bit map with thresholds and from a 32-bit
+    map: the oracle's lists, loss and gradients."""
+    h, w, n, npass = 96, 128, 1500, 14
+    p = synth.sites(900 + n, n, h, w, synth.WIDE_SCALES)
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p))
+    m = ref.propagate_schedule(d, h, w, None, synth.jfa_strides(h, w, npass), 43, 0, 64)
+    probe = torch.empty((n, 4), dtype=torch.float32, device=dev())
+    scratch = torch.empty((h, w, 8), dtype=torch.int32, device=dev())
+    sad.propagate_topk(dg, h, w, to_gpu(m), scratch, stride=2, seed=43, pass_index=99, inject=64, out_probe=probe)
+    m1 = ref.propagate(d, h, w, m, 1, 43, npass, 64)
+    tgt = synth.target_noise_edges(910 + n, h, w)
+    g_ref, _, loss_ref, img_ref = ref.render_bwd(d, h, w, m1, tgt)
+    thr = torch.from_numpy(eighth_logits(ref, d, m)).to(dev())
+    for prev, prev_thr in ((map16_from_np(m), thr), (to_gpu(m), None)):
+        out = torch.empty((h, w, 8), dtype=torch.int32, device=dev())
+        grad = torch.zeros((n, 12), dtype=torch.float32, device=dev())
+        loss = torch.zeros(1, dtype=torch.float32, device=dev())
+        img = torch.empty((h, w, 3), dtype=torch.float32, device=dev())
+        sad.step_fused(dg, h, w, prev, out, to_gpu(tgt), grad, stride=1, seed=43, pass_index=npass, inject=64,
+                       loss=loss, image=img, prev_thr=prev_thr, prev_probe=probe)
+        assert np.array_equal(map_to_np(out), m1), "lists"
+        assert_colour_close(to_np(img), img_ref, "image")
+        assert abs(loss.item() - loss_ref) <= 1e-5 * loss_ref
+        assert_grad_close(to_np(grad), g_ref, "gradients with probe records")
 
 
 def test_step_fused_from_16bit_map(sad, ref, c2_state):

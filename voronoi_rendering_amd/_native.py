@@ -15,7 +15,18 @@ SAD_EINVAL = -1
 SAD_EUNSUPPORTED = -2
 SAD_EHIP = -3
 
-# every symbol include/sad.h declares, with (restype, argtypes)
+
+
+class PassMaps(C.Structure):
+    """struct sad_pass_maps of include/sad.h (device addresses, 0 for NULL)."""
+    _fields_ = [("topk_prev", C.c_void_p), ("scores_prev", C.c_void_p), ("thr_prev", C.c_void_p),
+                ("probe_prev", C.c_void_p), ("topk_next", C.c_void_p), ("scores_next", C.c_void_p),
+                ("thr_next", C.c_void_p), ("probe_next", C.c_void_p), ("prev_bits", C.c_int32),
+                ("next_bits", C.c_int32)]
+
+
+# every symbol include/sad.h declares, with (restype, argtypes); a
+# PassMaps argument is passed as C.byref(...) to a c_void_p slot
 _f32p = C.c_void_p
 _SIGS = {
     "sad_abi_version": (C.c_int, []),
@@ -24,13 +35,11 @@ _SIGS = {
     "sad_propagate_topk": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                      C.c_void_p, C.c_void_p, C.c_int32, C.c_uint64, C.c_uint32, C.c_int32,
                                      C.c_void_p]),
-    "sad_propagate_topk_widths": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_int32,
-                                            C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
-                                            C.c_int32, C.c_uint64, C.c_uint32, C.c_int32, C.c_void_p]),
-    "sad_step_fused_widths": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_int32,
-                                        C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_uint64,
-                                        C.c_uint32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
-                                        C.c_void_p]),
+    "sad_propagate_pass": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_int32,
+                                     C.c_uint64, C.c_uint32, C.c_int32, C.c_void_p]),
+    "sad_step_fused_pass": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_int32,
+                                      C.c_uint64, C.c_uint32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                      C.c_void_p, C.c_void_p]),
     "sad_render_fwd": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                  C.c_void_p]),
     "sad_render_bwd": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,

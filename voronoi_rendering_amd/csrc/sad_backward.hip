@@ -635,22 +635,23 @@ extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_
     return bwd_launch(b, stream);
 }
 
-// Checks and launch of the fused last pass + backward (prev_bits: the id
-// width of topk_prev; the new lists are written with 32-bit ids).
-static int step_fused(const float* derived, int32_t n, int32_t h, int32_t w, const void* topk_prev, int32_t prev_bits,
-                      const float* scores_prev, const float* thr_prev, uint32_t* topk_next, float* scores_next,
-                      int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, const float* target,
-                      float* grad, float* loss, float* image, void* stream) {
+// Checks and launch of the fused last pass + backward (the new lists are
+// written with 32-bit ids).
+static int step_fused(const float* derived, int32_t n, int32_t h, int32_t w, const sad_pass_maps& m, int32_t stride,
+                      uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, const float* target, float* grad,
+                      float* loss, float* image, void* stream) {
+    // the pass writes 32-bit lists and, optionally, their logits: nothing else
+    if (m.next_bits != 32 || m.thr_next || m.probe_next) return SAD_EINVAL;
     PropArgs pa;
-    int st = prop_setup(derived, n, h, w, topk_prev, prev_bits, scores_prev, thr_prev, topk_next, 32, scores_next,
-                        nullptr, stride, seed, pass_index, inject_per_tile, pa);
+    int st = prop_setup(derived, n, h, w, m, stride, seed, pass_index, inject_per_tile, pa);
     if (st != SAD_OK) return st;
+    uint32_t* const topk_next = static_cast<uint32_t*>(m.topk_next);
     BwdArgs b;
     st = bwd_setup(derived, n, h, w, topk_next, target, grad, loss, image, b);
     if (st != SAD_OK) return st;
     // the pass's outputs must not share memory with anything else the step reads or writes
     const int64_t pix = int64_t(h) * w, mbytes = pix * K * 4, gbytes = int64_t(n) * REC * 4;
-    const void* outs[2] = {topk_next, scores_next};
+    const void* outs[2] = {topk_next, m.scores_next};
     const void* others[5] = {target, grad, loss, image, derived};
     const int64_t obytes[5] = {pix * 12, gbytes, 4, pix * 12, gbytes};
     for (int o = 0; o < 2; ++o)
@@ -659,10 +660,10 @@ static int step_fused(const float* derived, int32_t n, int32_t h, int32_t w, con
     // nor may the backward's outputs share memory with the pass's inputs
     const void* bouts[3] = {grad, loss, image};
     const int64_t bbytes[3] = {gbytes, 4, pix * 12};
-    const void* pins[3] = {topk_prev, scores_prev, thr_prev};
-    const int64_t pbytes[3] = {pix * K * (prev_bits / 8), pix * K * 4, pix * 4};
+    const void* pins[4] = {m.topk_prev, m.scores_prev, m.thr_prev, m.probe_prev};
+    const int64_t pbytes[4] = {pix * K * (m.prev_bits / 8), pix * K * 4, pix * 4, int64_t(n) * 16};
     for (int o = 0; o < 3; ++o)
-        for (int q = 0; q < 3; ++q)
+        for (int q = 0; q < 4; ++q)
             if (overlap(bouts[o], bbytes[o], pins[q], pbytes[q])) return SAD_EINVAL;
     if (pix == 0) return SAD_OK;
     // every check has passed: one kernel, one workgroup per backward region
@@ -694,15 +695,14 @@ extern "C" int sad_step_fused(const float* derived, int32_t n, int32_t h, int32_
                               const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride,
                               uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, const float* target,
                               float* grad, float* loss, float* image, void* stream) {
-    return step_fused(derived, n, h, w, topk_prev, 32, scores_prev, nullptr, topk_next, scores_next, stride, seed,
+    return step_fused(derived, n, h, w, maps32(topk_prev, scores_prev, topk_next, scores_next), stride, seed,
                       pass_index, inject_per_tile, target, grad, loss, image, stream);
 }
 
-extern "C" int sad_step_fused_widths(const float* derived, int32_t n, int32_t h, int32_t w, const void* topk_prev,
-                                     int32_t prev_bits, const float* scores_prev, const float* thr_prev,
-                                     uint32_t* topk_next, float* scores_next, int32_t stride, uint64_t seed,
-                                     uint32_t pass_index, int32_t inject_per_tile, const float* target, float* grad,
-                                     float* loss, float* image, void* stream) {
-    return step_fused(derived, n, h, w, topk_prev, prev_bits, scores_prev, thr_prev, topk_next, scores_next, stride,
-                      seed, pass_index, inject_per_tile, target, grad, loss, image, stream);
+extern "C" int sad_step_fused_pass(const float* derived, int32_t n, int32_t h, int32_t w, const sad_pass_maps* maps,
+                                   int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject_per_tile,
+                                   const float* target, float* grad, float* loss, float* image, void* stream) {
+    if (!maps) return SAD_EINVAL;
+    return step_fused(derived, n, h, w, *maps, stride, seed, pass_index, inject_per_tile, target, grad, loss, image,
+                      stream);
 }

@@ -46,6 +46,8 @@ struct PropArgs {
     uint16_t* next16;          // with 16-bit ids (exactly one of the two)
     float* next_scores;        // nullable: logits of next's entries are written here
     float* next_thr;           // nullable: the logit of each next list's 8th entry is written here
+    const float4* probe_prev;  // nullable: the sites' probe records (probe_record), for the tile cull
+    float4* probe_next;        // nullable: the sites' probe records are written here
     uint64_t seed;
     int32_t n, h, w, stride, inject, tiles_x, n_tiles;
     uint32_t pass_index;
@@ -64,15 +66,15 @@ constexpr int QCAP = 2 * K;  // queued neighbour ids per lane (2 lists of 8)
 // + 2 |r|), u = 2^-24, kappa = M/m the anisotropy ratio; for kappa <= 1024
 // this is below 2^-8 (tau sqrt(q) + tau |r|).  The bound therefore keeps a
 // 2^-8 relative margin on both terms, which also covers the rounding of the
-// bound's own evaluation.  Sites with non-finite values or extreme anisotropy
-// are never culled.
+// bound's own evaluation.  Sites with non-finite values, tau <= 0 (a logit
+// that does not fall with distance) or extreme anisotropy are never culled.
 __device__ __forceinline__ bool probe_may_enter(const Geo& g, float thr, float bx0, float bx1, float by0,
                                                 float by1) {
     float tau = g.g0.z, r = g.g0.w, is1 = g.g1.z, is2 = g.g1.w;
     float m = fminf(is1, is2), M = fmaxf(is1, is2);
     const bool fin_x = finitef(g.g0.x), fin_y = finitef(g.g0.y), fin_tau = finitef(tau), fin_r = finitef(r),
                fin_m = finitef(M);
-    const bool boundable = fin_x & fin_y & fin_tau & fin_r & fin_m & (m > 0.0f) & (M <= 1024.0f * m);
+    const bool boundable = fin_x & fin_y & fin_tau & fin_r & fin_m & (tau > 0.0f) & (m > 0.0f) & (M <= 1024.0f * m);
     float ex = fmaxf(fmaxf(bx0 - g.g0.x, g.g0.x - bx1), 0.0f);
     float ey = fmaxf(fmaxf(by0 - g.g0.y, g.g0.y - by1), 0.0f);
     float dist = __builtin_sqrtf(ex * ex + ey * ey);
@@ -80,6 +82,32 @@ __device__ __forceinline__ bool probe_may_enter(const Geo& g, float thr, float b
     float C = tau * r;
     float ub = (C - A * (1.0f - 0x1p-8f)) + 0x1p-8f * (tau * fabsf(r));
     return !boundable | !(ub < thr);  // values of an unboundable site are not used
+}
+
+// The probe record of a site: what probe_may_enter needs of it in 16 bytes,
+// (x, y, tau m, tau r) with m the smaller inverse scale, so that a pass that
+// probes sites it has no other use for gathers 16 instead of 32 bytes per
+// probe (and the records of all sites, 16 bytes each, stay in each XCD's L2).
+// A site the bound cannot cover gets (x, y, 0, +inf): never culled.
+__device__ __forceinline__ float4 probe_record(const Geo& g) {
+    const float tau = g.g0.z, r = g.g0.w, is1 = g.g1.z, is2 = g.g1.w;
+    const float m = fminf(is1, is2), M = fmaxf(is1, is2);
+    const bool boundable = finitef(g.g0.x) & finitef(g.g0.y) & finitef(tau) & finitef(r) & finitef(M) & (tau > 0.0f) &
+                           (m > 0.0f) & (M <= 1024.0f * m);
+    return make_float4(g.g0.x, g.g0.y, boundable ? tau * m : 0.0f, boundable ? tau * r : __builtin_inff());
+}
+
+// probe_may_enter from a probe record: the same bound with tau m and tau r
+// rounded once more (a few float32 roundings, far inside its 2^-8 margin);
+// an unboundable site's infinite tau r passes, as does anything NaN.
+__device__ __forceinline__ bool probe_record_may_enter(const float4 pr, float thr, float bx0, float bx1, float by0,
+                                                       float by1) {
+    const float ex = fmaxf(fmaxf(bx0 - pr.x, pr.x - bx1), 0.0f);
+    const float ey = fmaxf(fmaxf(by0 - pr.y, pr.y - by1), 0.0f);
+    const float dist = __builtin_sqrtf(ex * ex + ey * ey);
+    const float A = pr.z * dist, C = pr.w;
+    const float ub = (C - A * (1.0f - 0x1p-8f)) + 0x1p-8f * fabsf(C);
+    return !(ub < thr);
 }
 
 // A cheap screen in front of the exact logit of a queued neighbour id: false
@@ -217,6 +245,13 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
     const uint32_t n = (uint32_t)a.n;
     const bool have_prev = inside && has_prev;
 
+    // the sites' probe records for later passes: the wavefront of tile T writes
+    // those of sites 64 T + lane, 64 (T + n_tiles) + lane, ...
+    if (a.probe_next) {
+        for (int64_t si = (int64_t)tile * WAVE + lane; si < a.n; si += (int64_t)a.n_tiles * WAVE)
+            a.probe_next[si] = probe_record(load_geo(a.derived, (uint32_t)si));
+    }
+
     // Issue every independent load first: the pixel's list, the 4 neighbour
     // lists and this lane's probe site.  Every list load reads a pixel inside
     // the image (coordinates clamped), so no load waits on a branch; nb_ok
@@ -337,7 +372,7 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
                     for (int k = 0; k < K / 2; ++k) {
                         const int kk = half * 4 + k;
                         const float s = usable_logit(og[k], t.id[kk] < n, px, py);
-                        t.s[kk] = need & (t.id[kk] < n) ? s : t.s[kk];
+                        t.s[kk] = (need & (t.id[kk] < n)) ? s : t.s[kk];
                     }
                 }
                 lazy &= !need;
@@ -449,21 +484,27 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
 
     // 3. the tile's probe ids, culled by the tile bound
     if (a.inject > 0) {
+        const float bx0 = (float)(tx * TILE) + 0.5f, by0 = (float)(ty * TILE) + 0.5f;
+        const float bx1 = (float)min(tx * TILE + TILE - 1, a.w - 1) + 0.5f;
+        const float by1 = (float)min(ty * TILE + TILE - 1, a.h - 1) + 0.5f;
+        const float thr = wave_min(inside ? t.s[K - 1] : __builtin_inff());
         Geo pg;
         pg.g0 = make_float4(-1.f, -1.f, 0.f, 0.f);
         pg.g1 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (lane < a.inject) pg = load_geo(a.derived, pid);
-        const float thr = wave_min(inside ? t.s[K - 1] : __builtin_inff());
-        bool keep = false;
-        if (pg.g0.x >= 0.0f) {
-            const float bx0 = (float)(tx * TILE) + 0.5f, by0 = (float)(ty * TILE) + 0.5f;
-            const float bx1 = (float)min(tx * TILE + TILE - 1, a.w - 1) + 0.5f;
-            const float by1 = (float)min(ty * TILE + TILE - 1, a.h - 1) + 0.5f;
-            keep = probe_may_enter(pg, thr, bx0, bx1, by0, by1);
+        uint64_t mask;
+        if (a.probe_prev) {  // uniform
+            // cull on the 16-byte records; the survivors' lanes then fetch their full records at once
+            float4 pr = make_float4(-1.f, -1.f, 0.f, 0.f);
+            if (lane < a.inject) pr = a.probe_prev[pid];
+            const bool keep = (pr.x >= 0.0f) && probe_record_may_enter(pr, thr, bx0, bx1, by0, by1);
+            if (keep) pg = load_geo(a.derived, pid);
+            mask = __ballot(keep);
+        } else {
+            if (lane < a.inject) pg = load_geo(a.derived, pid);
+            mask = __ballot((pg.g0.x >= 0.0f) && probe_may_enter(pg, thr, bx0, bx1, by0, by1));
         }
-        uint64_t mask = __ballot(keep);
         while (mask) {
-            // the survivor's record is already in lane q's registers: broadcast it
+            // the survivor's record is in lane q's registers: broadcast it
             const int q = __builtin_ctzll(mask);
             mask &= mask - 1;
             const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)pid, q);
@@ -514,47 +555,51 @@ __device__ __forceinline__ void propagate_tile(const PropArgs& a, int tile, Queu
 // Argument checks of a propagation pass (shared by the entry points that run
 // one) and its kernel arguments.  Returns SAD_OK with a filled in, or the
 // error status.
-inline int prop_setup(const float* derived, int32_t n, int32_t h, int32_t w, const void* topk_prev,
-                      int32_t prev_bits, const float* scores_prev, const float* thr_prev, void* topk_next,
-                      int32_t next_bits, float* scores_next, float* thr_next, int32_t stride, uint64_t seed,
-                      uint32_t pass_index, int32_t inject_per_tile, PropArgs& a) {
+inline int prop_setup(const float* derived, int32_t n, int32_t h, int32_t w, const sad_pass_maps& m, int32_t stride,
+                      uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, PropArgs& a) {
     if (!sites_ok(n) || !image_ok(h, w) || stride < 1 || inject_per_tile < 0) return SAD_EINVAL;
-    if ((prev_bits != 16 && prev_bits != 32) || (next_bits != 16 && next_bits != 32)) return SAD_EINVAL;
+    if ((m.prev_bits != 16 && m.prev_bits != 32) || (m.next_bits != 16 && m.next_bits != 32)) return SAD_EINVAL;
     if (inject_per_tile > SAD_MAX_INJECT) return SAD_EUNSUPPORTED;
     // a 16-bit map needs every usable id below 0xffff, its empty slot
-    if ((prev_bits == 16 || next_bits == 16) && n > SMALL_IDS_MAX) return SAD_EUNSUPPORTED;
+    if ((m.prev_bits == 16 || m.next_bits == 16) && n > SMALL_IDS_MAX) return SAD_EUNSUPPORTED;
     const int64_t pix = int64_t(h) * w;
-    const int64_t pbytes = pix * K * (prev_bits / 8), nbytes = pix * K * (next_bits / 8), sbytes = pix * K * 4;
-    if (!array_ok(derived, n, 16) || !array_ok(topk_next, pix, 16)) return SAD_EINVAL;
-    if ((topk_prev && !aligned(topk_prev, 16)) || (scores_prev && !aligned(scores_prev, 16)) ||
-        (scores_next && !aligned(scores_next, 16)))
+    const int64_t pbytes = pix * K * (m.prev_bits / 8), nbytes = pix * K * (m.next_bits / 8), sbytes = pix * K * 4;
+    const int64_t tbytes = pix * 4, rbytes = int64_t(n) * 16, dbytes = int64_t(n) * REC * 4;
+    if (!array_ok(derived, n, 16) || !array_ok(m.topk_next, pix, 16)) return SAD_EINVAL;
+    if ((m.topk_prev && !aligned(m.topk_prev, 16)) || (m.scores_prev && !aligned(m.scores_prev, 16)) ||
+        (m.scores_next && !aligned(m.scores_next, 16)) || (m.probe_prev && !aligned(m.probe_prev, 16)) ||
+        (m.probe_next && !aligned(m.probe_next, 16)))
         return SAD_EINVAL;
-    if ((scores_prev || thr_prev) && !topk_prev) return SAD_EINVAL;
-    if (scores_prev && thr_prev) return SAD_EINVAL;
-    if ((thr_prev && !aligned(thr_prev, 4)) || (thr_next && !aligned(thr_next, 4))) return SAD_EINVAL;
-    const int64_t tbytes = pix * 4;
-    const void* outs[3] = {topk_next, scores_next, thr_next};
-    const int64_t obytes[3] = {nbytes, sbytes, tbytes};
-    const void* ins[3] = {topk_prev, scores_prev, thr_prev};
-    const int64_t ibytes[3] = {pbytes, sbytes, tbytes};
-    for (int o = 0; o < 3; ++o) {
-        for (int q = 0; q < 3; ++q)
+    if ((m.scores_prev || m.thr_prev) && !m.topk_prev) return SAD_EINVAL;
+    if (m.scores_prev && m.thr_prev) return SAD_EINVAL;
+    if ((m.thr_prev && !aligned(m.thr_prev, 4)) || (m.thr_next && !aligned(m.thr_next, 4))) return SAD_EINVAL;
+    // no two buffers may share memory
+    const void* outs[4] = {m.topk_next, m.scores_next, m.thr_next, m.probe_next};
+    const int64_t obytes[4] = {nbytes, sbytes, tbytes, rbytes};
+    const void* ins[5] = {m.topk_prev, m.scores_prev, m.thr_prev, m.probe_prev, derived};
+    const int64_t ibytes[5] = {pbytes, sbytes, tbytes, rbytes, dbytes};
+    for (int o = 0; o < 4; ++o) {
+        for (int q = 0; q < 5; ++q)
             if (overlap(outs[o], obytes[o], ins[q], ibytes[q])) return SAD_EINVAL;
-        for (int q = o + 1; q < 3; ++q)
-            if (overlap(outs[o], obytes[o], outs[q], obytes[q]) || overlap(ins[o], ibytes[o], ins[q], ibytes[q]))
-                return SAD_EINVAL;
+        for (int q = o + 1; q < 4; ++q)
+            if (overlap(outs[o], obytes[o], outs[q], obytes[q])) return SAD_EINVAL;
     }
+    for (int o = 0; o < 5; ++o)
+        for (int q = o + 1; q < 5; ++q)
+            if (overlap(ins[o], ibytes[o], ins[q], ibytes[q])) return SAD_EINVAL;
     const int64_t ntiles = int64_t(tiles_x(w)) * tiles_y(h);
     if (ntiles > MAX_TILES) return SAD_EINVAL;
     a.derived = derived;
-    a.prev = prev_bits == 32 ? static_cast<const uint32_t*>(topk_prev) : nullptr;
-    a.prev16 = prev_bits == 16 ? static_cast<const uint16_t*>(topk_prev) : nullptr;
-    a.prev_scores = scores_prev;
-    a.prev_thr = thr_prev;
-    a.next = next_bits == 32 ? static_cast<uint32_t*>(topk_next) : nullptr;
-    a.next16 = next_bits == 16 ? static_cast<uint16_t*>(topk_next) : nullptr;
-    a.next_scores = scores_next;
-    a.next_thr = thr_next;
+    a.prev = m.prev_bits == 32 ? static_cast<const uint32_t*>(m.topk_prev) : nullptr;
+    a.prev16 = m.prev_bits == 16 ? static_cast<const uint16_t*>(m.topk_prev) : nullptr;
+    a.prev_scores = m.scores_prev;
+    a.prev_thr = m.thr_prev;
+    a.next = m.next_bits == 32 ? static_cast<uint32_t*>(m.topk_next) : nullptr;
+    a.next16 = m.next_bits == 16 ? static_cast<uint16_t*>(m.topk_next) : nullptr;
+    a.next_scores = m.scores_next;
+    a.next_thr = m.thr_next;
+    a.probe_prev = reinterpret_cast<const float4*>(m.probe_prev);
+    a.probe_next = reinterpret_cast<float4*>(m.probe_next);
     a.seed = seed;
     a.n = n;
     a.h = h;
@@ -565,6 +610,19 @@ inline int prop_setup(const float* derived, int32_t n, int32_t h, int32_t w, con
     a.n_tiles = (int32_t)ntiles;
     a.pass_index = pass_index;
     return SAD_OK;
+}
+
+// The maps of sad_propagate_topk and sad_step_fused in a sad_pass_maps.
+inline sad_pass_maps maps32(const uint32_t* topk_prev, const float* scores_prev, uint32_t* topk_next,
+                            float* scores_next) {
+    sad_pass_maps m = {};
+    m.topk_prev = topk_prev;
+    m.prev_bits = 32;
+    m.scores_prev = scores_prev;
+    m.topk_next = topk_next;
+    m.next_bits = 32;
+    m.scores_next = scores_next;
+    return m;
 }
 
 }  // namespace sad

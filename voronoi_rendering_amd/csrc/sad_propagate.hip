@@ -62,20 +62,18 @@ extern "C" int sad_propagate_topk(const float* derived, int32_t n, int32_t h, in
                                   const float* scores_prev, uint32_t* topk_next, float* scores_next, int32_t stride,
                                   uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, void* stream) {
     PropArgs a;
-    const int st = prop_setup(derived, n, h, w, topk_prev, 32, scores_prev, nullptr, topk_next, 32, scores_next,
-                              nullptr, stride, seed, pass_index, inject_per_tile, a);
+    const int st = prop_setup(derived, n, h, w, maps32(topk_prev, scores_prev, topk_next, scores_next), stride, seed,
+                              pass_index, inject_per_tile, a);
     if (st != SAD_OK) return st;
     return prop_launch(a, stream);
 }
 
-extern "C" int sad_propagate_topk_widths(const float* derived, int32_t n, int32_t h, int32_t w, const void* topk_prev,
-                                         int32_t prev_bits, const float* scores_prev, const float* thr_prev,
-                                         void* topk_next, int32_t next_bits, float* scores_next, float* thr_next,
-                                         int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject_per_tile,
-                                         void* stream) {
+extern "C" int sad_propagate_pass(const float* derived, int32_t n, int32_t h, int32_t w, const sad_pass_maps* maps,
+                                  int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject_per_tile,
+                                  void* stream) {
+    if (!maps) return SAD_EINVAL;
     PropArgs a;
-    const int st = prop_setup(derived, n, h, w, topk_prev, prev_bits, scores_prev, thr_prev, topk_next, next_bits,
-                              scores_next, thr_next, stride, seed, pass_index, inject_per_tile, a);
+    const int st = prop_setup(derived, n, h, w, *maps, stride, seed, pass_index, inject_per_tile, a);
     if (st != SAD_OK) return st;
     return prop_launch(a, stream);
 }

@@ -67,39 +67,50 @@ def _map_bits(t: torch.Tensor, name: str, h: int, w: int) -> int:
     return 32
 
 
-def propagate_topk(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor | None = None,
-                   *, stride: int, seed: int, pass_index: int, inject: int = 64,
-                   prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None,
-                   prev_thr: torch.Tensor | None = None, out_thr: torch.Tensor | None = None) -> torch.Tensor:
-    """One propagation pass.  ``prev_scores`` (optional) must hold the logits of
-    ``prev``'s entries under ``derived`` as a previous pass wrote them to its
-    ``out_scores``; pass it only while the sites are unchanged.  ``prev`` and
-    ``out`` may be int16 maps (16-bit ids), and ``prev_thr`` / ``out_thr``
-    ([h][w] float32) hand on only each list's 8th logit instead
-    (sad_propagate_topk_widths)."""
-    n = derived.shape[0]
-    _need(derived, "derived", torch.float32, (n, REC))
+def _pass_maps(h: int, w: int, n: int, prev, prev_scores, prev_thr, prev_probe, out, out_scores, out_thr,
+               out_probe) -> _native.PassMaps:
+    """Checked tensors of a propagation pass as a sad_pass_maps."""
     pbits = _map_bits(prev, "prev", h, w) if prev is not None else 32
-    if prev_scores is not None:
-        _need(prev_scores, "prev_scores", torch.float32, (h, w, K))
-    if out is None:
-        out = torch.empty((h, w, K), dtype=torch.int32, device=derived.device)
     obits = _map_bits(out, "out", h, w)
-    if out_scores is not None:
-        _need(out_scores, "out_scores", torch.float32, (h, w, K))
+    for t, name in ((prev_scores, "prev_scores"), (out_scores, "out_scores")):
+        if t is not None:
+            _need(t, name, torch.float32, (h, w, K))
     for t, name in ((prev_thr, "prev_thr"), (out_thr, "out_thr")):
         if t is not None:
             _need(t, name, torch.float32, (h, w))
+    for t, name in ((prev_probe, "prev_probe"), (out_probe, "out_probe")):
+        if t is not None:
+            _need(t, name, torch.float32, (n, 4))
+    return _native.PassMaps(_ptr(prev), _ptr(prev_scores), _ptr(prev_thr), _ptr(prev_probe), _ptr(out),
+                            _ptr(out_scores), _ptr(out_thr), _ptr(out_probe), pbits, obits)
+
+
+def propagate_topk(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor | None = None,
+                   *, stride: int, seed: int, pass_index: int, inject: int = 64,
+                   prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None,
+                   prev_thr: torch.Tensor | None = None, out_thr: torch.Tensor | None = None,
+                   prev_probe: torch.Tensor | None = None, out_probe: torch.Tensor | None = None) -> torch.Tensor:
+    """One propagation pass.  ``prev_scores`` (optional) must hold the logits of
+    ``prev``'s entries under ``derived`` as a previous pass wrote them to its
+    ``out_scores``; pass it only while the sites are unchanged.  ``prev`` and
+    ``out`` may be int16 maps (16-bit ids); ``prev_thr`` / ``out_thr``
+    ([h][w] float32) hand on only each list's 8th logit instead, and
+    ``prev_probe`` / ``out_probe`` ([n][4] float32) the sites' probe records
+    (sad_propagate_pass)."""
+    n = derived.shape[0]
+    _need(derived, "derived", torch.float32, (n, REC))
+    if out is None:
+        out = torch.empty((h, w, K), dtype=torch.int32, device=derived.device)
+    maps = _pass_maps(h, w, n, prev, prev_scores, prev_thr, prev_probe, out, out_scores, out_thr, out_probe)
     tail = (int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF, int(pass_index) & 0xFFFFFFFF, int(inject), _stream(derived))
-    if pbits == 32 and obits == 32 and prev_thr is None and out_thr is None:
+    if (maps.prev_bits, maps.next_bits) == (32, 32) and not (maps.thr_prev or maps.thr_next or maps.probe_prev
+                                                             or maps.probe_next):
         st = _native.lib().sad_propagate_topk(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
                                               _ptr(out_scores), *tail)
         _native.check("sad_propagate_topk", st)
     else:
-        st = _native.lib().sad_propagate_topk_widths(_ptr(derived), n, h, w, _ptr(prev), pbits, _ptr(prev_scores),
-                                                     _ptr(prev_thr), _ptr(out), obits, _ptr(out_scores),
-                                                     _ptr(out_thr), *tail)
-        _native.check("sad_propagate_topk_widths", st)
+        st = _native.lib().sad_propagate_pass(_ptr(derived), n, h, w, C.byref(maps), *tail)
+        _native.check("sad_propagate_pass", st)
     return out
 
 
@@ -331,19 +342,16 @@ def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None,
                target: torch.Tensor, grad: torch.Tensor, *, stride: int, seed: int, pass_index: int,
                inject: int = 64, prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None,
                loss: torch.Tensor | None = None, image: torch.Tensor | None = None,
-               prev_thr: torch.Tensor | None = None) -> torch.Tensor:
+               prev_thr: torch.Tensor | None = None, prev_probe: torch.Tensor | None = None) -> torch.Tensor:
     """propagate_topk(...) into ``out`` followed by render_bwd over ``out``, in
     one call (both launches checked before either is enqueued).  ``prev`` may
     be an int16 map (16-bit ids) and come with ``prev_thr`` (each list's 8th
-    logit) instead of ``prev_scores``; ``out`` has 32-bit ids."""
+    logit) instead of ``prev_scores``, and the pass may read the sites' probe
+    records ``prev_probe``; ``out`` has 32-bit ids."""
     n = derived.shape[0]
     _need(derived, "derived", torch.float32, (n, REC))
-    pbits = _map_bits(prev, "prev", h, w) if prev is not None else 32
-    if prev_scores is not None:
-        _need(prev_scores, "prev_scores", torch.float32, (h, w, K))
     _need(out, "out", torch.int32, (h, w, K))
-    if out_scores is not None:
-        _need(out_scores, "out_scores", torch.float32, (h, w, K))
+    maps = _pass_maps(h, w, n, prev, prev_scores, prev_thr, prev_probe, out, out_scores, None, None)
     _need(target, "target", torch.float32, (h, w, 3))
     _need(grad, "grad", torch.float32, (n, REC))
     if loss is not None:
@@ -352,16 +360,13 @@ def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None,
         _need(image, "image", torch.float32, (h, w, 3))
     tail = (int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF, int(pass_index) & 0xFFFFFFFF, int(inject), _ptr(target),
             _ptr(grad), _ptr(loss), _ptr(image), _stream(derived))
-    if prev_thr is not None:
-        _need(prev_thr, "prev_thr", torch.float32, (h, w))
-    if pbits == 32 and prev_thr is None:
+    if maps.prev_bits == 32 and not (maps.thr_prev or maps.probe_prev):
         st = _native.lib().sad_step_fused(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
                                           _ptr(out_scores), *tail)
         _native.check("sad_step_fused", st)
     else:
-        st = _native.lib().sad_step_fused_widths(_ptr(derived), n, h, w, _ptr(prev), pbits, _ptr(prev_scores),
-                                                 _ptr(prev_thr), _ptr(out), _ptr(out_scores), *tail)
-        _native.check("sad_step_fused_widths", st)
+        st = _native.lib().sad_step_fused_pass(_ptr(derived), n, h, w, C.byref(maps), *tail)
+        _native.check("sad_step_fused_pass", st)
     return out
 
 

@@ -79,6 +79,7 @@ class SadField:
         # on their lists (made on first use; only when every id fits in 16 bits)
         self.maps16 = None
         self.thr = None
+        self.probe = None  # [n][4] probe records of the sites, written by a step's first pass
         self.cur = 0
         self.pass_index = 0
         self.adam_t = 0
@@ -161,24 +162,32 @@ class SadField:
             self.propagate(strides)
             self.forward_backward(target)
             return
-        if self.params.shape[0] > 0xFFFF or len(strides) < 2:
+        n = self.params.shape[0]
+        probe = None
+        if n > 0xFFFF or len(strides) < 2:
             self.propagate(strides[:-1])
             prev, prev_thr = self.maps[self.cur], None
             prev_scores = self.scores[self.cur] if self.scores_valid else None
         else:
             # the passes before the last hand their lists on with 16-bit ids and
-            # only each list's 8th logit (20 instead of 64 bytes per pixel each way)
+            # only each list's 8th logit (20 instead of 64 bytes per pixel each
+            # way); the first also writes the sites' probe records, from which
+            # the later passes cull their probes
+            dev = self.params.device
             if self.maps16 is None:
-                dev = self.params.device
                 self.maps16 = [torch.empty((self.h, self.w, ops.K), dtype=torch.int16, device=dev) for _ in range(2)]
                 self.thr = [torch.empty((self.h, self.w), dtype=torch.float32, device=dev) for _ in range(2)]
+            if self.probe is None or self.probe.shape[0] != n:
+                self.probe = torch.empty((n, 4), dtype=torch.float32, device=dev)
+            probe = self.probe
             prev, prev_thr = self.maps[self.cur], None
             prev_scores = self.scores[self.cur] if self.scores_valid else None
             for k, s in enumerate(strides[:-1]):
                 out, out_thr = self.maps16[k % 2], self.thr[k % 2]
                 ops.propagate_topk(self.derived, self.h, self.w, prev, out, stride=int(s), seed=self.seed,
                                    pass_index=self.pass_index, inject=self.inject, prev_scores=prev_scores,
-                                   prev_thr=prev_thr, out_thr=out_thr)
+                                   prev_thr=prev_thr, out_thr=out_thr, prev_probe=probe if k > 0 else None,
+                                   out_probe=probe if k == 0 else None)
                 prev, prev_scores, prev_thr = out, None, out_thr
                 self.pass_index += 1
         if before_last is not None:
@@ -187,7 +196,8 @@ class SadField:
         # sites next, so the following pass recomputes them anyway.
         ops.step_fused(self.derived, self.h, self.w, prev, self.maps[1 - self.cur], target, self.grad,
                        stride=int(strides[-1]), seed=self.seed, pass_index=self.pass_index, inject=self.inject,
-                       prev_scores=prev_scores, out_scores=None, loss=self.loss, prev_thr=prev_thr)
+                       prev_scores=prev_scores, out_scores=None, loss=self.loss, prev_thr=prev_thr,
+                       prev_probe=probe)
         self.cur = 1 - self.cur
         self.pass_index += 1
         self.scores_valid = False
