@@ -154,6 +154,14 @@ __device__ __forceinline__ int slot_of(const uint32_t (&slot16)[K / 2], int k) {
     return v == 0xFFFFu ? -1 : (int)v;
 }
 
+// What phase B needs of a pixel, in one 32-byte record (two 16-byte LDS
+// reads): the largest logit, dL/dc (float32, formed in float64), 1/Z and
+// dL/dc . c (float64, c the blended colour).
+struct __attribute__((aligned(16))) PixState {
+    float m, g0, g1, g2;
+    double iz, gc;
+};
+
 // The backward's LDS.
 struct BwdLds {
     uint32_t keys[SLOTS];
@@ -163,12 +171,7 @@ struct BwdLds {
     uint32_t wtot[SLOT_WAVES][2];   // entries and pieces of each planning wavefront's slots
     uint32_t mine[BWD_THREADS];     // one word per lane that never holds EMPTY (see claim)
     uint16_t order[REGION_PIX * K];  // pixels of the region's entries, grouped by slot
-    // what phase B needs of each pixel: the largest logit, dL/dc (float32,
-    // formed in float64), 1/Z and dL/dc . c (float64, c the blended colour)
-    float ps_m[REGION_PIX];
-    float ps_g[REGION_PIX][3];
-    double ps_iz[REGION_PIX];
-    double ps_gc[REGION_PIX];
+    PixState ps[REGION_PIX];         // what phase B needs of each pixel
     // the claimed sites' records during the forward, then the per-slot sums
     // of phase B
     __attribute__((aligned(16))) double shared_sums[SLOTS * NGRAD];
@@ -309,12 +312,14 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
             a.image[p * 3 + 1] = (float)c[1];
             a.image[p * 3 + 2] = (float)c[2];
         }
-        L.ps_m[tid] = mx == -__builtin_inff() ? 0.0f : mx;
-        L.ps_g[tid][0] = g[0];
-        L.ps_g[tid][1] = g[1];
-        L.ps_g[tid][2] = g[2];
-        L.ps_iz[tid] = iz;
-        L.ps_gc[tid] = gc;
+        PixState st;
+        st.m = mx == -__builtin_inff() ? 0.0f : mx;
+        st.g0 = g[0];
+        st.g1 = g[1];
+        st.g2 = g[2];
+        st.iz = iz;
+        st.gc = gc;
+        L.ps[tid] = st;
     };
     if (__all(slotted))
         forward(std::true_type{});
@@ -390,7 +395,8 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
             lone |= 1u << k;
     }
     if (lone) {
-        const double g[3] = {(double)L.ps_g[tid][0], (double)L.ps_g[tid][1], (double)L.ps_g[tid][2]};
+        const PixState st = L.ps[tid];
+        const double g[3] = {(double)st.g0, (double)st.g1, (double)st.g2};
         for (; lone; lone &= lone - 1) {
             const int k = __builtin_ctz(lone);
             uint32_t id = ids[0];
@@ -400,9 +406,9 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
             const float l = usable_logit(gk, true, px, py);
             if (!finitef(l)) continue;
             const float4 col = reinterpret_cast<const float4*>(a.derived + (size_t)id * REC)[2];
-            const double wk = (double)__expf(l - L.ps_m[tid]) * L.ps_iz[tid];
+            const double wk = (double)__expf(l - st.m) * st.iz;
             const double delta =
-                wk * (fma(g[0], (double)col.x, fma(g[1], (double)col.y, g[2] * (double)col.z)) - L.ps_gc[tid]);
+                wk * (fma(g[0], (double)col.x, fma(g[1], (double)col.y, g[2] * (double)col.z)) - st.gc);
             double t[NGRAD];
 #pragma unroll
             for (int q = 0; q < NGRAD; ++q) t[q] = 0.0;
@@ -436,17 +442,24 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
         double sum[NGRAD];
 #pragma unroll
         for (int q = 0; q < NGRAD; ++q) sum[q] = 0.0;
+        // the next entry's pixel is read one trip ahead (len >= 1)
+        const int last = start + len - 1;
+        int pp = L.order[start];
         for (int it = 0; it < len; ++it) {
-            const int pp = L.order[start + it];
+            const PixState st = L.ps[pp];
+            const int pp_next = L.order[min(start + it + 1, last)];
             int pi, pj;
             region_pixel(rx, ry, pp / WAVE, pp & (WAVE - 1), pi, pj);
             const float fx = (float)pi + 0.5f, fy = (float)pj + 0.5f;
             const float l = logit(geo, fx, fy);
-            if (!(active & finitef(l))) continue;  // unusable entries take no part (as in the forward)
-            const double wk = (double)__expf(l - L.ps_m[pp]) * L.ps_iz[pp];
-            const double g[3] = {(double)L.ps_g[pp][0], (double)L.ps_g[pp][1], (double)L.ps_g[pp][2]};
-            const double delta = wk * (fma(g[0], cr, fma(g[1], cg, g[2] * cb)) - L.ps_gc[pp]);
-            add_entry_terms(sd, (double)fx, (double)fy, l, wk, delta, g, sum);
+            // unusable entries take no part (as in the forward)
+            if (active & finitef(l)) {
+                const double wk = (double)__expf(l - st.m) * st.iz;
+                const double g[3] = {(double)st.g0, (double)st.g1, (double)st.g2};
+                const double delta = wk * (fma(g[0], cr, fma(g[1], cg, g[2] * cb)) - st.gc);
+                add_entry_terms(sd, (double)fx, (double)fy, l, wk, delta, g, sum);
+            }
+            pp = pp_next;
         }
 #pragma unroll
         for (int q = 0; q < NGRAD; ++q) atomicAdd(&acc[s * NGRAD + q], sum[q]);
