@@ -250,6 +250,42 @@ def test_c2_map_quality(sad, ref):
     assert refreshed >= 0.5 and settled >= 0.99
 
 
+def test_pipeline_step_with_32bit_ids(sad, ref):
+    """SadField.step with more than 65,535 sites (512x512, 70,000 sites): the
+    passes hand on 32-bit maps with only their 8th logits and cull probes from
+    the probe records; from the GPU's map after a full refresh and two steps,
+    a further step's lists are the oracle's chain bit for bit and its loss
+    and gradients the oracle's backward's."""
+    from voronoi_rendering_amd.pipeline import SadField
+
+    h, w, n = 512, 512, 70_000
+    p = synth.sites(1717, n, h, w)
+    p[::97, 0] = -1.0  # inactive sites
+    d = ref.prepare_sites(p)
+    tgt_np = synth.target_noise_edges(1718, h, w)
+    tgt = to_gpu(tgt_np)
+    strides = [8, 4, 2, 1]
+    f = SadField(to_gpu(p), h, w, 29, inject=64)
+    f.refresh(16)
+    for _ in range(2):
+        f.sites_changed()
+        f.step(strides, tgt, fused=True)
+    assert f.inter is not None and f.inter[0].dtype == torch.int32
+    f.sites_changed()
+    prev = map_to_np(f.topk)
+    first = f.pass_index
+    f.grad.zero_()
+    f.loss.zero_()
+    f.step(strides, tgt, fused=True)
+    for k, s in enumerate(strides):
+        prev = ref.propagate(d, h, w, prev, s, 29, first + k, 64)
+    got = map_to_np(f.topk)
+    assert np.array_equal(got, prev), f"{(got != prev).any(-1).sum()} pixels differ"
+    g_ref, _, loss_ref, _ = ref.render_bwd(d, h, w, prev, tgt_np)
+    assert abs(f.loss.item() - loss_ref) <= 1e-5 * loss_ref
+    assert_grad_close(to_np(f.grad), g_ref, "32-bit step gradients")
+
+
 def test_bench_map_step(sad, ref):
     """The launch configuration the bench times: the 768x512 / 50k-site map
     built by the full refresh and settled by 500 steps, then one more step

@@ -77,7 +77,7 @@ class SadField:
         self.scores_valid = False
         # 16-bit-id maps and 8th-logit maps through which a step's passes hand
         # on their lists (made on first use; only when every id fits in 16 bits)
-        self.maps16 = None
+        self.inter = None  # the maps a step's passes hand on (int16 ids when n <= 65535)
         self.thr = None
         self.probe = None  # [n][4] probe records of the sites, written by a step's first pass
         self.cur = 0
@@ -164,18 +164,20 @@ class SadField:
             return
         n = self.params.shape[0]
         probe = None
-        if n > 0xFFFF or len(strides) < 2:
-            self.propagate(strides[:-1])
+        if len(strides) < 2:
             prev, prev_thr = self.maps[self.cur], None
             prev_scores = self.scores[self.cur] if self.scores_valid else None
         else:
-            # the passes before the last hand their lists on with 16-bit ids and
-            # only each list's 8th logit (20 instead of 64 bytes per pixel each
-            # way); the first also writes the sites' probe records, from which
-            # the later passes cull their probes
+            # the passes before the last hand their lists on with only each
+            # list's 8th logit, and with 16-bit ids when every id fits (20
+            # instead of 64 bytes per pixel each way; 36 with 32-bit ids); the
+            # first also writes the sites' probe records, from which the later
+            # passes cull their probes
             dev = self.params.device
-            if self.maps16 is None:
-                self.maps16 = [torch.empty((self.h, self.w, ops.K), dtype=torch.int16, device=dev) for _ in range(2)]
+            dt = torch.int16 if n <= 0xFFFF else torch.int32
+            if self.inter is None or self.inter[0].dtype != dt:
+                self.inter = [torch.empty((self.h, self.w, ops.K), dtype=dt, device=dev) for _ in range(2)]
+            if self.thr is None:
                 self.thr = [torch.empty((self.h, self.w), dtype=torch.float32, device=dev) for _ in range(2)]
             if self.probe is None or self.probe.shape[0] != n:
                 self.probe = torch.empty((n, 4), dtype=torch.float32, device=dev)
@@ -183,7 +185,7 @@ class SadField:
             prev, prev_thr = self.maps[self.cur], None
             prev_scores = self.scores[self.cur] if self.scores_valid else None
             for k, s in enumerate(strides[:-1]):
-                out, out_thr = self.maps16[k % 2], self.thr[k % 2]
+                out, out_thr = self.inter[k % 2], self.thr[k % 2]
                 ops.propagate_topk(self.derived, self.h, self.w, prev, out, stride=int(s), seed=self.seed,
                                    pass_index=self.pass_index, inject=self.inject, prev_scores=prev_scores,
                                    prev_thr=prev_thr, out_thr=out_thr, prev_probe=probe if k > 0 else None,
