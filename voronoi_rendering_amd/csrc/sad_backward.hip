@@ -36,6 +36,12 @@
 namespace sad {
 
 constexpr int PIECE = 10;  // entries of one site per phase-B lane
+// The per-slot sums are term-major with a row of SLOTS + 1 doubles: the
+// lanes of one phase-B add (different slots, one term) and of one phase-C
+// read (one slot, different terms) fall in different LDS banks.
+constexpr int ACC_ROW = SLOTS + 1;
+// at most ceil(cnt / PIECE) pieces per slot: sum over slots <= entries / PIECE + SLOTS
+constexpr int MAX_PIECES = REGION_PIX * K / PIECE + SLOTS;
 constexpr int BWD_THREADS = WAVE * REGION_WAVES;
 constexpr int SLOT_WAVES = SLOTS / WAVE;  // wavefronts that plan the buckets, one slot per lane
 static_assert(SLOTS % WAVE == 0 && SLOT_WAVES <= REGION_WAVES, "slot planning layout");
@@ -168,17 +174,18 @@ struct BwdLds {
     uint32_t cnt[SLOTS];            // entries per slot
     uint32_t bstart[SLOTS];         // the slot's first position in `order`
     uint32_t pstart[SLOTS];         // the slot's first piece
+    uint8_t piece_slot[(MAX_PIECES + 15) / 16 * 16];  // each piece's slot
     uint32_t wtot[SLOT_WAVES][2];   // entries and pieces of each planning wavefront's slots
     uint32_t mine[BWD_THREADS];     // one word per lane that never holds EMPTY (see claim)
     uint16_t order[REGION_PIX * K];  // pixels of the region's entries, grouped by slot
     PixState ps[REGION_PIX];         // what phase B needs of each pixel
     // the claimed sites' records during the forward, then the per-slot sums
     // of phase B
-    __attribute__((aligned(16))) double shared_sums[SLOTS * NGRAD];
+    __attribute__((aligned(16))) double shared_sums[NGRAD * ACC_ROW];
     double wsum[REGION_WAVES];
     uint32_t npieces;
 };
-static_assert(sizeof(float4) * 3 * SLOTS <= sizeof(double) * SLOTS * NGRAD, "records fit where the sums go");
+static_assert(sizeof(float4) * 3 * SLOTS <= sizeof(double) * NGRAD * ACC_ROW, "records fit where the sums go");
 
 // Rotate the lane's 8 entries left by (lane + lane / 8) mod 8 (anti-diagonal
 // of the tile), so that neighbouring pixels listing the same site at the same
@@ -225,7 +232,7 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
     const size_t p = (size_t)j * a.w + i;
     const float px = (float)i + 0.5f, py = (float)j + 0.5f;
     float4* recs = reinterpret_cast<float4*>(L.shared_sums);  // [SLOTS][3]
-    double* acc = L.shared_sums;                              // [SLOTS][NGRAD]
+    double* acc = L.shared_sums;                              // [NGRAD][ACC_ROW]
 
     // A1. a slot for every listed site
     uint32_t slot16[K / 2];
@@ -364,7 +371,7 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
             L.wtot[wv][1] = ip;
         }
     } else {
-        for (int s = tid - SLOT_WAVES * WAVE; s < NGRAD * SLOTS; s += BWD_THREADS - SLOT_WAVES * WAVE) acc[s] = 0.0;
+        for (int s = tid - SLOT_WAVES * WAVE; s < NGRAD * ACC_ROW; s += BWD_THREADS - SLOT_WAVES * WAVE) acc[s] = 0.0;
     }
     __syncthreads();  // wavefront totals
     if (wv < SLOT_WAVES) {
@@ -378,6 +385,7 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
         }
         L.bstart[tid] = bc + ex_c;
         L.pstart[tid] = bp + ex_pc;
+        for (uint32_t k = 0; k < my_pc; ++k) L.piece_slot[bp + ex_pc + k] = (uint8_t)tid;  // tid < SLOTS
         if (tid == 0) L.npieces = tp;
         (void)tc;
     }
@@ -425,11 +433,7 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
     for (uint32_t base = 0; base < np; base += BWD_THREADS) {
         const uint32_t pc = base + (uint32_t)(lane * REGION_WAVES + wv);
         if (pc >= np) continue;
-        // the piece's slot: the last slot whose first piece is <= pc (slots
-        // without entries have no pieces and are passed over)
-        int s = 0;
-#pragma unroll
-        for (int half = SLOTS / 2; half >= 1; half >>= 1) s = L.pstart[s + half] <= pc ? s + half : s;
+        const int s = L.piece_slot[pc];
         const uint32_t kp = pc - L.pstart[s];
         const int start = (int)(L.bstart[s] + kp * PIECE);
         const int len = (int)min((uint32_t)PIECE, L.cnt[s] - kp * PIECE);
@@ -462,7 +466,7 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
             pp = pp_next;
         }
 #pragma unroll
-        for (int q = 0; q < NGRAD; ++q) atomicAdd(&acc[s * NGRAD + q], sum[q]);
+        for (int q = 0; q < NGRAD; ++q) atomicAdd(&acc[q * ACC_ROW + s], sum[q]);
     }
     __syncthreads();
 
@@ -473,7 +477,7 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
         const int s = pr / NGRAD, q = pr % NGRAD;
         const uint32_t id = L.keys[s];
         if (id == EMPTY) continue;
-        const double v = acc[pr];
+        const double v = acc[q * ACC_ROW + s];
         if (v != 0.0) unsafeAtomicAdd(&a.grad[(size_t)id * REC + q], (float)v);
     }
     if (a.loss && tid == 0) {
