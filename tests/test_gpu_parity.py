@@ -103,6 +103,37 @@ def test_propagate_ragged_and_edge_cases(sad, ref, h, w, n, strides, inject):
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
+@pytest.mark.parametrize("h,w,n,strides,inject", [
+    (1, 1, 3, (1, 1, 1), 64),
+    (13, 29, 300, (8, 4, 2, 1), 64),
+    (40, 40, 0, (1, 1), 64),  # no sites: no probe records, lists stay empty
+    (24, 31, 5, (1, 3, 1), 1),
+    (67, 9, 70, (16, 4, 1), 64),
+    (1, 1, 150, (1, 1, 1), 64),  # 150 sites, one tile of 64 lanes: each lane writes up to 3 probe records
+])
+def test_propagate_step_forms_edge_cases(sad, ref, h, w, n, strides, inject):
+    """The forms a training step hands on (16-bit maps, 8th logits, probe
+    records written by the first pass and culled from by the later ones) on
+    ragged and degenerate images and site counts: the oracle's lists."""
+    p = synth.sites(90 + h + n, n, h, w)
+    if n >= 10:
+        p[3, 0] = -1.0  # an inactive site
+    d = ref.prepare_sites(p)
+    dg = sad.prepare_sites(to_gpu(p)) if n > 0 else torch.zeros((0, 12), dtype=torch.float32, device=dev())
+    m = ref.propagate_schedule(d, h, w, None, (8, 4, 2, 1), 13, 0, inject)
+    prev, thr = to_gpu(m), None
+    probe = torch.empty((n, 4), dtype=torch.float32, device=dev())
+    for t, s_ in enumerate(strides):
+        want = ref.propagate(d, h, w, m, s_, 13, 4 + t, inject)
+        out = torch.empty((h, w, 8), dtype=torch.int16, device=dev())
+        out_thr = torch.empty((h, w), dtype=torch.float32, device=dev())
+        sad.propagate_topk(dg, h, w, prev, out, stride=s_, seed=13, pass_index=4 + t, inject=inject, prev_thr=thr,
+                           out_thr=out_thr, prev_probe=probe if t > 0 else None, out_probe=probe if t == 0 else None)
+        got = map16_to_np(out)
+        assert np.array_equal(got, want), f"pass {t}: {np.argwhere(got != want)[:4]}"
+        m, prev, thr = want, out, out_thr
+
+
 def test_propagate_from_given_map_with_stale_ids(sad, ref):
     """A previous map with out-of-range ids, inactive sites and duplicates."""
     h, w, n = 30, 42, 200
