@@ -168,6 +168,11 @@ struct __attribute__((aligned(16))) PixState {
     double iz, gc;
 };
 
+// With n <= SMALL_IDS_MAX sites, slots are the ranks of the region's listed
+// ids (claim_ranked) from a bitmap of RANK_WORDS words.
+constexpr int RANK_WORDS = (SMALL_IDS_MAX + 1) / 32;
+static_assert(RANK_WORDS == 4 * BWD_THREADS, "each thread ranks four bitmap words");
+
 // The backward's LDS.
 struct BwdLds {
     uint32_t keys[SLOTS];
@@ -177,8 +182,17 @@ struct BwdLds {
     uint8_t piece_slot[(MAX_PIECES + 15) / 16 * 16];  // each piece's slot
     uint32_t wtot[SLOT_WAVES][2];   // entries and pieces of each planning wavefront's slots
     uint32_t mine[BWD_THREADS];     // one word per lane that never holds EMPTY (see claim)
-    uint16_t order[REGION_PIX * K];  // pixels of the region's entries, grouped by slot
-    PixState ps[REGION_PIX];         // what phase B needs of each pixel
+    uint32_t wscan[REGION_WAVES];   // per-wavefront totals of the rank scan (claim_ranked)
+    union {
+        struct {
+            uint16_t order[REGION_PIX * K];  // pixels of the region's entries, grouped by slot
+            PixState ps[REGION_PIX];         // what phase B needs of each pixel
+        } ph;
+        struct {                                // during claim_ranked only
+            uint32_t bits[RANK_WORDS];          // one bit per site id listed in the region
+            uint16_t rank[RANK_WORDS];          // listed sites below each word's first id
+        } cl;
+    } x;
     // the claimed sites' records during the forward, then the per-slot sums
     // of phase B
     __attribute__((aligned(16))) double shared_sums[NGRAD * ACC_ROW];
@@ -186,6 +200,74 @@ struct BwdLds {
     uint32_t npieces;
 };
 static_assert(sizeof(float4) * 3 * SLOTS <= sizeof(double) * NGRAD * ACC_ROW, "records fit where the sums go");
+
+// The slots of the lane's entries when every id fits the bitmap (n <=
+// SMALL_IDS_MAX): every listed id sets its bit (one OR per entry, no retries),
+// a prefix count over the bitmap gives each id its rank among the region's
+// distinct listed ids, and that rank is its slot; ids ranked SLOTS or later
+// get none (0xFFFF, as in claim).  The bitmap must be zero and a barrier
+// passed before the call; ends with the slots' keys written but not yet
+// visible to other wavefronts (the caller's barrier follows).
+__device__ __forceinline__ void claim_ranked(BwdLds& L, const uint32_t (&ids)[K], uint32_t n,
+                                             uint32_t (&slot16)[K / 2]) {
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        if (ids[k] < n) atomicOr(&L.x.cl.bits[ids[k] >> 5], 1u << (ids[k] & 31));
+    __syncthreads();
+    // thread t ranks words 4t .. 4t + 3: an exclusive prefix of the set bits
+    uint32_t c[4], tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        c[j] = __builtin_popcount(L.x.cl.bits[4 * tid + j]);
+        tot += c[j];
+    }
+    uint32_t inc = tot;
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+        const uint32_t u = __shfl_up(inc, off, WAVE);
+        if (lane >= off) inc += u;
+    }
+    if (lane == WAVE - 1) L.wscan[wv] = inc;
+    __syncthreads();
+    uint32_t base = inc - tot;
+#pragma unroll
+    for (int w2 = 0; w2 < REGION_WAVES; ++w2) base += w2 < wv ? L.wscan[w2] : 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        L.x.cl.rank[4 * tid + j] = (uint16_t)base;  // <= REGION_PIX * K
+        base += c[j];
+    }
+    __syncthreads();
+    uint32_t sl[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        sl[k] = 0xFFFFu;
+        if (ids[k] < n) {
+            const uint32_t w = ids[k] >> 5;
+            const uint32_t r = L.x.cl.rank[w] + __builtin_popcount(L.x.cl.bits[w] & ((1u << (ids[k] & 31)) - 1u));
+            if (r < (uint32_t)SLOTS) {
+                sl[k] = r;
+                L.keys[r] = ids[k];  // every lane listing the id writes the same value
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K; k += 2) slot16[k / 2] = sl[k] | (sl[k + 1] << 16);
+}
+
+// The tables of the region cleared (call on every thread, then a barrier).
+__device__ __forceinline__ void clear_tables(BwdLds& L, uint32_t n) {
+    const int tid = threadIdx.x;
+    for (int s = tid; s < SLOTS; s += BWD_THREADS) {
+        L.keys[s] = EMPTY;
+        L.cnt[s] = 0;
+    }
+    L.mine[tid] = 0;
+    if (n <= (uint32_t)SMALL_IDS_MAX)  // uniform
+#pragma unroll
+        for (int j = 0; j < 4; ++j) L.x.cl.bits[4 * tid + j] = 0u;
+}
 
 // Rotate the lane's 8 entries left by (lane + lane / 8) mod 8 (anti-diagonal
 // of the tile), so that neighbouring pixels listing the same site at the same
@@ -219,8 +301,8 @@ __device__ __forceinline__ Row8<T> rotate_lane(Row8<T> r, int lane) {
 // The backward of one region, from each lane's list (ids, in any order) and
 // target colour; with GIVEN_LOGITS, given[k] is entry k's float32 logit at
 // the pixel (as the propagation pass computed it) and the forward does not
-// evaluate it again.  The table of L must be cleared (keys EMPTY, cnt 0,
-// mine 0) and a barrier passed before the call.
+// evaluate it again.  The tables of L must be cleared (clear_tables) and a
+// barrier passed before the call.
 template <bool GIVEN_LOGITS>
 __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int rx, int ry, uint32_t (&ids)[K],
                                                 const float (&given)[K], const float (&tg)[3]) {
@@ -236,7 +318,10 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
 
     // A1. a slot for every listed site
     uint32_t slot16[K / 2];
-    claim(L.keys, &L.mine[tid], ids, n, slot16);
+    if (n <= (uint32_t)SMALL_IDS_MAX)  // uniform
+        claim_ranked(L, ids, n, slot16);
+    else
+        claim(L.keys, &L.mine[tid], ids, n, slot16);
     __syncthreads();
 
     // A2. every claimed site's record is read from memory once, into LDS
@@ -326,7 +411,7 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
         st.g2 = g[2];
         st.iz = iz;
         st.gc = gc;
-        L.ps[tid] = st;
+        L.x.ph.ps[tid] = st;
     };
     if (__all(slotted))
         forward(std::true_type{});
@@ -398,12 +483,12 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         if (sp[k] != NOSLOT)
-            L.order[L.bstart[sp[k] & 0xFFu] + (sp[k] >> 8)] = (uint16_t)tid;
+            L.x.ph.order[L.bstart[sp[k] & 0xFFu] + (sp[k] >> 8)] = (uint16_t)tid;
         else if (ids[k] < n)
             lone |= 1u << k;
     }
     if (lone) {
-        const PixState st = L.ps[tid];
+        const PixState st = L.x.ph.ps[tid];
         const double g[3] = {(double)st.g0, (double)st.g1, (double)st.g2};
         for (; lone; lone &= lone - 1) {
             const int k = __builtin_ctz(lone);
@@ -448,10 +533,10 @@ __device__ __forceinline__ void backward_region(const BwdArgs& a, BwdLds& L, int
         for (int q = 0; q < NGRAD; ++q) sum[q] = 0.0;
         // the next entry's pixel is read one trip ahead (len >= 1)
         const int last = start + len - 1;
-        int pp = L.order[start];
+        int pp = L.x.ph.order[start];
         for (int it = 0; it < len; ++it) {
-            const PixState st = L.ps[pp];
-            const int pp_next = L.order[min(start + it + 1, last)];
+            const PixState st = L.x.ph.ps[pp];
+            const int pp_next = L.x.ph.order[min(start + it + 1, last)];
             int pi, pj;
             region_pixel(rx, ry, pp / WAVE, pp & (WAVE - 1), pi, pj);
             const float fx = (float)pi + 0.5f, fy = (float)pj + 0.5f;
@@ -497,11 +582,7 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(6))
     const bool inside = i < a.w && j < a.h;
     const size_t p = (size_t)j * a.w + i;
 
-    for (int s = tid; s < SLOTS; s += BWD_THREADS) {
-        L.keys[s] = EMPTY;
-        L.cnt[s] = 0;
-    }
-    L.mine[tid] = 0;
+    clear_tables(L, (uint32_t)a.n);
 
     uint32_t ids[K];
     float tg[3] = {0.f, 0.f, 0.f};
@@ -585,11 +666,7 @@ void k_step_last(PropArgs pa, BwdArgs a) {
         }
     }
     __syncthreads();  // the pass's queues are no longer read
-    for (int s = tid; s < SLOTS; s += BWD_THREADS) {
-        lds.bwd.keys[s] = EMPTY;
-        lds.bwd.cnt[s] = 0;
-    }
-    lds.bwd.mine[tid] = 0;
+    clear_tables(lds.bwd, (uint32_t)a.n);
     __syncthreads();  // table cleared
     // with only the 8th logits given (THR_IN) the lanes' other logits are not
     // all known: the forward evaluates them from the site records it stages
