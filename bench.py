@@ -11,8 +11,9 @@ H*W per step / step time.  All inputs are synthetic (synth.C2) and already
 resident in GPU memory when the timed region starts.
 
 The first pass of each step recomputes the logits of the pixels' previous
-lists (as after an Adam update); the following passes reuse the logits the
-previous pass wrote.  The passes before the last hand their lists on with
+lists (as after an Adam update, which also rewrites the sites' probe
+records, so that every pass culls its probes from them); the following
+passes reuse the logits the previous pass wrote.  The passes before the last hand their lists on with
 16-bit ids (every id of the 50,000 fits), the last pass writes 32-bit ids.
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events in up to 50
@@ -382,7 +383,7 @@ def secondary(torch, synth, ops, SadField) -> dict:
     f.warm(wl.warm_passes)
 
     def step4():
-        f.sites_changed()
+        f.sites_changed(probe_records_current=True)  # as after an Adam update
         f.step(list(wl.strides), tgt, fused=True)
 
     t = per_call(step4, 10)
@@ -512,8 +513,9 @@ def main() -> int:
 
     def step(record: bool):
         # In training the Adam update rewrites the sites between steps, so the
-        # first pass of every step recomputes the previous lists' logits.
-        f.sites_changed()
+        # first pass of every step recomputes the previous lists' logits; it
+        # rewrites the sites' probe records with them.
+        f.sites_changed(probe_records_current=True)
         if not record:
             f.step(strides, target, fused=True)
             return

@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 9
+#define SAD_ABI_VERSION 10
 #define SAD_K 8
 #define SAD_SITE_STRIDE 12
 #define SAD_EMPTY 0xffffffffu
@@ -464,6 +464,21 @@ int sad_step_fused_pass(const float *derived, int32_t n, int32_t h, int32_t w, c
 int sad_adam_step(float *params, float *grad, float *m, float *v, int32_t n, int32_t h, int32_t w, const float *lr,
                   float beta1, float beta2, float eps, float bias_corr1, float bias_corr2, float *derived,
                   void *stream);
+
+/*
+ * sad_adam_step that also rewrites the sites' probe records from the new
+ * prepared records (the probe records of sad_pass_maps, bit for bit what a
+ * pass writes to probe_next from these prepared sites), so that the first
+ * pass after the update can cull its probes from them instead of writing
+ * them (Sec. 4.3: the probes are drawn afresh every pass; Sec. 5: the sites
+ * change only in the optimiser step).
+ *   probe    NULL (then as sad_adam_step), or [n][4] float32, 16-byte
+ *            aligned, written; requires derived.  May overlap none of the
+ *            other buffers (SAD_EINVAL).
+ */
+int sad_adam_step_probe(float *params, float *grad, float *m, float *v, int32_t n, int32_t h, int32_t w,
+                        const float *lr, float beta1, float beta2, float eps, float bias_corr1, float bias_corr2,
+                        float *derived, float *probe, void *stream);
 
 /*
  * Random access (Sec. 6.6, the render-only path from cached lists): point t

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
                  "sad_jfa_flood", "sad_budget_workspace_bytes", "sad_densify_prune", "sad_init_workspace_bytes",
                  "sad_init_sites", "sad_pack_sites", "sad_query_packed",
                  "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version",
-                 "sad_propagate_pass", "sad_step_fused_pass"):
+                 "sad_propagate_pass", "sad_step_fused_pass", "sad_adam_step_probe"):
         assert name in syms
 
 
@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sad_abi_version() == 9
+    assert lib.sad_abi_version() == 10
     for st in (0, -1, -2, -3, 7):
         assert lib.sad_status_string(st)
 
@@ -185,6 +185,21 @@ def test_render_query_adam_reject(lib):
                              None) == EINVAL  # params aliases grad
     assert lib.sad_adam_step(P, P + 4096, P + 8192, P + 12288, -3, 8, 8, lr, .9, .999, 1e-8, .1, .001, None,
                              None) == EINVAL
+    # the Adam step that also writes probe records (10 sites: 480-byte records, 160-byte probe records)
+    adam_p = lib.sad_adam_step_probe
+    D = P + 16384
+    assert adam_p(P, P + 4096, P + 8192, P + 12288, 10, 8, 8, lr, .9, .999, 1e-8, .1, .001, None, P + 20480,
+                  None) == EINVAL  # probe records without prepared records
+    assert adam_p(P, P + 4096, P + 8192, P + 12288, 10, 8, 8, lr, .9, .999, 1e-8, .1, .001, D, P + 20488,
+                  None) == EINVAL  # misaligned probe records
+    assert adam_p(P, P + 4096, P + 8192, P + 12288, 10, 8, 8, lr, .9, .999, 1e-8, .1, .001, D, D + 464,
+                  None) == EINVAL  # probe records over the prepared records
+    assert adam_p(P, P + 4096, P + 8192, P + 12288, 10, 8, 8, lr, .9, .999, 1e-8, .1, .001, D, P + 4096 + 320,
+                  None) == EINVAL  # probe records over the gradients
+    assert adam_p(P, P + 4096, P + 8192, P + 12288, 10, 8, 8, lr, .9, .999, 1e-8, .1, .001, D, P - 144,
+                  None) == EINVAL  # probe records reaching into params
+    assert adam_p(P, P + 4096, P + 8192, P + 12288, 0, 8, 8, lr, .9, .999, 1e-8, .1, .001, D, P + 20480,
+                  None) == 0  # no sites: nothing to do
 
 
 def test_step_fused_rejects(lib):

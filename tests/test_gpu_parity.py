@@ -1394,12 +1394,19 @@ def test_adam_bit_exact(sad, ref):
     lr = np.array([1e-2, 1e-3, 2e-3, 3e-3, 4e-3], np.float32)
     bc1, bc2 = ref.bias_corrections(0.9, 0.999, 7)
     want = ref.adam_step(p, g, m, v, h, w, lr, 0.9, 0.999, 1e-8, bc1, bc2)
-    P, G, M, V = (to_gpu(x.copy()) for x in (p, g, m, v))
-    D = torch.empty_like(P)
-    sad.adam_step(P, G, M, V, h, w, lr.tolist(), 0.9, 0.999, 1e-8, bc1, bc2, D)
-    for name, gt, wt in zip(("params", "grad", "m", "v", "derived"), (P, G, M, V, D), want):
-        a = to_np(gt)
-        assert np.array_equal(a.view(np.uint32), wt.view(np.uint32)), (name, np.argwhere(a != wt)[:5])
+    for with_probe in (False, True):
+        P, G, M, V = (to_gpu(x.copy()) for x in (p, g, m, v))
+        D = torch.empty_like(P)
+        probe = torch.full((n, 4), np.nan, dtype=torch.float32, device=dev()) if with_probe else None
+        sad.adam_step(P, G, M, V, h, w, lr.tolist(), 0.9, 0.999, 1e-8, bc1, bc2, D, probe)
+        for name, gt, wt in zip(("params", "grad", "m", "v", "derived"), (P, G, M, V, D), want):
+            a = to_np(gt)
+            assert np.array_equal(a.view(np.uint32), wt.view(np.uint32)), (name, np.argwhere(a != wt)[:5])
+        if with_probe:
+            # the probe records of the new prepared sites, as a pass writes them
+            got_rec, want_rec = to_np(probe), probe_records_np(want[4])
+            assert np.array_equal(got_rec.view(np.uint32), want_rec.view(np.uint32)), \
+                np.argwhere(got_rec.view(np.uint32) != want_rec.view(np.uint32))[:4]
 
 
 # ---------------------------------------------------------------- queries

@@ -160,4 +160,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ bool finitef(float v) { return __builtin_isfinite(v); }
 
+// The probe record of a site: what the tile cull of a propagation pass
+// (probe_may_enter) needs of it in 16 bytes, (x, y, tau m, tau r) with m the
+// smaller inverse scale, so that a pass that probes sites it has no other
+// use for gathers 16 instead of 32 bytes per probe (and the records of all
+// sites, 16 bytes each, stay in each XCD's L2).  A site the bound cannot
+// cover gets (x, y, 0, +inf): never culled.  Written by a pass or, with the
+// prepared records, by the Adam step.
+__device__ __forceinline__ float4 probe_record(const Geo& g) {
+    const float tau = g.g0.z, r = g.g0.w, is1 = g.g1.z, is2 = g.g1.w;
+    const float m = fminf(is1, is2), M = fmaxf(is1, is2);
+    const bool boundable = finitef(g.g0.x) & finitef(g.g0.y) & finitef(tau) & finitef(r) & finitef(M) & (tau > 0.0f) &
+                           (m > 0.0f) & (M <= 1024.0f * m);
+    return make_float4(g.g0.x, g.g0.y, boundable ? tau * m : 0.0f, boundable ? tau * r : __builtin_inff());
+}
+
 }  // namespace sad

@@ -10,8 +10,8 @@ namespace sad {
 
 constexpr float THETA_LIMIT = 1048576.0f;  // 2^20
 
-// Prepared record of one site (format in sad.h).
-__device__ __forceinline__ void prepare_one(const float4 p0, const float4 p1, const float4 p2, float4* out) {
+// Prepared record of one site (format in sad.h); returns its geometry part.
+__device__ __forceinline__ Geo prepare_one(const float4 p0, const float4 p1, const float4 p2, float4* out) {
     // p0 = (x, y, log_tau, r), p1 = (c_r, c_g, c_b, theta), p2 = (log_s1, log_s2, -, -)
     float theta = p1.w;
     bool active = p0.x >= 0.0f && fabsf(theta) <= THETA_LIMIT;
@@ -33,6 +33,10 @@ __device__ __forceinline__ void prepare_one(const float4 p0, const float4 p1, co
     out[0] = o0;
     out[1] = o1;
     out[2] = o2;
+    Geo g;
+    g.g0 = o0;
+    g.g1 = o1;
+    return g;
 }
 
 }  // namespace sad

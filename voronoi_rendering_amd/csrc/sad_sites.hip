@@ -37,7 +37,8 @@ __device__ __forceinline__ float adam_one(float p, float g, float& m, float& v, 
 
 __global__ __launch_bounds__(256) void k_adam(float* __restrict__ params, float* __restrict__ grad,
                                                float* __restrict__ mom1, float* __restrict__ mom2, int32_t n,
-                                               AdamArgs a, float* __restrict__ derived) {
+                                               AdamArgs a, float* __restrict__ derived,
+                                               float4* __restrict__ probe) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     float4* P = reinterpret_cast<float4*>(params + (size_t)i * REC);
@@ -78,7 +79,10 @@ __global__ __launch_bounds__(256) void k_adam(float* __restrict__ params, float*
     G[0] = z;
     G[1] = z;
     G[2] = z;
-    if (derived) prepare_one(p0, p1, p2, reinterpret_cast<float4*>(derived + (size_t)i * REC));
+    if (derived) {
+        const Geo g = prepare_one(p0, p1, p2, reinterpret_cast<float4*>(derived + (size_t)i * REC));
+        if (probe) probe[i] = probe_record(g);
+    }
 }
 
 }  // namespace sad
@@ -94,18 +98,20 @@ extern "C" int sad_prepare_sites(const float* params, int32_t n, float* derived,
     return launch_status();
 }
 
-extern "C" int sad_adam_step(float* params, float* grad, float* m, float* v, int32_t n, int32_t h, int32_t w,
-                             const float* lr, float beta1, float beta2, float eps, float bias_corr1,
-                             float bias_corr2, float* derived, void* stream) {
+extern "C" int sad_adam_step_probe(float* params, float* grad, float* m, float* v, int32_t n, int32_t h, int32_t w,
+                                   const float* lr, float beta1, float beta2, float eps, float bias_corr1,
+                                   float bias_corr2, float* derived, float* probe, void* stream) {
     if (!sites_ok(n) || !image_ok(h, w) || lr == nullptr) return SAD_EINVAL;
     if (!array_ok(params, n, 16) || !array_ok(grad, n, 16) || !array_ok(m, n, 16) || !array_ok(v, n, 16))
         return SAD_EINVAL;
     if (derived && !aligned(derived, 16)) return SAD_EINVAL;
+    if (probe && (!derived || !aligned(probe, 16))) return SAD_EINVAL;  // records of the prepared sites
     const int64_t bytes = int64_t(n) * REC * 4;
-    const void* bufs[5] = {params, grad, m, v, derived};
-    for (int a = 0; a < 5; ++a)
-        for (int b = a + 1; b < 5; ++b)
-            if (overlap(bufs[a], bytes, bufs[b], bytes)) return SAD_EINVAL;
+    const void* bufs[6] = {params, grad, m, v, derived, probe};
+    const int64_t sizes[6] = {bytes, bytes, bytes, bytes, bytes, int64_t(n) * 16};
+    for (int a = 0; a < 6; ++a)
+        for (int b = a + 1; b < 6; ++b)
+            if (overlap(bufs[a], sizes[a], bufs[b], sizes[b])) return SAD_EINVAL;
     if (n == 0) return SAD_OK;
     AdamArgs args;
     for (int k = 0; k < 5; ++k) args.lr[k] = lr[k];
@@ -118,6 +124,13 @@ extern "C" int sad_adam_step(float* params, float* grad, float* m, float* v, int
     args.h = (float)h;
     clear_error();
     hipLaunchKernelGGL(k_adam, dim3((n + 255) / 256), dim3(256), 0, as_stream(stream), params, grad, m, v, n, args,
-                       derived);
+                       derived, reinterpret_cast<float4*>(probe));
     return launch_status();
+}
+
+extern "C" int sad_adam_step(float* params, float* grad, float* m, float* v, int32_t n, int32_t h, int32_t w,
+                             const float* lr, float beta1, float beta2, float eps, float bias_corr1,
+                             float bias_corr2, float* derived, void* stream) {
+    return sad_adam_step_probe(params, grad, m, v, n, h, w, lr, beta1, beta2, eps, bias_corr1, bias_corr2, derived,
+                               nullptr, stream);
 }

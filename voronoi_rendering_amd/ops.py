@@ -372,16 +372,21 @@ def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None,
 
 def adam_step(params: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor, h: int, w: int,
               lr: Sequence[float], beta1: float, beta2: float, eps: float, bias_corr1: float, bias_corr2: float,
-              derived: torch.Tensor | None = None) -> None:
+              derived: torch.Tensor | None = None, probe: torch.Tensor | None = None) -> None:
+    """One Adam step; ``derived`` (optional) receives the new prepared
+    records and ``probe`` (optional, [n][4] float32, needs ``derived``) the
+    sites' probe records from them (sad_adam_step_probe)."""
     n = params.shape[0]
     for t, name in ((params, "params"), (grad, "grad"), (m, "m"), (v, "v")):
         _need(t, name, torch.float32, (n, REC))
     if derived is not None:
         _need(derived, "derived", torch.float32, (n, REC))
+    if probe is not None:
+        _need(probe, "probe", torch.float32, (n, 4))
     lr_arr = (C.c_float * 5)(*[float(x) for x in lr])
-    st = _native.lib().sad_adam_step(_ptr(params), _ptr(grad), _ptr(m), _ptr(v), n, h, w, lr_arr, beta1, beta2, eps,
-                                     bias_corr1, bias_corr2, _ptr(derived), _stream(params))
-    _native.check("sad_adam_step", st)
+    st = _native.lib().sad_adam_step_probe(_ptr(params), _ptr(grad), _ptr(m), _ptr(v), n, h, w, lr_arr, beta1, beta2,
+                                           eps, bias_corr1, bias_corr2, _ptr(derived), _ptr(probe), _stream(params))
+    _native.check("sad_adam_step_probe", st)
 
 
 def query_points(derived: torch.Tensor, h: int, w: int, topk: torch.Tensor, xy: torch.Tensor,

@@ -79,7 +79,8 @@ class SadField:
         # on their lists (made on first use; only when every id fits in 16 bits)
         self.inter = None  # the maps a step's passes hand on (int16 ids when n <= 65535)
         self.thr = None
-        self.probe = None  # [n][4] probe records of the sites, written by a step's first pass
+        self.probe = None  # [n][4] probe records of the sites (a step's first pass or the Adam step writes them)
+        self.probe_valid = False  # whether they are those of the current prepared sites
         self.cur = 0
         self.pass_index = 0
         self.adam_t = 0
@@ -109,9 +110,12 @@ class SadField:
             self.pass_index += 1
             self.scores_valid = True
 
-    def sites_changed(self) -> None:
-        """The prepared sites were rewritten: the cached logits are stale."""
+    def sites_changed(self, probe_records_current: bool = False) -> None:
+        """The prepared sites were rewritten: the cached logits are stale, and
+        so are the probe records unless they were rewritten with the sites
+        (``probe_records_current``, as the Adam step does)."""
         self.scores_valid = False
+        self.probe_valid = self.probe_valid and probe_records_current
 
     def warm(self, n_pass: int) -> None:
         """Fill the map from scratch with the warm-up jump schedule."""
@@ -171,8 +175,8 @@ class SadField:
             # the passes before the last hand their lists on with only each
             # list's 8th logit, and with 16-bit ids when every id fits (20
             # instead of 64 bytes per pixel each way; 36 with 32-bit ids); the
-            # first also writes the sites' probe records, from which the later
-            # passes cull their probes
+            # passes cull their probes from the sites' probe records, which the
+            # first pass writes unless the Adam step already has
             dev = self.params.device
             dt = torch.int16 if n <= 0xFFFF else torch.int32
             if self.inter is None or self.inter[0].dtype != dt:
@@ -181,15 +185,18 @@ class SadField:
                 self.thr = [torch.empty((self.h, self.w), dtype=torch.float32, device=dev) for _ in range(2)]
             if self.probe is None or self.probe.shape[0] != n:
                 self.probe = torch.empty((n, 4), dtype=torch.float32, device=dev)
+                self.probe_valid = False
             probe = self.probe
             prev, prev_thr = self.maps[self.cur], None
             prev_scores = self.scores[self.cur] if self.scores_valid else None
             for k, s in enumerate(strides[:-1]):
                 out, out_thr = self.inter[k % 2], self.thr[k % 2]
+                write = not self.probe_valid
                 ops.propagate_topk(self.derived, self.h, self.w, prev, out, stride=int(s), seed=self.seed,
                                    pass_index=self.pass_index, inject=self.inject, prev_scores=prev_scores,
-                                   prev_thr=prev_thr, out_thr=out_thr, prev_probe=probe if k > 0 else None,
-                                   out_probe=probe if k == 0 else None)
+                                   prev_thr=prev_thr, out_thr=out_thr, prev_probe=None if write else probe,
+                                   out_probe=probe if write else None)
+                self.probe_valid = True
                 prev, prev_scores, prev_thr = out, None, out_thr
                 self.pass_index += 1
         if before_last is not None:
@@ -207,9 +214,13 @@ class SadField:
     def adam_step(self) -> None:
         self.adam_t += 1
         bc1, bc2 = bias_corrections(self.adam.beta1, self.adam.beta2, self.adam_t)
+        # the probe records (once a step has made them) are rewritten with the
+        # prepared sites, so the next step's first pass culls from them
+        probe = self.probe if self.probe is not None and self.probe.shape[0] == self.params.shape[0] else None
         ops.adam_step(self.params, self.grad, self.m, self.v, self.h, self.w, self.adam.lr, self.adam.beta1,
-                      self.adam.beta2, self.adam.eps, bc1, bc2, self.derived)
-        self.sites_changed()
+                      self.adam.beta2, self.adam.eps, bc1, bc2, self.derived, probe)
+        self.probe_valid = probe is not None
+        self.sites_changed(probe_records_current=True)
 
     def train_iter(self, strides: Sequence[int], target: torch.Tensor, fused: bool = True) -> None:
         self.step(strides, target, fused)
