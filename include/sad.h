@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SAD_ABI_VERSION 10
+#define SAD_ABI_VERSION 11
 #define SAD_K 8
 #define SAD_SITE_STRIDE 12
 #define SAD_EMPTY 0xffffffffu
@@ -200,6 +200,15 @@ typedef struct sad_pass_maps {
  */
 int sad_propagate_pass(const float *derived, int32_t n, int32_t h, int32_t w, const sad_pass_maps *maps,
                        int32_t stride, uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, void *stream);
+
+/*
+ * A map of width 16 (see sad_pass_maps) as the same lists of width 32: every
+ * id copied, the empty slot 0xffff written as 0xffffffff (Sec. 4.3 keeps one
+ * list per pixel; this only changes how its ids are stored).
+ *   topk16  [h][w][8] uint16, read;  topk  [h][w][8] uint32, written.
+ * Both 16-byte aligned and not overlapping (SAD_EINVAL otherwise).
+ */
+int sad_widen_map(const uint16_t *topk16, int32_t h, int32_t w, uint32_t *topk, void *stream);
 
 /*
  * Soft additively weighted render (Sec. 4.2): per pixel, the softmax of the
@@ -435,8 +444,9 @@ int sad_step_fused(const float *derived, int32_t n, int32_t h, int32_t w, const 
  * sad_step_fused on the maps of a sad_pass_maps (maps: a HOST pointer, read
  * during the call): the last pass of a step whose earlier passes handed their
  * lists on at width 16, with thresholds or probe records.  The pass writes
- * 32-bit ids (next_bits = 32) and no thresholds or probe records (thr_next
- * and probe_next NULL; SAD_EINVAL otherwise).  With thr_prev the backward
+ * 32-bit ids (next_bits = 32), or 16-bit ones (next_bits = 16, n <= 65535)
+ * for the next step's first pass, and no thresholds or probe records
+ * (thr_next and probe_next NULL; SAD_EINVAL otherwise).  With thr_prev the backward
  * evaluates the pixels' logits from the site records it stages anyway,
  * rather than taking them from the pass.  In addition to the checks of
  * sad_step_fused, grad, loss and image must not overlap topk_prev,

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
                  "sad_jfa_flood", "sad_budget_workspace_bytes", "sad_densify_prune", "sad_init_workspace_bytes",
                  "sad_init_sites", "sad_pack_sites", "sad_query_packed",
                  "sad_adam_step", "sad_query_points", "sad_status_string", "sad_abi_version",
-                 "sad_propagate_pass", "sad_step_fused_pass", "sad_adam_step_probe"):
+                 "sad_propagate_pass", "sad_step_fused_pass", "sad_adam_step_probe", "sad_widen_map"):
         assert name in syms
 
 
@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sad_abi_version() == 10
+    assert lib.sad_abi_version() == 11
     for st in (0, -1, -2, -3, 7):
         assert lib.sad_status_string(st)
 
@@ -144,7 +144,10 @@ def test_propagate_pass_rejects(lib):
     assert g(P, 10, 8, 8, None, 1, 0, 0, 64, T, G, None, None, None) == EINVAL  # no maps
     assert fused(n=65536) == EUNSUP
     assert fused(prev_bits=24) == EINVAL
-    assert fused(next_bits=16) == EINVAL  # the fused pass writes 32-bit lists
+    assert fused(next_bits=8) == EINVAL  # the fused pass writes 32- or 16-bit lists
+    assert fused(next_bits=16, n=65536) == EUNSUP  # 16-bit lists need n <= 65535
+    assert fused(next_bits=16, grad=P + 4096 + 1008) == EINVAL  # gradients over the 16-bit map's last 16 bytes
+    assert fused(next_bits=16, scores_next=P + 4096 + 1008) == EINVAL  # logits over the 16-bit map
     assert fused(thr_next=P + 8192) == EINVAL  # and no thresholds
     assert fused(probe_next=P + 8192) == EINVAL  # or probe records
     assert fused(grad=None) == EINVAL
@@ -153,6 +156,21 @@ def test_propagate_pass_rejects(lib):
     assert fused(image=P + 65536 + 512) == EINVAL  # image over the previous map
     assert fused(probe_prev=P + 8192, loss=P + 8192 + 152) == EINVAL  # loss inside the probe records
     assert fused(probe_prev=G + 48) == EINVAL  # gradients over the probe records
+
+
+def test_widen_map_rejects(lib):
+    """Widening a 16-bit map (8x8 pixels: 1 KiB in, 2 KiB out): misaligned or
+    missing maps, overlapping maps, bad sizes; an empty image does nothing."""
+    wm = lib.sad_widen_map
+    assert wm(P, 8, 8, None, None) == EINVAL
+    assert wm(None, 8, 8, P + 4096, None) == EINVAL
+    assert wm(P + 8, 8, 8, P + 4096, None) == EINVAL  # misaligned input
+    assert wm(P, 8, 8, P + 4104, None) == EINVAL  # misaligned output
+    assert wm(P, 8, 8, P + 1008, None) == EINVAL  # output over the input's last 16 bytes
+    assert wm(P + 2032, 8, 8, P, None) == EINVAL  # input over the output's last 16 bytes
+    assert wm(P, -1, 8, P + 4096, None) == EINVAL
+    assert wm(P, 8, 1 << 20, P + 4096, None) == EINVAL
+    assert wm(None, 0, 8, None, None) == 0  # empty image: nothing to do
 
 
 def test_render_query_adam_reject(lib):

@@ -1378,6 +1378,56 @@ def test_step_fused_from_16bit_map(sad, ref, c2_state):
     assert_grad_close(g16, g_ref, "fused from 16-bit gradients")
 
 
+def test_step_fused_to_16bit_map(sad, ref, c2_state):
+    """The fused last pass + backward writing 16-bit-id lists (as a training
+    step hands them to the next step): the same lists, id for id, as the
+    call that writes 32-bit ones (the oracle's), the same image bit for bit,
+    the loss (summed across regions by float atomics, so its last bits vary
+    from call to call) and the gradients within the bar; the next step's first pass
+    reads that map (recomputing its logits) and gives the oracle's lists;
+    widened, the map is the 32-bit one."""
+    wl, p, d, dg, m_ref, m_gpu = c2_state
+    h, w = wl.h, wl.w
+    tgt = wl.make_target()
+    m1 = ref.propagate(d, h, w, m_ref, 1, wl.inject_seed, 702, wl.inject)
+    g_ref, _, loss_ref, img_ref = ref.render_bwd(d, h, w, m1, tgt)
+    res = []
+    for dt in (torch.int16, torch.int32):
+        out = torch.empty((h, w, 8), dtype=dt, device=dev())
+        grad = torch.zeros((wl.n, 12), dtype=torch.float32, device=dev())
+        loss = torch.zeros(1, dtype=torch.float32, device=dev())
+        img = torch.empty((h, w, 3), dtype=torch.float32, device=dev())
+        sad.step_fused(dg, h, w, map16_from_np(m_ref), out, to_gpu(tgt), grad, stride=1, seed=wl.inject_seed,
+                       pass_index=702, inject=wl.inject, loss=loss, image=img)
+        res.append((out, to_np(grad), loss.item(), to_np(img)))
+    (o16, g16, loss16, i16), (o32, _, loss32, i32) = res
+    assert np.array_equal(map16_to_np(o16), m1) and np.array_equal(map_to_np(o32), m1)
+    assert np.array_equal(map_to_np(sad.widen_map(o16)), m1)
+    assert np.array_equal(i16.view(np.uint32), i32.view(np.uint32))
+    for lv in (loss16, loss32):
+        assert abs(lv - loss_ref) <= 1e-5 * loss_ref
+    assert_colour_close(i16, img_ref, "fused to 16-bit image")
+    assert_grad_close(g16, g_ref, "fused to 16-bit gradients")
+    m2 = ref.propagate(d, h, w, m1, 8, wl.inject_seed, 703, wl.inject)
+    nxt = torch.empty((h, w, 8), dtype=torch.int16, device=dev())
+    sad.propagate_topk(dg, h, w, o16, nxt, stride=8, seed=wl.inject_seed, pass_index=703, inject=wl.inject)
+    assert np.array_equal(map16_to_np(nxt), m2)
+
+
+@pytest.mark.parametrize("h,w", [(1, 1), (13, 29), (67, 72), (512, 768)])
+def test_widen_map(sad, h, w):
+    """A 16-bit-id map widened to 32-bit ids: every id kept, 0xffff (empty)
+    written as 0xffffffff; ragged and single-pixel images."""
+    rng = np.random.default_rng(h * 1000 + w)
+    m = rng.integers(0, 0x10000, (h, w, 8), dtype=np.uint32)
+    m[rng.random((h, w, 8)) < 0.2] = 0xFFFF
+    m[0, 0, :2] = (0, 0xFFFE)
+    want = m.copy()
+    want[want == 0xFFFF] = 0xFFFFFFFF
+    m16 = torch.from_numpy(np.ascontiguousarray(m.astype(np.uint16)).view(np.int16)).to(dev())
+    assert np.array_equal(map_to_np(sad.widen_map(m16)), want)
+
+
 # ---------------------------------------------------------------- Adam
 
 def test_adam_bit_exact(sad, ref):

@@ -69,6 +69,7 @@ _SIGS = {
     "sad_adam_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                                 C.POINTER(C.c_float), C.c_float, C.c_float, C.c_float, C.c_float, C.c_float,
                                 C.c_void_p, C.c_void_p]),
+    "sad_widen_map": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
     "sad_adam_step_probe": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                       C.c_int32, C.POINTER(C.c_float), C.c_float, C.c_float, C.c_float, C.c_float,
                                       C.c_float, C.c_void_p, C.c_void_p, C.c_void_p]),

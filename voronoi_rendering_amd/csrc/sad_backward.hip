@@ -621,7 +621,7 @@ struct PassLds {
 // starts from them in the same LDS: no list is read back and no logit of the
 // forward is evaluated again, and regions start their backward while others
 // still run their pass.
-template <bool SMALL_IDS, bool PREV16, bool THR_IN>
+template <bool SMALL_IDS, bool PREV16, bool THR_IN, bool NEXT16>
 __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(SMALL_IDS ? 6 : 1)))
 void k_step_last(PropArgs pa, BwdArgs a) {
     __shared__ union {
@@ -636,7 +636,7 @@ void k_step_last(PropArgs pa, BwdArgs a) {
     TopK t;
     t.clear();
     if (tx < pa.tiles_x && ty * pa.tiles_x + tx < pa.n_tiles)  // uniform per wavefront
-        propagate_tile<SMALL_IDS, PREV16, false, THR_IN>(pa, ty * pa.tiles_x + tx, lds.pass.queue[wv],
+        propagate_tile<SMALL_IDS, PREV16, NEXT16, THR_IN>(pa, ty * pa.tiles_x + tx, lds.pass.queue[wv],
                                                          lds.pass.qscore[wv], t);
     int i, j;
     region_pixel(rx, ry, wv, lane, i, j);  // the pixel the pass just listed
@@ -677,7 +677,7 @@ void k_step_last(PropArgs pa, BwdArgs a) {
 // Argument checks of a backward pass over the list map topk, and its kernel
 // arguments.  Returns SAD_OK with b filled in, or the error status.
 inline int bwd_setup(const float* derived, int32_t n, int32_t h, int32_t w, const uint32_t* topk,
-                     const float* target, float* grad, float* loss, float* image, BwdArgs& b) {
+                     const float* target, float* grad, float* loss, float* image, BwdArgs& b, int id_bits = 32) {
     if (!sites_ok(n) || !image_ok(h, w)) return SAD_EINVAL;
     const int64_t pix = int64_t(h) * w;
     if (!array_ok(derived, n, 16) || !array_ok(topk, pix, 16)) return SAD_EINVAL;
@@ -688,7 +688,7 @@ inline int bwd_setup(const float* derived, int32_t n, int32_t h, int32_t w, cons
     const void* outs[3] = {grad, loss, image};
     const int64_t obytes[3] = {gbytes, 4, pix * 12};
     const void* ins[3] = {derived, topk, target};
-    const int64_t ibytes[3] = {gbytes, pix * K * 4, pix * 12};
+    const int64_t ibytes[3] = {gbytes, pix * K * (id_bits / 8), pix * 12};
     for (int o = 0; o < 3; ++o) {
         for (int q = 0; q < 3; ++q)
             if (overlap(outs[o], obytes[o], ins[q], ibytes[q])) return SAD_EINVAL;
@@ -730,27 +730,29 @@ extern "C" int sad_render_bwd(const float* derived, int32_t n, int32_t h, int32_
 }
 
 // Checks and launch of the fused last pass + backward (the new lists are
-// written with 32-bit ids).
+// written with 32-bit ids, or 16-bit ones for the next step's first pass).
 static int step_fused(const float* derived, int32_t n, int32_t h, int32_t w, const sad_pass_maps& m, int32_t stride,
                       uint64_t seed, uint32_t pass_index, int32_t inject_per_tile, const float* target, float* grad,
                       float* loss, float* image, void* stream) {
-    // the pass writes 32-bit lists and, optionally, their logits: nothing else
-    if (m.next_bits != 32 || m.thr_next || m.probe_next) return SAD_EINVAL;
+    // the pass writes lists and, optionally, all their logits: nothing else
+    if (m.thr_next || m.probe_next) return SAD_EINVAL;
     PropArgs pa;
     int st = prop_setup(derived, n, h, w, m, stride, seed, pass_index, inject_per_tile, pa);
     if (st != SAD_OK) return st;
-    uint32_t* const topk_next = static_cast<uint32_t*>(m.topk_next);
+    const bool next16 = pa.next16 != nullptr;
     BwdArgs b;
-    st = bwd_setup(derived, n, h, w, topk_next, target, grad, loss, image, b);
+    st = bwd_setup(derived, n, h, w, static_cast<const uint32_t*>(m.topk_next), target, grad, loss, image, b,
+                   m.next_bits);
     if (st != SAD_OK) return st;
     // the pass's outputs must not share memory with anything else the step reads or writes
-    const int64_t pix = int64_t(h) * w, mbytes = pix * K * 4, gbytes = int64_t(n) * REC * 4;
-    const void* outs[2] = {topk_next, m.scores_next};
+    const int64_t pix = int64_t(h) * w, gbytes = int64_t(n) * REC * 4;
+    const void* outs[2] = {m.topk_next, m.scores_next};
+    const int64_t mbytes[2] = {pix * K * (next16 ? 2 : 4), pix * K * 4};
     const void* others[5] = {target, grad, loss, image, derived};
     const int64_t obytes[5] = {pix * 12, gbytes, 4, pix * 12, gbytes};
     for (int o = 0; o < 2; ++o)
         for (int q = 0; q < 5; ++q)
-            if (overlap(outs[o], mbytes, others[q], obytes[q])) return SAD_EINVAL;
+            if (overlap(outs[o], mbytes[o], others[q], obytes[q])) return SAD_EINVAL;
     // nor may the backward's outputs share memory with the pass's inputs
     const void* bouts[3] = {grad, loss, image};
     const int64_t bbytes[3] = {gbytes, 4, pix * 12};
@@ -766,21 +768,30 @@ static int step_fused(const float* derived, int32_t n, int32_t h, int32_t w, con
     clear_error();
     const dim3 grid((unsigned)nreg), block(BWD_THREADS);
     const bool thr = pa.prev_thr != nullptr;
-    if (pa.n > SMALL_IDS_MAX) {
+    if (pa.n > SMALL_IDS_MAX) {  // 32-bit maps only (prop_setup refuses 16-bit ones)
         if (thr)
-            hipLaunchKernelGGL((k_step_last<false, false, true>), grid, block, 0, s, pa, b);
+            hipLaunchKernelGGL((k_step_last<false, false, true, false>), grid, block, 0, s, pa, b);
         else
-            hipLaunchKernelGGL((k_step_last<false, false, false>), grid, block, 0, s, pa, b);
+            hipLaunchKernelGGL((k_step_last<false, false, false, false>), grid, block, 0, s, pa, b);
+    } else if (next16) {  // the lists go to the next step's first pass
+        if (pa.prev16 && thr)
+            hipLaunchKernelGGL((k_step_last<true, true, true, true>), grid, block, 0, s, pa, b);
+        else if (pa.prev16)
+            hipLaunchKernelGGL((k_step_last<true, true, false, true>), grid, block, 0, s, pa, b);
+        else if (thr)
+            hipLaunchKernelGGL((k_step_last<true, false, true, true>), grid, block, 0, s, pa, b);
+        else
+            hipLaunchKernelGGL((k_step_last<true, false, false, true>), grid, block, 0, s, pa, b);
     } else if (pa.prev16) {
         if (thr)
-            hipLaunchKernelGGL((k_step_last<true, true, true>), grid, block, 0, s, pa, b);
+            hipLaunchKernelGGL((k_step_last<true, true, true, false>), grid, block, 0, s, pa, b);
         else
-            hipLaunchKernelGGL((k_step_last<true, true, false>), grid, block, 0, s, pa, b);
+            hipLaunchKernelGGL((k_step_last<true, true, false, false>), grid, block, 0, s, pa, b);
     } else {
         if (thr)
-            hipLaunchKernelGGL((k_step_last<true, false, true>), grid, block, 0, s, pa, b);
+            hipLaunchKernelGGL((k_step_last<true, false, true, false>), grid, block, 0, s, pa, b);
         else
-            hipLaunchKernelGGL((k_step_last<true, false, false>), grid, block, 0, s, pa, b);
+            hipLaunchKernelGGL((k_step_last<true, false, false, false>), grid, block, 0, s, pa, b);
     }
     return launch_status();
 }

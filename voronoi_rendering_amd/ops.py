@@ -338,6 +338,18 @@ def jfa_flood(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor, step: i
     return out
 
 
+def widen_map(topk16: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The lists of an int16 (16-bit-id) map as an int32 map (sad_widen_map)."""
+    h, w = int(topk16.shape[0]), int(topk16.shape[1])
+    _need(topk16, "topk16", torch.int16, (h, w, K))
+    if out is None:
+        out = torch.empty((h, w, K), dtype=torch.int32, device=topk16.device)
+    _need(out, "out", torch.int32, (h, w, K))
+    st = _native.lib().sad_widen_map(_ptr(topk16), h, w, _ptr(out), _stream(topk16))
+    _native.check("sad_widen_map", st)
+    return out
+
+
 def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None, out: torch.Tensor,
                target: torch.Tensor, grad: torch.Tensor, *, stride: int, seed: int, pass_index: int,
                inject: int = 64, prev_scores: torch.Tensor | None = None, out_scores: torch.Tensor | None = None,
@@ -347,10 +359,10 @@ def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None,
     one call (both launches checked before either is enqueued).  ``prev`` may
     be an int16 map (16-bit ids) and come with ``prev_thr`` (each list's 8th
     logit) instead of ``prev_scores``, and the pass may read the sites' probe
-    records ``prev_probe``; ``out`` has 32-bit ids."""
+    records ``prev_probe``; ``out`` has 32-bit ids, or 16-bit ones (an int16
+    map, n <= 65535) for the next step's first pass."""
     n = derived.shape[0]
     _need(derived, "derived", torch.float32, (n, REC))
-    _need(out, "out", torch.int32, (h, w, K))
     maps = _pass_maps(h, w, n, prev, prev_scores, prev_thr, prev_probe, out, out_scores, None, None)
     _need(target, "target", torch.float32, (h, w, 3))
     _need(grad, "grad", torch.float32, (n, REC))
@@ -360,7 +372,7 @@ def step_fused(derived: torch.Tensor, h: int, w: int, prev: torch.Tensor | None,
         _need(image, "image", torch.float32, (h, w, 3))
     tail = (int(stride), int(seed) & 0xFFFFFFFFFFFFFFFF, int(pass_index) & 0xFFFFFFFF, int(inject), _ptr(target),
             _ptr(grad), _ptr(loss), _ptr(image), _stream(derived))
-    if maps.prev_bits == 32 and not (maps.thr_prev or maps.probe_prev):
+    if maps.prev_bits == 32 and maps.next_bits == 32 and not (maps.thr_prev or maps.probe_prev):
         st = _native.lib().sad_step_fused(_ptr(derived), n, h, w, _ptr(prev), _ptr(prev_scores), _ptr(out),
                                           _ptr(out_scores), *tail)
         _native.check("sad_step_fused", st)

@@ -81,6 +81,11 @@ class SadField:
         self.thr = None
         self.probe = None  # [n][4] probe records of the sites (a step's first pass or the Adam step writes them)
         self.probe_valid = False  # whether they are those of the current prepared sites
+        # a training step's last pass hands its lists to the next step at width 16
+        # (when every id fits): then map16 holds the current lists and
+        # maps[cur] is refreshed from it only when a 32-bit map is asked for
+        self.map16 = None
+        self.cur16 = False
         self.cur = 0
         self.pass_index = 0
         self.adam_t = 0
@@ -98,9 +103,15 @@ class SadField:
 
     @property
     def topk(self) -> torch.Tensor:
+        """The current lists as a 32-bit-id map."""
+        if self.cur16:
+            ops.widen_map(self.map16, self.maps[self.cur])
+            self.cur16 = False
         return self.maps[self.cur]
 
     def propagate(self, strides: Sequence[int]) -> None:
+        if strides:
+            self.topk  # noqa: B018 -- the passes below read the 32-bit map
         for s in strides:
             ops.propagate_topk(self.derived, self.h, self.w, self.maps[self.cur], self.maps[1 - self.cur],
                                stride=int(s), seed=self.seed, pass_index=self.pass_index, inject=self.inject,
@@ -135,6 +146,7 @@ class SadField:
         one JFA round (seed, then flood passes B/2, ..., 1, the last one writing
         the top-K map), then n_pass propagation passes on the warm-up schedule."""
         steps = ops.jfa_steps(self.h, self.w)
+        self.cur16 = False  # the lists are rebuilt into maps[cur]
         if not steps:  # a 1x1 image: the seed alone
             self.maps[self.cur].fill_(-1)
             self.maps[self.cur][..., :ops.JFA_K] = ops.jfa_seed(self.derived, self.h, self.w)
@@ -168,8 +180,9 @@ class SadField:
             return
         n = self.params.shape[0]
         probe = None
+        out = self.maps[1 - self.cur]
         if len(strides) < 2:
-            prev, prev_thr = self.maps[self.cur], None
+            prev, prev_thr = self.topk, None
             prev_scores = self.scores[self.cur] if self.scores_valid else None
         else:
             # the passes before the last hand their lists on with only each
@@ -187,8 +200,11 @@ class SadField:
                 self.probe = torch.empty((n, 4), dtype=torch.float32, device=dev)
                 self.probe_valid = False
             probe = self.probe
-            prev, prev_thr = self.maps[self.cur], None
-            prev_scores = self.scores[self.cur] if self.scores_valid else None
+            if self.cur16:  # the previous step's lists (their logits are recomputed)
+                prev, prev_thr, prev_scores = self.map16, None, None
+            else:
+                prev, prev_thr = self.maps[self.cur], None
+                prev_scores = self.scores[self.cur] if self.scores_valid else None
             for k, s in enumerate(strides[:-1]):
                 out, out_thr = self.inter[k % 2], self.thr[k % 2]
                 write = not self.probe_valid
@@ -199,15 +215,27 @@ class SadField:
                 self.probe_valid = True
                 prev, prev_scores, prev_thr = out, None, out_thr
                 self.pass_index += 1
+            if dt == torch.int16:
+                # the last pass writes 16-bit lists for the next step's first pass
+                # (the first pass has read map16 by then)
+                if self.map16 is None:
+                    self.map16 = torch.empty((self.h, self.w, ops.K), dtype=torch.int16, device=dev)
+                out = self.map16
+            else:
+                out = self.maps[1 - self.cur]
         if before_last is not None:
             before_last()
         # The last pass's logits are not kept: a training iteration rewrites the
         # sites next, so the following pass recomputes them anyway.
-        ops.step_fused(self.derived, self.h, self.w, prev, self.maps[1 - self.cur], target, self.grad,
+        ops.step_fused(self.derived, self.h, self.w, prev, out, target, self.grad,
                        stride=int(strides[-1]), seed=self.seed, pass_index=self.pass_index, inject=self.inject,
                        prev_scores=prev_scores, out_scores=None, loss=self.loss, prev_thr=prev_thr,
                        prev_probe=probe)
-        self.cur = 1 - self.cur
+        if out is self.map16:
+            self.cur16 = True
+        else:
+            self.cur = 1 - self.cur
+            self.cur16 = False
         self.pass_index += 1
         self.scores_valid = False
 
