@@ -104,6 +104,11 @@ class SadField:
     @property
     def topk(self) -> torch.Tensor:
         """The current lists as a 32-bit-id map."""
+        return self._map32()
+
+    def _map32(self) -> torch.Tensor:
+        """maps[cur], first widened from map16 when a step's last pass left
+        the current lists there."""
         if self.cur16:
             ops.widen_map(self.map16, self.maps[self.cur])
             self.cur16 = False
@@ -111,7 +116,7 @@ class SadField:
 
     def propagate(self, strides: Sequence[int]) -> None:
         if strides:
-            self.topk  # noqa: B018 -- the passes below read the 32-bit map
+            self._map32()  # the passes below read and write the 32-bit maps
         for s in strides:
             ops.propagate_topk(self.derived, self.h, self.w, self.maps[self.cur], self.maps[1 - self.cur],
                                stride=int(s), seed=self.seed, pass_index=self.pass_index, inject=self.inject,
@@ -182,7 +187,7 @@ class SadField:
         probe = None
         out = self.maps[1 - self.cur]
         if len(strides) < 2:
-            prev, prev_thr = self.topk, None
+            prev, prev_thr = self._map32(), None
             prev_scores = self.scores[self.cur] if self.scores_valid else None
         else:
             # the passes before the last hand their lists on with only each
