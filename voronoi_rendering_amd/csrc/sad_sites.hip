@@ -1,20 +1,16 @@
 // sad_sites.hip -- per-site kernels: site preparation and the Adam step.
 //
-// One thread per site, in workgroups of one wavefront: 50,000 sites make 782
-// workgroups, which reach all 256 CUs (256-thread workgroups, the per-site
-// dispatch shape of the paper's Table B13, made 196 and left a quarter of the
-// CUs idle).  Both kernels are small next to the pixel kernels: they touch
-// 48-byte records of N sites, while a pixel pass touches 32 bytes of every
-// pixel's list.
+// One thread per site, 256-thread workgroups (the per-site dispatch shape of
+// the paper's Table B13).  Both kernels are small next to the pixel kernels:
+// they touch 48-byte records of N sites, while a pixel pass touches 32 bytes
+// of every pixel's list.
 #include "sad_device.h"
 #include "sad_host.h"
 #include "sad_prepare.h"
 
 namespace sad {
 
-constexpr int SITE_THREADS = 64;
-
-__global__ __launch_bounds__(SITE_THREADS) void k_prepare(const float* __restrict__ params, int32_t n,
+__global__ __launch_bounds__(256) void k_prepare(const float* __restrict__ params, int32_t n,
                                                   float* __restrict__ derived) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -39,7 +35,7 @@ __device__ __forceinline__ float adam_one(float p, float g, float& m, float& v, 
     return p - lr * step;
 }
 
-__global__ __launch_bounds__(SITE_THREADS) void k_adam(float* __restrict__ params, float* __restrict__ grad,
+__global__ __launch_bounds__(256) void k_adam(float* __restrict__ params, float* __restrict__ grad,
                                                float* __restrict__ mom1, float* __restrict__ mom2, int32_t n,
                                                AdamArgs a, float* __restrict__ derived,
                                                float4* __restrict__ probe) {
@@ -98,8 +94,7 @@ extern "C" int sad_prepare_sites(const float* params, int32_t n, float* derived,
     if (overlap(params, int64_t(n) * REC * 4, derived, int64_t(n) * REC * 4)) return SAD_EINVAL;
     if (n == 0) return SAD_OK;
     clear_error();
-    hipLaunchKernelGGL(k_prepare, dim3((n + SITE_THREADS - 1) / SITE_THREADS), dim3(SITE_THREADS), 0,
-                       as_stream(stream), params, n, derived);
+    hipLaunchKernelGGL(k_prepare, dim3((n + 255) / 256), dim3(256), 0, as_stream(stream), params, n, derived);
     return launch_status();
 }
 
@@ -128,8 +123,8 @@ extern "C" int sad_adam_step_probe(float* params, float* grad, float* m, float* 
     args.w = (float)w;
     args.h = (float)h;
     clear_error();
-    hipLaunchKernelGGL(k_adam, dim3((n + SITE_THREADS - 1) / SITE_THREADS), dim3(SITE_THREADS), 0, as_stream(stream),
-                       params, grad, m, v, n, args, derived, reinterpret_cast<float4*>(probe));
+    hipLaunchKernelGGL(k_adam, dim3((n + 255) / 256), dim3(256), 0, as_stream(stream), params, grad, m, v, n, args,
+                       derived, reinterpret_cast<float4*>(probe));
     return launch_status();
 }
 
