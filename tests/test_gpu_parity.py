@@ -335,19 +335,23 @@ def test_bench_map_step(sad, ref):
     for _ in range(500):
         f.sites_changed()
         f.step(list(wl.strides), tgt, fused=True)
-    # the step as the bench runs it (16-bit hand-off, thresholds, probe
-    # records, the fused last pass): each pass's lists are the oracle's, so
-    # the last map must be the oracle's chain, and the gradients its backward's
-    f.sites_changed()
-    prev = map_to_np(f.topk)
+    # the step as the bench runs it (the previous step's 16-bit map, thresholds,
+    # probe records current with the sites, the fused last pass writing the
+    # next 16-bit map): each pass's lists are the oracle's, so the last map
+    # must be the oracle's chain, and the gradients its backward's
+    f.sites_changed(probe_records_current=True)
+    assert f.cur16 and f.probe_valid
+    prev = field_lists(f)
     first = f.pass_index
     f.grad.zero_()
     f.loss.zero_()
     f.step(list(wl.strides), tgt, fused=True)
     for k, s in enumerate(wl.strides):
         prev = ref.propagate(d, wl.h, wl.w, prev, s, wl.inject_seed, first + k, wl.inject)
-    got = map_to_np(f.topk)
+    assert f.cur16
+    got = field_lists(f)
     assert np.array_equal(got, prev), f"step: {(got != prev).any(-1).sum()} pixels differ"
+    assert np.array_equal(map_to_np(f.topk), prev)  # widened on request
     g_ref, _, loss_ref, _ = ref.render_bwd(d, wl.h, wl.w, prev, tgt_np)
     assert abs(f.loss.item() - loss_ref) <= 1e-5 * loss_ref
     assert_grad_close(to_np(f.grad), g_ref, "step gradients")
@@ -1150,6 +1154,13 @@ def map16_from_np(m: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(m.astype(np.uint16)).view(np.int16)).to(dev())
 
 
+def field_lists(f) -> np.ndarray:
+    """A field's current lists as 32-bit ids, read without changing its state:
+    from the 16-bit map a step's last pass left (which the next step's first
+    pass then reads, as in training) or from the 32-bit map."""
+    return map16_to_np(f.map16) if f.cur16 else map_to_np(f.maps[f.cur])
+
+
 @pytest.mark.parametrize("h,w,n", [(64, 64, 256), (13, 29, 300), (67, 72, 1000), (37, 70, 65535)])
 def test_propagate_16bit_maps(sad, ref, h, w, n):
     """Passes that read and write 16-bit-id maps (every combination of the two
@@ -1414,6 +1425,41 @@ def test_step_fused_to_16bit_map(sad, ref, c2_state):
     assert np.array_equal(map16_to_np(nxt), m2)
 
 
+@pytest.mark.parametrize("h,w,n", [(1, 1, 3), (13, 29, 300), (67, 72, 1000), (45, 131, 65535)])
+def test_field_steps_16bit_handoff(sad, ref, h, w, n):
+    """A field's fused steps on ragged and degenerate images: the last pass
+    hands its lists to the next step as a 16-bit map, and the next step's
+    first pass reads it with the probe records current (as after an Adam
+    step); two steps, every map and both backwards against the oracle chain
+    from the same warm-up, up to 65,535 sites."""
+    from voronoi_rendering_amd.pipeline import SadField
+
+    p = synth.sites(7100 + n, n, h, w, synth.WIDE_SCALES)
+    d = ref.prepare_sites(p)
+    tgt_np = synth.target_noise_edges(7200 + n, h, w)
+    tgt = to_gpu(tgt_np)
+    f = SadField(to_gpu(p), h, w, 77, inject=64)
+    warm = synth.jfa_strides(h, w, 10)
+    f.warm(10)
+    m = ref.propagate_schedule(d, h, w, None, warm, 77, 0, 64)
+    assert np.array_equal(field_lists(f), m)
+    strides = [8, 4, 2, 1]
+    for step in range(2):
+        first = f.pass_index
+        f.grad.zero_()
+        f.loss.zero_()
+        f.step(strides, tgt, fused=True)
+        f.sites_changed(probe_records_current=True)
+        assert f.cur16 and f.probe_valid
+        m = ref.propagate_schedule(d, h, w, m, strides, 77, first, 64)
+        got = field_lists(f)
+        assert np.array_equal(got, m), f"{h}x{w} step {step}: {(got != m).any(-1).sum()} pixels differ"
+        g_ref, _, loss_ref, _ = ref.render_bwd(d, h, w, m, tgt_np)
+        assert abs(f.loss.item() - loss_ref) <= 1e-5 * max(loss_ref, 1e-30)
+        assert_grad_close(to_np(f.grad), g_ref, f"{h}x{w} step {step} gradients")
+    assert np.array_equal(map_to_np(f.topk), m) and not f.cur16  # widened on request
+
+
 @pytest.mark.parametrize("h,w", [(1, 1), (13, 29), (67, 72), (512, 768)])
 def test_widen_map(sad, h, w):
     """A 16-bit-id map widened to 32-bit ids: every id kept, 0xffff (empty)
@@ -1562,11 +1608,14 @@ def test_training_reanchored(sad, ref):
     lr = np.asarray(f.adam.lr, np.float32)
     for it in range(1, 11):
         p0, m0, v0, d0 = (to_np(x).copy() for x in (f.params, f.m, f.v, f.derived))
-        map0, pi0 = map_to_np(f.topk).copy(), f.pass_index
+        # the lists are read without widening the step's 16-bit map, so every
+        # iteration after the first starts from it, as a fit does
+        map0, pi0 = field_lists(f).copy(), f.pass_index
+        assert (it == 1) or (f.cur16 and f.probe_valid)
         assert np.array_equal(d0.view(np.uint32), ref.prepare_sites(p0).view(np.uint32))
         f.loss.zero_()
         f.step(list(wl.strides), target)
-        map1, g_gpu, loss_gpu = map_to_np(f.topk), to_np(f.grad).copy(), f.loss.item()
+        map1, g_gpu, loss_gpu = field_lists(f), to_np(f.grad).copy(), f.loss.item()
         f.adam_step()
         p1, m1, v1, d1 = (to_np(x) for x in (f.params, f.m, f.v, f.derived))
         # the oracle from the GPU's state before the iteration
