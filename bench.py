@@ -13,8 +13,9 @@ resident in GPU memory when the timed region starts.
 The first pass of each step recomputes the logits of the pixels' previous
 lists (as after an Adam update, which also rewrites the sites' probe
 records, so that every pass culls its probes from them); the following
-passes reuse the logits the previous pass wrote.  The passes before the last hand their lists on with
-16-bit ids (every id of the 50,000 fits), the last pass writes 32-bit ids.
+passes reuse the logits the previous pass wrote.  Every pass hands its lists on
+with 16-bit ids (every id of the 50,000 fits): the last pass writes the 16-bit
+map the next step's first pass reads.
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events in up to 50
 further steps made of the same launches, on the stream the kernels run on

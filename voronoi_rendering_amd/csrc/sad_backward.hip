@@ -615,8 +615,9 @@ struct PassLds {
 // A training iteration's last propagation pass and the backward over its
 // lists in one kernel (Sec. 6.6 / Table 9 one-pass update, then Sec. 4.8 /
 // Appendix B.4).  A workgroup takes one region: each wavefront runs the pass
-// on its tile of the region (propagate_tile: the next lists and logits are
-// written as by sad_propagate_topk), keeps the tile's new lists with their
+// on its tile of the region (propagate_tile: the next lists, with 32-bit or
+// 16-bit ids, and logits are written as by sad_propagate_pass), keeps the
+// tile's new lists with their
 // float32 logits in registers, and after a barrier the region's backward
 // starts from them in the same LDS: no list is read back and no logit of the
 // forward is evaluated again, and regions start their backward while others
